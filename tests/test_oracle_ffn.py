@@ -1,0 +1,295 @@
+"""Pins of the oracle's FFN arithmetic: hand-worked closed forms, a dense
+no-routing equivalence, E=1 against an independent torch float64 chain,
+routing invariances and requantisation properties (CPU only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from oracle import (Geometry, build_plan, combine, expert_rows, forward, forward_tokens, mx_exponent,
+                    requant_fp8_block128, requant_mx, silu, swiglu_clamped)
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def test_silu_anchor_values():
+    for z, v in GOLD["silu"]["points"]:
+        assert abs(silu(np.array([z]))[0] - v) <= 1e-15 * max(1.0, abs(v))
+    z = np.array([-800.0, -50.0, 50.0, 800.0])
+    s = silu(z)
+    assert np.all(np.isfinite(s))
+    assert np.allclose(silu(z) - silu(-z), z, rtol=1e-15, atol=0)  # silu(z) - silu(-z) = z
+
+
+def test_swiglu_clamp_sides():
+    g = np.array([20.0, -20.0, 3.0])
+    u = np.array([-30.0, 30.0, 2.0])
+    h = swiglu_clamped(g, u, 10.0)
+    # gate is clamped above only, up on both sides
+    assert h[0] == silu(np.array([10.0]))[0] * -10.0
+    assert h[1] == silu(np.array([-20.0]))[0] * 10.0
+    assert h[2] == silu(np.array([3.0]))[0] * 2.0
+
+
+def _unit_case(fmt, gate=1.0, up=1.0):
+    H, I, E = 256, 128, 2
+    geo = Geometry(H, I, E, 1, fmt)
+    if fmt == "fp8_block128":
+        one = 0x38  # E4M3 1.0
+        x = np.zeros((1, H), np.uint8)
+        x[0, 0] = one
+        x_sf = np.ones((1, H // 128), np.float32)
+        w13 = np.zeros((E, 2 * I, H), np.uint8)
+        w13_sf = np.ones((E, 2, 2), np.float32)
+        w2 = np.zeros((E, H, I), np.uint8)
+        w2_sf = np.ones((E, 2, 1), np.float32)
+        # E4M3 codes of the gate/up entries (exactly representable values)
+        enc = {1.0: 0x38, 20.0: 0x5A, -30.0: 0xDF}
+        w13[0, 0, 0] = enc[gate]
+        w13[0, I, 0] = enc[up]
+        w2[0, 5, 0] = one
+    elif fmt == "bf16":
+        x = np.zeros((1, H), np.uint16)
+        x[0, 0] = 0x3F80
+        x_sf = w13_sf = w2_sf = None
+        w13 = np.zeros((E, 2 * I, H), np.uint16)
+        w13[0, 0, 0] = w13[0, I, 0] = 0x3F80
+        w2 = np.zeros((E, H, I), np.uint16)
+        w2[0, 5, 0] = 0x3F80
+    else:  # w4a8_mx
+        x = np.zeros((1, H), np.uint8)
+        x[0, 0] = 0x38
+        x_sf = np.full((1, H // 32), 127, np.uint8)
+        w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+        w13[0, 0, 0] = w13[0, I, 0] = 0x02  # E2M1 1.0 in the low nibble = element 0
+        w13_sf = np.full((E, 2 * I, H // 32), 127, np.uint8)
+        w2 = np.zeros((E, H, I // 2), np.uint8)
+        w2[0, 5, 0] = 0x02
+        w2_sf = np.full((E, H, I // 32), 127, np.uint8)
+    ids = np.array([[0]])
+    w = np.array([[1.0]], np.float32)
+    return geo, (x, x_sf, w13, w13_sf, w2, w2_sf), ids, w
+
+
+def test_e4m3_codes_used_by_hand_cases():
+    from oracle import e4m3_decode
+    assert e4m3_decode(np.array([0x38, 0x5A, 0xDF], np.uint8)).tolist() == [1.0, 20.0, -30.0]
+
+
+@pytest.mark.parametrize("key,gate,up", [("unit_path_fp8", 1.0, 1.0), ("clamp_path_fp8", 20.0, -30.0)])
+def test_hand_case_fp8(key, gate, up):
+    gold = GOLD[key]
+    geo, ops, ids, w = _unit_case("fp8_block128", gate, up)
+    res = forward(geo, *ops, topk_idx=ids, topk_weights=w)
+    out = res["out"]
+    assert out[0, 5] == pytest.approx(gold["out_0_5"], rel=1e-15, abs=0)
+    assert np.count_nonzero(out) == 1
+    h = swiglu_clamped(np.array([[gate] + [0.0] * 127]), np.array([[up] + [0.0] * 127]), 10.0)
+    assert h[0, 0] == pytest.approx(gold["h0"], rel=1e-15)
+    _, s = requant_fp8_block128(h)
+    assert s[0, 0] == gold["scale0"]
+
+
+def test_hand_case_bf16():
+    geo, ops, ids, w = _unit_case("bf16")
+    out = forward(geo, *ops, topk_idx=ids, topk_weights=w)["out"]
+    assert out[0, 5] == GOLD["unit_path_bf16"]["out_0_5"]
+    assert np.count_nonzero(out) == 1
+
+
+def test_hand_case_mx():
+    geo, ops, ids, w = _unit_case("w4a8_mx")
+    out = forward(geo, *ops, topk_idx=ids, topk_weights=w)["out"]
+    assert out[0, 5] == GOLD["unit_path_mx"]["out_0_5"]
+    assert np.count_nonzero(out) == 1
+    h = np.zeros((1, 128))
+    h[0, 0] = silu(np.array([1.0]))[0]
+    _, b = requant_mx(h)
+    assert b[0, 0] == GOLD["unit_path_mx"]["scale_byte0"]
+
+
+def test_mx_exponent_brute_force():
+    rng = np.random.default_rng(3)
+    a = np.concatenate([np.exp(rng.uniform(-90, 90, 3000)), 448.0 * 2.0 ** np.arange(-20, 20),
+                        np.nextafter(448.0 * 2.0 ** np.arange(-20, 20), 0), [0.0, 1e-45, 3e38]])
+    got = mx_exponent(a)
+    for v, e in zip(a, got):
+        if v == 0:
+            assert e == -127
+            continue
+        cand = [x for x in range(-127, 128) if 448.0 * 2.0 ** x >= v]
+        assert e == (min(cand) if cand else 127)
+
+
+def test_requant_fp8_idempotent_on_grid():
+    rng = np.random.default_rng(4)
+    grid = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    grid = grid[~np.isnan(grid)]
+    q = rng.choice(grid, size=(5, 256))
+    q[:, 0], q[:, 128] = 448.0, -448.0  # each block's amax is 448 so that s is the block scale exactly
+    s = np.array([2.0 ** -7, 0.75, 3.0, 1.0, 0.125])
+    h = q * s[:, None]
+    hd, sc = requant_fp8_block128(h)
+    assert np.array_equal(hd, h)
+    assert np.array_equal(sc, np.repeat(s[:, None], 2, axis=1))
+
+
+def test_requant_zero_block():
+    h = np.zeros((2, 256))
+    h[1, 130] = 1.0
+    hd, s = requant_fp8_block128(h)
+    assert s[0].tolist() == [1.0, 1.0] and s[1, 0] == 1.0
+    assert hd[1, 130] == pytest.approx(1.0, rel=2 ** -4)
+    hd2, b = requant_mx(h)
+    assert b[0, 0] == 0 and np.all(hd2[0] == 0)
+
+
+def _small_inputs(fmt, T=24, H=256, I=128, E=4, k=2, seed=7, x_scale=1.0):
+    routing = "from_logits" if fmt == "w4a8_mx" else "precomputed"
+    sh = moe_synth.MoEShape("t", seed, T, H, I, E, k, fmt, routing, x_scale=x_scale)
+    return sh, moe_synth.make_inputs(sh)
+
+
+def _ops(inp):
+    return inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"]
+
+
+@pytest.mark.parametrize("fmt", ["fp8_block128", "bf16", "w4a8_mx"])
+def test_dense_equivalence_topk_equals_E(fmt):
+    sh, inp = _small_inputs(fmt, E=3, k=3)
+    geo = Geometry(sh.hidden, sh.inter, sh.experts, sh.topk, fmt)
+    T = sh.tokens
+    ids = np.tile(np.arange(3), (T, 1))
+    w = np.full((T, 3), 1.0 / 3)
+    res = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w)
+    # no routing code: every expert over every token, averaged
+    from oracle import dequant_activations, dequant_expert
+    xd = dequant_activations(geo, inp["x"], inp["x_sf"])
+    dense = np.zeros((T, sh.hidden))
+    for e in range(3):
+        w13d, w2d = dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e)
+        dense += expert_rows(geo, xd, w13d, w2d) / 3
+    assert np.allclose(res["out"], dense, rtol=1e-12, atol=1e-12 * np.abs(dense).max())
+
+
+# ---- independent torch float64 chain for E = 1, k = 1 (the textbook dense FFN)
+_E2M1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0],
+                     dtype=torch.float64)
+
+
+def _torch_deq(fmt, codes, scales, br=1, bc=128, fp4=False):
+    c = torch.from_numpy(np.ascontiguousarray(codes))
+    if fmt == "bf16":
+        return c.view(torch.bfloat16).to(torch.float64)
+    if fmt == "fp8_block128":
+        v = c.view(torch.float8_e4m3fn).to(torch.float64)
+        s = torch.from_numpy(scales).to(torch.float64)
+        return v * s.repeat_interleave(br, 0).repeat_interleave(bc, 1)
+    if fp4:
+        v = torch.stack([_E2M1[(c & 15).long()], _E2M1[(c >> 4).long()]], dim=-1).reshape(c.shape[0], -1)
+    else:
+        v = c.view(torch.float8_e4m3fn).to(torch.float64)
+    s = torch.from_numpy(scales).view(torch.float8_e8m0fnu).to(torch.float64)
+    return v * s.repeat_interleave(32, 1)
+
+
+def _torch_requant(fmt, h):
+    if fmt == "bf16":
+        return h.to(torch.bfloat16).to(torch.float64)
+    R, C = h.shape
+    if fmt == "fp8_block128":
+        hb = h.reshape(R, C // 128, 128)
+        a = hb.abs().amax(-1, keepdim=True)
+        s = (a / 448).to(torch.float32).to(torch.float64)
+        s = torch.where(a == 0, torch.ones_like(s), s)
+    else:
+        hb = h.reshape(R, C // 32, 32)
+        a = hb.abs().amax(-1, keepdim=True)
+        e = torch.ceil(torch.log2(a / 448)).clamp(-127, 127)
+        e = torch.where(448 * torch.exp2(e - 1) >= a, e - 1, e)  # guard log2 rounding up
+        e = torch.where(448 * torch.exp2(e) < a, e + 1, e)  # guard log2 rounding down
+        s = torch.where(a == 0, torch.full_like(a, 2.0 ** -127), torch.exp2(e))
+    q = (hb / s).clamp(-448, 448).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64)
+    return (q * s).reshape(R, C)
+
+
+@pytest.mark.parametrize("fmt,x_scale", [("fp8_block128", 1.0), ("fp8_block128", 20.0), ("bf16", 1.0),
+                                         ("bf16", 20.0), ("w4a8_mx", 1.0)])
+def test_single_expert_matches_torch_chain(fmt, x_scale):
+    sh, inp = _small_inputs(fmt, T=16, E=1, k=1, x_scale=x_scale, H=256, I=256)
+    geo = Geometry(sh.hidden, sh.inter, 1, 1, fmt)
+    ids = np.zeros((sh.tokens, 1), np.int64)
+    w = np.ones((sh.tokens, 1), np.float32)
+    out = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w)["out"]
+    H, I = sh.hidden, sh.inter
+    if fmt == "w4a8_mx":
+        x = _torch_deq(fmt, inp["x"], inp["x_sf"])
+        w13 = _torch_deq(fmt, inp["w13"][0], inp["w13_sf"][0], fp4=True)
+        w2 = _torch_deq(fmt, inp["w2"][0], inp["w2_sf"][0], fp4=True)
+    else:
+        x = _torch_deq(fmt, inp["x"], inp["x_sf"], 1, 128)
+        w13 = _torch_deq(fmt, inp["w13"][0], None if inp["w13_sf"] is None else inp["w13_sf"][0], 128, 128)
+        w2 = _torch_deq(fmt, inp["w2"][0], None if inp["w2_sf"] is None else inp["w2_sf"][0], 128, 128)
+    g = x @ w13[:I].T
+    u = x @ w13[I:].T
+    if x_scale > 1:
+        assert (g > 10).any() and (u.abs() > 10).any()  # the clamp fires
+    h = torch.nn.functional.silu(torch.clamp(g, max=10.0)) * torch.clamp(u, -10.0, 10.0)
+    ref = (_torch_requant(fmt, h) @ w2.T).numpy()
+    err = np.abs(out - ref).max() / np.abs(ref).max()
+    assert err < 1e-9, err
+
+
+def test_invariances():
+    sh, inp = _small_inputs("fp8_block128", T=20, E=5, k=3, seed=9)
+    geo = Geometry(sh.hidden, sh.inter, sh.experts, sh.topk, sh.fmt)
+    ops = _ops(inp)
+    ids, w = inp["topk_idx"].copy(), inp["topk_weights"].astype(np.float64)
+    ids[2, 1] = -1  # a masked slot
+    base = forward(geo, *ops, topk_idx=ids, topk_weights=w)["out"]
+    # token permutation permutes rows exactly
+    perm = np.random.default_rng(0).permutation(sh.tokens)
+    xs = (ops[0][perm], ops[1][perm]) + ops[2:]
+    o = forward(geo, *xs, topk_idx=ids[perm], topk_weights=w[perm])["out"]
+    assert np.allclose(o, base[perm], rtol=1e-12, atol=1e-12)  # BLAS blocking may reorder sums
+    # slot permutation: same sum up to float order
+    sp = [2, 0, 1]
+    o = forward(geo, *ops, topk_idx=ids[:, sp], topk_weights=w[:, sp])["out"]
+    assert np.allclose(o, base, rtol=1e-13, atol=1e-13)
+    # relabelling experts together with their weights leaves the output unchanged
+    rl = np.array([3, 0, 4, 1, 2])  # expert e -> rl[e]
+    inv = np.argsort(rl)
+    w13, w13s, w2, w2s = ops[2][inv], ops[3][inv], ops[4][inv], ops[5][inv]
+    ids2 = np.where(ids >= 0, rl[np.maximum(ids, 0)], -1)
+    o = forward(geo, ops[0], ops[1], w13, w13s, w2, w2s, topk_idx=ids2, topk_weights=w)["out"]
+    assert np.array_equal(o, base)
+    # linear in the router weights (x2 is exact)
+    o = forward(geo, *ops, topk_idx=ids, topk_weights=2 * w)["out"]
+    assert np.array_equal(o, 2 * base)
+    # duplicate tokens give identical rows
+    xs = (ops[0][[4, 4]], ops[1][[4, 4]]) + ops[2:]
+    o = forward(geo, *xs, topk_idx=ids[[4, 4]], topk_weights=w[[4, 4]])["out"]
+    assert np.array_equal(o[0], o[1]) and np.allclose(o[0], base[4], rtol=1e-12, atol=1e-12)
+
+
+def test_forward_tokens_matches_forward():
+    for fmt in ("fp8_block128", "bf16", "w4a8_mx"):
+        sh, inp = _small_inputs(fmt, T=12, E=4, k=2, seed=12)
+        geo = Geometry(sh.hidden, sh.inter, sh.experts, sh.topk, fmt)
+        res = forward(geo, *_ops(inp), topk_idx=inp.get("topk_idx"), topk_weights=inp.get("topk_weights"),
+                      logits=inp["logits"])
+        toks = [0, 5, 11, 3]
+        part = forward_tokens(geo, toks, *_ops(inp), res["topk_idx"], res["topk_weights"])
+        assert np.allclose(part, res["out"][toks], rtol=1e-12, atol=1e-12)
+
+
+def test_combine_masked_token_is_zero():
+    y = np.arange(12.0).reshape(3, 4)
+    pr = np.array([0, -1, -1, -1, 2, 1])
+    out = combine(y, np.array([[0.5, 9.0], [1.0, 1.0], [0.25, 2.0]]), pr, 4)
+    assert out[1].tolist() == [0, 0, 0, 0]
+    assert np.allclose(out[0], 0.5 * y[0])
+    assert np.allclose(out[2], 0.25 * y[2] + 2.0 * y[1])
