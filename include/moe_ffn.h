@@ -1,0 +1,175 @@
+/*
+ * moe_ffn.h — C ABI of the routed MoE expert-FFN library for MI355X (gfx950).
+ *
+ * One GPU's share of experts, end to end:
+ *   top-k routing -> per-expert permutation (expert_start_indices, src_info)
+ *   -> gate/up grouped GEMM with clamped SwiGLU and intermediate requantisation
+ *   -> down grouped GEMM -> router-weighted combine back into token order.
+ *
+ * Sources (API documentation pages; cited by page title and parameter):
+ *   [SymmBuffer]  flashinfer.megamoe.MegaMoESymmBuffer — geometry (hidden,
+ *                 intermediate_hidden, num_experts, num_topk,
+ *                 num_max_tokens_per_rank, activation_clamp, fast_math) and the
+ *                 staging views x / x_sf / topk_idx / topk_weights.
+ *   [MegaFFN]     Struct_mega_ffn_ep_combine_send (MAX mega_ffn) — the fused FFN's
+ *                 operands: gate_up_weight, down_weight and their scale tiles,
+ *                 expert_start_indices, expert_ids, num_active_experts, src_info,
+ *                 estimated_total_m (tile-regime gate), clamp_activation.
+ *   [ActPack]     flashinfer.fused_moe.MoEActivationPack — operand encodings
+ *                 (DeepSeek FP8, MXFP8, MXFP4 x MXFP8, BF16) and routing input
+ *                 modes (precomputed ids/weights, FromLogits).
+ *   [EPCombine]   DistributedEPCombine (MAX ep) — router_weights scale each
+ *                 expert's contribution in the combine.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer; the library keeps only its immutable host-side handle.
+ *   - Calls are asynchronous on the given hipStream_t, never allocate device
+ *     memory, never synchronise and never read device data on the host, so a
+ *     sequence of calls can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed validation launches nothing and returns a status != MOE_OK.
+ *   - Data errors found on the device (an expert id outside [0, E) that is not
+ *     -1) never trap: that slot is treated as masked and counted in
+ *     plan->status[0].
+ *   - T = 0 tokens is a valid no-op.
+ *   - Bytes of every tensor are row-major with the last dimension contiguous.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FFN_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* bad geometry, null pointer, T out of range */
+  MOE_ERR_UNSUPPORTED = 2,        /* a valid but unsupported combination (raised, never degraded) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a launch failed; see hipGetLastError() */
+} moe_status;
+
+/* Operand encodings ([ActPack] encodings list). */
+typedef enum {
+  /* "DeepSeek FP8": x E4M3 [T,H] + fp32 scales [T,H/128] (token-major, as the
+     [SymmBuffer] x_sf view); w13 E4M3 [E,2I,H] + fp32 [E,2I/128,H/128];
+     w2 E4M3 [E,H,I] + fp32 [E,H/128,I/128].  H and I multiples of 128. */
+  MOE_FMT_FP8_BLOCK128 = 0,
+  /* "BF16": x [T,H], w13 [E,2I,H], w2 [E,H,I] bf16, no scales.  H, I multiples of 128. */
+  MOE_FMT_BF16 = 1,
+  /* "MXFP4 x MXFP8 (W4A8)": x E4M3 [T,H] + UE8M0 bytes [T,H/32] (token-major);
+     w13 packed E2M1 [E,2I,H/2] + UE8M0 [E,2I,H/32]; w2 packed E2M1 [E,H,I/2]
+     + UE8M0 [E,H,I/32].  Element 2i is the low nibble of byte i.
+     H and I multiples of 32. */
+  MOE_FMT_W4A8_MX = 2
+} moe_format;
+
+/* Routing input modes ([ActPack] routing_input_mode). */
+typedef enum {
+  MOE_ROUTE_PRECOMPUTED = 0,   /* caller passes topk_idx + topk_weights */
+  MOE_ROUTE_FROM_LOGITS = 1    /* caller passes routing_logits [T,E] fp32; the
+                                  library selects top-k (ties -> lower expert id)
+                                  and writes ids + softmax-over-k weights */
+} moe_route_mode;
+
+/* GEMM tile regime ([MegaFFN] estimated_total_m gates the tile regime).
+   AUTO picks from the mean rows per expert T*k/E known on the host. */
+typedef enum { MOE_TILES_AUTO = 0, MOE_TILES_DECODE = 1, MOE_TILES_PREFILL = 2 } moe_tile_regime;
+
+/* (host) Problem statement, copied by moe_create ([SymmBuffer] constructor). */
+typedef struct moe_config {
+  int32_t hidden;               /* H */
+  int32_t intermediate_hidden;  /* I */
+  int32_t num_experts;          /* E: experts resident on this GPU ([MegaFFN]: local count) */
+  int32_t num_topk;             /* k, 1 <= k <= E, k <= 32 */
+  int32_t max_num_tokens;       /* capacity, like num_max_tokens_per_rank */
+  float activation_clamp;       /* SwiGLU clamp c > 0 (default 10.0); +inf disables */
+  int32_t format;               /* moe_format */
+  int32_t route_mode;           /* moe_route_mode */
+  int32_t topk_idx_bits;        /* 64 (INT64 ids, [SymmBuffer]) or 32 (int32 ids, [ActPack]) */
+  int32_t fast_math;            /* 1: hardware exp/reciprocal in SiLU and softmax ([SymmBuffer]) */
+  int32_t tile_regime;          /* moe_tile_regime */
+} moe_config;
+
+/* (host struct of device pointers) Expert weights of this GPU, as given. */
+typedef struct moe_weights {
+  const void* w13;     /* gate_up_weight: rows [0,I) gate, rows [I,2I) up */
+  const void* w13_sf;  /* its scales (NULL for BF16) */
+  const void* w2;      /* down_weight */
+  const void* w2_sf;   /* its scales (NULL for BF16) */
+} moe_weights;
+
+/* (host struct of device pointers) Routing plan, int32 each ([MegaFFN] Args). */
+typedef struct moe_plan_buffers {
+  int32_t* expert_counts;         /* [E]   valid pairs per expert */
+  int32_t* expert_start_indices;  /* [E+1] exclusive prefix sum of the counts */
+  int32_t* expert_ids;            /* [E]   active experts ascending, then -1 */
+  int32_t* num_active_experts;    /* [1] */
+  int32_t* src_info;              /* [T*k] row -> pair p = t*k + j (rows of an expert keep p order) */
+  int32_t* pair_row;              /* [T*k] pair -> row, -1 for a masked slot */
+  int32_t* status;                /* [1]   count of ids outside [0,E) other than -1 */
+} moe_plan_buffers;
+
+typedef struct moe_handle moe_handle;
+
+/* Validate *cfg and create a host handle.  Returns MOE_ERR_INVALID_ARGUMENT for
+   bad geometry (see moe_format for the divisibility rules), k > E, k > 32,
+   E > 1024, clamp <= 0 or NaN, an unknown enum; MOE_ERR_UNSUPPORTED for
+   FROM_LOGITS with E > 512. */
+moe_status moe_create(const moe_config* cfg /* host */, moe_handle** out /* host */);
+void moe_destroy(moe_handle* h);
+
+/* Bytes of workspace moe_plan / moe_ffn / moe_forward need for num_tokens tokens
+   (0 if num_tokens is out of range).  The workspace is caller-owned device memory,
+   256-byte aligned; one workspace per concurrently running stream. */
+size_t moe_workspace_size(const moe_handle* h, int32_t num_tokens);
+
+/* Routing plan ([MegaFFN] expert_start_indices, expert_ids, num_active_experts,
+   src_info; [ActPack] routing modes).
+   PRECOMPUTED: topk_idx_in [T,k] int64/int32 ids (-1 = masked slot).
+   FROM_LOGITS: routing_logits [T,E] fp32 in; topk_idx_out [T,k] (dtype per
+   topk_idx_bits) and topk_weights_out [T,k] fp32 out.
+   Writes every buffer of *plan. */
+moe_status moe_plan(const moe_handle* h, int32_t num_tokens, const void* topk_idx_in,
+                    const float* routing_logits, void* topk_idx_out, float* topk_weights_out,
+                    const moe_plan_buffers* plan /* host struct */, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Expert FFN over the plan's rows ([MegaFFN]: gate/up GEMM -> clamped SwiGLU ->
+   intermediate requantisation -> down GEMM).  x, x_sf per the format; y [T,k,H]
+   bf16 receives each row's result at its pair slot p = src_info[row]; slots of
+   masked pairs are left untouched. */
+moe_status moe_ffn(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
+                   const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
+                   void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Router-weighted combine ([EPCombine] router_weights): out[t] = sum over valid
+   slots j in ascending order of topk_weights[t,j] * y[t,j,:], accumulated in
+   fp32, written as bf16 [T,H].  A token with no valid slot gets zeros. */
+moe_status moe_combine(const moe_handle* h, int32_t num_tokens, const void* y, const float* topk_weights,
+                       const moe_plan_buffers* plan /* host struct */, void* out, hipStream_t stream);
+
+/* The whole path in one call: plan (into ws), FFN (y in ws), combine into out
+   [T,H] bf16.  PRECOMPUTED: topk_idx / topk_weights are inputs and are not
+   modified.  FROM_LOGITS: routing_logits is the input and topk_idx / topk_weights
+   receive the routing result. */
+moe_status moe_forward(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
+                       void* topk_idx, float* topk_weights, const float* routing_logits,
+                       const moe_weights* w /* host struct */, void* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+const char* moe_status_string(moe_status s);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

@@ -1,0 +1,200 @@
+"""Python binding of libmoe_ffn.so — the routed MoE expert-FFN library for MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory and the HIP stream; the binding passes
+``tensor.data_ptr()`` and sizes through ctypes to the C ABI of
+``include/moe_ffn.h`` (same entry-point names).
+
+The library must have been built (``python -m mixture_experts_ffn_topk_amd.build``
+or ``__graft_entry__.build()``); if it is missing, loading fails loudly — there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
+
+# ------------------------------------------------------------------ enums (include/moe_ffn.h)
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+                3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+FORMATS = {"fp8_block128": 0, "bf16": 1, "w4a8_mx": 2}
+ROUTE_MODES = {"precomputed": 0, "from_logits": 1}
+TILE_REGIMES = {"auto": 0, "decode": 1, "prefill": 2}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("intermediate_hidden", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("num_topk", ctypes.c_int32),
+                ("max_num_tokens", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
+                ("format", ctypes.c_int32), ("route_mode", ctypes.c_int32),
+                ("topk_idx_bits", ctypes.c_int32), ("fast_math", ctypes.c_int32),
+                ("tile_regime", ctypes.c_int32)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_sf", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("expert_counts", "expert_start_indices", "expert_ids",
+                                               "num_active_experts", "src_info", "pair_row", "status")]
+
+
+PLAN_FIELDS = [f for f, _ in _Plan._fields_]
+EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_plan", "moe_ffn", "moe_combine",
+            "moe_forward", "moe_status_string", "moe_abi_version"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe_ffn.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_ffn_topk_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.moe_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(vp)]
+    lib.moe_create.restype = i32
+    lib.moe_destroy.argtypes = [vp]
+    lib.moe_destroy.restype = None
+    lib.moe_workspace_size.argtypes = [vp, i32]
+    lib.moe_workspace_size.restype = sz
+    lib.moe_plan.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.POINTER(_Plan), vp, sz, vp]
+    lib.moe_plan.restype = i32
+    lib.moe_ffn.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp, sz, vp]
+    lib.moe_ffn.restype = i32
+    lib.moe_combine.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Plan), vp, vp]
+    lib.moe_combine.restype = i32
+    lib.moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, sz, vp]
+    lib.moe_forward.restype = i32
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_abi_version.argtypes = []
+    lib.moe_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(st: int, what: str):
+    if st != MOE_OK:
+        raise MoEError(st, what)
+
+
+class MoEFFN:
+    """One GPU's share of experts with a fixed geometry (moe_create / moe_destroy).
+
+    Tensors are torch tensors on the GPU (or raw device addresses as ints); their
+    dtype and layout must match include/moe_ffn.h — the binding only forwards
+    pointers."""
+
+    def __init__(self, hidden: int, intermediate_hidden: int, num_experts: int, num_topk: int,
+                 max_num_tokens: int, fmt: str = "fp8_block128", route_mode: str = "precomputed",
+                 activation_clamp: float = 10.0, topk_idx_bits: int = 64, fast_math: bool = True,
+                 tile_regime: str = "auto"):
+        self.lib = load_library()
+        self.cfg = _Config(hidden, intermediate_hidden, num_experts, num_topk, max_num_tokens,
+                           float(activation_clamp), FORMATS[fmt], ROUTE_MODES[route_mode], topk_idx_bits,
+                           int(bool(fast_math)), TILE_REGIMES[tile_regime])
+        self.fmt, self.route_mode = fmt, route_mode
+        self.hidden, self.inter, self.experts, self.topk = hidden, intermediate_hidden, num_experts, num_topk
+        self.max_num_tokens = max_num_tokens
+        self.topk_idx_bits = topk_idx_bits
+        h = ctypes.c_void_p()
+        _check(self.lib.moe_create(ctypes.byref(self.cfg), ctypes.byref(h)), "moe_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self.lib.moe_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---------------------------------------------------------------- helpers (torch allocation)
+    def workspace_size(self, num_tokens: int) -> int:
+        return int(self.lib.moe_workspace_size(self._h, num_tokens))
+
+    def alloc_workspace(self, num_tokens: int, device="cuda"):
+        import torch
+        return torch.empty(max(1, self.workspace_size(num_tokens)), dtype=torch.uint8, device=device)
+
+    def alloc_plan(self, num_tokens: int, device="cuda") -> dict:
+        import torch
+        E, np_ = self.experts, max(1, num_tokens * self.topk)
+        sizes = {"expert_counts": E, "expert_start_indices": E + 1, "expert_ids": E, "num_active_experts": 1,
+                 "src_info": np_, "pair_row": np_, "status": 1}
+        return {k: torch.empty(v, dtype=torch.int32, device=device) for k, v in sizes.items()}
+
+    @staticmethod
+    def _plan_struct(plan: dict) -> _Plan:
+        return _Plan(*[_ptr(plan[f]) for f in PLAN_FIELDS])
+
+    @staticmethod
+    def _weights_struct(w: dict) -> _Weights:
+        return _Weights(_ptr(w["w13"]), _ptr(w.get("w13_sf")), _ptr(w["w2"]), _ptr(w.get("w2_sf")))
+
+    @staticmethod
+    def _nbytes(t) -> int:
+        return 0 if t is None else (t.numel() * t.element_size())
+
+    # ---------------------------------------------------------------- entry points
+    def plan(self, num_tokens, plan: dict, topk_idx=None, routing_logits=None, topk_idx_out=None,
+             topk_weights_out=None, ws=None, stream=None):
+        ps = self._plan_struct(plan)
+        _check(self.lib.moe_plan(self._h, num_tokens, _ptr(topk_idx), _ptr(routing_logits), _ptr(topk_idx_out),
+                                 _ptr(topk_weights_out), ctypes.byref(ps), _ptr(ws), self._nbytes(ws),
+                                 _stream(stream)), "moe_plan")
+
+    def ffn(self, num_tokens, x, x_sf, weights: dict, plan: dict, y, ws, stream=None):
+        ws_ = self._weights_struct(weights)
+        ps = self._plan_struct(plan)
+        _check(self.lib.moe_ffn(self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps),
+                                _ptr(y), _ptr(ws), self._nbytes(ws), _stream(stream)), "moe_ffn")
+
+    def combine(self, num_tokens, y, topk_weights, plan: dict, out, stream=None):
+        ps = self._plan_struct(plan)
+        _check(self.lib.moe_combine(self._h, num_tokens, _ptr(y), _ptr(topk_weights), ctypes.byref(ps), _ptr(out),
+                                    _stream(stream)), "moe_combine")
+
+    def forward(self, num_tokens, x, x_sf, topk_idx, topk_weights, routing_logits, weights: dict, out, ws,
+                stream=None):
+        ws_ = self._weights_struct(weights)
+        _check(self.lib.moe_forward(self._h, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
+                                    _ptr(routing_logits), ctypes.byref(ws_), _ptr(out), _ptr(ws), self._nbytes(ws),
+                                    _stream(stream)), "moe_forward")
+
+
+__all__ = ["MoEFFN", "MoEError", "load_library", "LIB_PATH", "EXPORTED", "FORMATS", "ROUTE_MODES", "TILE_REGIMES"]

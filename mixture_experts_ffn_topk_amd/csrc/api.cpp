@@ -1,0 +1,241 @@
+// Host runtime behind the C ABI declared in include/moe_ffn.h: argument
+// validation, tile-regime choice, workspace carving and launch sequencing.
+// Nothing here allocates device memory, synchronises, or reads device data.
+#include "moe_ffn.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "launch.h"
+
+struct moe_handle {
+  moe_config cfg;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  // moe_forward: [plan buffers][y][union(plan scratch, h + h_sf)]
+  size_t counts, start, ids, nact, status, src, prow, plan_end;
+  size_t y, y_end;
+  size_t scratch;  // plan scratch or h, h_sf
+  size_t h_off, hsf_off, ffn_bytes, plan_scratch_bytes, total;
+};
+
+moe::Fmt to_fmt(int f) { return f == MOE_FMT_FP8_BLOCK128 ? moe::Fmt::FP8 : (f == MOE_FMT_BF16 ? moe::Fmt::BF16 : moe::Fmt::MX); }
+
+Layout layout_for(const moe_config& c, int T) {
+  Layout L{};
+  const size_t E = (size_t)c.num_experts, np = (size_t)T * c.num_topk;
+  size_t o = 0;
+  L.counts = o; o = align_up(o + E * 4);
+  L.start = o; o = align_up(o + (E + 1) * 4);
+  L.ids = o; o = align_up(o + E * 4);
+  L.nact = o; o = align_up(o + 4);
+  L.status = o; o = align_up(o + 4);
+  L.src = o; o = align_up(o + np * 4);
+  L.prow = o; o = align_up(o + np * 4);
+  L.plan_end = o;
+  L.y = o; o = align_up(o + np * (size_t)c.hidden * 2);
+  L.y_end = o;
+  L.scratch = o;
+  const moe::Fmt f = to_fmt(c.format);
+  L.h_off = 0;
+  L.hsf_off = align_up(moe::ffn_h_bytes(f, (int)np, c.intermediate_hidden));
+  L.ffn_bytes = align_up(L.hsf_off + moe::ffn_hsf_bytes(f, (int)np, c.intermediate_hidden));
+  L.plan_scratch_bytes = align_up(moe::plan_workspace_bytes((int)np, c.num_experts));
+  L.total = L.scratch + (L.ffn_bytes > L.plan_scratch_bytes ? L.ffn_bytes : L.plan_scratch_bytes);
+  return L;
+}
+
+bool valid_T(const moe_handle* h, int32_t T) { return h && T >= 0 && T <= h->cfg.max_num_tokens; }
+
+moe::PlanPtrs plan_ptrs(const moe_plan_buffers* p) {
+  return moe::PlanPtrs{p->expert_counts, p->expert_start_indices, p->expert_ids, p->num_active_experts,
+                       p->src_info,      p->pair_row,             p->status};
+}
+
+bool plan_complete(const moe_plan_buffers* p) {
+  return p && p->expert_counts && p->expert_start_indices && p->expert_ids && p->num_active_experts && p->src_info &&
+         p->pair_row && p->status;
+}
+
+int choose_bm(const moe_config& c, int T) {
+  if (c.tile_regime == MOE_TILES_DECODE) return 64;
+  if (c.tile_regime == MOE_TILES_PREFILL) return 128;
+  // Regime gate on the host-known mean rows per expert (the pages' estimated_total_m).
+  const long long mean = ((long long)T * c.num_topk + c.num_experts - 1) / c.num_experts;
+  return mean <= 96 ? 64 : 128;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const float* logits, void* idx_out,
+                   float* w_out, const moe_plan_buffers* plan, void* scratch, hipStream_t s) {
+  const moe_config& c = h->cfg;
+  const bool idx64 = c.topk_idx_bits == 64;
+  const void* ids = idx_in;
+  if (c.route_mode == MOE_ROUTE_FROM_LOGITS) {
+    hipError_t e = moe::launch_route_logits_topk(logits, T, c.num_experts, c.num_topk, idx_out, idx64, w_out,
+                                                 c.fast_math != 0, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    ids = idx_out;
+  }
+  return hip_status(moe::launch_plan(ids, idx64, T * c.num_topk, c.num_experts, plan_ptrs(plan), (int*)scratch, s));
+}
+
+moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
+                  const moe_plan_buffers* plan, void* y, void* ffn_ws, hipStream_t s) {
+  const moe_config& c = h->cfg;
+  const Layout L = layout_for(c, T);
+  moe::FfnArgs a{};
+  a.fmt = to_fmt(c.format);
+  a.T = T;
+  a.E = c.num_experts;
+  a.topk = c.num_topk;
+  a.H = c.hidden;
+  a.I = c.intermediate_hidden;
+  a.clamp = c.activation_clamp;
+  a.fast = c.fast_math != 0;
+  a.bm = choose_bm(c, T);
+  a.start = plan->expert_start_indices;
+  a.src_info = plan->src_info;
+  a.x = x;
+  a.x_sf = x_sf;
+  a.w13 = w->w13;
+  a.w13_sf = w->w13_sf;
+  a.w2 = w->w2;
+  a.w2_sf = w->w2_sf;
+  a.h = (char*)ffn_ws + L.h_off;
+  a.h_sf = (char*)ffn_ws + L.hsf_off;
+  a.y = y;
+  return hip_status(moe::launch_ffn(a, s));
+}
+
+bool weights_ok(const moe_config& c, const moe_weights* w) {
+  if (!w || !w->w13 || !w->w2) return false;
+  if (c.format != MOE_FMT_BF16 && (!w->w13_sf || !w->w2_sf)) return false;
+  return true;
+}
+
+bool x_ok(const moe_config& c, const void* x, const void* x_sf) {
+  return x && (c.format == MOE_FMT_BF16 || x_sf);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported combination";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+moe_status moe_create(const moe_config* cfg, moe_handle** out) {
+  if (!cfg || !out) return MOE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const moe_config& c = *cfg;
+  if (c.hidden <= 0 || c.intermediate_hidden <= 0 || c.num_experts <= 0 || c.num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.num_topk <= 0 || c.num_topk > c.num_experts || c.num_topk > 32) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.max_num_tokens < 0 || (long long)c.max_num_tokens * c.num_topk > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(c.activation_clamp > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;  // also rejects NaN
+  if (c.topk_idx_bits != 32 && c.topk_idx_bits != 64) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.route_mode != MOE_ROUTE_PRECOMPUTED && c.route_mode != MOE_ROUTE_FROM_LOGITS) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.tile_regime < MOE_TILES_AUTO || c.tile_regime > MOE_TILES_PREFILL) return MOE_ERR_INVALID_ARGUMENT;
+  switch (c.format) {
+    case MOE_FMT_FP8_BLOCK128:
+      if (c.hidden % 128 || c.intermediate_hidden % 128) return MOE_ERR_INVALID_ARGUMENT;
+      break;
+    case MOE_FMT_BF16:
+      if (c.hidden % 64 || c.intermediate_hidden % 64) return MOE_ERR_INVALID_ARGUMENT;
+      break;
+    case MOE_FMT_W4A8_MX:
+      if (c.hidden % 32 || c.intermediate_hidden % 32) return MOE_ERR_INVALID_ARGUMENT;
+      break;
+    default:
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if (c.route_mode == MOE_ROUTE_FROM_LOGITS && c.num_experts > 512) return MOE_ERR_UNSUPPORTED;
+  moe_handle* h = new (std::nothrow) moe_handle;
+  if (!h) return MOE_ERR_INVALID_ARGUMENT;
+  h->cfg = c;
+  *out = h;
+  return MOE_OK;
+}
+
+void moe_destroy(moe_handle* h) { delete h; }
+
+size_t moe_workspace_size(const moe_handle* h, int32_t T) {
+  if (!valid_T(h, T)) return 0;
+  return layout_for(h->cfg, T).total;
+}
+
+moe_status moe_plan(const moe_handle* h, int32_t T, const void* topk_idx_in, const float* routing_logits,
+                    void* topk_idx_out, float* topk_weights_out, const moe_plan_buffers* plan, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (!valid_T(h, T) || !plan_complete(plan)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = h->cfg;
+  if (c.route_mode == MOE_ROUTE_PRECOMPUTED) {
+    if (T > 0 && !topk_idx_in) return MOE_ERR_INVALID_ARGUMENT;
+  } else if (T > 0 && (!routing_logits || !topk_idx_out || !topk_weights_out)) {
+    return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const size_t need = layout_for(c, T).plan_scratch_bytes;
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return do_plan(h, T, topk_idx_in, routing_logits, topk_idx_out, topk_weights_out, plan, ws, stream);
+}
+
+moe_status moe_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
+                   const moe_plan_buffers* plan, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !y)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = layout_for(h->cfg, T).ffn_bytes;
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (T == 0) return MOE_OK;
+  return do_ffn(h, T, x, x_sf, w, plan, y, ws, stream);
+}
+
+moe_status moe_combine(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
+                       const moe_plan_buffers* plan, void* out, hipStream_t stream) {
+  if (!valid_T(h, T) || !plan || !plan->pair_row) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!y || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_combine(y, topk_weights, plan->pair_row, T, h->cfg.num_topk, h->cfg.hidden, out,
+                                        stream));
+}
+
+moe_status moe_forward(const moe_handle* h, int32_t T, const void* x, const void* x_sf, void* topk_idx,
+                       float* topk_weights, const float* routing_logits, const moe_weights* w, void* out, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  if (!valid_T(h, T) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = h->cfg;
+  if (T > 0) {
+    if (!x_ok(c, x, x_sf) || !out || !topk_idx || !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.route_mode == MOE_ROUTE_FROM_LOGITS && !routing_logits) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const Layout L = layout_for(c, T);
+  if (ws_bytes < L.total || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  char* base = (char*)ws;
+  moe_plan_buffers plan{(int32_t*)(base + L.counts), (int32_t*)(base + L.start), (int32_t*)(base + L.ids),
+                        (int32_t*)(base + L.nact),   (int32_t*)(base + L.src),   (int32_t*)(base + L.prow),
+                        (int32_t*)(base + L.status)};
+  moe_status st = do_plan(h, T, topk_idx, routing_logits, topk_idx, topk_weights, &plan, base + L.scratch, stream);
+  if (st != MOE_OK || T == 0) return st;
+  void* y = base + L.y;
+  st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch, stream);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, out, stream));
+}
+
+}  // extern "C"

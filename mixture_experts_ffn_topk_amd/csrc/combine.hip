@@ -1,0 +1,50 @@
+// Router-weighted combine: out[t, :] = sum over valid slots j (ascending) of
+// w[t, j] * y[t, j, :] (DistributedEPCombine page: router_weights scale each
+// expert's contribution; the per-pair rows y are the expert outputs).
+// HBM-bound gather-reduce: each thread owns 8 consecutive bf16 columns and reads
+// the k slot rows with 16-byte loads; fp32 accumulation; bf16 store.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kCombineThreads = 256;
+constexpr int kCombineCols = kCombineThreads * 8;  // columns per workgroup
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
+                                                                  const float* __restrict__ w,
+                                                                  const int* __restrict__ pair_row, int topk, int H,
+                                                                  uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int col = blockIdx.y * kCombineCols + threadIdx.x * 8;
+  if (col >= H) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const long long p0 = (long long)t * topk;
+  for (int j = 0; j < topk; ++j) {
+    if (pair_row[p0 + j] < 0) continue;  // masked slot
+    const float wj = w[p0 + j];
+    const i32x4 v = *(const i32x4*)(y + (p0 + j) * H + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t u = (uint32_t)v[q];
+      acc[2 * q] = fmaf(wj, bf16_to_f32((uint16_t)(u & 0xFFFFu)), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(wj, bf16_to_f32((uint16_t)(u >> 16)), acc[2 * q + 1]);
+    }
+  }
+  i32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
+  *(i32x4*)(out + (long long)t * H + col) = o;
+}
+
+hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H, void* out,
+                          hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid(T, (H + kCombineCols - 1) / kCombineCols);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row, topk, H,
+                     (uint16_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

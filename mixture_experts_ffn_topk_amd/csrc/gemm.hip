@@ -1,0 +1,565 @@
+// Grouped (per-expert, variable-M) GEMMs of the expert FFN on gfx950 MFMA.
+//
+//   gate_up:  [rows of expert e] x W13[e]^T -> g, u  -> clamped SwiGLU -> requant -> h
+//   down:     h[rows of expert e] x W2[e]^T          -> y[src_info[row]] (bf16)
+//
+// Both legs walk one shared expert list (Struct_mega_ffn_ep_combine_send page:
+// num_active_experts / expert_start_indices); each workgroup finds its tile
+// from the per-expert prefix sums, so no device-side tile list is needed.
+//
+// Workgroup: 4 wavefronts, BM rows x 256 weight rows per tile.
+//   * A (activation rows, gathered through src_info for gate_up) is staged in
+//     LDS, double buffered, one 128-byte K-step segment per row.
+//   * B (weights) streams from HBM straight into VGPRs in MFMA operand order,
+//     three K-steps deep, each wave owning 64 weight rows.  Every weight byte
+//     of a tile is read once.
+// All global loads are buffer loads: a uniform base, a loop-invariant 32-bit
+// lane offset and the K-step offset in a scalar register; a lane offset past
+// the end of the resource reads zeros, which masks rows and columns outside
+// the problem.
+// MFMA per format (16x16 output tiles, 4 f32 per lane: column l%16, rows 4*(l/16)+i):
+//   FP8 block-128: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales per
+//                  K-step of 128, then acc += (sa[row] * sb) * partial with the
+//                  fp32 block scales of the DeepSeek FP8 encoding.
+//   BF16:          2 x v_mfma_f32_16x16x32_bf16 per K-step of 64.
+//   MX (W4A8):     v_mfma_scale_f32_16x16x128_f8f6f4, A = E4M3 + UE8M0,
+//                  B = E2M1 + UE8M0, the block scales applied by the hardware.
+// Operand lane layout (lane l, g = l/16): an FP8/BF16 row segment of 128 bytes
+// is fed as bytes [16g, 16g+16) and [64+16g, 64+16g+16); an E2M1 segment of
+// 64 bytes as bytes [16g, 16g+16); the scale byte of lane l belongs to
+// K-block g (32 elements) of row l%16.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBRows = 256;       // weight rows per workgroup tile
+constexpr int kWRows = 64;        // weight rows per wave
+constexpr int kNT = kWRows / 16;  // 16-wide MFMA column tiles per wave
+constexpr int kARowBytes = 144;   // 128-byte K-step segment + 16 bytes of bank padding
+constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
+
+struct GemmParams {
+  const int* start;     // expert_start_indices [E+1]
+  const int* src_info;  // [npairs]
+  int E, topk;
+  int m_tiles_max, n_tiles;
+  int K;       // reduction length in elements
+  int ksteps;  // K-steps of 128 (FP8, MX) or 64 (BF16) elements
+  int N;       // output columns: I (gate_up) or H (down)
+  int n_rows;  // weight rows per expert: 2I (gate_up) or H (down)
+  const uint8_t* A;
+  uint32_t a_bytes;  // size of the A tensor
+  uint32_t a_row_bytes;
+  const void* A_sf;
+  uint32_t a_sf_bytes;
+  int a_sf_row;  // FP8: floats per row; MX: bytes per row
+  const uint8_t* B;
+  uint32_t b_row_bytes;
+  uint32_t b_expert_bytes;
+  const void* B_sf;
+  int b_sf_row;  // FP8: K/128 floats per 128-row block; MX: K/32 bytes per row
+  void* C;
+  long long c_row_bytes;
+  void* C_sf;
+  int c_sf_row;
+  float clamp;
+};
+
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+MOE_DEV i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+MOE_DEV int xcd_remap(int bid, int G) {
+  // Work-groups are dealt round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of logical tiles so neighbours share its L2.
+  const int q = G >> 3, r = G & 7, x = bid & 7, i = bid >> 3;
+  return x * q + min(x, r) + i;
+}
+
+template <Fmt F>
+struct BFrag {
+  // FP8 / BF16: 32 bytes per lane (two 16-byte pieces); MX: 16 bytes of E2M1 + a scale byte
+  i32x8 d[kNT];
+  int sc[kNT];
+};
+
+template <Fmt F, bool GATEUP, int BM>
+struct Tile {
+  static constexpr int MT = BM / 16;
+  static constexpr int kAChunks = BM * 8 / kThreads;  // 16-byte chunks of the A tile per thread
+  static constexpr int kOutRowBytes = GATEUP ? (F == Fmt::BF16 ? 256 : 128) : 512;
+  static constexpr int kOutStride = kOutRowBytes + 16;
+  static constexpr int kABytes = 2 * BM * kARowBytes;
+  static constexpr int kOutBytes = BM * kOutStride;
+  static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
+  static constexpr int kLds = kUnion + 2 * BM * 4 + kWaves * BM * 4;
+};
+
+template <Fmt F, bool GATEUP, int BM, bool FAST>
+__global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void ffn_gemm_kernel(GemmParams p) {
+  using TL = Tile<F, GATEUP, BM>;
+  constexpr int MT = TL::MT;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kLds];
+  uint8_t* a_lds = lds;                                      // [2][BM][144]
+  uint8_t* out_lds = lds;                                    // aliases a_lds after the K loop
+  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);          // [2][BM] (fp32 bits or 4 UE8M0 bytes)
+  float* red_lds = (float*)(lds + TL::kUnion + 2 * BM * 4);  // [kWaves][BM]
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+
+  // ---------------------------------------------------------------- tile decode
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_tile = L / p.m_tiles_max;
+  const int m_tile = L - n_tile * p.m_tiles_max;
+  int expert = -1, tile_in_e = 0;
+  {
+    int base = 0;
+    for (int e0 = 0; e0 < p.E; e0 += 64) {
+      const int e = e0 + lane;
+      const int cnt = e < p.E ? p.start[e + 1] - p.start[e] : 0;
+      const int tiles = (cnt + BM - 1) / BM;
+      int incl = tiles;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      const int excl = incl - tiles;
+      const bool hit = m_tile >= base + excl && m_tile < base + incl;
+      const uint64_t bal = __ballot(hit);
+      if (bal) {
+        const int src = __ffsll((unsigned long long)bal) - 1;
+        expert = e0 + src;
+        tile_in_e = m_tile - base - __shfl(excl, src);
+        break;
+      }
+      base += __shfl(incl, 63);
+    }
+  }
+  expert = __builtin_amdgcn_readfirstlane(expert);
+  tile_in_e = __builtin_amdgcn_readfirstlane(tile_in_e);
+  if (expert < 0) return;  // beyond the real tile count (grid is sized for the worst case)
+  const int row0 = p.start[expert] + tile_in_e * BM;
+  const int rows = min(BM, p.start[expert + 1] - row0);
+
+  // ---------------------------------------------------------------- A (activation) addressing
+  // Thread tid loads 16-byte chunks c = tid + 256*i of the BM x 128-byte tile: row c/8, chunk c%8.
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
+  uint32_t a_off[TL::kAChunks];
+#pragma unroll
+  for (int i = 0; i < TL::kAChunks; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 3;
+    if (r < rows) {
+      const int grow = row0 + r;
+      const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
+      a_off[i] = arow * p.a_row_bytes + (uint32_t)(c & 7) * 16u;
+    } else {
+      a_off[i] = kOOB;
+    }
+  }
+  // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step)
+  const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
+  uint32_t asf_off = kOOB;
+  if (F != Fmt::BF16 && tid < rows) {
+    const int grow = row0 + tid;
+    const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
+    asf_off = arow * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u);
+  }
+
+  // Loads past the last K-step read zeros (no branch, so the register rings stay static).
+  auto load_a = [&](i32x4 (&v)[TL::kAChunks], uint32_t& s, int ks) {
+    const bool live = ks < p.ksteps;
+#pragma unroll
+    for (int i = 0; i < TL::kAChunks; ++i) {
+      uint32_t o = live ? a_off[i] : kOOB;
+      if (F == Fmt::MX && ks * 128 + (((tid + kThreads * i) & 7) * 16) >= p.K) o = kOOB;  // K tail
+      v[i] = bload16(a_rs, o, (uint32_t)ks * 128u);
+    }
+    if (F == Fmt::FP8) {
+      s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, live ? asf_off : kOOB, (uint32_t)ks * 4u, 0);
+    } else if (F == Fmt::MX) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t o = (ks * 4 + j < p.a_sf_row) ? asf_off + (uint32_t)j : kOOB;
+        w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, o, (uint32_t)ks * 4u, 0) << (8 * j);
+      }
+      s = w;
+    }
+  };
+  auto store_a = [&](const i32x4 (&v)[TL::kAChunks], uint32_t s, int buf) {
+    uint8_t* base = a_lds + buf * BM * kARowBytes;
+#pragma unroll
+    for (int i = 0; i < TL::kAChunks; ++i) {
+      const int c = tid + kThreads * i;
+      *(i32x4*)(base + (c >> 3) * kARowBytes + (c & 7) * 16) = v[i];
+    }
+    if (F != Fmt::BF16 && tid < BM) sa_lds[buf * BM + tid] = s;
+  };
+
+  // ---------------------------------------------------------------- B (weight) addressing
+  const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + (size_t)expert * p.b_expert_bytes, p.b_expert_bytes);
+  __amdgpu_buffer_rsrc_t bsc_rs = b_rs;
+  uint32_t b_off[kNT], bsc_off[kNT];
+  const float* b_sf_fp8[2] = {nullptr, nullptr};  // FP8: scale rows of the wave's (gate, up) blocks
+  {
+    if (F == Fmt::MX)
+      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.n_rows * p.b_sf_row,
+                         (uint32_t)p.n_rows * (uint32_t)p.b_sf_row);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      int wrow, ocol;
+      if (GATEUP) {
+        ocol = n_tile * 128 + wave * 32 + 16 * (nt & 1) + r16;  // h column
+        wrow = (nt < 2 ? 0 : p.N) + ocol;                        // gate rows, then up rows
+      } else {
+        ocol = n_tile * kBRows + wave * kWRows + 16 * nt + r16;
+        wrow = ocol;
+      }
+      const bool ok = ocol < p.N;
+      b_off[nt] = ok ? (uint32_t)wrow * p.b_row_bytes + (uint32_t)(16 * g) : kOOB;
+      bsc_off[nt] = ok ? (uint32_t)wrow * (uint32_t)p.b_sf_row + (uint32_t)g : kOOB;
+    }
+    if (F == Fmt::FP8) {
+      const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
+      if (GATEUP) {
+        b_sf_fp8[0] = sfe + (size_t)n_tile * p.b_sf_row;
+        b_sf_fp8[1] = sfe + (size_t)(p.N / 128 + n_tile) * p.b_sf_row;
+      } else {
+        const int blk = min((n_tile * kBRows + wave * kWRows) / 128, p.n_rows / 128 - 1);
+        b_sf_fp8[0] = b_sf_fp8[1] = sfe + (size_t)blk * p.b_sf_row;
+      }
+    }
+  }
+  auto load_b = [&](BFrag<F>& b, int ks) {
+    const bool live = ks < p.ksteps;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      if (F == Fmt::MX) {
+        const bool tail = ks * 128 + 32 * g >= p.K;  // also true past the last K-step
+        const i32x4 v = bload16(b_rs, tail ? kOOB : b_off[nt], (uint32_t)ks * 64u);
+        b.d[nt] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, tail ? kOOB : bsc_off[nt], (uint32_t)ks * 4u, 0);
+      } else {
+        const uint32_t o = live ? b_off[nt] : kOOB;
+        const i32x4 lo = bload16(b_rs, o, (uint32_t)ks * 128u);
+        const i32x4 hi = bload16(b_rs, o + 64u, (uint32_t)ks * 128u);
+        b.d[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  f32x4 acc[MT][kNT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  BFrag<F> bq0, bq1, bq2;
+  i32x4 av0[TL::kAChunks], av1[TL::kAChunks];
+  uint32_t as0 = 0, as1 = 0;
+  const int KS = p.ksteps;
+  load_b(bq0, 0);
+  load_b(bq1, 1);
+  load_b(bq2, 2);
+  load_a(av0, as0, 0);
+  load_a(av1, as1, 1);
+  store_a(av0, as0, 0);
+
+  // One K-step: A(ks) is in LDS buffer ks&1; A(ks+1) is in flight in `an`;
+  // B(ks) is in `bq`.  Issues A(ks+2) into `ap` and B(ks+3) into `bq`.
+  auto step = [&](BFrag<F>& bq, i32x4 (&ap)[TL::kAChunks], uint32_t& sp, i32x4 (&an)[TL::kAChunks], uint32_t& sn,
+                  int ks) {
+    load_a(ap, sp, ks + 2);
+    __syncthreads();
+    const uint8_t* abuf = a_lds + (ks & 1) * BM * kARowBytes;
+    float sbv0 = 1.f, sbv1 = 1.f;
+    if (F == Fmt::FP8) {
+      const int kc = min(ks, KS - 1);  // a step past the end multiplies zeros
+      sbv0 = b_sf_fp8[0][kc];
+      sbv1 = b_sf_fp8[1][kc];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint8_t* ar = abuf + (mt * 16 + r16) * kARowBytes + 16 * g;
+      const i32x8 a8 = __builtin_shufflevector(*(const i32x4*)ar, *(const i32x4*)(ar + 64), 0, 1, 2, 3, 4, 5, 6, 7);
+      if (F == Fmt::FP8) {
+        const f32x4 sa = *(const f32x4*)(sa_lds + (ks & 1) * BM + mt * 16 + 4 * g);
+        const f32x4 s0 = sa * sbv0, s1 = sa * sbv1;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a8, bq.d[nt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          acc[mt][nt] += part * ((GATEUP && nt >= 2) ? s1 : s0);
+        }
+      } else if (F == Fmt::BF16) {
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a8, a8, 0, 1, 2, 3));
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a8, a8, 4, 5, 6, 7));
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const bf16x8 blo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(bq.d[nt], bq.d[nt], 0, 1, 2, 3));
+          const bf16x8 bhi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(bq.d[nt], bq.d[nt], 4, 5, 6, 7));
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[mt][nt], 0, 0, 0);
+        }
+      } else {
+        const uint32_t sw = sa_lds[(ks & 1) * BM + mt * 16 + r16];
+        const int sa = (int)((sw >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, bq.d[nt], acc[mt][nt], 0, 4, 0, sa, 0,
+                                                                         bq.sc[nt]);
+      }
+    }
+    load_b(bq, ks + 3);
+    store_a(an, sn, (ks + 1) & 1);
+  };
+
+  // unrolled by 6 so that both rings (3 weight buffers, 2 activation register sets) index statically
+  for (int ks = 0;; ks += 6) {
+    step(bq0, av0, as0, av1, as1, ks);
+    if (ks + 1 >= KS) break;
+    step(bq1, av1, as1, av0, as0, ks + 1);
+    if (ks + 2 >= KS) break;
+    step(bq2, av0, as0, av1, as1, ks + 2);
+    if (ks + 3 >= KS) break;
+    step(bq0, av1, as1, av0, as0, ks + 3);
+    if (ks + 4 >= KS) break;
+    step(bq1, av0, as0, av1, as1, ks + 4);
+    if (ks + 5 >= KS) break;
+    step(bq2, av1, as1, av0, as0, ks + 5);
+    if (ks + 6 >= KS) break;
+  }
+  __syncthreads();  // every wave is done with the A buffers; the output tile reuses them
+
+  // ---------------------------------------------------------------- epilogue
+  if (GATEUP) {
+    const float c = p.clamp;
+    float h[MT][2][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[mt][j][i] = swiglu_clamped<FAST>(acc[mt][j][i], acc[mt][j + 2][i], c);
+    const int hcol0 = n_tile * 128 + wave * 32;  // first h column of this wave
+    const bool wave_valid = hcol0 < p.N;
+    if (F == Fmt::BF16) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * 32 + 16 * j + r16) * 2) =
+                f32_to_bf16_rne(h[mt][j][i]);
+          }
+    } else {
+      // per-row amax over this wave's 32 columns (16 lanes x 2 column tiles)
+      float am[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float m = fmaxf(fabsf(h[mt][0][i]), fabsf(h[mt][1][i]));
+          m = fmaxf(m, __shfl_xor(m, 1));
+          m = fmaxf(m, __shfl_xor(m, 2));
+          m = fmaxf(m, __shfl_xor(m, 4));
+          m = fmaxf(m, __shfl_xor(m, 8));
+          am[mt][i] = m;
+        }
+      float qscale[MT][4];
+      if (F == Fmt::FP8) {
+        // one scale per (row, 128 columns): combine the 4 waves' partial maxima
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r16 == 0) red_lds[wave * BM + mt * 16 + 4 * g + i] = am[mt][i];
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            float a = red_lds[r];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red_lds[w * BM + r]);
+            const float s = a > 0.f ? a / 448.0f : 1.0f;
+            qscale[mt][i] = 1.0f / s;
+            if (wave == 0 && r16 == 0 && r < rows)
+              ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + n_tile] = s;
+          }
+      } else {
+        // MX: one UE8M0 exponent per (row, 32 columns) = this wave's columns
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            const int e = mx_exponent_for_amax(am[mt][i]);
+            qscale[mt][i] = exp2i(-e);
+            if (wave_valid && r16 == 0 && r < rows)
+              ((uint8_t*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + hcol0 / 32] = (uint8_t)(e + 127);
+          }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            const uint32_t q = f32x2_to_e4m3_sat(h[mt][j][i] * qscale[mt][i], 0.f);
+            out_lds[r * TL::kOutStride + wave * 32 + 16 * j + r16] = (uint8_t)(q & 0xFFu);
+          }
+    }
+    __syncthreads();
+    // coalesced copy of the tile's h rows: 16-byte chunks
+    constexpr int CPR = TL::kOutRowBytes / 16;  // chunks per row
+    constexpr int elem = F == Fmt::BF16 ? 2 : 1;
+    for (int c = tid; c < BM * CPR; c += kThreads) {
+      const int r = c / CPR, cc = c % CPR;
+      const int col = n_tile * 128 + cc * 16 / elem;
+      if (r < rows && col < p.N) {
+        *(i32x4*)((uint8_t*)p.C + (long long)(row0 + r) * p.c_row_bytes + (long long)n_tile * 128 * elem + cc * 16) =
+            *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
+      }
+    }
+  } else {
+    // down: bf16 rows scattered to their pair slots y[src_info[row]]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 16 + 4 * g + i;
+          *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * kWRows + 16 * nt + r16) * 2) =
+              f32_to_bf16_rne(acc[mt][nt][i]);
+        }
+    __syncthreads();
+    constexpr int CPR = 512 / 16;
+    for (int c = tid; c < BM * CPR; c += kThreads) {
+      const int r = c / CPR, cc = c % CPR;
+      const int col = n_tile * kBRows + cc * 8;
+      if (r < rows && col < p.N) {
+        const long long pair = p.src_info[row0 + r];
+        *(i32x4*)((uint8_t*)p.C + pair * p.c_row_bytes + (long long)col * 2) =
+            *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+size_t ffn_h_bytes(Fmt f, int rows, int I) { return (size_t)rows * I * (f == Fmt::BF16 ? 2 : 1); }
+size_t ffn_hsf_bytes(Fmt f, int rows, int I) {
+  if (f == Fmt::FP8) return (size_t)rows * (I / 128) * 4;
+  if (f == Fmt::MX) return (size_t)rows * (I / 32);
+  return 0;
+}
+int ffn_max_m_tiles(int npairs, int E, int bm) {
+  const long long act = npairs < E ? npairs : E;
+  return (int)(((long long)npairs + act * (bm - 1)) / bm);
+}
+
+template <Fmt F, bool GATEUP, int BM>
+static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
+  const int grid = gp.m_tiles_max * gp.n_tiles;
+  if (grid <= 0) return;
+  if (fast)
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, true>), dim3(grid), dim3(kThreads), 0, s, gp);
+  else
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, false>), dim3(grid), dim3(kThreads), 0, s, gp);
+}
+
+template <Fmt F, int BM>
+static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s) {
+  launch_one<F, true, BM>(g1, fast, s);
+  launch_one<F, false, BM>(g2, fast, s);
+}
+
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+  const int npairs = a.T * a.topk;
+  if (npairs == 0) return hipSuccess;
+  const int elem_k = a.fmt == Fmt::BF16 ? 64 : 128;
+  const uint32_t esz = a.fmt == Fmt::BF16 ? 2 : 1;
+  const int sf_div = a.fmt == Fmt::FP8 ? 128 : 32;
+  GemmParams g1{}, g2{};
+  // gate_up: A = x rows gathered through src_info, B = w13 [E, 2I, H]
+  g1.start = a.start;
+  g1.src_info = a.src_info;
+  g1.E = a.E;
+  g1.topk = a.topk;
+  g1.m_tiles_max = ffn_max_m_tiles(npairs, a.E, a.bm);
+  g1.n_tiles = (a.I + 127) / 128;
+  g1.K = a.H;
+  g1.ksteps = (a.H + elem_k - 1) / elem_k;
+  g1.N = a.I;
+  g1.n_rows = 2 * a.I;
+  g1.A = (const uint8_t*)a.x;
+  g1.a_row_bytes = (uint32_t)a.H * esz;
+  g1.a_bytes = g1.a_row_bytes * (uint32_t)a.T;
+  g1.A_sf = a.x_sf;
+  g1.a_sf_row = a.H / sf_div;
+  g1.a_sf_bytes = (uint32_t)a.T * (uint32_t)g1.a_sf_row * (a.fmt == Fmt::FP8 ? 4u : 1u);
+  g1.B = (const uint8_t*)a.w13;
+  g1.b_row_bytes = a.fmt == Fmt::MX ? (uint32_t)a.H / 2 : (uint32_t)a.H * esz;
+  g1.b_expert_bytes = g1.b_row_bytes * 2u * (uint32_t)a.I;
+  g1.B_sf = a.w13_sf;
+  g1.b_sf_row = a.H / sf_div;
+  g1.C = a.h;
+  g1.c_row_bytes = (long long)a.I * esz;
+  g1.C_sf = a.h_sf;
+  g1.c_sf_row = a.I / sf_div;
+  g1.clamp = a.clamp;
+  // down: A = h rows, B = w2 [E, H, I]
+  g2 = g1;
+  g2.n_tiles = (a.H + kBRows - 1) / kBRows;
+  g2.K = a.I;
+  g2.ksteps = (a.I + elem_k - 1) / elem_k;
+  g2.N = a.H;
+  g2.n_rows = a.H;
+  g2.A = (const uint8_t*)a.h;
+  g2.a_row_bytes = (uint32_t)a.I * esz;
+  g2.a_bytes = g2.a_row_bytes * (uint32_t)npairs;
+  g2.A_sf = a.h_sf;
+  g2.a_sf_row = a.I / sf_div;
+  g2.a_sf_bytes = (uint32_t)npairs * (uint32_t)g2.a_sf_row * (a.fmt == Fmt::FP8 ? 4u : 1u);
+  g2.B = (const uint8_t*)a.w2;
+  g2.b_row_bytes = a.fmt == Fmt::MX ? (uint32_t)a.I / 2 : (uint32_t)a.I * esz;
+  g2.b_expert_bytes = g2.b_row_bytes * (uint32_t)a.H;
+  g2.B_sf = a.w2_sf;
+  g2.b_sf_row = a.I / sf_div;
+  g2.C = a.y;
+  g2.c_row_bytes = (long long)a.H * 2;
+  g2.C_sf = nullptr;
+  g2.c_sf_row = 0;
+  switch (a.fmt) {
+    case Fmt::FP8:
+      if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s);
+      else launch_pair<Fmt::FP8, 64>(g1, g2, a.fast, s);
+      break;
+    case Fmt::BF16:
+      if (a.bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s);
+      else launch_pair<Fmt::BF16, 64>(g1, g2, a.fast, s);
+      break;
+    case Fmt::MX:
+      if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s);
+      else launch_pair<Fmt::MX, 64>(g1, g2, a.fast, s);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

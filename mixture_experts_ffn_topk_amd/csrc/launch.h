@@ -1,0 +1,61 @@
+// Internal launcher interface between the host runtime (api.cpp) and the
+// gfx950 kernels.  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum class Fmt : int { FP8 = 0, BF16 = 1, MX = 2 };
+
+struct PlanPtrs {
+  int* expert_counts;
+  int* expert_start_indices;
+  int* expert_ids;
+  int* num_active;
+  int* src_info;
+  int* pair_row;
+  int* status;
+};
+
+// Routing plan: one fused block up to this many pairs, else count/scan/scatter
+// over blocks of kPlanPairsPerBlock pairs.
+constexpr int kPlanFusedMaxPairs = 4096;
+constexpr int kPlanPairsPerBlock = 1024;
+
+int plan_num_blocks(int npairs);
+size_t plan_workspace_bytes(int npairs, int E);
+hipError_t launch_plan(const void* ids, bool idx64, int npairs, int E, const PlanPtrs& out, int* ws,
+                       hipStream_t s);
+hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, void* idx_out, bool idx64,
+                                    float* w_out, bool fast, hipStream_t s);
+
+// Grouped GEMMs.  Tile rows per workgroup (BM) by regime.
+struct FfnArgs {
+  Fmt fmt;
+  int T, E, topk, H, I;
+  float clamp;
+  bool fast;
+  int bm;  // 64 or 128
+  const int* start;     // expert_start_indices [E+1]
+  const int* src_info;  // [T*k]
+  const void* x;
+  const void* x_sf;
+  const void* w13;
+  const void* w13_sf;
+  const void* w2;
+  const void* w2_sf;
+  void* h;     // intermediate [T*k, I] (E4M3 or bf16)
+  void* h_sf;  // its scales: fp32 [T*k, I/128] (FP8) or UE8M0 [T*k, I/32] (MX)
+  void* y;     // [T*k, H] bf16, row p = src_info[row]
+};
+size_t ffn_h_bytes(Fmt f, int rows, int I);
+size_t ffn_hsf_bytes(Fmt f, int rows, int I);
+int ffn_max_m_tiles(int npairs, int E, int bm);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H, void* out,
+                          hipStream_t s);
+
+}  // namespace moe

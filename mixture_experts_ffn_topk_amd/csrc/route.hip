@@ -1,0 +1,362 @@
+// Routing kernels: top-k from router logits, and the routing plan
+// (per-expert counts, prefix-sum start offsets, active-expert list and the
+// stable (token, slot) -> row permutation).
+//
+// Plan outputs follow the fused FFN's operands on the Struct_mega_ffn_ep_combine_send
+// page: expert_start_indices (per-expert prefix-sum offsets), expert_ids (active
+// local experts, -1 = masked), num_active_experts, src_info (per-row origin).
+// FromLogits routing follows the routing_input_mode entry of the
+// flashinfer.fused_moe MoEActivationPack page.
+//
+// Everything here is integer work except the softmax weights, so the plan is
+// bit-exact and deterministic: rows of one expert are ordered by pair index
+// p = t*k + j, built from wavefront ballots (no global sort, no atomics whose
+// order could leak into the result).
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kPlanThreads = 256;  // 4 waves
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// ------------------------------------------------------------------ top-k
+// One wavefront per token.  Each lane holds logits e = lane + 64*i (i < 8),
+// k rounds of wave-wide argmax with key (logit desc, index asc), then a
+// softmax over the k selected logits.
+template <typename IdxT, bool FAST>
+__global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                                int k, IdxT* __restrict__ idx_out,
+                                                                float* __restrict__ w_out) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[8];
+  const float* row = logits + (size_t)t * E;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int e = lane + 64 * i;
+    float x = e < E ? row[e] : -INFINITY;
+    v[i] = (x != x) ? -INFINITY : x;  // NaN ranks as -inf
+  }
+  unsigned taken = 0;
+  float my_v = -INFINITY;
+  int my_i = 0;
+  for (int s = 0; s < k; ++s) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int e = lane + 64 * i;
+      bool ok = e < E && !((taken >> i) & 1u);
+      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      float ov = __shfl_xor(bv, m);
+      int oi = __shfl_xor(bi, m);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == s) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  const float vmax = __shfl(my_v, 0);  // the first selected logit is the largest
+  float ex = 0.0f;
+  if (lane < k) ex = FAST ? __builtin_amdgcn_exp2f((my_v - vmax) * 1.4426950408889634f) : expf(my_v - vmax);
+  float sum = ex;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  if (lane < k) {
+    idx_out[(size_t)t * k + lane] = (IdxT)my_i;
+    w_out[(size_t)t * k + lane] = FAST ? ex * __builtin_amdgcn_rcpf(sum) : ex / sum;
+  }
+}
+
+// ------------------------------------------------------------------ plan pieces
+template <typename IdxT>
+MOE_DEV int load_expert(const IdxT* ids, int p, int E, int* bad) {
+  long long e = (long long)ids[p];
+  if (e >= 0 && e < E) return (int)e;
+  if (e != -1) *bad += 1;
+  return -1;
+}
+
+// Exclusive scan of cnt[0..E) (LDS) by one block of kPlanThreads threads.
+// Writes out_start[0..E] (E+1 entries) to global and returns nothing; also
+// fills the active list.  cnt must be final; uses scratch LDS of kPlanWaves ints.
+MOE_DEV void plan_scan_and_active(const int* cnt, int E, int* __restrict__ counts_out, int* __restrict__ start_out,
+                                  int* __restrict__ ids_out, int* __restrict__ num_active_out, int* base_lds,
+                                  int* wave_tot) {
+  // each thread owns up to 4 consecutive experts
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int per = (E + kPlanThreads - 1) / kPlanThreads;  // <= 4 for E <= 1024
+  const int e0 = tid * per;
+  int c[4] = {0, 0, 0, 0}, a[4] = {0, 0, 0, 0};
+  int csum = 0, asum = 0;
+  for (int i = 0; i < per; ++i) {
+    int e = e0 + i;
+    if (e < E) {
+      c[i] = cnt[e];
+      a[i] = c[i] > 0;
+    }
+    csum += c[i];
+    asum += a[i];
+  }
+  // inclusive wave scan of (csum, asum) packed: counts < 2^31, actives < 2^11
+  int cs = csum, as = asum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int oc = __shfl_up(cs, d), oa = __shfl_up(as, d);
+    if (lane >= d) {
+      cs += oc;
+      as += oa;
+    }
+  }
+  if (lane == 63) {
+    wave_tot[wave] = cs;
+    wave_tot[kPlanWaves + wave] = as;
+  }
+  __syncthreads();
+  int cb = 0, ab = 0;
+  for (int w = 0; w < wave; ++w) {
+    cb += wave_tot[w];
+    ab += wave_tot[kPlanWaves + w];
+  }
+  int run_c = cb + cs - csum, run_a = ab + as - asum;  // exclusive
+  for (int i = 0; i < per; ++i) {
+    int e = e0 + i;
+    if (e < E) {
+      counts_out[e] = c[i];
+      start_out[e] = run_c;
+      if (base_lds) base_lds[e] = run_c;
+      if (a[i]) ids_out[run_a] = e;
+      run_c += c[i];
+      run_a += a[i];
+    }
+  }
+  if (tid == kPlanThreads - 1) {
+    start_out[E] = run_c;
+    *num_active_out = run_a;
+  }
+  __syncthreads();
+  // pad the active list with -1
+  int nact = 0;
+  for (int w = 0; w < kPlanWaves; ++w) nact += wave_tot[kPlanWaves + w];
+  for (int e = nact + tid; e < E; e += kPlanThreads) ids_out[e] = -1;
+}
+
+// Stable scatter of pairs [begin, end) in chunks of kPlanThreads.  run[e] (LDS)
+// holds the next free row of expert e and is advanced.  wcnt is LDS scratch of
+// kPlanWaves * E ints.
+template <typename IdxT>
+MOE_DEV void plan_scatter(const IdxT* __restrict__ ids, int begin, int end, int E, int* run, int* wcnt,
+                          int* __restrict__ src_info, int* __restrict__ pair_row) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int ebits = 1;
+  while ((1 << ebits) < E + 1) ++ebits;
+  for (int c0 = begin; c0 < end; c0 += kPlanThreads) {
+    const int p = c0 + tid;
+    int dummy = 0;
+    int e = p < end ? load_expert(ids, p, E, &dummy) : -1;
+    // lanes holding the same expert id: intersect ballots over the bits of (e + 1)
+    const int key = e + 1;  // 0 for masked / out of chunk
+    uint64_t match = ~0ull;
+    for (int b = 0; b < ebits; ++b) {
+      uint64_t bal = __ballot((key >> b) & 1);
+      match &= ((key >> b) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(match & lt_mask);
+    const int total = __popcll(match);
+    // the lowest lane of each group publishes the group's size for this wave
+    for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcnt[i] = 0;
+    __syncthreads();
+    if (e >= 0 && rank == 0) wcnt[wave * E + e] = total;
+    __syncthreads();
+    if (e >= 0) {
+      int off = run[e] + rank;
+      for (int w = 0; w < wave; ++w) off += wcnt[w * E + e];
+      src_info[off] = p;
+      pair_row[p] = off;
+    } else if (p < end) {
+      pair_row[p] = -1;
+    }
+    __syncthreads();
+    for (int ex = tid; ex < E; ex += kPlanThreads) {
+      int s = 0;
+      for (int w = 0; w < kPlanWaves; ++w) s += wcnt[w * E + ex];
+      run[ex] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ fused plan (one block)
+template <typename IdxT>
+__global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(const IdxT* __restrict__ ids, int npairs, int E,
+                                                                  PlanPtrs out) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                    // [E]
+  int* run = lds + E;                // [E]
+  int* wcnt = lds + 2 * E;           // [kPlanWaves * E]
+  int* misc = lds + (2 + kPlanWaves) * E;  // [2*kPlanWaves + 1]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
+  if (tid == 0) misc[2 * kPlanWaves] = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int p = tid; p < npairs; p += kPlanThreads) {
+    int e = load_expert(ids, p, E, &bad);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  if (bad) atomicAdd(&misc[2 * kPlanWaves], bad);
+  __syncthreads();
+  plan_scan_and_active(cnt, E, out.expert_counts, out.expert_start_indices, out.expert_ids, out.num_active, run,
+                       misc);
+  if (tid == 0) *out.status = misc[2 * kPlanWaves];
+  __syncthreads();
+  plan_scatter(ids, 0, npairs, E, run, wcnt, out.src_info, out.pair_row);
+}
+
+// ------------------------------------------------------------------ multi-block plan
+// 1) per-block histograms of contiguous pair ranges
+template <typename IdxT>
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const IdxT* __restrict__ ids, int npairs, int E,
+                                                                  int per_block, int* __restrict__ hist,
+                                                                  int* __restrict__ bad_out) {
+  extern __shared__ int lds[];
+  int* cnt = lds;
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
+  if (tid == 0) lds[E] = 0;
+  __syncthreads();
+  const int begin = b * per_block, end = min(npairs, begin + per_block);
+  int bad = 0;
+  for (int p = begin + tid; p < end; p += kPlanThreads) {
+    int e = load_expert(ids, p, E, &bad);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  if (bad) atomicAdd(&lds[E], bad);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) hist[(size_t)b * E + e] = cnt[e];
+  if (tid == 0) bad_out[b] = lds[E];
+}
+
+// 2) one block: totals, prefix sums, active list, per-block bases (in place over hist)
+__global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(int nblocks, int E, int* __restrict__ hist,
+                                                                 const int* __restrict__ bad_in, PlanPtrs out) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                 // [E]
+  int* base = lds + E;            // [E]
+  int* misc = lds + 2 * E;        // [2*kPlanWaves + 1]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int s = 0;
+    for (int b = 0; b < nblocks; ++b) s += hist[(size_t)b * E + e];
+    cnt[e] = s;
+  }
+  if (tid == 0) {
+    int s = 0;
+    for (int b = 0; b < nblocks; ++b) s += bad_in[b];
+    misc[2 * kPlanWaves] = s;
+  }
+  __syncthreads();
+  plan_scan_and_active(cnt, E, out.expert_counts, out.expert_start_indices, out.expert_ids, out.num_active, base,
+                       misc);
+  if (tid == 0) *out.status = misc[2 * kPlanWaves];
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int run = base[e];
+    for (int b = 0; b < nblocks; ++b) {
+      int c = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += c;
+    }
+  }
+}
+
+// 3) per-block stable scatter starting from the block's bases
+template <typename IdxT>
+__global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(const IdxT* __restrict__ ids, int npairs, int E,
+                                                                    int per_block, const int* __restrict__ bases,
+                                                                    PlanPtrs out) {
+  extern __shared__ int lds[];
+  int* run = lds;          // [E]
+  int* wcnt = lds + E;     // [kPlanWaves * E]
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) run[e] = bases[(size_t)b * E + e];
+  __syncthreads();
+  const int begin = b * per_block, end = min(npairs, begin + per_block);
+  plan_scatter(ids, begin, end, E, run, wcnt, out.src_info, out.pair_row);
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, void* idx_out, bool idx64,
+                                    float* w_out, bool fast, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4), block(256);
+  if (idx64) {
+    if (fast)
+      hipLaunchKernelGGL((route_logits_topk_kernel<long long, true>), grid, block, 0, s, logits, T, E, k,
+                         (long long*)idx_out, w_out);
+    else
+      hipLaunchKernelGGL((route_logits_topk_kernel<long long, false>), grid, block, 0, s, logits, T, E, k,
+                         (long long*)idx_out, w_out);
+  } else {
+    if (fast)
+      hipLaunchKernelGGL((route_logits_topk_kernel<int, true>), grid, block, 0, s, logits, T, E, k,
+                         (int*)idx_out, w_out);
+    else
+      hipLaunchKernelGGL((route_logits_topk_kernel<int, false>), grid, block, 0, s, logits, T, E, k,
+                         (int*)idx_out, w_out);
+  }
+  return hipGetLastError();
+}
+
+size_t plan_workspace_bytes(int npairs, int E) {
+  int nb = plan_num_blocks(npairs);
+  if (nb <= 1) return 0;
+  return ((size_t)nb * E + nb) * sizeof(int);
+}
+
+int plan_num_blocks(int npairs) {
+  if (npairs <= kPlanFusedMaxPairs) return 1;
+  return (npairs + kPlanPairsPerBlock - 1) / kPlanPairsPerBlock;
+}
+
+template <typename IdxT>
+static hipError_t launch_plan_t(const IdxT* ids, int npairs, int E, const PlanPtrs& out, int* ws, hipStream_t s) {
+  const int nb = plan_num_blocks(npairs);
+  if (nb <= 1) {
+    size_t lds = (size_t)((2 + kPlanWaves) * E + 2 * kPlanWaves + 1) * sizeof(int);
+    hipLaunchKernelGGL(plan_fused_kernel<IdxT>, dim3(1), dim3(kPlanThreads), lds, s, ids, npairs, E, out);
+    return hipGetLastError();
+  }
+  int* hist = ws;
+  int* bad = ws + (size_t)nb * E;
+  hipLaunchKernelGGL(plan_count_kernel<IdxT>, dim3(nb), dim3(kPlanThreads), (E + 1) * sizeof(int), s, ids, npairs,
+                     E, kPlanPairsPerBlock, hist, bad);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), (2 * E + 2 * kPlanWaves + 1) * sizeof(int), s,
+                     nb, E, hist, (const int*)bad, out);
+  hipLaunchKernelGGL(plan_scatter_kernel<IdxT>, dim3(nb), dim3(kPlanThreads),
+                     (size_t)(1 + kPlanWaves) * E * sizeof(int), s, ids, npairs, E, kPlanPairsPerBlock,
+                     (const int*)hist, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const void* ids, bool idx64, int npairs, int E, const PlanPtrs& out, int* ws,
+                       hipStream_t s) {
+  if (idx64) return launch_plan_t((const long long*)ids, npairs, E, out, ws, s);
+  return launch_plan_t((const int*)ids, npairs, E, out, ws, s);
+}
+
+}  // namespace moe

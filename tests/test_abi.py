@@ -1,0 +1,109 @@
+"""The C ABI library on the CPU: it loads, exports every entry point that
+include/moe_ffn.h declares, and validates arguments on the host before any
+launch (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_topk_amd as mx
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_ffn.h")
+
+
+def _lib():
+    try:
+        return mx.load_library()
+    except ImportError as e:  # pragma: no cover
+        pytest.fail(f"library not built: {e}")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_plan", "moe_ffn", "moe_combine", "moe_forward", "moe_create", "moe_destroy",
+              "moe_workspace_size"):
+        assert n in names
+    assert sorted(names) == sorted(mx.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(0) == b"ok"
+
+
+def _cfg(**kw):
+    base = dict(hidden=7168, intermediate_hidden=2048, num_experts=32, num_topk=8, max_num_tokens=256,
+                activation_clamp=10.0, format=0, route_mode=0, topk_idx_bits=64, fast_math=1, tile_regime=0)
+    base.update(kw)
+    return mx._Config(**base)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, 0),
+    ({"hidden": 7168 + 64}, 1),                 # FP8: hidden % 128
+    ({"intermediate_hidden": 2000}, 1),
+    ({"num_topk": 33, "num_experts": 64}, 1),
+    ({"num_topk": 9, "num_experts": 8}, 1),     # k > E
+    ({"num_experts": 0}, 1),
+    ({"activation_clamp": 0.0}, 1),
+    ({"activation_clamp": float("nan")}, 1),
+    ({"topk_idx_bits": 16}, 1),
+    ({"format": 7}, 1),
+    ({"route_mode": 3}, 1),
+    ({"tile_regime": 5}, 1),
+    ({"format": 1, "hidden": 4096, "intermediate_hidden": 14336 + 64}, 0),  # BF16: multiples of 64
+    ({"format": 2, "hidden": 2880, "intermediate_hidden": 2880, "num_experts": 128, "num_topk": 4,
+      "route_mode": 1}, 0),                    # MX: multiples of 32, logits routing
+    ({"format": 2, "hidden": 2880 + 16, "intermediate_hidden": 2880}, 1),
+    ({"route_mode": 1, "num_experts": 600, "num_topk": 4}, 2),   # FromLogits over > 512 experts
+    ({"max_num_tokens": -1}, 1),
+])
+def test_create_validation(kw, expect):
+    lib = _lib()
+    h = ctypes.c_void_p()
+    st = lib.moe_create(ctypes.byref(_cfg(**kw)), ctypes.byref(h))
+    assert st == expect
+    if st == 0:
+        assert h.value
+        lib.moe_destroy(h)
+    else:
+        assert not h.value
+
+
+def test_workspace_size_and_host_validation():
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg()), ctypes.byref(h)) == 0
+    ws0 = lib.moe_workspace_size(h, 0)
+    ws = lib.moe_workspace_size(h, 256)
+    assert ws > ws0 > 0
+    # y [T*k, H] bf16 alone is part of the forward workspace
+    assert ws >= 256 * 8 * 7168 * 2
+    assert lib.moe_workspace_size(h, 257) == 0  # above capacity
+    assert lib.moe_workspace_size(h, -1) == 0
+    plan = mx._Plan(*([None] * 7))
+    # invalid arguments are rejected before anything is launched
+    assert lib.moe_plan(h, 300, None, None, None, None, ctypes.byref(plan), None, 0, None) == 1  # T > capacity
+    assert lib.moe_plan(h, 10, None, None, None, None, ctypes.byref(plan), None, 0, None) == 1   # null plan bufs
+    w = mx._Weights(None, None, None, None)
+    assert lib.moe_forward(h, 10, None, None, None, None, None, ctypes.byref(w), None, None, 0, None) == 1
+    w = mx._Weights(1, 1, 1, 1)
+    assert lib.moe_forward(h, 10, 1, 1, 1, 1, None, ctypes.byref(w), 1, 1, 16, None) == 3  # workspace too small
+    assert lib.moe_forward(h, 10, 1, None, 1, 1, None, ctypes.byref(w), 1, 1, ws, None) == 1  # FP8 needs x_sf
+    assert lib.moe_combine(h, 10, None, None, ctypes.byref(plan), None, None) == 1
+    lib.moe_destroy(h)
+
+
+def test_binding_raises_on_bad_config():
+    with pytest.raises(mx.MoEError):
+        mx.MoEFFN(7168 + 64, 2048, 32, 8, 256)
