@@ -151,6 +151,20 @@ moe_status moe_ffn(const moe_handle* h, int32_t num_tokens, const void* x, const
                    const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
                    void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The two legs of moe_ffn, for callers that schedule or time them separately.
+   The requantised intermediate is caller-owned here:
+     h    [T*k, I]   E4M3 bytes (FP8, MX) or bf16 (BF16), row = plan row
+     h_sf            fp32 [T*k, I/128] (FP8), UE8M0 bytes [T*k, I/32] (MX), NULL (BF16)
+   moe_ffn_gate_up: gate/up GEMM of every plan row, clamped SwiGLU, requantisation
+   ([MegaFFN]: L1 GEMM, clamp_activation, the re-quant ahead of L2).
+   moe_ffn_down: down GEMM of every plan row into y [T,k,H] bf16 at p = src_info[row]. */
+moe_status moe_ffn_gate_up(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
+                           const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
+                           void* h_out, void* h_sf_out, hipStream_t stream);
+moe_status moe_ffn_down(const moe_handle* h, int32_t num_tokens, const void* h_in, const void* h_sf_in,
+                        const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
+                        void* y, hipStream_t stream);
+
 /* Router-weighted combine ([EPCombine] router_weights): out[t] = sum over valid
    slots j in ascending order of topk_weights[t,j] * y[t,j,:], accumulated in
    fp32, written as bf16 [T,H].  A token with no valid slot gets zeros. */

@@ -52,8 +52,8 @@ class _Plan(ctypes.Structure):
 
 
 PLAN_FIELDS = [f for f, _ in _Plan._fields_]
-EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_plan", "moe_ffn", "moe_combine",
-            "moe_forward", "moe_status_string", "moe_abi_version"]
+EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_plan", "moe_ffn", "moe_ffn_gate_up",
+            "moe_ffn_down", "moe_combine", "moe_forward", "moe_status_string", "moe_abi_version"]
 
 _lib = None
 
@@ -77,6 +77,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_plan.restype = i32
     lib.moe_ffn.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp, sz, vp]
     lib.moe_ffn.restype = i32
+    lib.moe_ffn_gate_up.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp, vp]
+    lib.moe_ffn_gate_up.restype = i32
+    lib.moe_ffn_down.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp]
+    lib.moe_ffn_down.restype = i32
     lib.moe_combine.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Plan), vp, vp]
     lib.moe_combine.restype = i32
     lib.moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, sz, vp]
@@ -183,6 +187,29 @@ class MoEFFN:
         ps = self._plan_struct(plan)
         _check(self.lib.moe_ffn(self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps),
                                 _ptr(y), _ptr(ws), self._nbytes(ws), _stream(stream)), "moe_ffn")
+
+    def alloc_intermediate(self, num_tokens: int, device="cuda"):
+        """(h, h_sf) buffers for moe_ffn_gate_up / moe_ffn_down."""
+        import torch
+        n = max(1, num_tokens * self.topk)
+        if self.fmt == "bf16":
+            return torch.empty((n, self.inter), dtype=torch.bfloat16, device=device), None
+        h = torch.empty((n, self.inter), dtype=torch.uint8, device=device)
+        if self.fmt == "fp8_block128":
+            return h, torch.empty((n, self.inter // 128), dtype=torch.float32, device=device)
+        return h, torch.empty((n, self.inter // 32), dtype=torch.uint8, device=device)
+
+    def ffn_gate_up(self, num_tokens, x, x_sf, weights: dict, plan: dict, h, h_sf, stream=None):
+        ws_ = self._weights_struct(weights)
+        ps = self._plan_struct(plan)
+        _check(self.lib.moe_ffn_gate_up(self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps),
+                                        _ptr(h), _ptr(h_sf), _stream(stream)), "moe_ffn_gate_up")
+
+    def ffn_down(self, num_tokens, h, h_sf, weights: dict, plan: dict, y, stream=None):
+        ws_ = self._weights_struct(weights)
+        ps = self._plan_struct(plan)
+        _check(self.lib.moe_ffn_down(self._h, num_tokens, _ptr(h), _ptr(h_sf), ctypes.byref(ws_), ctypes.byref(ps),
+                                     _ptr(y), _stream(stream)), "moe_ffn_down")
 
     def combine(self, num_tokens, y, topk_weights, plan: dict, out, stream=None):
         ps = self._plan_struct(plan)

@@ -89,9 +89,8 @@ moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const flo
 }
 
 moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
-                  const moe_plan_buffers* plan, void* y, void* ffn_ws, hipStream_t s) {
+                  const moe_plan_buffers* plan, void* y, void* hbuf, void* hsf, hipStream_t s, int stage) {
   const moe_config& c = h->cfg;
-  const Layout L = layout_for(c, T);
   moe::FfnArgs a{};
   a.fmt = to_fmt(c.format);
   a.T = T;
@@ -110,10 +109,10 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
   a.w13_sf = w->w13_sf;
   a.w2 = w->w2;
   a.w2_sf = w->w2_sf;
-  a.h = (char*)ffn_ws + L.h_off;
-  a.h_sf = (char*)ffn_ws + L.hsf_off;
+  a.h = hbuf;
+  a.h_sf = hsf;
   a.y = y;
-  return hip_status(moe::launch_ffn(a, s));
+  return hip_status(moe::launch_ffn(a, s, stage));
 }
 
 bool weights_ok(const moe_config& c, const moe_weights* w) {
@@ -204,7 +203,25 @@ moe_status moe_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_
   const size_t need = layout_for(h->cfg, T).ffn_bytes;
   if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (T == 0) return MOE_OK;
-  return do_ffn(h, T, x, x_sf, w, plan, y, ws, stream);
+  const Layout L = layout_for(h->cfg, T);
+  return do_ffn(h, T, x, x_sf, w, plan, y, (char*)ws + L.h_off, (char*)ws + L.hsf_off, stream, 0);
+}
+
+moe_status moe_ffn_gate_up(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
+                           const moe_plan_buffers* plan, void* h_out, void* h_sf_out, hipStream_t stream) {
+  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (h->cfg.format != MOE_FMT_BF16 && !h_sf_out)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1);
+}
+
+moe_status moe_ffn_down(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in, const moe_weights* w,
+                        const moe_plan_buffers* plan, void* y, hipStream_t stream) {
+  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!h_in || !y || (h->cfg.format != MOE_FMT_BF16 && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2);
 }
 
 moe_status moe_combine(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
@@ -233,7 +250,7 @@ moe_status moe_forward(const moe_handle* h, int32_t T, const void* x, const void
   moe_status st = do_plan(h, T, topk_idx, routing_logits, topk_idx, topk_weights, &plan, base + L.scratch, stream);
   if (st != MOE_OK || T == 0) return st;
   void* y = base + L.y;
-  st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch, stream);
+  st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, out, stream));
 }

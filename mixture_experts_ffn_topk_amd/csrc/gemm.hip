@@ -484,12 +484,12 @@ static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
 }
 
 template <Fmt F, int BM>
-static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s) {
-  launch_one<F, true, BM>(g1, fast, s);
-  launch_one<F, false, BM>(g2, fast, s);
+static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
+  if (stage != 2) launch_one<F, true, BM>(g1, fast, s);
+  if (stage != 1) launch_one<F, false, BM>(g2, fast, s);
 }
 
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   const int npairs = a.T * a.topk;
   if (npairs == 0) return hipSuccess;
   const int elem_k = a.fmt == Fmt::BF16 ? 64 : 128;
@@ -547,16 +547,16 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   g2.c_sf_row = 0;
   switch (a.fmt) {
     case Fmt::FP8:
-      if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s);
-      else launch_pair<Fmt::FP8, 64>(g1, g2, a.fast, s);
+      if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::FP8, 64>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::BF16:
-      if (a.bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s);
-      else launch_pair<Fmt::BF16, 64>(g1, g2, a.fast, s);
+      if (a.bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::BF16, 64>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::MX:
-      if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s);
-      else launch_pair<Fmt::MX, 64>(g1, g2, a.fast, s);
+      if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::MX, 64>(g1, g2, a.fast, s, stage);
       break;
   }
   return hipGetLastError();

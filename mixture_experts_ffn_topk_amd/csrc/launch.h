@@ -53,7 +53,8 @@ struct FfnArgs {
 size_t ffn_h_bytes(Fmt f, int rows, int I);
 size_t ffn_hsf_bytes(Fmt f, int rows, int I);
 int ffn_max_m_tiles(int npairs, int E, int bm);
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// stage: 0 = both legs, 1 = gate_up only, 2 = down only
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage = 0);
 
 hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H, void* out,
                           hipStream_t s);

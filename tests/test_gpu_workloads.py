@@ -23,7 +23,7 @@ SAMPLE = 24
 
 
 def _gather_intermediate(moe, d, T, rows):
-    """Run moe_plan + moe_ffn and return (plan, y, h codes, h scales) for the given rows."""
+    """moe_plan, moe_ffn_gate_up, moe_ffn_down; return (plan, y, h codes, h scales) of the given rows."""
     plan = moe.alloc_plan(T)
     ws = moe.alloc_workspace(T)
     if moe.route_mode == "precomputed":
@@ -31,24 +31,16 @@ def _gather_intermediate(moe, d, T, rows):
     else:
         moe.plan(T, plan, routing_logits=d["logits"], topk_idx_out=d["topk_idx"], topk_weights_out=d["topk_weights"],
                  ws=ws)
+    h, hsf = moe.alloc_intermediate(T)
+    moe.ffn_gate_up(T, d["x"], d["x_sf"], d["weights"], plan, h, hsf)
     y = torch.zeros((T * moe.topk, moe.hidden), dtype=torch.bfloat16, device="cuda")
-    moe.ffn(T, d["x"], d["x_sf"], d["weights"], plan, y, ws)
+    moe.ffn_down(T, h, hsf, d["weights"], plan, y)
     torch.cuda.synchronize()
-    npairs, I = T * moe.topk, moe.inter
-    esz = 2 if moe.fmt == "bf16" else 1
-    hb = npairs * I * esz
     ridx = torch.as_tensor(rows, dtype=torch.int64, device="cuda")
-    h = ws[:hb].view(npairs, I * esz).index_select(0, ridx).cpu().numpy()
-    o = (hb + 255) // 256 * 256
-    if moe.fmt == "bf16":
-        h, hsf = h.view(np.uint16), None
-    elif moe.fmt == "fp8_block128":
-        n = npairs * (I // 128) * 4
-        hsf = ws[o:o + n].view(npairs, (I // 128) * 4).index_select(0, ridx).cpu().numpy().view(np.float32)
-    else:
-        n = npairs * (I // 32)
-        hsf = ws[o:o + n].view(npairs, I // 32).index_select(0, ridx).cpu().numpy()
-    return plan, y, h, hsf
+    hc = h.index_select(0, ridx).cpu()
+    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt == "bf16" else hc.numpy()
+    hs = None if hsf is None else hsf.index_select(0, ridx).cpu().numpy()
+    return plan, y, hc, hs
 
 
 @pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER)
