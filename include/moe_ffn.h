@@ -123,7 +123,10 @@ typedef struct moe_handle moe_handle;
 /* Validate *cfg and create a host handle.  Returns MOE_ERR_INVALID_ARGUMENT for
    bad geometry (see moe_format for the divisibility rules), k > E, k > 32,
    E > 1024, clamp <= 0 or NaN, an unknown enum; MOE_ERR_UNSUPPORTED for
-   FROM_LOGITS with E > 512. */
+   FROM_LOGITS with E > 512, for FP8 with hidden or intermediate_hidden above
+   32768, and where max_num_tokens x hidden (activations), max_num_tokens x k x
+   intermediate_hidden (intermediate) or one expert's gate_up weight reaches
+   2^31 bytes. */
 moe_status moe_create(const moe_config* cfg /* host */, moe_handle** out /* host */);
 void moe_destroy(moe_handle* h);
 

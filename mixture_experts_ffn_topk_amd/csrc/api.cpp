@@ -65,11 +65,12 @@ bool plan_complete(const moe_plan_buffers* p) {
 }
 
 int choose_bm(const moe_config& c, int T) {
-  if (c.tile_regime == MOE_TILES_DECODE) return 64;
+  if (c.tile_regime == MOE_TILES_DECODE) return 96;
   if (c.tile_regime == MOE_TILES_PREFILL) return 128;
-  // Regime gate on the host-known mean rows per expert (the pages' estimated_total_m).
+  // Regime gate on the host-known mean rows per expert (the pages' estimated_total_m):
+  // up to 64 rows on average, one 96-row tile holds a whole expert under uniform load.
   const long long mean = ((long long)T * c.num_topk + c.num_experts - 1) / c.num_experts;
-  return mean <= 96 ? 64 : 128;
+  return mean <= 64 ? 96 : 128;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -125,6 +126,22 @@ bool x_ok(const moe_config& c, const void* x, const void* x_sf) {
   return x && (c.format == MOE_FMT_BF16 || x_sf);
 }
 
+// The GEMM kernels address every operand through buffer resources with 32-bit
+// lane offsets (an offset of 2^31 or more reads zeros), and FP8 stages the
+// weight scales of at most 256 K-steps of 128 in LDS.
+bool sizes_supported(const moe_config& c) {
+  constexpr unsigned long long kMaxBytes = 0x7FFFFFFFull;
+  const unsigned long long T = (unsigned long long)c.max_num_tokens, H = (unsigned long long)c.hidden,
+                           I = (unsigned long long)c.intermediate_hidden, k = (unsigned long long)c.num_topk;
+  const unsigned long long act = c.format == MOE_FMT_BF16 ? 2 : 1;  // bytes per activation element
+  if (T * H * act > kMaxBytes || T * k * I * act > kMaxBytes) return false;
+  // weight bytes per expert (E2M1: half a byte per element)
+  const unsigned long long w13 = c.format == MOE_FMT_BF16 ? 4 * I * H : c.format == MOE_FMT_FP8_BLOCK128 ? 2 * I * H : I * H;
+  if (w13 > kMaxBytes) return false;
+  if (c.format == MOE_FMT_FP8_BLOCK128 && (H / 128 > 256 || I / 128 > 256)) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +184,7 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
       return MOE_ERR_INVALID_ARGUMENT;
   }
   if (c.route_mode == MOE_ROUTE_FROM_LOGITS && c.num_experts > 512) return MOE_ERR_UNSUPPORTED;
+  if (!sizes_supported(c)) return MOE_ERR_UNSUPPORTED;
   moe_handle* h = new (std::nothrow) moe_handle;
   if (!h) return MOE_ERR_INVALID_ARGUMENT;
   h->cfg = c;

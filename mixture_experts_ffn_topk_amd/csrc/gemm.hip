@@ -7,20 +7,20 @@
 // num_active_experts / expert_start_indices); each workgroup finds its tile
 // from the per-expert prefix sums, so no device-side tile list is needed.
 //
-// Workgroup: 4 wavefronts, BM rows x 256 weight rows per tile.
+// Workgroup: WAVES wavefronts, BM rows x 256 weight rows per tile.
 //   * A (activation rows, gathered through src_info for gate_up) is staged in
 //     LDS, double buffered, one 128-byte K-step segment per row.
 //   * B (weights) streams from HBM straight into VGPRs in MFMA operand order,
-//     three K-steps deep, each wave owning 64 weight rows.  Every weight byte
+//     DEPTH K-steps deep, each wave owning 16*NT weight rows.  Every weight byte
 //     of a tile is read once.
 // All global loads are buffer loads: a uniform base, a loop-invariant 32-bit
 // lane offset and the K-step offset in a scalar register; a lane offset past
 // the end of the resource reads zeros, which masks rows and columns outside
 // the problem.
 // MFMA per format (16x16 output tiles, 4 f32 per lane: column l%16, rows 4*(l/16)+i):
-//   FP8 block-128: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales per
-//                  K-step of 128, then acc += (sa[row] * sb) * partial with the
-//                  fp32 block scales of the DeepSeek FP8 encoding.
+//   FP8 block-128: 4 x v_mfma_f32_16x16x32_fp8_fp8 per K-step of 128 into a
+//                  partial, then acc += (sa[row] * sb) * partial with the fp32
+//                  block scales of the DeepSeek FP8 encoding.
 //   BF16:          2 x v_mfma_f32_16x16x32_bf16 per K-step of 64.
 //   MX (W4A8):     v_mfma_scale_f32_16x16x128_f8f6f4, A = E4M3 + UE8M0,
 //                  B = E2M1 + UE8M0, the block scales applied by the hardware.
@@ -33,12 +33,9 @@
 
 namespace moe {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBRows = 256;       // weight rows per workgroup tile
-constexpr int kWRows = 64;        // weight rows per wave
-constexpr int kNT = kWRows / 16;  // 16-wide MFMA column tiles per wave
-constexpr int kARowBytes = 144;   // 128-byte K-step segment + 16 bytes of bank padding
+constexpr int kBRows = 256;      // weight rows per workgroup tile (WAVES * 16 * NT)
+constexpr int kHCols = 128;      // gate_up: h columns per workgroup tile (one FP8 requant block)
+constexpr int kARowBytes = 144;  // 128-byte K-step segment + 16 bytes of bank padding
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
 
 struct GemmParams {
@@ -82,34 +79,51 @@ MOE_DEV int xcd_remap(int bid, int G) {
   return x * q + min(x, r) + i;
 }
 
-template <Fmt F>
+template <Fmt F, int NT>
 struct BFrag {
-  // FP8 / BF16: 32 bytes per lane (two 16-byte pieces); MX: 16 bytes of E2M1 + a scale byte
-  i32x8 d[kNT];
-  int sc[kNT];
+  // 16-byte pieces of the lane's weight K-step segment: FP8 / BF16 use bytes
+  // [16g, 16g+16) (lo) and [64+16g, 64+16g+16) (hi); MX uses lo (32 E2M1 values)
+  // and a scale byte.  Kept as separate 4-register values so that each load
+  // lands in the registers the MFMA reads.
+  i32x4 lo[NT], hi[NT];
+  int sc[NT];
 };
 
-template <Fmt F, bool GATEUP, int BM>
+MOE_DEV long long lo64(i32x4 v) { return (long long)(((unsigned long long)(uint32_t)v[1] << 32) | (uint32_t)v[0]); }
+MOE_DEV long long hi64(i32x4 v) { return (long long)(((unsigned long long)(uint32_t)v[3] << 32) | (uint32_t)v[2]); }
+
+template <Fmt F, bool GATEUP, int BM, int WAVES>
 struct Tile {
+  static constexpr int kThreads = 64 * WAVES;
   static constexpr int MT = BM / 16;
-  static constexpr int kAChunks = BM * 8 / kThreads;  // 16-byte chunks of the A tile per thread
+  static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte chunks of the A tile per thread
+  // A buffer rows: BM rounded up so that every thread stores every chunk it loads
+  // (chunks past BM rows are zeros landing in spare rows): no divergent stores in the loop
+  static constexpr int kARows = kAChunks * kThreads / 8;
   static constexpr int kOutRowBytes = GATEUP ? (F == Fmt::BF16 ? 256 : 128) : 512;
   static constexpr int kOutStride = kOutRowBytes + 16;
-  static constexpr int kABytes = 2 * BM * kARowBytes;
+  static constexpr int kABytes = 2 * kARows * kARowBytes;
   static constexpr int kOutBytes = BM * kOutStride;
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
-  static constexpr int kLds = kUnion + 2 * BM * 4 + kWaves * BM * 4;
+  static constexpr int kSA = kThreads > BM ? kThreads : BM;  // A-scale slots per buffer (one per thread)
+  static constexpr int kMaxKSteps = 256;  // FP8 weight scales of up to 256 K-steps staged in LDS
+  static constexpr int kLds = kUnion + 2 * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? 2 * kMaxKSteps * 4 : 0);
 };
 
-template <Fmt F, bool GATEUP, int BM, bool FAST>
-__global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void ffn_gemm_kernel(GemmParams p) {
-  using TL = Tile<F, GATEUP, BM>;
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, bool FAST>
+__global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
+  static_assert(WAVES * 16 * NT == kBRows, "a workgroup tile covers 256 weight rows");
+  static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
+  using TL = Tile<F, GATEUP, BM, WAVES>;
   constexpr int MT = TL::MT;
+  constexpr int kThreads = TL::kThreads;
+  constexpr int HW = 8 * NT;  // gate_up: h columns per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kLds];
-  uint8_t* a_lds = lds;                                      // [2][BM][144]
-  uint8_t* out_lds = lds;                                    // aliases a_lds after the K loop
-  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);          // [2][BM] (fp32 bits or 4 UE8M0 bytes)
-  float* red_lds = (float*)(lds + TL::kUnion + 2 * BM * 4);  // [kWaves][BM]
+  uint8_t* a_lds = lds;                                          // [2][kARows][144]
+  uint8_t* out_lds = lds;                                        // aliases a_lds after the K loop
+  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [2][kSA] (fp32 bits or 4 UE8M0 bytes)
+  float* red_lds = (float*)(lds + TL::kUnion + 2 * TL::kSA * 4);  // [WAVES][BM]
+  float* sb_lds = red_lds + WAVES * BM;                      // FP8: [2][kMaxKSteps] weight scales
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
 
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void
   const int rows = min(BM, p.start[expert + 1] - row0);
 
   // ---------------------------------------------------------------- A (activation) addressing
-  // Thread tid loads 16-byte chunks c = tid + 256*i of the BM x 128-byte tile: row c/8, chunk c%8.
+  // Thread tid loads 16-byte chunks c = tid + threads*i of the BM x 128-byte tile: row c/8, chunk c%8.
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
   uint32_t a_off[TL::kAChunks];
 #pragma unroll
@@ -166,7 +180,7 @@ __global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void
   }
   // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step)
   const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
-  uint32_t asf_off = kOOB;
+  uint32_t asf_off = kOOB;  // threads past the tile's rows load zeros
   if (F != Fmt::BF16 && tid < rows) {
     const int grow = row0 + tid;
     const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
@@ -195,32 +209,31 @@ __global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void
     }
   };
   auto store_a = [&](const i32x4 (&v)[TL::kAChunks], uint32_t s, int buf) {
-    uint8_t* base = a_lds + buf * BM * kARowBytes;
+    uint8_t* base = a_lds + buf * TL::kARows * kARowBytes;
 #pragma unroll
     for (int i = 0; i < TL::kAChunks; ++i) {
       const int c = tid + kThreads * i;
       *(i32x4*)(base + (c >> 3) * kARowBytes + (c & 7) * 16) = v[i];
     }
-    if (F != Fmt::BF16 && tid < BM) sa_lds[buf * BM + tid] = s;
+    if (F != Fmt::BF16) sa_lds[buf * TL::kSA + tid] = s;
   };
 
   // ---------------------------------------------------------------- B (weight) addressing
   const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + (size_t)expert * p.b_expert_bytes, p.b_expert_bytes);
   __amdgpu_buffer_rsrc_t bsc_rs = b_rs;
-  uint32_t b_off[kNT], bsc_off[kNT];
-  const float* b_sf_fp8[2] = {nullptr, nullptr};  // FP8: scale rows of the wave's (gate, up) blocks
+  uint32_t b_off[NT], bsc_off[NT];
   {
     if (F == Fmt::MX)
       bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.n_rows * p.b_sf_row,
                          (uint32_t)p.n_rows * (uint32_t)p.b_sf_row);
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       int wrow, ocol;
       if (GATEUP) {
-        ocol = n_tile * 128 + wave * 32 + 16 * (nt & 1) + r16;  // h column
-        wrow = (nt < 2 ? 0 : p.N) + ocol;                        // gate rows, then up rows
+        ocol = n_tile * kHCols + wave * HW + 16 * (nt % (NT / 2)) + r16;  // h column
+        wrow = (nt < NT / 2 ? 0 : p.N) + ocol;                             // gate rows, then up rows
       } else {
-        ocol = n_tile * kBRows + wave * kWRows + 16 * nt + r16;
+        ocol = n_tile * kBRows + wave * 16 * NT + 16 * nt + r16;
         wrow = ocol;
       }
       const bool ok = ocol < p.N;
@@ -228,199 +241,206 @@ __global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void
       bsc_off[nt] = ok ? (uint32_t)wrow * (uint32_t)p.b_sf_row + (uint32_t)g : kOOB;
     }
     if (F == Fmt::FP8) {
+      // the tile's weight-scale rows, staged in LDS: [0] the gate block (gate_up) or
+      // the first 128-row block (down), [1] the up block or the second 128-row block
       const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
-      if (GATEUP) {
-        b_sf_fp8[0] = sfe + (size_t)n_tile * p.b_sf_row;
-        b_sf_fp8[1] = sfe + (size_t)(p.N / 128 + n_tile) * p.b_sf_row;
-      } else {
-        const int blk = min((n_tile * kBRows + wave * kWRows) / 128, p.n_rows / 128 - 1);
-        b_sf_fp8[0] = b_sf_fp8[1] = sfe + (size_t)blk * p.b_sf_row;
-      }
+      const int blk0 = GATEUP ? n_tile : min(n_tile * 2, p.n_rows / 128 - 1);
+      const int blk1 = GATEUP ? p.N / 128 + n_tile : min(n_tile * 2 + 1, p.n_rows / 128 - 1);
+      for (int i = tid; i < 2 * p.ksteps; i += kThreads)
+        sb_lds[(i >= p.ksteps) * TL::kMaxKSteps + i % p.ksteps] =
+            sfe[(size_t)(i >= p.ksteps ? blk1 : blk0) * p.b_sf_row + i % p.ksteps];
     }
   }
-  auto load_b = [&](BFrag<F>& b, int ks) {
+  // FP8: which staged scale row this wave's column tile nt uses
+  auto sb_row = [&](int nt) {
+    if (GATEUP) return nt >= NT / 2 ? 1 : 0;
+    return ((wave * 16 * NT + 16 * nt) % 256) >= 128 ? 1 : 0;
+  };
+  auto load_b = [&](BFrag<F, NT>& b, int ks) {
     const bool live = ks < p.ksteps;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       if (F == Fmt::MX) {
         const bool tail = ks * 128 + 32 * g >= p.K;  // also true past the last K-step
-        const i32x4 v = bload16(b_rs, tail ? kOOB : b_off[nt], (uint32_t)ks * 64u);
-        b.d[nt] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        b.lo[nt] = bload16(b_rs, tail ? kOOB : b_off[nt], (uint32_t)ks * 64u);
         b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, tail ? kOOB : bsc_off[nt], (uint32_t)ks * 4u, 0);
       } else {
         const uint32_t o = live ? b_off[nt] : kOOB;
-        const i32x4 lo = bload16(b_rs, o, (uint32_t)ks * 128u);
-        const i32x4 hi = bload16(b_rs, o + 64u, (uint32_t)ks * 128u);
-        b.d[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        b.lo[nt] = bload16(b_rs, o, (uint32_t)ks * 128u);
+        b.hi[nt] = bload16(b_rs, o + 64u, (uint32_t)ks * 128u);
       }
     }
   };
 
   // ---------------------------------------------------------------- main loop
-  f32x4 acc[MT][kNT];
+  f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  BFrag<F> bq0, bq1, bq2;
-  i32x4 av0[TL::kAChunks], av1[TL::kAChunks];
-  uint32_t as0 = 0, as1 = 0;
+  // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed
+  BFrag<F, NT> bq[DEPTH];
+  i32x4 av[2][TL::kAChunks];
+  uint32_t as[2] = {0u, 0u};
   const int KS = p.ksteps;
-  load_b(bq0, 0);
-  load_b(bq1, 1);
-  load_b(bq2, 2);
-  load_a(av0, as0, 0);
-  load_a(av1, as1, 1);
-  store_a(av0, as0, 0);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load_b(bq[d], d);
+  load_a(av[0], as[0], 0);
+  load_a(av[1], as[1], 1);
+  store_a(av[0], as[0], 0);
 
   // One K-step: A(ks) is in LDS buffer ks&1; A(ks+1) is in flight in `an`;
-  // B(ks) is in `bq`.  Issues A(ks+2) into `ap` and B(ks+3) into `bq`.
-  auto step = [&](BFrag<F>& bq, i32x4 (&ap)[TL::kAChunks], uint32_t& sp, i32x4 (&an)[TL::kAChunks], uint32_t& sn,
-                  int ks) {
+  // B(ks) is in `bq_`.  Issues A(ks+2) into `ap` and B(ks+DEPTH) into `bq_`.
+  auto step = [&](BFrag<F, NT>& bq_, i32x4 (&ap)[TL::kAChunks], uint32_t& sp, i32x4 (&an)[TL::kAChunks],
+                  uint32_t& sn, int ks) {
     load_a(ap, sp, ks + 2);
     __syncthreads();
-    const uint8_t* abuf = a_lds + (ks & 1) * BM * kARowBytes;
-    float sbv0 = 1.f, sbv1 = 1.f;
+    const uint8_t* abuf = a_lds + (ks & 1) * TL::kARows * kARowBytes;
+    auto rd_lo = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * kARowBytes + 16 * g); };
+    auto rd_hi = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * kARowBytes + 64 + 16 * g); };
     if (F == Fmt::FP8) {
+      // Per 16-row slice and column tile: four 16x16x32 FP8 MFMAs (one K-step of
+      // 128) into a fresh partial, then acc += (sa * sb) * partial.  Each MFMA
+      // operand is half of one 16-byte load, so loads land where the MFMA reads.
       const int kc = min(ks, KS - 1);  // a step past the end multiplies zeros
-      sbv0 = b_sf_fp8[0][kc];
-      sbv1 = b_sf_fp8[1][kc];
-    }
+      const float sbv0 = sb_lds[kc], sbv1 = sb_lds[TL::kMaxKSteps + kc];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint8_t* ar = abuf + (mt * 16 + r16) * kARowBytes + 16 * g;
-      const i32x8 a8 = __builtin_shufflevector(*(const i32x4*)ar, *(const i32x4*)(ar + 64), 0, 1, 2, 3, 4, 5, 6, 7);
-      if (F == Fmt::FP8) {
-        const f32x4 sa = *(const f32x4*)(sa_lds + (ks & 1) * BM + mt * 16 + 4 * g);
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x4 alo = rd_lo(mt), ahi = rd_hi(mt);
+        const f32x4 sa = *(const f32x4*)(sa_lds + (ks & 1) * TL::kSA + mt * 16 + 4 * g);
         const f32x4 s0 = sa * sbv0, s1 = sa * sbv1;
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              a8, bq.d[nt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-          acc[mt][nt] += part * ((GATEUP && nt >= 2) ? s1 : s0);
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo64(alo), lo64(bq_.lo[nt]),
+                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi64(alo), hi64(bq_.lo[nt]), part, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo64(ahi), lo64(bq_.hi[nt]), part, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi64(ahi), hi64(bq_.hi[nt]), part, 0, 0, 0);
+          acc[mt][nt] += part * (sb_row(nt) ? s1 : s0);
         }
-      } else if (F == Fmt::BF16) {
-        const bf16x8 alo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a8, a8, 0, 1, 2, 3));
-        const bf16x8 ahi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a8, a8, 4, 5, 6, 7));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const bf16x8 blo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(bq.d[nt], bq.d[nt], 0, 1, 2, 3));
-          const bf16x8 bhi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(bq.d[nt], bq.d[nt], 4, 5, 6, 7));
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[mt][nt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x4 alo = rd_lo(mt), ahi = rd_hi(mt);
+        if (F == Fmt::BF16) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo),
+                                                                  __builtin_bit_cast(bf16x8, bq_.lo[nt]), acc[mt][nt],
+                                                                  0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi),
+                                                                  __builtin_bit_cast(bf16x8, bq_.hi[nt]), acc[mt][nt],
+                                                                  0, 0, 0);
+          }
+        } else {
+          const i32x8 a8 = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const uint32_t sw = sa_lds[(ks & 1) * TL::kSA + mt * 16 + r16];
+          const int sa = (int)((sw >> (8 * g)) & 0xFFu);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const i32x8 b8 = {bq_.lo[nt][0], bq_.lo[nt][1], bq_.lo[nt][2], bq_.lo[nt][3], 0, 0, 0, 0};
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[mt][nt], 0, 4, 0, sa, 0,
+                                                                           bq_.sc[nt]);
+          }
         }
-      } else {
-        const uint32_t sw = sa_lds[(ks & 1) * BM + mt * 16 + r16];
-        const int sa = (int)((sw >> (8 * g)) & 0xFFu);
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, bq.d[nt], acc[mt][nt], 0, 4, 0, sa, 0,
-                                                                         bq.sc[nt]);
       }
     }
-    load_b(bq, ks + 3);
+    // The refill of this ring slot must not be hoisted above the MFMAs that read
+    // its previous contents (the two values would then both be live): tie the
+    // load's scalar offset to the step's last accumulator update.
+    int ks_next = ks + DEPTH;
+    asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
+    load_b(bq_, ks_next);
     store_a(an, sn, (ks + 1) & 1);
   };
 
-  // unrolled by 6 so that both rings (3 weight buffers, 2 activation register sets) index statically
-  for (int ks = 0;; ks += 6) {
-    step(bq0, av0, as0, av1, as1, ks);
-    if (ks + 1 >= KS) break;
-    step(bq1, av1, as1, av0, as0, ks + 1);
-    if (ks + 2 >= KS) break;
-    step(bq2, av0, as0, av1, as1, ks + 2);
-    if (ks + 3 >= KS) break;
-    step(bq0, av1, as1, av0, as0, ks + 3);
-    if (ks + 4 >= KS) break;
-    step(bq1, av0, as0, av1, as1, ks + 4);
-    if (ks + 5 >= KS) break;
-    step(bq2, av1, as1, av0, as0, ks + 5);
-    if (ks + 6 >= KS) break;
+  // Unrolled so that both rings (DEPTH weight buffers, 2 activation register
+  // sets) index statically.  The trip count is rounded up to the unroll: the
+  // extra steps load zeros and add zeros, and the loop has no early exit (an exit
+  // per step would make the compiler drain every outstanding load there).
+  constexpr int UNROLL = (DEPTH % 2 == 0) ? DEPTH : 2 * DEPTH;
+  const int KS_PAD = (KS + UNROLL - 1) / UNROLL * UNROLL;
+  for (int ks0 = 0; ks0 < KS_PAD; ks0 += UNROLL) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      step(bq[u % DEPTH], av[u & 1], as[u & 1], av[(u + 1) & 1], as[(u + 1) & 1], ks0 + u);
   }
   __syncthreads();  // every wave is done with the A buffers; the output tile reuses them
 
   // ---------------------------------------------------------------- epilogue
   if (GATEUP) {
+    constexpr int NJ = NT / 2;  // gate (and up) column tiles per wave
     const float c = p.clamp;
-    float h[MT][2][4];
+    float h[MT][NJ][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[mt][j][i] = swiglu_clamped<FAST>(acc[mt][j][i], acc[mt][j + 2][i], c);
-    const int hcol0 = n_tile * 128 + wave * 32;  // first h column of this wave
-    const bool wave_valid = hcol0 < p.N;
+        for (int i = 0; i < 4; ++i) h[mt][j][i] = swiglu_clamped<FAST>(acc[mt][j][i], acc[mt][j + NJ][i], c);
     if (F == Fmt::BF16) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = mt * 16 + 4 * g + i;
-            *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * 32 + 16 * j + r16) * 2) =
-                f32_to_bf16_rne(h[mt][j][i]);
+            *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * HW + 16 * j + r16) * 2) = f32_to_bf16_rne(h[mt][j][i]);
           }
     } else {
-      // per-row amax over this wave's 32 columns (16 lanes x 2 column tiles)
-      float am[MT][4];
+      // per-row amax over this wave's HW columns (16 lanes x NJ column tiles), then
+      // over the waves sharing a requantisation block (all of them for FP8's 128
+      // columns, 32/HW of them for MX's 32)
+      constexpr int WPB = F == Fmt::FP8 ? WAVES : (32 / HW > 0 ? 32 / HW : 1);  // waves per block
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float m = fmaxf(fabsf(h[mt][0][i]), fabsf(h[mt][1][i]));
+          float m = fabsf(h[mt][0][i]);
+#pragma unroll
+          for (int j = 1; j < NJ; ++j) m = fmaxf(m, fabsf(h[mt][j][i]));
           m = fmaxf(m, __shfl_xor(m, 1));
           m = fmaxf(m, __shfl_xor(m, 2));
           m = fmaxf(m, __shfl_xor(m, 4));
           m = fmaxf(m, __shfl_xor(m, 8));
-          am[mt][i] = m;
+          if (r16 == 0) red_lds[wave * BM + mt * 16 + 4 * g + i] = m;
         }
+      __syncthreads();
+      const int w0 = wave - wave % WPB;  // first wave of this wave's block
+      const int hcol_blk = n_tile * kHCols + w0 * HW;
       float qscale[MT][4];
-      if (F == Fmt::FP8) {
-        // one scale per (row, 128 columns): combine the 4 waves' partial maxima
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (r16 == 0) red_lds[wave * BM + mt * 16 + 4 * g + i] = am[mt][i];
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * g + i;
-            float a = red_lds[r];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red_lds[w * BM + r]);
-            const float s = a > 0.f ? a / 448.0f : 1.0f;
-            qscale[mt][i] = 1.0f / s;
-            if (wave == 0 && r16 == 0 && r < rows)
-              ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + n_tile] = s;
-          }
-      } else {
-        // MX: one UE8M0 exponent per (row, 32 columns) = this wave's columns
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * g + i;
-            const int e = mx_exponent_for_amax(am[mt][i]);
-            qscale[mt][i] = exp2i(-e);
-            if (wave_valid && r16 == 0 && r < rows)
-              ((uint8_t*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + hcol0 / 32] = (uint8_t)(e + 127);
-          }
-      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 16 + 4 * g + i;
+          float a = red_lds[w0 * BM + r];
+#pragma unroll
+          for (int w = 1; w < WPB; ++w) a = fmaxf(a, red_lds[(w0 + w) * BM + r]);
+          const bool writer = wave == w0 && r16 == 0 && r < rows && hcol_blk < p.N;
+          if (F == Fmt::FP8) {
+            const float s = a > 0.f ? a / 448.0f : 1.0f;
+            qscale[mt][i] = 1.0f / s;
+            if (writer) ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + n_tile] = s;
+          } else {
+            const int e = mx_exponent_for_amax(a);
+            qscale[mt][i] = exp2i(-e);
+            if (writer) ((uint8_t*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + hcol_blk / 32] = (uint8_t)(e + 127);
+          }
+        }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = mt * 16 + 4 * g + i;
             const uint32_t q = f32x2_to_e4m3_sat(h[mt][j][i] * qscale[mt][i], 0.f);
-            out_lds[r * TL::kOutStride + wave * 32 + 16 * j + r16] = (uint8_t)(q & 0xFFu);
+            out_lds[r * TL::kOutStride + wave * HW + 16 * j + r16] = (uint8_t)(q & 0xFFu);
           }
     }
     __syncthreads();
@@ -429,10 +449,10 @@ __global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void
     constexpr int elem = F == Fmt::BF16 ? 2 : 1;
     for (int c = tid; c < BM * CPR; c += kThreads) {
       const int r = c / CPR, cc = c % CPR;
-      const int col = n_tile * 128 + cc * 16 / elem;
+      const int col = n_tile * kHCols + cc * 16 / elem;
       if (r < rows && col < p.N) {
-        *(i32x4*)((uint8_t*)p.C + (long long)(row0 + r) * p.c_row_bytes + (long long)n_tile * 128 * elem + cc * 16) =
-            *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
+        *(i32x4*)((uint8_t*)p.C + (long long)(row0 + r) * p.c_row_bytes + (long long)n_tile * kHCols * elem +
+                  cc * 16) = *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
       }
     }
   } else {
@@ -440,11 +460,11 @@ __global__ __launch_bounds__(kThreads, (BM == 64 && F != Fmt::FP8) ? 2 : 1) void
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = mt * 16 + 4 * g + i;
-          *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * kWRows + 16 * nt + r16) * 2) =
+          *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * 16 * NT + 16 * nt + r16) * 2) =
               f32_to_bf16_rne(acc[mt][nt][i]);
         }
     __syncthreads();
@@ -473,20 +493,29 @@ int ffn_max_m_tiles(int npairs, int E, int bm) {
   return (int)(((long long)npairs + act * (bm - 1)) / bm);
 }
 
-template <Fmt F, bool GATEUP, int BM>
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH>
 static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
   const int grid = gp.m_tiles_max * gp.n_tiles;
   if (grid <= 0) return;
   if (fast)
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, true>), dim3(grid), dim3(kThreads), 0, s, gp);
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, true>), dim3(grid), dim3(64 * WAVES), 0, s,
+                       gp);
   else
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, false>), dim3(grid), dim3(kThreads), 0, s, gp);
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, false>), dim3(grid), dim3(64 * WAVES), 0, s,
+                       gp);
+}
+
+// 8 waves x 32 weight rows; weight-ring depth per format and tile height, sized
+// to the registers of two waves per SIMD
+template <Fmt F, int BM>
+constexpr int ring_depth() {
+  return F == Fmt::FP8 ? (BM <= 96 ? 4 : 3) : F == Fmt::BF16 ? (BM <= 96 ? 8 : 5) : (BM <= 96 ? 8 : 6);
 }
 
 template <Fmt F, int BM>
 static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
-  if (stage != 2) launch_one<F, true, BM>(g1, fast, s);
-  if (stage != 1) launch_one<F, false, BM>(g2, fast, s);
+  if (stage != 2) launch_one<F, true, BM, 8, 2, ring_depth<F, BM>()>(g1, fast, s);
+  if (stage != 1) launch_one<F, false, BM, 8, 2, ring_depth<F, BM>()>(g2, fast, s);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
@@ -502,7 +531,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.E = a.E;
   g1.topk = a.topk;
   g1.m_tiles_max = ffn_max_m_tiles(npairs, a.E, a.bm);
-  g1.n_tiles = (a.I + 127) / 128;
+  g1.n_tiles = (a.I + kHCols - 1) / kHCols;
   g1.K = a.H;
   g1.ksteps = (a.H + elem_k - 1) / elem_k;
   g1.N = a.I;
@@ -548,15 +577,15 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   switch (a.fmt) {
     case Fmt::FP8:
       if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::FP8, 64>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::FP8, 96>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::BF16:
       if (a.bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::BF16, 64>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::BF16, 96>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::MX:
       if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::MX, 64>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::MX, 96>(g1, g2, a.fast, s, stage);
       break;
   }
   return hipGetLastError();

@@ -21,8 +21,8 @@ struct PlanPtrs {
 
 // Routing plan: one fused block up to this many pairs, else count/scan/scatter
 // over blocks of kPlanPairsPerBlock pairs.
-constexpr int kPlanFusedMaxPairs = 4096;
-constexpr int kPlanPairsPerBlock = 1024;
+constexpr int kPlanFusedMaxPairs = 8192;
+constexpr int kPlanPairsPerBlock = 4096;
 
 int plan_num_blocks(int npairs);
 size_t plan_workspace_bytes(int npairs, int E);

@@ -17,7 +17,7 @@
 
 namespace moe {
 
-constexpr int kPlanThreads = 256;  // 4 waves
+constexpr int kPlanThreads = 1024;  // 16 waves; also the largest expert count
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // ------------------------------------------------------------------ top-k
@@ -82,6 +82,8 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __r
 }
 
 // ------------------------------------------------------------------ plan pieces
+// Expert of pair p: its id if in [0, E), else -1 (a masked slot); ids other
+// than -1 outside [0, E) are counted as bad.
 template <typename IdxT>
 MOE_DEV int load_expert(const IdxT* ids, int p, int E, int* bad) {
   long long e = (long long)ids[p];
@@ -90,32 +92,20 @@ MOE_DEV int load_expert(const IdxT* ids, int p, int E, int* bad) {
   return -1;
 }
 
-// Exclusive scan of cnt[0..E) (LDS) by one block of kPlanThreads threads.
-// Writes out_start[0..E] (E+1 entries) to global and returns nothing; also
-// fills the active list.  cnt must be final; uses scratch LDS of kPlanWaves ints.
+// Exclusive scan of cnt[0..E) (LDS) by one block of kPlanThreads threads:
+// writes counts, E+1 start offsets, the active list (ascending, -1 padded) and
+// num_active; base_lds (if given) receives the start offsets.  wave_tot is LDS
+// scratch of 2*kPlanWaves ints.
 MOE_DEV void plan_scan_and_active(const int* cnt, int E, int* __restrict__ counts_out, int* __restrict__ start_out,
                                   int* __restrict__ ids_out, int* __restrict__ num_active_out, int* base_lds,
                                   int* wave_tot) {
-  // each thread owns up to 4 consecutive experts
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int per = (E + kPlanThreads - 1) / kPlanThreads;  // <= 4 for E <= 1024
-  const int e0 = tid * per;
-  int c[4] = {0, 0, 0, 0}, a[4] = {0, 0, 0, 0};
-  int csum = 0, asum = 0;
-  for (int i = 0; i < per; ++i) {
-    int e = e0 + i;
-    if (e < E) {
-      c[i] = cnt[e];
-      a[i] = c[i] > 0;
-    }
-    csum += c[i];
-    asum += a[i];
-  }
-  // inclusive wave scan of (csum, asum) packed: counts < 2^31, actives < 2^11
-  int cs = csum, as = asum;
+  const int c = tid < E ? cnt[tid] : 0;  // one expert per thread (E <= kPlanThreads)
+  const int a = c > 0;
+  int cs = c, as = a;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int oc = __shfl_up(cs, d), oa = __shfl_up(as, d);
+    const int oc = __shfl_up(cs, d), oa = __shfl_up(as, d);
     if (lane >= d) {
       cs += oc;
       as += oa;
@@ -126,77 +116,70 @@ MOE_DEV void plan_scan_and_active(const int* cnt, int E, int* __restrict__ count
     wave_tot[kPlanWaves + wave] = as;
   }
   __syncthreads();
-  int cb = 0, ab = 0;
-  for (int w = 0; w < wave; ++w) {
-    cb += wave_tot[w];
-    ab += wave_tot[kPlanWaves + w];
-  }
-  int run_c = cb + cs - csum, run_a = ab + as - asum;  // exclusive
-  for (int i = 0; i < per; ++i) {
-    int e = e0 + i;
-    if (e < E) {
-      counts_out[e] = c[i];
-      start_out[e] = run_c;
-      if (base_lds) base_lds[e] = run_c;
-      if (a[i]) ids_out[run_a] = e;
-      run_c += c[i];
-      run_a += a[i];
+  int cb = 0, ab = 0, ctot = 0, atot = 0;
+  for (int w = 0; w < kPlanWaves; ++w) {
+    if (w < wave) {
+      cb += wave_tot[w];
+      ab += wave_tot[kPlanWaves + w];
     }
+    ctot += wave_tot[w];
+    atot += wave_tot[kPlanWaves + w];
   }
-  if (tid == kPlanThreads - 1) {
-    start_out[E] = run_c;
-    *num_active_out = run_a;
+  const int run_c = cb + cs - c, run_a = ab + as - a;  // exclusive
+  if (tid < E) {
+    counts_out[tid] = c;
+    start_out[tid] = run_c;
+    if (base_lds) base_lds[tid] = run_c;
+    if (a) ids_out[run_a] = tid;
   }
+  if (tid == 0) {
+    start_out[E] = ctot;
+    *num_active_out = atot;
+  }
+  if (tid >= atot && tid < E) ids_out[tid] = -1;
   __syncthreads();
-  // pad the active list with -1
-  int nact = 0;
-  for (int w = 0; w < kPlanWaves; ++w) nact += wave_tot[kPlanWaves + w];
-  for (int e = nact + tid; e < E; e += kPlanThreads) ids_out[e] = -1;
 }
 
-// Stable scatter of pairs [begin, end) in chunks of kPlanThreads.  run[e] (LDS)
-// holds the next free row of expert e and is advanced.  wcnt is LDS scratch of
-// kPlanWaves * E ints.
-template <typename IdxT>
-MOE_DEV void plan_scatter(const IdxT* __restrict__ ids, int begin, int end, int E, int* run, int* wcnt,
+// Stable scatter of the pairs whose experts are in ex_lds[0..n) (pair index
+// p0 + i), in chunks of kPlanThreads.  run[e] (LDS) holds the next free row of
+// expert e and is advanced.  wcnt is LDS scratch of kPlanWaves * E bytes, zero
+// on entry and on exit.
+MOE_DEV void plan_scatter(const short* ex_lds, int p0, int n, int E, int* run, uint8_t* wcnt,
                           int* __restrict__ src_info, int* __restrict__ pair_row) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int ebits = 1;
   while ((1 << ebits) < E + 1) ++ebits;
-  for (int c0 = begin; c0 < end; c0 += kPlanThreads) {
-    const int p = c0 + tid;
-    int dummy = 0;
-    int e = p < end ? load_expert(ids, p, E, &dummy) : -1;
-    // lanes holding the same expert id: intersect ballots over the bits of (e + 1)
-    const int key = e + 1;  // 0 for masked / out of chunk
+  for (int c0 = 0; c0 < n; c0 += kPlanThreads) {
+    const int i = c0 + tid;
+    const int e = i < n ? (int)ex_lds[i] : -1;
+    // lanes holding the same expert: intersect ballots over the bits of (e + 1)
+    const int key = e + 1;  // 0 for a masked slot or past the end
     uint64_t match = ~0ull;
     for (int b = 0; b < ebits; ++b) {
-      uint64_t bal = __ballot((key >> b) & 1);
+      const uint64_t bal = __ballot((key >> b) & 1);
       match &= ((key >> b) & 1) ? bal : ~bal;
     }
     const int rank = __popcll(match & lt_mask);
-    const int total = __popcll(match);
     // the lowest lane of each group publishes the group's size for this wave
-    for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcnt[i] = 0;
-    __syncthreads();
-    if (e >= 0 && rank == 0) wcnt[wave * E + e] = total;
+    if (e >= 0 && rank == 0) wcnt[wave * E + e] = (uint8_t)__popcll(match);
     __syncthreads();
     if (e >= 0) {
       int off = run[e] + rank;
       for (int w = 0; w < wave; ++w) off += wcnt[w * E + e];
-      src_info[off] = p;
-      pair_row[p] = off;
-    } else if (p < end) {
-      pair_row[p] = -1;
+      src_info[off] = p0 + i;
+      pair_row[p0 + i] = off;
+    } else if (i < n) {
+      pair_row[p0 + i] = -1;
     }
     __syncthreads();
-    for (int ex = tid; ex < E; ex += kPlanThreads) {
-      int s = 0;
-      for (int w = 0; w < kPlanWaves; ++w) s += wcnt[w * E + ex];
-      run[ex] += s;
+    if (tid < E) {
+      int sum = 0;
+      for (int w = 0; w < kPlanWaves; ++w) sum += wcnt[w * E + tid];
+      run[tid] += sum;
     }
     __syncthreads();
+    if (e >= 0 && rank == 0) wcnt[wave * E + e] = 0;
   }
 }
 
@@ -204,18 +187,21 @@ MOE_DEV void plan_scatter(const IdxT* __restrict__ ids, int begin, int end, int 
 template <typename IdxT>
 __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(const IdxT* __restrict__ ids, int npairs, int E,
                                                                   PlanPtrs out) {
-  extern __shared__ int lds[];
-  int* cnt = lds;                    // [E]
-  int* run = lds + E;                // [E]
-  int* wcnt = lds + 2 * E;           // [kPlanWaves * E]
-  int* misc = lds + (2 + kPlanWaves) * E;  // [2*kPlanWaves + 1]
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  int* cnt = lds;                                      // [E]
+  int* run = lds + E;                                  // [E]
+  int* misc = lds + 2 * E;                             // [2*kPlanWaves + 1]
+  uint8_t* wcnt = (uint8_t*)(misc + 2 * kPlanWaves + 1);  // [kPlanWaves * E]
+  short* ex = (short*)(wcnt + ((kPlanWaves * E + 15) & ~15));  // [npairs]
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
+  for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcnt[i] = 0;
   if (tid == 0) misc[2 * kPlanWaves] = 0;
   __syncthreads();
   int bad = 0;
   for (int p = tid; p < npairs; p += kPlanThreads) {
-    int e = load_expert(ids, p, E, &bad);
+    const int e = load_expert(ids, p, E, &bad);
+    ex[p] = (short)e;
     if (e >= 0) atomicAdd(&cnt[e], 1);
   }
   if (bad) atomicAdd(&misc[2 * kPlanWaves], bad);
@@ -223,8 +209,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(const IdxT* __
   plan_scan_and_active(cnt, E, out.expert_counts, out.expert_start_indices, out.expert_ids, out.num_active, run,
                        misc);
   if (tid == 0) *out.status = misc[2 * kPlanWaves];
-  __syncthreads();
-  plan_scatter(ids, 0, npairs, E, run, wcnt, out.src_info, out.pair_row);
+  plan_scatter(ex, 0, npairs, E, run, wcnt, out.src_info, out.pair_row);
 }
 
 // ------------------------------------------------------------------ multi-block plan
@@ -233,7 +218,7 @@ template <typename IdxT>
 __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const IdxT* __restrict__ ids, int npairs, int E,
                                                                   int per_block, int* __restrict__ hist,
                                                                   int* __restrict__ bad_out) {
-  extern __shared__ int lds[];
+  extern __shared__ __attribute__((aligned(16))) int lds[];
   int* cnt = lds;
   const int tid = threadIdx.x, b = blockIdx.x;
   for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
@@ -242,7 +227,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const IdxT* __
   const int begin = b * per_block, end = min(npairs, begin + per_block);
   int bad = 0;
   for (int p = begin + tid; p < end; p += kPlanThreads) {
-    int e = load_expert(ids, p, E, &bad);
+    const int e = load_expert(ids, p, E, &bad);
     if (e >= 0) atomicAdd(&cnt[e], 1);
   }
   if (bad) atomicAdd(&lds[E], bad);
@@ -254,15 +239,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const IdxT* __
 // 2) one block: totals, prefix sums, active list, per-block bases (in place over hist)
 __global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(int nblocks, int E, int* __restrict__ hist,
                                                                  const int* __restrict__ bad_in, PlanPtrs out) {
-  extern __shared__ int lds[];
-  int* cnt = lds;                 // [E]
-  int* base = lds + E;            // [E]
-  int* misc = lds + 2 * E;        // [2*kPlanWaves + 1]
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  int* cnt = lds;           // [E]
+  int* base = lds + E;      // [E]
+  int* misc = lds + 2 * E;  // [2*kPlanWaves + 1]
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kPlanThreads) {
+  if (tid < E) {
     int s = 0;
-    for (int b = 0; b < nblocks; ++b) s += hist[(size_t)b * E + e];
-    cnt[e] = s;
+    for (int b = 0; b < nblocks; ++b) s += hist[(size_t)b * E + tid];
+    cnt[tid] = s;
   }
   if (tid == 0) {
     int s = 0;
@@ -273,12 +258,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(int nblocks, in
   plan_scan_and_active(cnt, E, out.expert_counts, out.expert_start_indices, out.expert_ids, out.num_active, base,
                        misc);
   if (tid == 0) *out.status = misc[2 * kPlanWaves];
-  __syncthreads();
-  for (int e = tid; e < E; e += kPlanThreads) {
-    int run = base[e];
+  if (tid < E) {
+    int run = base[tid];
     for (int b = 0; b < nblocks; ++b) {
-      int c = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;
+      const int c = hist[(size_t)b * E + tid];
+      hist[(size_t)b * E + tid] = run;
       run += c;
     }
   }
@@ -289,14 +273,18 @@ template <typename IdxT>
 __global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(const IdxT* __restrict__ ids, int npairs, int E,
                                                                     int per_block, const int* __restrict__ bases,
                                                                     PlanPtrs out) {
-  extern __shared__ int lds[];
-  int* run = lds;          // [E]
-  int* wcnt = lds + E;     // [kPlanWaves * E]
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  int* run = lds;                        // [E]
+  uint8_t* wcnt = (uint8_t*)(lds + E);   // [kPlanWaves * E]
+  short* ex = (short*)(wcnt + ((kPlanWaves * E + 15) & ~15));  // [per_block]
   const int tid = threadIdx.x, b = blockIdx.x;
   for (int e = tid; e < E; e += kPlanThreads) run[e] = bases[(size_t)b * E + e];
-  __syncthreads();
+  for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcnt[i] = 0;
   const int begin = b * per_block, end = min(npairs, begin + per_block);
-  plan_scatter(ids, begin, end, E, run, wcnt, out.src_info, out.pair_row);
+  int dummy = 0;
+  for (int p = begin + tid; p < end; p += kPlanThreads) ex[p - begin] = (short)load_expert(ids, p, E, &dummy);
+  __syncthreads();
+  plan_scatter(ex, begin, end - begin, E, run, wcnt, out.src_info, out.pair_row);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -333,11 +321,13 @@ int plan_num_blocks(int npairs) {
   return (npairs + kPlanPairsPerBlock - 1) / kPlanPairsPerBlock;
 }
 
+static size_t wcnt_bytes(int E) { return (size_t)((kPlanWaves * E + 15) & ~15); }
+
 template <typename IdxT>
 static hipError_t launch_plan_t(const IdxT* ids, int npairs, int E, const PlanPtrs& out, int* ws, hipStream_t s) {
   const int nb = plan_num_blocks(npairs);
   if (nb <= 1) {
-    size_t lds = (size_t)((2 + kPlanWaves) * E + 2 * kPlanWaves + 1) * sizeof(int);
+    const size_t lds = (2 * (size_t)E + 2 * kPlanWaves + 1) * sizeof(int) + wcnt_bytes(E) + (size_t)npairs * 2;
     hipLaunchKernelGGL(plan_fused_kernel<IdxT>, dim3(1), dim3(kPlanThreads), lds, s, ids, npairs, E, out);
     return hipGetLastError();
   }
@@ -348,8 +338,8 @@ static hipError_t launch_plan_t(const IdxT* ids, int npairs, int E, const PlanPt
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), (2 * E + 2 * kPlanWaves + 1) * sizeof(int), s,
                      nb, E, hist, (const int*)bad, out);
   hipLaunchKernelGGL(plan_scatter_kernel<IdxT>, dim3(nb), dim3(kPlanThreads),
-                     (size_t)(1 + kPlanWaves) * E * sizeof(int), s, ids, npairs, E, kPlanPairsPerBlock,
-                     (const int*)hist, out);
+                     E * sizeof(int) + wcnt_bytes(E) + (size_t)kPlanPairsPerBlock * 2, s, ids, npairs, E,
+                     kPlanPairsPerBlock, (const int*)hist, out);
   return hipGetLastError();
 }
 

@@ -67,6 +67,12 @@ def _cfg(**kw):
     ({"format": 2, "hidden": 2880 + 16, "intermediate_hidden": 2880}, 1),
     ({"route_mode": 1, "num_experts": 600, "num_topk": 4}, 2),   # FromLogits over > 512 experts
     ({"max_num_tokens": -1}, 1),
+    ({"hidden": 32768 + 128}, 2),                # FP8 weight scales of > 256 K-steps
+    ({"intermediate_hidden": 32768 + 128}, 2),
+    ({"hidden": 32768, "intermediate_hidden": 32768, "max_num_tokens": 16}, 2),  # 2 GiB of W13 per expert
+    ({"max_num_tokens": 300000, "num_topk": 1, "num_experts": 8}, 2),  # x of 300000 x 7168 bytes
+    ({"format": 1, "hidden": 4096, "intermediate_hidden": 14336, "num_experts": 8, "num_topk": 2,
+      "max_num_tokens": 40000}, 2),              # bf16 intermediate of 80000 x 14336 x 2 bytes
 ])
 def test_create_validation(kw, expect):
     lib = _lib()
