@@ -17,13 +17,14 @@
 // lane offset and the K-step offset in a scalar register; a lane offset past
 // the end of the resource reads zeros, which masks rows and columns outside
 // the problem.
-// MFMA per format (16x16 output tiles, 4 f32 per lane: column l%16, rows 4*(l/16)+i):
-//   FP8 block-128: 4 x v_mfma_f32_16x16x32_fp8_fp8 per K-step of 128 into a
-//                  partial, then acc += (sa[row] * sb) * partial with the fp32
-//                  block scales of the DeepSeek FP8 encoding.
+// MFMA per format, weights as the first operand and activations as the second
+// (16x16 output tiles, 4 f32 per lane: token l%16, weight rows 4*(l/16)+i):
+//   FP8 block-128: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales per
+//                  K-step of 128 into a partial, then acc += (sa[token] * sb) *
+//                  partial with the fp32 block scales of the DeepSeek FP8 encoding.
 //   BF16:          2 x v_mfma_f32_16x16x32_bf16 per K-step of 64.
-//   MX (W4A8):     v_mfma_scale_f32_16x16x128_f8f6f4, A = E4M3 + UE8M0,
-//                  B = E2M1 + UE8M0, the block scales applied by the hardware.
+//   MX (W4A8):     v_mfma_scale_f32_16x16x128_f8f6f4, weights E2M1 + UE8M0,
+//                  activations E4M3 + UE8M0, the block scales applied by the hardware.
 // Operand lane layout (lane l, g = l/16): an FP8/BF16 row segment of 128 bytes
 // is fed as bytes [16g, 16g+16) and [64+16g, 64+16g+16); an E2M1 segment of
 // 64 bytes as bytes [16g, 16g+16); the scale byte of lane l belongs to
@@ -89,8 +90,6 @@ struct BFrag {
   int sc[NT];
 };
 
-MOE_DEV long long lo64(i32x4 v) { return (long long)(((unsigned long long)(uint32_t)v[1] << 32) | (uint32_t)v[0]); }
-MOE_DEV long long hi64(i32x4 v) { return (long long)(((unsigned long long)(uint32_t)v[3] << 32) | (uint32_t)v[2]); }
 
 template <Fmt F, bool GATEUP, int BM, int WAVES>
 struct Tile {
@@ -297,29 +296,29 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
     load_a(ap, sp, ks + 2);
     __syncthreads();
     const uint8_t* abuf = a_lds + (ks & 1) * TL::kARows * kARowBytes;
+    const uint32_t* sbuf = sa_lds + (ks & 1) * TL::kSA;
+    // activation fragment of token slice mt: token row mt*16 + r16, bytes [16g, 16g+16) and [64+16g, 64+16g+16)
     auto rd_lo = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * kARowBytes + 16 * g); };
     auto rd_hi = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * kARowBytes + 64 + 16 * g); };
+    // The weights are the MFMA's first operand and the activations its second, so
+    // a lane's outputs are 4 weight rows (16*nt + 4g + i) of one token (mt*16 + r16):
+    // the activation scale of a lane is one value per token slice.
     if (F == Fmt::FP8) {
-      // Per 16-row slice and column tile: four 16x16x32 FP8 MFMAs (one K-step of
-      // 128) into a fresh partial, then acc += (sa * sb) * partial.  Each MFMA
-      // operand is half of one 16-byte load, so loads land where the MFMA reads.
+      // one 16x16x128 FP8 MFMA per K-step (unit hardware scales) into a fresh
+      // partial, then acc += (sa[token] * sb[block]) * partial
       const int kc = min(ks, KS - 1);  // a step past the end multiplies zeros
       const float sbv0 = sb_lds[kc], sbv1 = sb_lds[TL::kMaxKSteps + kc];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const i32x4 alo = rd_lo(mt), ahi = rd_hi(mt);
-        const f32x4 sa = *(const f32x4*)(sa_lds + (ks & 1) * TL::kSA + mt * 16 + 4 * g);
-        const f32x4 s0 = sa * sbv0, s1 = sa * sbv1;
+        const i32x8 a8 = __builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7);
+        const float sa = __builtin_bit_cast(float, sbuf[mt * 16 + r16]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo64(alo), lo64(bq_.lo[nt]),
-                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi64(alo), hi64(bq_.lo[nt]), part, 0, 0, 0);
-          part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo64(ahi), lo64(bq_.hi[nt]), part, 0, 0, 0);
-          part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi64(ahi), hi64(bq_.hi[nt]), part, 0, 0, 0);
-          acc[mt][nt] += part * (sb_row(nt) ? s1 : s0);
+          const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                              0, 127, 0, 127);
+          acc[mt][nt] += part * (sa * (sb_row(nt) ? sbv1 : sbv0));
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
@@ -328,22 +327,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
         if (F == Fmt::BF16) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo),
-                                                                  __builtin_bit_cast(bf16x8, bq_.lo[nt]), acc[mt][nt],
-                                                                  0, 0, 0);
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi),
-                                                                  __builtin_bit_cast(bf16x8, bq_.hi[nt]), acc[mt][nt],
-                                                                  0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq_.lo[nt]),
+                                                                  __builtin_bit_cast(bf16x8, alo), acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq_.hi[nt]),
+                                                                  __builtin_bit_cast(bf16x8, ahi), acc[mt][nt], 0, 0, 0);
           }
         } else {
+          // weights E2M1 (first operand, format 4), activations E4M3 (format 0);
+          // each lane's scale byte: its row (weight row / token) in K-block g
           const i32x8 a8 = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const uint32_t sw = sa_lds[(ks & 1) * TL::kSA + mt * 16 + r16];
-          const int sa = (int)((sw >> (8 * g)) & 0xFFu);
+          const int sa = (int)((sbuf[mt * 16 + r16] >> (8 * g)) & 0xFFu);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             const i32x8 b8 = {bq_.lo[nt][0], bq_.lo[nt][1], bq_.lo[nt][2], bq_.lo[nt][3], 0, 0, 0, 0};
-            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[mt][nt], 0, 4, 0, sa, 0,
-                                                                           bq_.sc[nt]);
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[mt][nt], 4, 0, 0, bq_.sc[nt], 0,
+                                                                           sa);
           }
         }
       }
@@ -371,6 +369,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
   __syncthreads();  // every wave is done with the A buffers; the output tile reuses them
 
   // ---------------------------------------------------------------- epilogue
+  // Lane (r16, g) holds, for token slice mt, token row mt*16 + r16 and the wave's
+  // weight rows 16*nt + 4g + i (i < 4): four consecutive output columns.
   if (GATEUP) {
     constexpr int NJ = NT / 2;  // gate (and up) column tiles per wave
     const float c = p.clamp;
@@ -385,63 +385,55 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * g + i;
-            *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * HW + 16 * j + r16) * 2) = f32_to_bf16_rne(h[mt][j][i]);
-          }
+        for (int j = 0; j < NJ; ++j) {
+          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(h[mt][j][0]) | ((uint32_t)f32_to_bf16_rne(h[mt][j][1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(h[mt][j][2]) | ((uint32_t)f32_to_bf16_rne(h[mt][j][3]) << 16);
+          *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * HW + 16 * j + 4 * g) * 2) = uint2{w0, w1};
+        }
     } else {
-      // per-row amax over this wave's HW columns (16 lanes x NJ column tiles), then
-      // over the waves sharing a requantisation block (all of them for FP8's 128
-      // columns, 32/HW of them for MX's 32)
+      // per-row amax over this wave's HW columns (4 values x NJ tiles in a lane,
+      // then the 4 lanes g of the row), then over the waves sharing a
+      // requantisation block (all of them for FP8's 128 columns, 32/HW of them
+      // for MX's 32)
       constexpr int WPB = F == Fmt::FP8 ? WAVES : (32 / HW > 0 ? 32 / HW : 1);  // waves per block
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float m = fabsf(h[mt][0][i]);
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-          for (int j = 1; j < NJ; ++j) m = fmaxf(m, fabsf(h[mt][j][i]));
-          m = fmaxf(m, __shfl_xor(m, 1));
-          m = fmaxf(m, __shfl_xor(m, 2));
-          m = fmaxf(m, __shfl_xor(m, 4));
-          m = fmaxf(m, __shfl_xor(m, 8));
-          if (r16 == 0) red_lds[wave * BM + mt * 16 + 4 * g + i] = m;
-        }
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(h[mt][j][i]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (g == 0) red_lds[wave * BM + mt * 16 + r16] = m;
+      }
       __syncthreads();
       const int w0 = wave - wave % WPB;  // first wave of this wave's block
       const int hcol_blk = n_tile * kHCols + w0 * HW;
-      float qscale[MT][4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = mt * 16 + r16;
+        float a = red_lds[w0 * BM + r];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + 4 * g + i;
-          float a = red_lds[w0 * BM + r];
-#pragma unroll
-          for (int w = 1; w < WPB; ++w) a = fmaxf(a, red_lds[(w0 + w) * BM + r]);
-          const bool writer = wave == w0 && r16 == 0 && r < rows && hcol_blk < p.N;
-          if (F == Fmt::FP8) {
-            const float s = a > 0.f ? a / 448.0f : 1.0f;
-            qscale[mt][i] = 1.0f / s;
-            if (writer) ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + n_tile] = s;
-          } else {
-            const int e = mx_exponent_for_amax(a);
-            qscale[mt][i] = exp2i(-e);
-            if (writer) ((uint8_t*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + hcol_blk / 32] = (uint8_t)(e + 127);
-          }
+        for (int w = 1; w < WPB; ++w) a = fmaxf(a, red_lds[(w0 + w) * BM + r]);
+        const bool writer = wave == w0 && g == 0 && r < rows && hcol_blk < p.N;
+        float q;
+        if (F == Fmt::FP8) {
+          const float sc = a > 0.f ? a / 448.0f : 1.0f;
+          q = 1.0f / sc;
+          if (writer) ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + n_tile] = sc;
+        } else {
+          const int e = mx_exponent_for_amax(a);
+          q = exp2i(-e);
+          if (writer) ((uint8_t*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + hcol_blk / 32] = (uint8_t)(e + 127);
         }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * g + i;
-            const uint32_t q = f32x2_to_e4m3_sat(h[mt][j][i] * qscale[mt][i], 0.f);
-            out_lds[r * TL::kOutStride + wave * HW + 16 * j + r16] = (uint8_t)(q & 0xFFu);
-          }
+        for (int j = 0; j < NJ; ++j) {
+          const uint32_t lo = f32x2_to_e4m3_sat(h[mt][j][0] * q, h[mt][j][1] * q);
+          const uint32_t hi = f32x2_to_e4m3_sat(h[mt][j][2] * q, h[mt][j][3] * q);
+          *(uint32_t*)(out_lds + r * TL::kOutStride + wave * HW + 16 * j + 4 * g) = lo | (hi << 16);
+        }
+      }
     }
     __syncthreads();
     // coalesced copy of the tile's h rows: 16-byte chunks
@@ -460,13 +452,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + 4 * g + i;
-          *(uint16_t*)(out_lds + r * TL::kOutStride + (wave * 16 * NT + 16 * nt + r16) * 2) =
-              f32_to_bf16_rne(acc[mt][nt][i]);
-        }
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][0]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][3]) << 16);
+        *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * 16 * NT + 16 * nt + 4 * g) * 2) = uint2{w0, w1};
+      }
     __syncthreads();
     constexpr int CPR = 512 / 16;
     for (int c = tid; c < BM * CPR; c += kThreads) {
@@ -507,15 +497,16 @@ static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
 
 // 8 waves x 32 weight rows; weight-ring depth per format and tile height, sized
 // to the registers of two waves per SIMD
-template <Fmt F, int BM>
+// (measured on the decode and prefill shapes)
+template <Fmt F, bool GATEUP, int BM>
 constexpr int ring_depth() {
-  return F == Fmt::FP8 ? (BM <= 96 ? 4 : 3) : F == Fmt::BF16 ? (BM <= 96 ? 8 : 5) : (BM <= 96 ? 8 : 6);
+  return F == Fmt::FP8 ? (BM <= 96 || !GATEUP ? 2 : 3) : F == Fmt::BF16 ? (BM <= 96 ? 8 : 5) : (BM <= 96 ? 8 : 6);
 }
 
 template <Fmt F, int BM>
 static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
-  if (stage != 2) launch_one<F, true, BM, 8, 2, ring_depth<F, BM>()>(g1, fast, s);
-  if (stage != 1) launch_one<F, false, BM, 8, 2, ring_depth<F, BM>()>(g2, fast, s);
+  if (stage != 2) launch_one<F, true, BM, 8, 2, ring_depth<F, true, BM>()>(g1, fast, s);
+  if (stage != 1) launch_one<F, false, BM, 8, 2, ring_depth<F, false, BM>()>(g2, fast, s);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
