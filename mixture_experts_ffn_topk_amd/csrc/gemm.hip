@@ -36,8 +36,12 @@ namespace moe {
 
 constexpr int kBRows = 256;      // weight rows per workgroup tile (WAVES * 16 * NT)
 constexpr int kHCols = 128;      // gate_up: h columns per workgroup tile (one FP8 requant block)
-constexpr int kARowBytes = 144;  // 128-byte K-step segment + 16 bytes of bank padding
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
+
+// kOOB if dead, else 0: OR-ed into a lane offset below 2^31 it turns the load
+// into one that reads zeros, without a branch or a select (a uniform condition
+// would otherwise become a branch around the load)
+MOE_DEV uint32_t oob_if(bool dead) { return (uint32_t)dead << 31; }
 
 struct GemmParams {
   const int* start;     // expert_start_indices [E+1]
@@ -73,6 +77,9 @@ MOE_DEV i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
 MOE_DEV int xcd_remap(int bid, int G) {
   // Work-groups are dealt round-robin over the 8 XCDs; give each XCD a
   // contiguous range of logical tiles so neighbours share its L2.
@@ -91,37 +98,38 @@ struct BFrag {
 };
 
 
-template <Fmt F, bool GATEUP, int BM, int WAVES>
+template <Fmt F, bool GATEUP, int BM, int WAVES, int KSG>
 struct Tile {
   static constexpr int kThreads = 64 * WAVES;
   static constexpr int MT = BM / 16;
-  static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte chunks of the A tile per thread
+  static constexpr int kAStride = 128 * KSG + 16;  // LDS bytes per A row: KSG K-steps + bank padding
+  static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
   // A buffer rows: BM rounded up so that every thread stores every chunk it loads
   // (chunks past BM rows are zeros landing in spare rows): no divergent stores in the loop
   static constexpr int kARows = kAChunks * kThreads / 8;
   static constexpr int kOutRowBytes = GATEUP ? (F == Fmt::BF16 ? 256 : 128) : 512;
   static constexpr int kOutStride = kOutRowBytes + 16;
-  static constexpr int kABytes = 2 * kARows * kARowBytes;
+  static constexpr int kABytes = 2 * kARows * kAStride;
   static constexpr int kOutBytes = BM * kOutStride;
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
   static constexpr int kSA = kThreads > BM ? kThreads : BM;  // A-scale slots per buffer (one per thread)
   static constexpr int kMaxKSteps = 256;  // FP8 weight scales of up to 256 K-steps staged in LDS
-  static constexpr int kLds = kUnion + 2 * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? 2 * kMaxKSteps * 4 : 0);
+  static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? 2 * kMaxKSteps * 4 : 0);
 };
 
-template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, bool FAST>
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, bool FAST>
 __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
   static_assert(WAVES * 16 * NT == kBRows, "a workgroup tile covers 256 weight rows");
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
-  using TL = Tile<F, GATEUP, BM, WAVES>;
+  using TL = Tile<F, GATEUP, BM, WAVES, KSG>;
   constexpr int MT = TL::MT;
   constexpr int kThreads = TL::kThreads;
   constexpr int HW = 8 * NT;  // gate_up: h columns per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kLds];
-  uint8_t* a_lds = lds;                                          // [2][kARows][144]
+  uint8_t* a_lds = lds;                                          // [2][kARows][kAStride]
   uint8_t* out_lds = lds;                                        // aliases a_lds after the K loop
-  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [2][kSA] (fp32 bits or 4 UE8M0 bytes)
-  float* red_lds = (float*)(lds + TL::kUnion + 2 * TL::kSA * 4);  // [WAVES][BM]
+  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [2][KSG][kSA] (fp32 bits or 4 UE8M0 bytes)
+  float* red_lds = (float*)(lds + TL::kUnion + 2 * KSG * TL::kSA * 4);  // [WAVES][BM]
   float* sb_lds = red_lds + WAVES * BM;                      // FP8: [2][kMaxKSteps] weight scales
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -130,12 +138,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int n_tile = L / p.m_tiles_max;
   const int m_tile = L - n_tile * p.m_tiles_max;
-  int expert = -1, tile_in_e = 0;
+  int expert = -1, tile_in_e = 0, e_start = 0, e_count = 0;
   {
     int base = 0;
     for (int e0 = 0; e0 < p.E; e0 += 64) {
       const int e = e0 + lane;
-      const int cnt = e < p.E ? p.start[e + 1] - p.start[e] : 0;
+      const int st_e = e < p.E ? p.start[e] : 0;
+      const int cnt = e < p.E ? p.start[e + 1] - st_e : 0;
       const int tiles = (cnt + BM - 1) / BM;
       int incl = tiles;
 #pragma unroll
@@ -150,6 +159,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
         const int src = __ffsll((unsigned long long)bal) - 1;
         expert = e0 + src;
         tile_in_e = m_tile - base - __shfl(excl, src);
+        e_start = __shfl(st_e, src);
+        e_count = __shfl(cnt, src);
         break;
       }
       base += __shfl(incl, 63);
@@ -158,64 +169,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
   expert = __builtin_amdgcn_readfirstlane(expert);
   tile_in_e = __builtin_amdgcn_readfirstlane(tile_in_e);
   if (expert < 0) return;  // beyond the real tile count (grid is sized for the worst case)
-  const int row0 = p.start[expert] + tile_in_e * BM;
-  const int rows = min(BM, p.start[expert + 1] - row0);
-
-  // ---------------------------------------------------------------- A (activation) addressing
-  // Thread tid loads 16-byte chunks c = tid + threads*i of the BM x 128-byte tile: row c/8, chunk c%8.
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
-  uint32_t a_off[TL::kAChunks];
-#pragma unroll
-  for (int i = 0; i < TL::kAChunks; ++i) {
-    const int c = tid + kThreads * i;
-    const int r = c >> 3;
-    if (r < rows) {
-      const int grow = row0 + r;
-      const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
-      a_off[i] = arow * p.a_row_bytes + (uint32_t)(c & 7) * 16u;
-    } else {
-      a_off[i] = kOOB;
-    }
-  }
-  // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step)
-  const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
-  uint32_t asf_off = kOOB;  // threads past the tile's rows load zeros
-  if (F != Fmt::BF16 && tid < rows) {
-    const int grow = row0 + tid;
-    const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
-    asf_off = arow * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u);
-  }
-
-  // Loads past the last K-step read zeros (no branch, so the register rings stay static).
-  auto load_a = [&](i32x4 (&v)[TL::kAChunks], uint32_t& s, int ks) {
-    const bool live = ks < p.ksteps;
-#pragma unroll
-    for (int i = 0; i < TL::kAChunks; ++i) {
-      uint32_t o = live ? a_off[i] : kOOB;
-      if (F == Fmt::MX && ks * 128 + (((tid + kThreads * i) & 7) * 16) >= p.K) o = kOOB;  // K tail
-      v[i] = bload16(a_rs, o, (uint32_t)ks * 128u);
-    }
-    if (F == Fmt::FP8) {
-      s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, live ? asf_off : kOOB, (uint32_t)ks * 4u, 0);
-    } else if (F == Fmt::MX) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t o = (ks * 4 + j < p.a_sf_row) ? asf_off + (uint32_t)j : kOOB;
-        w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, o, (uint32_t)ks * 4u, 0) << (8 * j);
-      }
-      s = w;
-    }
-  };
-  auto store_a = [&](const i32x4 (&v)[TL::kAChunks], uint32_t s, int buf) {
-    uint8_t* base = a_lds + buf * TL::kARows * kARowBytes;
-#pragma unroll
-    for (int i = 0; i < TL::kAChunks; ++i) {
-      const int c = tid + kThreads * i;
-      *(i32x4*)(base + (c >> 3) * kARowBytes + (c & 7) * 16) = v[i];
-    }
-    if (F != Fmt::BF16) sa_lds[buf * TL::kSA + tid] = s;
-  };
+  const int row0 = __builtin_amdgcn_readfirstlane(e_start) + tile_in_e * BM;
+  const int rows = min(BM, __builtin_amdgcn_readfirstlane(e_count) - tile_in_e * BM);
 
   // ---------------------------------------------------------------- B (weight) addressing
   const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + (size_t)expert * p.b_expert_bytes, p.b_expert_bytes);
@@ -256,20 +211,29 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
     return ((wave * 16 * NT + 16 * nt) % 256) >= 128 ? 1 : 0;
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
-    const bool live = ks < p.ksteps;
+    const uint32_t dead = oob_if(ks >= p.ksteps);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if (F == Fmt::MX) {
-        const bool tail = ks * 128 + 32 * g >= p.K;  // also true past the last K-step
-        b.lo[nt] = bload16(b_rs, tail ? kOOB : b_off[nt], (uint32_t)ks * 64u);
-        b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, tail ? kOOB : bsc_off[nt], (uint32_t)ks * 4u, 0);
+        const uint32_t tail = oob_if(ks * 128 + 32 * g >= p.K);  // also set past the last K-step
+        b.lo[nt] = bload16(b_rs, b_off[nt] | tail, (uint32_t)ks * 64u);
+        b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, bsc_off[nt] | tail, (uint32_t)ks * 4u, 0);
       } else {
-        const uint32_t o = live ? b_off[nt] : kOOB;
+        const uint32_t o = b_off[nt] | dead;
         b.lo[nt] = bload16(b_rs, o, (uint32_t)ks * 128u);
         b.hi[nt] = bload16(b_rs, o + 64u, (uint32_t)ks * 128u);
       }
     }
   };
+
+  // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed.
+  // Issued first, before the activation rows' addresses are known.
+  const int KS = p.ksteps;
+  BFrag<F, NT> bq[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load_b(bq[d], d);
+  // down: the pair slot of each tile row, for the epilogue's scatter (loaded early)
+  const int pair_of_row = (!GATEUP && tid < rows) ? p.src_info[row0 + tid] : 0;
 
   // ---------------------------------------------------------------- main loop
   f32x4 acc[MT][NT];
@@ -278,28 +242,90 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed
-  BFrag<F, NT> bq[DEPTH];
-  i32x4 av[2][TL::kAChunks];
-  uint32_t as[2] = {0u, 0u};
-  const int KS = p.ksteps;
+  // ---------------------------------------------------------------- A (activation) addressing
+  // A is staged KSG K-steps at a time.  For each K-step of a stage, thread tid
+  // loads 16-byte chunks c = tid + threads*i of the BM x 128-byte tile: row c/8, chunk c%8.
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
+  uint32_t a_off[TL::kAChunks];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_b(bq[d], d);
+  for (int i = 0; i < TL::kAChunks; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 3;
+    if (r < rows) {
+      const int grow = row0 + r;
+      const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
+      a_off[i] = arow * p.a_row_bytes + (uint32_t)(c & 7) * 16u;
+    } else {
+      a_off[i] = kOOB;
+    }
+  }
+  // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step)
+  const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
+  uint32_t asf_off = kOOB;  // threads past the tile's rows load zeros
+  if (F != Fmt::BF16 && tid < rows) {
+    const int grow = row0 + tid;
+    const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
+    asf_off = arow * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u);
+  }
+
+  // Loads past the last K-step read zeros (no branch, so the register rings stay static).
+  auto load_a = [&](i32x4 (&v)[KSG][TL::kAChunks], uint32_t (&s)[KSG], int st) {
+#pragma unroll
+    for (int u = 0; u < KSG; ++u) {
+      const int ks = st * KSG + u;
+      const uint32_t dead = oob_if(ks >= p.ksteps);
+#pragma unroll
+      for (int i = 0; i < TL::kAChunks; ++i) {
+        uint32_t o = a_off[i] | dead;
+        if (F == Fmt::MX) o |= oob_if(ks * 128 + (((tid + kThreads * i) & 7) * 16) >= p.K);  // K tail
+        v[u][i] = bload16(a_rs, o, (uint32_t)ks * 128u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KSG; ++u) {
+      const int ks = st * KSG + u;
+      if (F == Fmt::FP8) {
+        s[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, (asf_off + 4u * u) | oob_if(ks >= p.ksteps),
+                                                              (uint32_t)st * (KSG * 4u), 0);
+      } else if (F == Fmt::MX) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t o = (asf_off + (uint32_t)(4 * u + j)) | oob_if(ks * 4 + j >= p.a_sf_row);
+          w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, o, (uint32_t)st * (KSG * 4u), 0) << (8 * j);
+        }
+        s[u] = w;
+      }
+    }
+  };
+  auto store_a = [&](const i32x4 (&v)[KSG][TL::kAChunks], const uint32_t (&s)[KSG], int buf) {
+    uint8_t* base = a_lds + buf * TL::kARows * TL::kAStride;
+#pragma unroll
+    for (int u = 0; u < KSG; ++u)
+#pragma unroll
+      for (int i = 0; i < TL::kAChunks; ++i) {
+        const int c = tid + kThreads * i;
+        *(i32x4*)(base + (c >> 3) * TL::kAStride + u * 128 + (c & 7) * 16) = v[u][i];
+      }
+    if (F != Fmt::BF16) {
+#pragma unroll
+      for (int u = 0; u < KSG; ++u) sa_lds[(buf * KSG + u) * TL::kSA + tid] = s[u];
+    }
+  };
+
+  i32x4 av[2][KSG][TL::kAChunks];
+  uint32_t as[2][KSG] = {};
   load_a(av[0], as[0], 0);
   load_a(av[1], as[1], 1);
   store_a(av[0], as[0], 0);
 
-  // One K-step: A(ks) is in LDS buffer ks&1; A(ks+1) is in flight in `an`;
-  // B(ks) is in `bq_`.  Issues A(ks+2) into `ap` and B(ks+DEPTH) into `bq_`.
-  auto step = [&](BFrag<F, NT>& bq_, i32x4 (&ap)[TL::kAChunks], uint32_t& sp, i32x4 (&an)[TL::kAChunks],
-                  uint32_t& sn, int ks) {
-    load_a(ap, sp, ks + 2);
-    __syncthreads();
-    const uint8_t* abuf = a_lds + (ks & 1) * TL::kARows * kARowBytes;
-    const uint32_t* sbuf = sa_lds + (ks & 1) * TL::kSA;
+  // One K-step on the staged A of LDS buffer `buf` (K-step u of the stage) and B(ks) in `bq_`.
+  auto kstep = [&](const BFrag<F, NT>& bq_, int buf, int u, int ks) {
+    const uint8_t* abuf = a_lds + buf * TL::kARows * TL::kAStride + u * 128;
+    const uint32_t* sbuf = sa_lds + (buf * KSG + u) * TL::kSA;
     // activation fragment of token slice mt: token row mt*16 + r16, bytes [16g, 16g+16) and [64+16g, 64+16g+16)
-    auto rd_lo = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * kARowBytes + 16 * g); };
-    auto rd_hi = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * kARowBytes + 64 + 16 * g); };
+    auto rd_lo = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * TL::kAStride + 16 * g); };
+    auto rd_hi = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * TL::kAStride + 64 + 16 * g); };
     // The weights are the MFMA's first operand and the activations its second, so
     // a lane's outputs are 4 weight rows (16*nt + 4g + i) of one token (mt*16 + r16):
     // the activation scale of a lane is one value per token slice.
@@ -310,6 +336,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
       const float sbv0 = sb_lds[kc], sbv1 = sb_lds[TL::kMaxKSteps + kc];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        if (mt * 16 >= rows) break;  // wave-uniform: no token rows left in this slice
         const i32x8 a8 = __builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7);
         const float sa = __builtin_bit_cast(float, sbuf[mt * 16 + r16]);
 #pragma unroll
@@ -323,6 +350,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        if (F == Fmt::BF16 && mt * 16 >= rows) break;  // wave-uniform: no token rows left in this slice
         const i32x4 alo = rd_lo(mt), ahi = rd_hi(mt);
         if (F == Fmt::BF16) {
 #pragma unroll
@@ -346,25 +374,43 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
         }
       }
     }
-    // The refill of this ring slot must not be hoisted above the MFMAs that read
-    // its previous contents (the two values would then both be live): tie the
-    // load's scalar offset to the step's last accumulator update.
-    int ks_next = ks + DEPTH;
-    asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
-    load_b(bq_, ks_next);
-    store_a(an, sn, (ks + 1) & 1);
   };
 
-  // Unrolled so that both rings (DEPTH weight buffers, 2 activation register
-  // sets) index statically.  The trip count is rounded up to the unroll: the
-  // extra steps load zeros and add zeros, and the loop has no early exit (an exit
-  // per step would make the compiler drain every outstanding load there).
-  constexpr int UNROLL = (DEPTH % 2 == 0) ? DEPTH : 2 * DEPTH;
-  const int KS_PAD = (KS + UNROLL - 1) / UNROLL * UNROLL;
-  for (int ks0 = 0; ks0 < KS_PAD; ks0 += UNROLL) {
+  // One stage of KSG K-steps: A(st) is in LDS buffer st&1 and A(st+1) in flight in
+  // `an`; issues A(st+2) into `ap`, and refills each consumed weight-ring slot.
+  auto stage = [&](int st, int su, i32x4 (&ap)[KSG][TL::kAChunks], uint32_t (&sp)[KSG],
+                   i32x4 (&an)[KSG][TL::kAChunks], uint32_t (&sn)[KSG]) {
+    load_a(ap, sp, st + 2);
+    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-      step(bq[u % DEPTH], av[u & 1], as[u & 1], av[(u + 1) & 1], as[(u + 1) & 1], ks0 + u);
+    for (int u = 0; u < KSG; ++u) {
+      const int ks = st * KSG + u;
+      BFrag<F, NT>& slot = bq[(su * KSG + u) % DEPTH];
+      kstep(slot, su & 1, u, ks);
+      // keep the next K-step's LDS reads from being hoisted over this one (register pressure)
+      if (u + 1 < KSG) __builtin_amdgcn_sched_barrier(0);
+      // The refill of this ring slot must not be hoisted above the MFMAs that read
+      // its previous contents (the two values would then both be live): tie the
+      // load's scalar offset to the step's last accumulator update.
+      int ks_next = ks + DEPTH;
+      asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
+      load_b(slot, ks_next);
+    }
+    store_a(an, sn, (su + 1) & 1);
+  };
+
+  // Unrolled so that both rings (DEPTH weight buffers, 2 activation stages)
+  // index statically: U K-steps = SU stages per trip.  The trip count is rounded
+  // up to the unroll: the extra steps load zeros and add zeros, and the loop has
+  // no early exit (an exit per step would make the compiler drain every
+  // outstanding load there).
+  constexpr int U = lcm_c(2 * KSG, DEPTH);
+  constexpr int SU = U / KSG;
+  const int KS_PAD = (KS + U - 1) / U * U;
+  for (int ks0 = 0; ks0 < KS_PAD; ks0 += U) {
+#pragma unroll
+    for (int su = 0; su < SU; ++su)
+      stage(ks0 / KSG + su, su, av[su & 1], as[su & 1], av[(su + 1) & 1], as[(su + 1) & 1]);
   }
   __syncthreads();  // every wave is done with the A buffers; the output tile reuses them
 
@@ -457,13 +503,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
         const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][3]) << 16);
         *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * 16 * NT + 16 * nt + 4 * g) * 2) = uint2{w0, w1};
       }
+    int* pair_lds = (int*)red_lds;  // [BM]
+    if (tid < BM) pair_lds[tid] = pair_of_row;
     __syncthreads();
     constexpr int CPR = 512 / 16;
     for (int c = tid; c < BM * CPR; c += kThreads) {
       const int r = c / CPR, cc = c % CPR;
       const int col = n_tile * kBRows + cc * 8;
       if (r < rows && col < p.N) {
-        const long long pair = p.src_info[row0 + r];
+        const long long pair = pair_lds[r];
         *(i32x4*)((uint8_t*)p.C + pair * p.c_row_bytes + (long long)col * 2) =
             *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
       }
@@ -483,16 +531,16 @@ int ffn_max_m_tiles(int npairs, int E, int bm) {
   return (int)(((long long)npairs + act * (bm - 1)) / bm);
 }
 
-template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH>
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG>
 static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
   const int grid = gp.m_tiles_max * gp.n_tiles;
   if (grid <= 0) return;
   if (fast)
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, true>), dim3(grid), dim3(64 * WAVES), 0, s,
-                       gp);
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, true>), dim3(grid), dim3(64 * WAVES), 0,
+                       s, gp);
   else
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, false>), dim3(grid), dim3(64 * WAVES), 0, s,
-                       gp);
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, false>), dim3(grid), dim3(64 * WAVES), 0,
+                       s, gp);
 }
 
 // 8 waves x 32 weight rows; weight-ring depth per format and tile height, sized
@@ -503,10 +551,16 @@ constexpr int ring_depth() {
   return F == Fmt::FP8 ? (BM <= 96 || !GATEUP ? 2 : 3) : F == Fmt::BF16 ? (BM <= 96 ? 8 : 5) : (BM <= 96 ? 8 : 6);
 }
 
+// K-steps per LDS stage of the activation tile
+template <Fmt F, bool GATEUP, int BM>
+constexpr int stage_ksteps() {
+  return F == Fmt::BF16 ? 1 : 2;
+}
+
 template <Fmt F, int BM>
 static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
-  if (stage != 2) launch_one<F, true, BM, 8, 2, ring_depth<F, true, BM>()>(g1, fast, s);
-  if (stage != 1) launch_one<F, false, BM, 8, 2, ring_depth<F, false, BM>()>(g2, fast, s);
+  if (stage != 2) launch_one<F, true, BM, 8, 2, ring_depth<F, true, BM>(), stage_ksteps<F, true, BM>()>(g1, fast, s);
+  if (stage != 1) launch_one<F, false, BM, 8, 2, ring_depth<F, false, BM>(), stage_ksteps<F, false, BM>()>(g2, fast, s);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
