@@ -65,12 +65,13 @@ bool plan_complete(const moe_plan_buffers* p) {
 }
 
 int choose_bm(const moe_config& c, int T) {
-  if (c.tile_regime == MOE_TILES_DECODE) return 96;
+  if (c.tile_regime == MOE_TILES_DECODE) return 80;
   if (c.tile_regime == MOE_TILES_PREFILL) return 128;
   // Regime gate on the host-known mean rows per expert (the pages' estimated_total_m):
-  // up to 64 rows on average, one 96-row tile holds a whole expert under uniform load.
+  // up to 64 rows on average, one 80-row tile holds almost every expert under
+  // uniform load, and the weight stream dominates.
   const long long mean = ((long long)T * c.num_topk + c.num_experts - 1) / c.num_experts;
-  return mean <= 64 ? 96 : 128;
+  return mean <= 64 ? 80 : 128;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }

@@ -7,7 +7,7 @@
 // num_active_experts / expert_start_indices); each workgroup finds its tile
 // from the per-expert prefix sums, so no device-side tile list is needed.
 //
-// Workgroup: WAVES wavefronts, BM rows x 256 weight rows per tile.
+// Workgroup: WAVES wavefronts, BM rows x BN = WAVES*16*NT weight rows per tile.
 //   * A (activation rows, gathered through src_info for gate_up) is staged in
 //     LDS, double buffered, one 128-byte K-step segment per row.
 //   * B (weights) streams from HBM straight into VGPRs in MFMA operand order,
@@ -34,7 +34,6 @@
 
 namespace moe {
 
-constexpr int kBRows = 256;      // weight rows per workgroup tile (WAVES * 16 * NT)
 constexpr int kHCols = 128;      // gate_up: h columns per workgroup tile (one FP8 requant block)
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
 
@@ -98,16 +97,17 @@ struct BFrag {
 };
 
 
-template <Fmt F, bool GATEUP, int BM, int WAVES, int KSG>
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int KSG>
 struct Tile {
   static constexpr int kThreads = 64 * WAVES;
+  static constexpr int BN = WAVES * 16 * NT;  // weight rows per workgroup tile
   static constexpr int MT = BM / 16;
   static constexpr int kAStride = 128 * KSG + 16;  // LDS bytes per A row: KSG K-steps + bank padding
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
   // A buffer rows: BM rounded up so that every thread stores every chunk it loads
   // (chunks past BM rows are zeros landing in spare rows): no divergent stores in the loop
   static constexpr int kARows = kAChunks * kThreads / 8;
-  static constexpr int kOutRowBytes = GATEUP ? (F == Fmt::BF16 ? 256 : 128) : 512;
+  static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (F == Fmt::BF16 ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
   static constexpr int kABytes = 2 * kARows * kAStride;
   static constexpr int kOutBytes = BM * kOutStride;
@@ -117,11 +117,13 @@ struct Tile {
   static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? 2 * kMaxKSteps * 4 : 0);
 };
 
+// WAVES waves per workgroup and 8 / WAVES workgroups per CU: two waves per SIMD.
 template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, bool FAST>
-__global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
-  static_assert(WAVES * 16 * NT == kBRows, "a workgroup tile covers 256 weight rows");
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmParams p) {
+  using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
+  constexpr int BN = TL::BN;
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
-  using TL = Tile<F, GATEUP, BM, WAVES, KSG>;
+  static_assert(!GATEUP || BN / 2 == kHCols, "a gate_up tile is one 128-column block of h");
   constexpr int MT = TL::MT;
   constexpr int kThreads = TL::kThreads;
   constexpr int HW = 8 * NT;  // gate_up: h columns per wave
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
         ocol = n_tile * kHCols + wave * HW + 16 * (nt % (NT / 2)) + r16;  // h column
         wrow = (nt < NT / 2 ? 0 : p.N) + ocol;                             // gate rows, then up rows
       } else {
-        ocol = n_tile * kBRows + wave * 16 * NT + 16 * nt + r16;
+        ocol = n_tile * BN + wave * 16 * NT + 16 * nt + r16;
         wrow = ocol;
       }
       const bool ok = ocol < p.N;
@@ -198,8 +200,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
       // the tile's weight-scale rows, staged in LDS: [0] the gate block (gate_up) or
       // the first 128-row block (down), [1] the up block or the second 128-row block
       const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
-      const int blk0 = GATEUP ? n_tile : min(n_tile * 2, p.n_rows / 128 - 1);
-      const int blk1 = GATEUP ? p.N / 128 + n_tile : min(n_tile * 2 + 1, p.n_rows / 128 - 1);
+      const int blk0 = GATEUP ? n_tile : min(n_tile * BN / 128, p.n_rows / 128 - 1);
+      const int blk1 = GATEUP ? p.N / 128 + n_tile : min(n_tile * BN / 128 + 1, p.n_rows / 128 - 1);
       for (int i = tid; i < 2 * p.ksteps; i += kThreads)
         sb_lds[(i >= p.ksteps) * TL::kMaxKSteps + i % p.ksteps] =
             sfe[(size_t)(i >= p.ksteps ? blk1 : blk0) * p.b_sf_row + i % p.ksteps];
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
   // FP8: which staged scale row this wave's column tile nt uses
   auto sb_row = [&](int nt) {
     if (GATEUP) return nt >= NT / 2 ? 1 : 0;
-    return ((wave * 16 * NT + 16 * nt) % 256) >= 128 ? 1 : 0;
+    return ((n_tile * BN) % 128 + wave * 16 * NT + 16 * nt) >= 128 ? 1 : 0;
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
     const uint32_t dead = oob_if(ks >= p.ksteps);
@@ -506,10 +508,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void ffn_gemm_kernel(GemmParams p) {
     int* pair_lds = (int*)red_lds;  // [BM]
     if (tid < BM) pair_lds[tid] = pair_of_row;
     __syncthreads();
-    constexpr int CPR = 512 / 16;
+    constexpr int CPR = BN * 2 / 16;
     for (int c = tid; c < BM * CPR; c += kThreads) {
       const int r = c / CPR, cc = c % CPR;
-      const int col = n_tile * kBRows + cc * 8;
+      const int col = n_tile * BN + cc * 8;
       if (r < rows && col < p.N) {
         const long long pair = pair_lds[r];
         *(i32x4*)((uint8_t*)p.C + pair * p.c_row_bytes + (long long)col * 2) =
@@ -554,13 +556,30 @@ constexpr int ring_depth() {
 // K-steps per LDS stage of the activation tile
 template <Fmt F, bool GATEUP, int BM>
 constexpr int stage_ksteps() {
-  return F == Fmt::BF16 ? 1 : 2;
+  return F == Fmt::BF16 || (F == Fmt::MX && !GATEUP && BM <= 96) ? 1 : 2;
 }
 
+// Output columns of a down tile.  Weight-bound tiles (BM <= 96): 4 waves x 32
+// rows and two workgroups per CU, so that one workgroup's prologue and epilogue
+// overlap the other's weight stream and the tail is finer; MFMA-bound tiles:
+// 8 waves x 32 rows.
+template <int BM>
+constexpr int down_tile_rows() {
+  return BM <= 96 ? 128 : 256;
+}
+
+// gate_up: one 128-column block of h per workgroup (256 weight rows): 4 waves x
+// 64 rows and two workgroups per CU for weight-bound tiles, 8 waves x 32 rows
+// for MFMA-bound ones
 template <Fmt F, int BM>
 static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
-  if (stage != 2) launch_one<F, true, BM, 8, 2, ring_depth<F, true, BM>(), stage_ksteps<F, true, BM>()>(g1, fast, s);
-  if (stage != 1) launch_one<F, false, BM, 8, 2, ring_depth<F, false, BM>(), stage_ksteps<F, false, BM>()>(g2, fast, s);
+  if (stage != 2) {
+    if constexpr (BM <= 96) launch_one<F, true, BM, 4, 4, 2, 1>(g1, fast, s);
+    else launch_one<F, true, BM, 8, 2, ring_depth<F, true, BM>(), stage_ksteps<F, true, BM>()>(g1, fast, s);
+  }
+  if (stage != 1)
+    launch_one<F, false, BM, down_tile_rows<BM>() / 32, 2, ring_depth<F, false, BM>(), stage_ksteps<F, false, BM>()>(
+        g2, fast, s);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
@@ -599,7 +618,8 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.clamp = a.clamp;
   // down: A = h rows, B = w2 [E, H, I]
   g2 = g1;
-  g2.n_tiles = (a.H + kBRows - 1) / kBRows;
+  const int down_bn = a.bm <= 96 ? 128 : 256;  // down_tile_rows<BM>()
+  g2.n_tiles = (a.H + down_bn - 1) / down_bn;
   g2.K = a.I;
   g2.ksteps = (a.I + elem_k - 1) / elem_k;
   g2.N = a.H;
@@ -622,15 +642,15 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   switch (a.fmt) {
     case Fmt::FP8:
       if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::FP8, 96>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::FP8, 80>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::BF16:
       if (a.bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::BF16, 96>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::BF16, 80>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::MX:
       if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::MX, 96>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::MX, 80>(g1, g2, a.fast, s, stage);
       break;
   }
   return hipGetLastError();

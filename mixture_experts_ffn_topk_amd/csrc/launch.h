@@ -37,7 +37,7 @@ struct FfnArgs {
   int T, E, topk, H, I;
   float clamp;
   bool fast;
-  int bm;  // 64 or 128
+  int bm;  // 80 (weight-bound tiles) or 128 (MFMA-bound tiles)
   const int* start;     // expert_start_indices [E+1]
   const int* src_info;  // [T*k]
   const void* x;
