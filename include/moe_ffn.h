@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+#define MOE_FFN_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -99,7 +99,9 @@ typedef struct moe_config {
   int32_t tile_regime;          /* moe_tile_regime */
 } moe_config;
 
-/* (host struct of device pointers) Expert weights of this GPU, as given. */
+/* (host struct of device pointers) Expert weights of this GPU: the canonical
+   tensors of moe_format (input of moe_prepare_weights) or their prepared
+   layout (input of every FFN entry point). */
 typedef struct moe_weights {
   const void* w13;     /* gate_up_weight: rows [0,I) gate, rows [I,2I) up */
   const void* w13_sf;  /* its scales (NULL for BF16) */
@@ -120,6 +122,11 @@ typedef struct moe_plan_buffers {
 
 typedef struct moe_handle moe_handle;
 
+/* (host) Byte sizes of the prepared weight tensors (0 where a tensor is absent). */
+typedef struct moe_prepared_sizes {
+  size_t w13, w13_sf, w2, w2_sf;
+} moe_prepared_sizes;
+
 /* Validate *cfg and create a host handle.  Returns MOE_ERR_INVALID_ARGUMENT for
    bad geometry (see moe_format for the divisibility rules), k > E, k > 32,
    E > 1024, clamp <= 0 or NaN, an unknown enum; MOE_ERR_UNSUPPORTED for
@@ -129,6 +136,30 @@ typedef struct moe_handle moe_handle;
    2^31 bytes. */
 moe_status moe_create(const moe_config* cfg /* host */, moe_handle** out /* host */);
 void moe_destroy(moe_handle* h);
+
+/* Prepared weight layout ([MegaFFN] takes its gate_up weight pre-permuted; here
+   both weights are).  A weight matrix of R rows and K elements per row (w13: R =
+   2I, K = H; w2: R = H, K = I) is cut into tiles of 16 rows x one K-step (128
+   elements; 64 for BF16).  Tiles are stored expert-major, then by row block
+   rb = row / 16, then by K-step ks, each tile contiguous, with lane l = 16*g + r
+   (g < 4, r < 16) standing for row 16*rb + r:
+     FP8, BF16  2048-byte tile: byte half*1024 + 16*l + b (half < 2, b < 16) holds
+                byte ks*128 + 64*half + 16*g + b of the row (its 128-byte K-step segment)
+     MX         1024-byte tile: byte 16*l + b holds byte ks*64 + 16*g + b of the
+                packed E2M1 row, zero past the row's end
+     MX scales  64-byte tile: byte l holds the UE8M0 byte of K-block 4*ks + g of
+                the row, zero past the row's end
+     FP8 scales unchanged.
+   moe_prepared_weights_size gives the sizes; moe_prepare_weights writes them. */
+moe_status moe_prepared_weights_size(const moe_handle* h, moe_prepared_sizes* out /* host */);
+
+/* One-time relayout of canonical weights (moe_format) into the prepared layout,
+   asynchronously on `stream`.  `prepared` points to caller-owned buffers of the
+   sizes above (16-byte aligned, not overlapping the canonical ones; for FP8 the
+   scale buffers may alias the canonical scales).  Canonical buffers must be
+   16-byte aligned.  Every FFN entry point below reads the prepared layout. */
+moe_status moe_prepare_weights(const moe_handle* h, const moe_weights* canonical /* host struct */,
+                               const moe_weights* prepared /* host struct */, hipStream_t stream);
 
 /* Bytes of workspace moe_plan / moe_ffn / moe_forward need for num_tokens tokens
    (0 if num_tokens is out of range).  The workspace is caller-owned device memory,
@@ -149,7 +180,7 @@ moe_status moe_plan(const moe_handle* h, int32_t num_tokens, const void* topk_id
 /* Expert FFN over the plan's rows ([MegaFFN]: gate/up GEMM -> clamped SwiGLU ->
    intermediate requantisation -> down GEMM).  x, x_sf per the format; y [T,k,H]
    bf16 receives each row's result at its pair slot p = src_info[row]; slots of
-   masked pairs are left untouched. */
+   masked pairs are left untouched.  w: prepared layout. */
 moe_status moe_ffn(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
                    const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
                    void* y, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -160,7 +191,8 @@ moe_status moe_ffn(const moe_handle* h, int32_t num_tokens, const void* x, const
      h_sf            fp32 [T*k, I/128] (FP8), UE8M0 bytes [T*k, I/32] (MX), NULL (BF16)
    moe_ffn_gate_up: gate/up GEMM of every plan row, clamped SwiGLU, requantisation
    ([MegaFFN]: L1 GEMM, clamp_activation, the re-quant ahead of L2).
-   moe_ffn_down: down GEMM of every plan row into y [T,k,H] bf16 at p = src_info[row]. */
+   moe_ffn_down: down GEMM of every plan row into y [T,k,H] bf16 at p = src_info[row].
+   w: prepared layout. */
 moe_status moe_ffn_gate_up(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
                            const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
                            void* h_out, void* h_sf_out, hipStream_t stream);
@@ -177,7 +209,7 @@ moe_status moe_combine(const moe_handle* h, int32_t num_tokens, const void* y, c
 /* The whole path in one call: plan (into ws), FFN (y in ws), combine into out
    [T,H] bf16.  PRECOMPUTED: topk_idx / topk_weights are inputs and are not
    modified.  FROM_LOGITS: routing_logits is the input and topk_idx / topk_weights
-   receive the routing result. */
+   receive the routing result.  w: prepared layout. */
 moe_status moe_forward(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
                        void* topk_idx, float* topk_weights, const float* routing_logits,
                        const moe_weights* w /* host struct */, void* out, void* ws, size_t ws_bytes,

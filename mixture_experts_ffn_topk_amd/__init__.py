@@ -51,9 +51,14 @@ class _Plan(ctypes.Structure):
                                                "num_active_experts", "src_info", "pair_row", "status")]
 
 
+class _PreparedSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("w13", "w13_sf", "w2", "w2_sf")]
+
+
 PLAN_FIELDS = [f for f, _ in _Plan._fields_]
-EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_plan", "moe_ffn", "moe_ffn_gate_up",
-            "moe_ffn_down", "moe_combine", "moe_forward", "moe_status_string", "moe_abi_version"]
+EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
+            "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
+            "moe_status_string", "moe_abi_version"]
 
 _lib = None
 
@@ -73,6 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_destroy.restype = None
     lib.moe_workspace_size.argtypes = [vp, i32]
     lib.moe_workspace_size.restype = sz
+    lib.moe_prepared_weights_size.argtypes = [vp, ctypes.POINTER(_PreparedSizes)]
+    lib.moe_prepared_weights_size.restype = i32
+    lib.moe_prepare_weights.argtypes = [vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Weights), vp]
+    lib.moe_prepare_weights.restype = i32
     lib.moe_plan.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.POINTER(_Plan), vp, sz, vp]
     lib.moe_plan.restype = i32
     lib.moe_ffn.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp, sz, vp]
@@ -154,6 +163,25 @@ class MoEFFN:
     def alloc_workspace(self, num_tokens: int, device="cuda"):
         import torch
         return torch.empty(max(1, self.workspace_size(num_tokens)), dtype=torch.uint8, device=device)
+
+    def prepared_weights_size(self) -> dict:
+        ps = _PreparedSizes()
+        _check(self.lib.moe_prepared_weights_size(self._h, ctypes.byref(ps)), "moe_prepared_weights_size")
+        return {n: int(getattr(ps, n)) for n, _ in _PreparedSizes._fields_}
+
+    def prepare_weights(self, weights: dict, out: dict | None = None, stream=None) -> dict:
+        """moe_prepare_weights: canonical weights -> the prepared layout every FFN
+        entry point reads.  Allocates the prepared tensors (uint8) unless `out`
+        gives them."""
+        import torch
+        if out is None:
+            dev = weights["w13"].device
+            out = {n: (torch.empty(b, dtype=torch.uint8, device=dev) if b else None)
+                   for n, b in self.prepared_weights_size().items()}
+        cw, pw = self._weights_struct(weights), self._weights_struct(out)
+        _check(self.lib.moe_prepare_weights(self._h, ctypes.byref(cw), ctypes.byref(pw), _stream(stream)),
+               "moe_prepare_weights")
+        return out
 
     def alloc_plan(self, num_tokens: int, device="cuda") -> dict:
         import torch

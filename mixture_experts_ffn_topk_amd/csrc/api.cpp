@@ -136,9 +136,11 @@ bool sizes_supported(const moe_config& c) {
                            I = (unsigned long long)c.intermediate_hidden, k = (unsigned long long)c.num_topk;
   const unsigned long long act = c.format == MOE_FMT_BF16 ? 2 : 1;  // bytes per activation element
   if (T * H * act > kMaxBytes || T * k * I * act > kMaxBytes) return false;
-  // weight bytes per expert (E2M1: half a byte per element)
-  const unsigned long long w13 = c.format == MOE_FMT_BF16 ? 4 * I * H : c.format == MOE_FMT_FP8_BLOCK128 ? 2 * I * H : I * H;
-  if (w13 > kMaxBytes) return false;
+  // prepared weight bytes per expert
+  const moe::Fmt f = to_fmt(c.format);
+  if (moe::prepared_expert_bytes(f, (int)(2 * I), (int)H) > kMaxBytes ||
+      moe::prepared_expert_bytes(f, (int)H, (int)I) > kMaxBytes)
+    return false;
   if (c.format == MOE_FMT_FP8_BLOCK128 && (H / 128 > 256 || I / 128 > 256)) return false;
   return true;
 }
@@ -194,6 +196,41 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
 }
 
 void moe_destroy(moe_handle* h) { delete h; }
+
+moe_status moe_prepared_weights_size(const moe_handle* h, moe_prepared_sizes* out) {
+  if (!h || !out) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = h->cfg;
+  const moe::Fmt f = to_fmt(c.format);
+  const size_t E = (size_t)c.num_experts;
+  const int H = c.hidden, I = c.intermediate_hidden;
+  out->w13 = E * moe::prepared_expert_bytes(f, 2 * I, H);
+  out->w2 = E * moe::prepared_expert_bytes(f, H, I);
+  if (f == moe::Fmt::FP8) {
+    out->w13_sf = E * (size_t)(2 * I / 128) * (H / 128) * 4;
+    out->w2_sf = E * (size_t)(H / 128) * (I / 128) * 4;
+  } else {
+    out->w13_sf = E * moe::prepared_scale_expert_bytes(f, 2 * I, H);
+    out->w2_sf = E * moe::prepared_scale_expert_bytes(f, H, I);
+  }
+  return MOE_OK;
+}
+
+moe_status moe_prepare_weights(const moe_handle* h, const moe_weights* canonical, const moe_weights* prepared,
+                               hipStream_t stream) {
+  if (!h || !weights_ok(h->cfg, canonical) || !weights_ok(h->cfg, prepared)) return MOE_ERR_INVALID_ARGUMENT;
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (!aligned(canonical->w13) || !aligned(canonical->w2) || !aligned(prepared->w13) || !aligned(prepared->w2))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (prepared->w13 == canonical->w13 || prepared->w2 == canonical->w2) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = h->cfg;
+  const moe::Fmt f = to_fmt(c.format);
+  hipError_t e = moe::launch_prepare(f, c.num_experts, 2 * c.intermediate_hidden, c.hidden, canonical->w13,
+                                     canonical->w13_sf, (void*)prepared->w13, (void*)prepared->w13_sf, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_prepare(f, c.num_experts, c.hidden, c.intermediate_hidden, canonical->w2, canonical->w2_sf,
+                          (void*)prepared->w2, (void*)prepared->w2_sf, stream);
+  return hip_status(e);
+}
 
 size_t moe_workspace_size(const moe_handle* h, int32_t T) {
   if (!valid_T(h, T)) return 0;

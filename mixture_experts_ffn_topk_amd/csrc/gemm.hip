@@ -58,10 +58,11 @@ struct GemmParams {
   uint32_t a_sf_bytes;
   int a_sf_row;  // FP8: floats per row; MX: bytes per row
   const uint8_t* B;
-  uint32_t b_row_bytes;
-  uint32_t b_expert_bytes;
+  uint32_t b_tile;          // bytes of one prepared weight tile (16 rows x one K-step)
+  uint32_t b_expert_bytes;  // prepared weight bytes per expert
+  uint32_t bsc_expert_bytes;  // MX: prepared scale bytes per expert
   const void* B_sf;
-  int b_sf_row;  // FP8: K/128 floats per 128-row block; MX: K/32 bytes per row
+  int b_sf_row;  // FP8: K/128 floats per 128-row block
   void* C;
   long long c_row_bytes;
   void* C_sf;
@@ -175,26 +176,30 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
   const int rows = min(BM, __builtin_amdgcn_readfirstlane(e_count) - tile_in_e * BM);
 
   // ---------------------------------------------------------------- B (weight) addressing
+  // Weights arrive in the prepared layout: per expert, tiles of 16 rows x one
+  // K-step, row block major then K-step, each tile contiguous in MFMA lane order
+  // (lane l's 16 bytes at 16*l, FP8/BF16 second halves 1 KB further), so one
+  // load instruction of a wave reads 1 KB of consecutive bytes.
   const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + (size_t)expert * p.b_expert_bytes, p.b_expert_bytes);
   __amdgpu_buffer_rsrc_t bsc_rs = b_rs;
   uint32_t b_off[NT], bsc_off[NT];
   {
     if (F == Fmt::MX)
-      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.n_rows * p.b_sf_row,
-                         (uint32_t)p.n_rows * (uint32_t)p.b_sf_row);
+      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      int wrow, ocol;
+      int wrow0, col0;  // first weight row and first output column of the 16-row tile
       if (GATEUP) {
-        ocol = n_tile * kHCols + wave * HW + 16 * (nt % (NT / 2)) + r16;  // h column
-        wrow = (nt < NT / 2 ? 0 : p.N) + ocol;                             // gate rows, then up rows
+        col0 = n_tile * kHCols + wave * HW + 16 * (nt % (NT / 2));  // h column
+        wrow0 = (nt < NT / 2 ? 0 : p.N) + col0;                      // gate rows, then up rows
       } else {
-        ocol = n_tile * BN + wave * 16 * NT + 16 * nt + r16;
-        wrow = ocol;
+        col0 = n_tile * BN + wave * 16 * NT + 16 * nt;
+        wrow0 = col0;
       }
-      const bool ok = ocol < p.N;
-      b_off[nt] = ok ? (uint32_t)wrow * p.b_row_bytes + (uint32_t)(16 * g) : kOOB;
-      bsc_off[nt] = ok ? (uint32_t)wrow * (uint32_t)p.b_sf_row + (uint32_t)g : kOOB;
+      const bool ok = col0 < p.N;
+      const uint32_t tiles0 = (uint32_t)(wrow0 / 16) * (uint32_t)p.ksteps;  // first tile of the row block
+      b_off[nt] = ok ? tiles0 * p.b_tile + (uint32_t)lane * 16u : kOOB;
+      bsc_off[nt] = ok ? tiles0 * 64u + (uint32_t)lane : kOOB;
     }
     if (F == Fmt::FP8) {
       // the tile's weight-scale rows, staged in LDS: [0] the gate block (gate_up) or
@@ -213,17 +218,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
     return ((n_tile * BN) % 128 + wave * 16 * NT + 16 * nt) >= 128 ? 1 : 0;
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
-    const uint32_t dead = oob_if(ks >= p.ksteps);
+    const uint32_t dead = oob_if(ks >= p.ksteps);  // (the prepared layout is zero past a row's end)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t o = b_off[nt] | dead;
+      b.lo[nt] = bload16(b_rs, o, (uint32_t)ks * p.b_tile);
       if (F == Fmt::MX) {
-        const uint32_t tail = oob_if(ks * 128 + 32 * g >= p.K);  // also set past the last K-step
-        b.lo[nt] = bload16(b_rs, b_off[nt] | tail, (uint32_t)ks * 64u);
-        b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, bsc_off[nt] | tail, (uint32_t)ks * 4u, 0);
+        b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, bsc_off[nt] | dead, (uint32_t)ks * 64u, 0);
       } else {
-        const uint32_t o = b_off[nt] | dead;
-        b.lo[nt] = bload16(b_rs, o, (uint32_t)ks * 128u);
-        b.hi[nt] = bload16(b_rs, o + 64u, (uint32_t)ks * 128u);
+        b.hi[nt] = bload16(b_rs, o + 1024u, (uint32_t)ks * p.b_tile);
       }
     }
   };
@@ -607,8 +610,9 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.a_sf_row = a.H / sf_div;
   g1.a_sf_bytes = (uint32_t)a.T * (uint32_t)g1.a_sf_row * (a.fmt == Fmt::FP8 ? 4u : 1u);
   g1.B = (const uint8_t*)a.w13;
-  g1.b_row_bytes = a.fmt == Fmt::MX ? (uint32_t)a.H / 2 : (uint32_t)a.H * esz;
-  g1.b_expert_bytes = g1.b_row_bytes * 2u * (uint32_t)a.I;
+  g1.b_tile = (uint32_t)prepared_tile_bytes(a.fmt);
+  g1.b_expert_bytes = (uint32_t)(prepared_expert_bytes(a.fmt, 2 * a.I, a.H));
+  g1.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(a.fmt, 2 * a.I, a.H));
   g1.B_sf = a.w13_sf;
   g1.b_sf_row = a.H / sf_div;
   g1.C = a.h;
@@ -631,8 +635,8 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g2.a_sf_row = a.I / sf_div;
   g2.a_sf_bytes = (uint32_t)npairs * (uint32_t)g2.a_sf_row * (a.fmt == Fmt::FP8 ? 4u : 1u);
   g2.B = (const uint8_t*)a.w2;
-  g2.b_row_bytes = a.fmt == Fmt::MX ? (uint32_t)a.I / 2 : (uint32_t)a.I * esz;
-  g2.b_expert_bytes = g2.b_row_bytes * (uint32_t)a.H;
+  g2.b_expert_bytes = (uint32_t)(prepared_expert_bytes(a.fmt, a.H, a.I));
+  g2.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(a.fmt, a.H, a.I));
   g2.B_sf = a.w2_sf;
   g2.b_sf_row = a.I / sf_div;
   g2.C = a.y;

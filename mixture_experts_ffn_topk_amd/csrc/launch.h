@@ -31,7 +31,16 @@ hipError_t launch_plan(const void* ids, bool idx64, int npairs, int E, const Pla
 hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, void* idx_out, bool idx64,
                                     float* w_out, bool fast, hipStream_t s);
 
-// Grouped GEMMs.  Tile rows per workgroup (BM) by regime.
+// Prepared weight layout: tiles of 16 rows x one K-step in MFMA lane order.
+size_t prepared_tile_bytes(Fmt f);                           // 2048 (FP8, BF16) or 1024 (MX)
+int prepared_ksteps(Fmt f, int K);                           // K-steps of 128 (64 for BF16) elements
+size_t prepared_expert_bytes(Fmt f, int rows, int K);        // one expert's weight tiles
+size_t prepared_scale_expert_bytes(Fmt f, int rows, int K);  // MX: one expert's scale tiles; else 0
+// Relayout E experts' [rows, K] weights (and MX scales; FP8 scales are copied).
+hipError_t launch_prepare(Fmt f, int E, int rows, int K, const void* w, const void* w_sf, void* out, void* out_sf,
+                          hipStream_t s);
+
+// Grouped GEMMs over prepared weights.  Tile rows per workgroup (BM) by regime.
 struct FfnArgs {
   Fmt fmt;
   int T, E, topk, H, I;
@@ -42,7 +51,7 @@ struct FfnArgs {
   const int* src_info;  // [T*k]
   const void* x;
   const void* x_sf;
-  const void* w13;
+  const void* w13;  // prepared layout
   const void* w13_sf;
   const void* w2;
   const void* w2_sf;

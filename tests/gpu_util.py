@@ -47,10 +47,41 @@ def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.i
     return d
 
 
+def prepared(moe: MoEFFN, d: dict) -> dict:
+    """The weights of d in the prepared layout (moe_prepare_weights), made once."""
+    if not d.get("weights_prepared"):
+        d["weights"] = moe.prepare_weights(d["weights"])
+        d["weights_prepared"] = True
+    return d["weights"]
+
+
+def prepared_layout_reference(fmt: str, w: np.ndarray, sf: np.ndarray | None, rows: int, K: int):
+    """The prepared layout written out from its definition in include/moe_ffn.h
+    (numpy index arithmetic, independent of the library)."""
+    E = w.shape[0]
+    rb = rows // 16
+    if fmt == "w4a8_mx":
+        ks = -(-K // 128)
+        wb = np.zeros((E, rows, ks * 64), np.uint8)
+        wb[:, :, :K // 2] = w.reshape(E, rows, K // 2)
+        # [E, rb, r, ks, g, b] -> [E, rb, ks, g, r, b]  (lane l = 16*g + r)
+        t = wb.reshape(E, rb, 16, ks, 4, 16).transpose(0, 1, 3, 4, 2, 5)
+        sfb = np.zeros((E, rows, ks * 4), np.uint8)
+        sfb[:, :, :K // 32] = sf.reshape(E, rows, K // 32)
+        ts = sfb.reshape(E, rb, 16, ks, 4).transpose(0, 1, 3, 4, 2)
+        return t.reshape(-1), ts.reshape(-1)
+    row_bytes = K * (2 if fmt == "bf16" else 1)
+    ks = row_bytes // 128
+    wb = np.ascontiguousarray(w).view(np.uint8).reshape(E, rows, row_bytes)
+    # [E, rb, r, ks, half, g, b] -> [E, rb, ks, half, g, r, b]
+    t = wb.reshape(E, rb, 16, ks, 2, 4, 16).transpose(0, 1, 3, 4, 5, 2, 6)
+    return t.reshape(-1), (None if sf is None else np.ascontiguousarray(sf).view(np.uint8).reshape(-1))
+
+
 def run_forward(moe: MoEFFN, d: dict, T: int):
     out = torch.full((max(T, 1), moe.hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
     ws = moe.alloc_workspace(T)
-    moe.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], d["weights"], out, ws)
+    moe.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], prepared(moe, d), out, ws)
     torch.cuda.synchronize()
     return out[:T]
 
@@ -65,7 +96,7 @@ def run_split(moe: MoEFFN, d: dict, T: int):
         moe.plan(T, plan, routing_logits=d["logits"], topk_idx_out=d["topk_idx"], topk_weights_out=d["topk_weights"],
                  ws=ws)
     y = torch.zeros((max(T, 1) * moe.topk, moe.hidden), dtype=torch.bfloat16, device="cuda")
-    moe.ffn(T, d["x"], d["x_sf"], d["weights"], plan, y, ws)
+    moe.ffn(T, d["x"], d["x_sf"], prepared(moe, d), plan, y, ws)
     out = torch.empty((max(T, 1), moe.hidden), dtype=torch.bfloat16, device="cuda")
     moe.combine(T, y, d["topk_weights"], plan, out)
     torch.cuda.synchronize()
@@ -103,9 +134,9 @@ def run_ffn_intermediates(moe: MoEFFN, d: dict, T: int):
         moe.plan(T, plan, routing_logits=d["logits"], topk_idx_out=d["topk_idx"], topk_weights_out=d["topk_weights"],
                  ws=ws)
     h, hsf = moe.alloc_intermediate(T)
-    moe.ffn_gate_up(T, d["x"], d["x_sf"], d["weights"], plan, h, hsf)
+    moe.ffn_gate_up(T, d["x"], d["x_sf"], prepared(moe, d), plan, h, hsf)
     y = torch.zeros((max(T, 1) * moe.topk, moe.hidden), dtype=torch.bfloat16, device="cuda")
-    moe.ffn_down(T, h, hsf, d["weights"], plan, y)
+    moe.ffn_down(T, h, hsf, prepared(moe, d), plan, y)
     out = torch.empty((max(T, 1), moe.hidden), dtype=torch.bfloat16, device="cuda")
     moe.combine(T, y, d["topk_weights"], plan, out)
     torch.cuda.synchronize()

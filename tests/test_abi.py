@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -107,6 +107,36 @@ def test_workspace_size_and_host_validation():
     assert lib.moe_forward(h, 10, 1, 1, 1, 1, None, ctypes.byref(w), 1, 1, 16, None) == 3  # workspace too small
     assert lib.moe_forward(h, 10, 1, None, 1, 1, None, ctypes.byref(w), 1, 1, ws, None) == 1  # FP8 needs x_sf
     assert lib.moe_combine(h, 10, None, None, ctypes.byref(plan), None, None) == 1
+    lib.moe_destroy(h)
+
+
+def test_prepared_weight_sizes_and_validation():
+    """Sizes follow the header's prepared layout: per expert, rows/16 row blocks x
+    K-steps (128 elements; 64 for BF16) x 2048-byte tiles (1024 for MX), MX scale
+    tiles of 64 bytes; FP8 scales unchanged."""
+    lib = _lib()
+    cases = [
+        (dict(), (32 * 256 * 56 * 2048, 32 * 32 * 56 * 4, 32 * 448 * 16 * 2048, 32 * 56 * 16 * 4)),
+        (dict(format=1, hidden=4096, intermediate_hidden=14336, num_experts=8, num_topk=2),
+         (8 * 1792 * 64 * 2048, 0, 8 * 256 * 224 * 2048, 0)),
+        # MX: K = 2880 -> 23 K-steps of 128 (the last one half empty, zero-padded)
+        (dict(format=2, hidden=2880, intermediate_hidden=2880, num_experts=128, num_topk=4),
+         (128 * 360 * 23 * 1024, 128 * 360 * 23 * 64, 128 * 180 * 23 * 1024, 128 * 180 * 23 * 64)),
+    ]
+    for kw, want in cases:
+        h = ctypes.c_void_p()
+        assert lib.moe_create(ctypes.byref(_cfg(**kw)), ctypes.byref(h)) == 0
+        ps = mx._PreparedSizes()
+        assert lib.moe_prepared_weights_size(h, ctypes.byref(ps)) == 0
+        assert (ps.w13, ps.w13_sf, ps.w2, ps.w2_sf) == want
+        lib.moe_destroy(h)
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg()), ctypes.byref(h)) == 0
+    assert lib.moe_prepared_weights_size(h, None) == 1
+    canon = mx._Weights(256, 512, 768, 1024)
+    assert lib.moe_prepare_weights(h, ctypes.byref(canon), ctypes.byref(mx._Weights(None, 1, 1, 1)), None) == 1
+    assert lib.moe_prepare_weights(h, ctypes.byref(canon), ctypes.byref(mx._Weights(4104, 16, 8192, 16)), None) == 1
+    assert lib.moe_prepare_weights(h, ctypes.byref(canon), ctypes.byref(mx._Weights(256, 16, 8192, 16)), None) == 1
     lib.moe_destroy(h)
 
 

@@ -9,7 +9,8 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import (compare_out, device_inputs, geometry, make_moe, run_ffn_intermediates, run_forward, run_split,
+from gpu_util import (compare_out, device_inputs, geometry, make_moe, prepared_layout_reference, run_ffn_intermediates,
+                      run_forward, run_split,
                       staged_check)
 
 pytestmark = pytest.mark.gpu
@@ -116,6 +117,29 @@ def test_combine_against_oracle():
     ref = oracle.combine(yy, w, np.where(ref_plan["pair_row"] >= 0, np.arange(T * k), -1), H)
     got = out.float().cpu().numpy()
     np.testing.assert_allclose(got, ref, rtol=2 ** -7, atol=1e-6)
+
+
+# ------------------------------------------------------------------ prepared weight layout (bit-exact)
+@pytest.mark.parametrize("fmt,H,I", [("fp8_block128", 512, 384), ("bf16", 448, 320), ("w4a8_mx", 576, 352)])
+def test_prepare_weights_layout(fmt, H, I):
+    sh = small("prep_" + fmt, 7, 16, H, I, 3, 2, fmt)
+    inp = moe_synth.make_inputs(sh)
+    moe = make_moe(sh)
+    d = device_inputs(inp)
+    pw = moe.prepare_weights(d["weights"])
+    torch.cuda.synchronize()
+    sizes = moe.prepared_weights_size()
+    for name, rows, K in (("w13", 2 * I, H), ("w2", H, I)):
+        want, want_sf = prepared_layout_reference(fmt, inp[name], inp[name + "_sf"], rows, K)
+        got = pw[name].cpu().numpy()
+        assert got.size == sizes[name] == want.size
+        assert np.array_equal(got, want), f"{name}: first mismatch at byte {int(np.argmax(got != want))}"
+        if want_sf is None:
+            assert pw[name + "_sf"] is None
+        else:
+            got_sf = pw[name + "_sf"].cpu().numpy().view(np.uint8)
+            assert got_sf.size == sizes[name + "_sf"] == want_sf.size
+            assert np.array_equal(got_sf, want_sf)
 
 
 # ------------------------------------------------------------------ FFN parity, small shapes (full comparison)

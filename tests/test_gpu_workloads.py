@@ -12,7 +12,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import check_intermediate, check_y_rows, compare_out, device_inputs, geometry, make_moe
+from gpu_util import check_intermediate, check_y_rows, compare_out, device_inputs, geometry, make_moe, prepared
 
 pytestmark = pytest.mark.gpu
 
@@ -32,9 +32,9 @@ def _gather_intermediate(moe, d, T, rows):
         moe.plan(T, plan, routing_logits=d["logits"], topk_idx_out=d["topk_idx"], topk_weights_out=d["topk_weights"],
                  ws=ws)
     h, hsf = moe.alloc_intermediate(T)
-    moe.ffn_gate_up(T, d["x"], d["x_sf"], d["weights"], plan, h, hsf)
+    moe.ffn_gate_up(T, d["x"], d["x_sf"], prepared(moe, d), plan, h, hsf)
     y = torch.zeros((T * moe.topk, moe.hidden), dtype=torch.bfloat16, device="cuda")
-    moe.ffn_down(T, h, hsf, d["weights"], plan, y)
+    moe.ffn_down(T, h, hsf, prepared(moe, d), plan, y)
     torch.cuda.synchronize()
     ridx = torch.as_tensor(rows, dtype=torch.int64, device="cuda")
     hc = h.index_select(0, ridx).cpu()
@@ -54,7 +54,7 @@ def test_named_workload_full_size(name):
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = moe.alloc_workspace(T)
     print(f"[fullsize] {name}: moe_forward T={T}", flush=True)
-    moe.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], d["weights"], out, ws)
+    moe.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], prepared(moe, d), out, ws)
     torch.cuda.synchronize()
     out_np = out.float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(out_np))
