@@ -550,39 +550,37 @@ static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
 
 // 8 waves x 32 weight rows; weight-ring depth per format and tile height, sized
 // to the registers of two waves per SIMD
-// (measured on the decode and prefill shapes)
+// Launch configuration per format, regime and leg: waves per workgroup, 16-row
+// column tiles per wave, weight-ring depth (K-steps) and K-steps per LDS stage
+// of the activations.  Chosen by measurement on the decode, prefill, Mixtral
+// BF16 and W4A8 shapes (deeper rings and stages cost registers and spill).
+struct LegConfig {
+  int waves, nt, depth, ksg;
+};
 template <Fmt F, bool GATEUP, int BM>
-constexpr int ring_depth() {
-  return F == Fmt::FP8 ? (BM <= 96 || !GATEUP ? 2 : 3) : F == Fmt::BF16 ? (BM <= 96 ? 8 : 5) : (BM <= 96 ? 8 : 6);
+constexpr LegConfig leg_config() {
+  if (BM <= 96) {  // weight-bound tiles
+    if (GATEUP) return {4, 4, 2, 1};  // 4 waves x 64 weight rows, two workgroups per CU
+    return {8, 2, 2, F == Fmt::FP8 ? 2 : 1};
+  }
+  // MFMA-bound tiles
+  if (F == Fmt::MX) return {8, 2, 6, 2};
+  return {8, 2, 2, F == Fmt::BF16 ? 1 : 2};
 }
+// output columns of a down tile
+constexpr int kDownBN = 256;
 
-// K-steps per LDS stage of the activation tile
 template <Fmt F, bool GATEUP, int BM>
-constexpr int stage_ksteps() {
-  return F == Fmt::BF16 || (F == Fmt::MX && !GATEUP && BM <= 96) ? 1 : 2;
+static void launch_leg(const GemmParams& gp, bool fast, hipStream_t s) {
+  constexpr LegConfig c = leg_config<F, GATEUP, BM>();
+  static_assert(GATEUP || c.waves * 16 * c.nt == kDownBN, "down tiles are kDownBN columns wide");
+  launch_one<F, GATEUP, BM, c.waves, c.nt, c.depth, c.ksg>(gp, fast, s);
 }
 
-// Output columns of a down tile.  Weight-bound tiles (BM <= 96): 4 waves x 32
-// rows and two workgroups per CU, so that one workgroup's prologue and epilogue
-// overlap the other's weight stream and the tail is finer; MFMA-bound tiles:
-// 8 waves x 32 rows.
-template <int BM>
-constexpr int down_tile_rows() {
-  return BM <= 96 ? 128 : 256;
-}
-
-// gate_up: one 128-column block of h per workgroup (256 weight rows): 4 waves x
-// 64 rows and two workgroups per CU for weight-bound tiles, 8 waves x 32 rows
-// for MFMA-bound ones
 template <Fmt F, int BM>
 static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
-  if (stage != 2) {
-    if constexpr (BM <= 96) launch_one<F, true, BM, 4, 4, 2, 1>(g1, fast, s);
-    else launch_one<F, true, BM, 8, 2, ring_depth<F, true, BM>(), stage_ksteps<F, true, BM>()>(g1, fast, s);
-  }
-  if (stage != 1)
-    launch_one<F, false, BM, down_tile_rows<BM>() / 32, 2, ring_depth<F, false, BM>(), stage_ksteps<F, false, BM>()>(
-        g2, fast, s);
+  if (stage != 2) launch_leg<F, true, BM>(g1, fast, s);
+  if (stage != 1) launch_leg<F, false, BM>(g2, fast, s);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
@@ -622,8 +620,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.clamp = a.clamp;
   // down: A = h rows, B = w2 [E, H, I]
   g2 = g1;
-  const int down_bn = a.bm <= 96 ? 128 : 256;  // down_tile_rows<BM>()
-  g2.n_tiles = (a.H + down_bn - 1) / down_bn;
+  g2.n_tiles = (a.H + kDownBN - 1) / kDownBN;
   g2.K = a.I;
   g2.ksteps = (a.I + elem_k - 1) / elem_k;
   g2.N = a.H;
