@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"fp8_block128": 5000.0, "bf16": 2500.0, "w4a8_mx": 5000.0}  # MX: f8 x f4 MFMA runs at the FP8 rate
 DTYPE = {"fp8_block128": "fp8_e4m3", "bf16": "bf16", "w4a8_mx": "mxfp4xmxfp8"}
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "device.h", "prepare.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -103,6 +103,44 @@ def cpu_baseline(sh, inp, ids, w, budget_s: float) -> dict:
                       f"BLAS threads={cores}, dequantisation single-threaded"}
 
 
+def write_counters(workload: str, fetch_dir: str, write_dir: str, command: str) -> int:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
+    both with --copy-calibration) into profiles/gate_up_counters.json: the gate_up
+    kernel's HBM bytes per launch, each counter scaled by what it reads for the
+    plain 1 GiB elementwise copy of the same run."""
+    import csv
+    import glob
+
+    def rows(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+
+    def gate_up(vals):
+        v = [x for n, x in vals if "ffn_gemm_kernel" in n and ", true, " in n.split(">")[0]]
+        return sum(v) / len(v)
+
+    def copy_kb(vals, want_kb):
+        v = [x for n, x in vals if "elementwise_kernel" in n and x > 0.25 * want_kb]
+        return sum(v) / len(v)
+
+    gib_kb = float(1 << 20)
+    fetch, write = rows(fetch_dir, "FETCH_SIZE"), rows(write_dir, "WRITE_SIZE")
+    f_kb, w_kb = gate_up(fetch), gate_up(write)
+    f_factor, w_factor = gib_kb / copy_kb(fetch, gib_kb), gib_kb / copy_kb(write, gib_kb)
+    traffic = (f_kb * f_factor + w_kb * w_factor) * 1024.0
+    out = {"workload": workload, "kernel_source_sha": kernel_source_hash(), "kernel": "ffn_gemm_kernel gate_up",
+           "fetch_kb_per_launch": f_kb, "write_kb_per_launch": w_kb, "fetch_copy_factor": f_factor,
+           "write_copy_factor": w_factor, "traffic_bytes_per_launch": round(traffic), "command": command}
+    with open(COUNTERS, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,9 +149,14 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_fp8")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/gate_up_counters.json from two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--counters-command", default="", help="the command the --pmc runs used (recorded)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
+    if args.write_counters:
+        return write_counters(args.workload, args.write_counters[0], args.write_counters[1], args.counters_command)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
