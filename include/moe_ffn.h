@@ -139,16 +139,20 @@ void moe_destroy(moe_handle* h);
 
 /* Prepared weight layout ([MegaFFN] takes its gate_up weight pre-permuted; here
    both weights are).  A weight matrix of R rows and K elements per row (w13: R =
-   2I, K = H; w2: R = H, K = I) is cut into tiles of 16 rows x one K-step (128
-   elements; 64 for BF16).  Tiles are stored expert-major, then by row block
-   rb = row / 16, then by K-step ks, each tile contiguous, with lane l = 16*g + r
-   (g < 4, r < 16) standing for row 16*rb + r:
-     FP8, BF16  2048-byte tile: byte half*1024 + 16*l + b (half < 2, b < 16) holds
-                byte ks*128 + 64*half + 16*g + b of the row (its 128-byte K-step segment)
-     MX         1024-byte tile: byte 16*l + b holds byte ks*64 + 16*g + b of the
-                packed E2M1 row, zero past the row's end
-     MX scales  64-byte tile: byte l holds the UE8M0 byte of K-block 4*ks + g of
-                the row, zero past the row's end
+   2I, K = H; w2: R = H, K = I) is cut into tiles of RT rows x one K-step,
+   stored expert-major, then by row block rb = row / RT, then by K-step ks, each
+   tile contiguous:
+     FP8   RT 16, K-step 128, 2048-byte tile: byte 1024*piece + 16*l + b
+           (piece < 2, l = 16*g + r, g < 4, r < 16, b < 16) holds byte
+           ks*128 + 64*piece + 16*g + b of row 16*rb + r
+     MX    RT 16, K-step 128, 1024-byte tile: byte 16*l + b (l = 16*g + r) holds
+           byte ks*64 + 16*g + b of packed E2M1 row 16*rb + r, zero past the row's end
+     MX scales: 64-byte tile: byte l (l = 16*g + r) holds the UE8M0 byte of
+           K-block 4*ks + g of row 16*rb + r, zero past the row's end
+     BF16  RT 32, K-step 64, 4096-byte tile: byte 1024*sub + 16*l + b
+           (sub < 4, l = 32*h + r, h < 2, r < 32) holds byte ks*128 + 32*sub + 16*h + b
+           of tile row 32*rb + r; for w13 tile row 32*j + q is gate row 16*j + q
+           (q < 16) or up row 16*j + q - 16 (q >= 16), for w2 it is row 32*j + q
      FP8 scales unchanged.
    moe_prepared_weights_size gives the sizes; moe_prepare_weights writes them. */
 moe_status moe_prepared_weights_size(const moe_handle* h, moe_prepared_sizes* out /* host */);

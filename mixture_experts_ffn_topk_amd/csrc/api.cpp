@@ -224,10 +224,10 @@ moe_status moe_prepare_weights(const moe_handle* h, const moe_weights* canonical
   if (prepared->w13 == canonical->w13 || prepared->w2 == canonical->w2) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = h->cfg;
   const moe::Fmt f = to_fmt(c.format);
-  hipError_t e = moe::launch_prepare(f, c.num_experts, 2 * c.intermediate_hidden, c.hidden, canonical->w13,
+  hipError_t e = moe::launch_prepare(f, c.num_experts, 2 * c.intermediate_hidden, c.hidden, true, canonical->w13,
                                      canonical->w13_sf, (void*)prepared->w13, (void*)prepared->w13_sf, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_prepare(f, c.num_experts, c.hidden, c.intermediate_hidden, canonical->w2, canonical->w2_sf,
+  e = moe::launch_prepare(f, c.num_experts, c.hidden, c.intermediate_hidden, false, canonical->w2, canonical->w2_sf,
                           (void*)prepared->w2, (void*)prepared->w2_sf, stream);
   return hip_status(e);
 }

@@ -118,11 +118,19 @@ struct Tile {
   static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? 2 * kMaxKSteps * 4 : 0);
 };
 
-// WAVES waves per workgroup and 8 / WAVES workgroups per CU: two waves per SIMD.
-template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, bool FAST>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmParams p) {
+// WAVES waves per workgroup and room for WGS workgroups per CU: the second
+// launch bound is the minimum number of waves per SIMD, which caps a wave's
+// registers at 512 / that number.
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, int WGS, bool FAST>
+__global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_kernel(GemmParams p) {
   using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
   constexpr int BN = TL::BN;
+  constexpr int MT32 = BM / 32, NT32 = NT / 2;  // BF16: 32-row token slices and weight tiles
+  static_assert(F != Fmt::BF16 || BM % 32 == 0, "BF16 tiles hold whole 32-token slices");
+  // Weight-bound tiles skip the 16-row token slices past the tile's rows (experts
+  // smaller than the tile).  MFMA-bound tiles are almost always full, and the
+  // branch would split the K-step into blocks the scheduler cannot interleave.
+  constexpr bool kSkipSlices = BM <= 96 || F == Fmt::BF16;  // (BF16 measured faster with the skip)
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
   static_assert(!GATEUP || BN / 2 == kHCols, "a gate_up tile is one 128-column block of h");
   constexpr int MT = TL::MT;
@@ -196,8 +204,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
         col0 = n_tile * BN + wave * 16 * NT + 16 * nt;
         wrow0 = col0;
       }
+      uint32_t tiles0 = (uint32_t)(wrow0 / 16) * (uint32_t)p.ksteps;  // first tile of the row block
+      if (F == Fmt::BF16) {
+        // 32-row tiles: gate_up tile j holds gate rows [16j, 16j+16) then the
+        // matching up rows; down tile j holds rows [32j, 32j+32)
+        const int t = nt < NT32 ? nt : 0;
+        col0 = GATEUP ? n_tile * kHCols + wave * HW + 16 * t : n_tile * BN + wave * 16 * NT + 32 * t;
+        tiles0 = (uint32_t)(GATEUP ? col0 / 16 : col0 / 32) * (uint32_t)p.ksteps;
+      }
       const bool ok = col0 < p.N;
-      const uint32_t tiles0 = (uint32_t)(wrow0 / 16) * (uint32_t)p.ksteps;  // first tile of the row block
       b_off[nt] = ok ? tiles0 * p.b_tile + (uint32_t)lane * 16u : kOOB;
       bsc_off[nt] = ok ? tiles0 * 64u + (uint32_t)lane : kOOB;
     }
@@ -219,6 +234,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
     const uint32_t dead = oob_if(ks >= p.ksteps);  // (the prepared layout is zero past a row's end)
+    if constexpr (F == Fmt::BF16) {
+      // 32-row tile t: four 1 KB sub-step pieces
+#pragma unroll
+      for (int t = 0; t < NT32; ++t) {
+        const uint32_t o = b_off[t] | dead;
+        b.lo[2 * t] = bload16(b_rs, o, (uint32_t)ks * p.b_tile);
+        b.lo[2 * t + 1] = bload16(b_rs, o + 1024u, (uint32_t)ks * p.b_tile);
+        b.hi[2 * t] = bload16(b_rs, o + 2048u, (uint32_t)ks * p.b_tile);
+        b.hi[2 * t + 1] = bload16(b_rs, o + 3072u, (uint32_t)ks * p.b_tile);
+      }
+      return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint32_t o = b_off[nt] | dead;
@@ -241,11 +268,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
   const int pair_of_row = (!GATEUP && tid < rows) ? p.src_info[row0 + tid] : 0;
 
   // ---------------------------------------------------------------- main loop
-  f32x4 acc[MT][NT];
+  // FP8, MX: 16x16 tiles acc[token slice][weight tile]; BF16: 32x32 tiles
+  // acc32[32-token slice][32-row weight tile] (v_mfma_f32_32x32x16_bf16)
+  f32x4 acc[F == Fmt::BF16 ? 1 : MT][F == Fmt::BF16 ? 1 : NT];
+  f32x16 acc32[F == Fmt::BF16 ? MT32 : 1][F == Fmt::BF16 ? NT32 : 1];
+  if constexpr (F == Fmt::BF16) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NT32; ++t) acc32[mt][t] = f32x16{};
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---------------------------------------------------------------- A (activation) addressing
   // A is staged KSG K-steps at a time.  For each K-step of a stage, thread tid
@@ -341,7 +378,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
       const float sbv0 = sb_lds[kc], sbv1 = sb_lds[TL::kMaxKSteps + kc];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (mt * 16 >= rows) break;  // wave-uniform: no token rows left in this slice
+        if (kSkipSlices && mt * 16 >= rows) break;  // wave-uniform: no token rows left
         const i32x8 a8 = __builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7);
         const float sa = __builtin_bit_cast(float, sbuf[mt * 16 + r16]);
 #pragma unroll
@@ -352,20 +389,31 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
           acc[mt][nt] += part * (sa * (sb_row(nt) ? sbv1 : sbv0));
         }
       }
+    } else if constexpr (F == Fmt::BF16) {
+      // 32x32x16 MFMAs: lane l = 32*h + r holds token mt*32 + r and bytes
+      // [32*sub + 16*h, +16) of the K-step segment; weight sub-step fragments
+      // are bq_.lo[2t], lo[2t+1], hi[2t], hi[2t+1] for sub = 0..3
+      const int r32 = lane & 31, h32 = lane >> 5;
+#pragma unroll
+      for (int mt = 0; mt < MT32; ++mt) {
+        if (kSkipSlices && mt * 32 >= rows) break;  // wave-uniform: no token rows left
+        const uint8_t* arow = abuf + (mt * 32 + r32) * TL::kAStride + 16 * h32;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const i32x4 a = *(const i32x4*)(arow + 32 * sub);
+#pragma unroll
+          for (int t = 0; t < NT32; ++t) {
+            const i32x4 b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
+            acc32[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
+                                                                   __builtin_bit_cast(bf16x8, a), acc32[mt][t], 0, 0, 0);
+          }
+        }
+      }
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (F == Fmt::BF16 && mt * 16 >= rows) break;  // wave-uniform: no token rows left in this slice
         const i32x4 alo = rd_lo(mt), ahi = rd_hi(mt);
-        if (F == Fmt::BF16) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq_.lo[nt]),
-                                                                  __builtin_bit_cast(bf16x8, alo), acc[mt][nt], 0, 0, 0);
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bq_.hi[nt]),
-                                                                  __builtin_bit_cast(bf16x8, ahi), acc[mt][nt], 0, 0, 0);
-          }
-        } else {
+        {
           // weights E2M1 (first operand, format 4), activations E4M3 (format 0);
           // each lane's scale byte: its row (weight row / token) in K-block g
           const i32x8 a8 = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -398,7 +446,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
       // its previous contents (the two values would then both be live): tie the
       // load's scalar offset to the step's last accumulator update.
       int ks_next = ks + DEPTH;
-      asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
+      if constexpr (F == Fmt::BF16)
+        asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc32[MT32 - 1][NT32 - 1][15]));
+      else
+        asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
       load_b(slot, ks_next);
     }
     store_a(an, sn, (su + 1) & 1);
@@ -422,26 +473,36 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
   // ---------------------------------------------------------------- epilogue
   // Lane (r16, g) holds, for token slice mt, token row mt*16 + r16 and the wave's
   // weight rows 16*nt + 4g + i (i < 4): four consecutive output columns.
+  // BF16 (32x32 tiles): lane l = 32*h32 + r32 holds token mt*32 + r32 and the
+  // tile's rows 8*(i/4) + 4*h32 + i%4 (i < 16); in a gate_up tile rows < 16 are
+  // gate rows and row 16 + j the up row of gate row j, so acc32[..][i] pairs with [i + 8].
+  const int r32 = lane & 31, h32 = lane >> 5;
   if (GATEUP) {
     constexpr int NJ = NT / 2;  // gate (and up) column tiles per wave
     const float c = p.clamp;
-    float h[MT][NJ][4];
+    if constexpr (F == Fmt::BF16) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+        for (int t = 0; t < NT32; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[mt][j][i] = swiglu_clamped<FAST>(acc[mt][j][i], acc[mt][j + NJ][i], c);
-    if (F == Fmt::BF16) {
+          for (int q = 0; q < 2; ++q) {  // gate rows 8q + 4*h32 + (0..3)
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = swiglu_clamped<FAST>(acc32[mt][t][4 * q + i], acc32[mt][t][4 * q + i + 8], c);
+            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            *(uint2*)(out_lds + (mt * 32 + r32) * TL::kOutStride + (wave * HW + 16 * t + 8 * q + 4 * h32) * 2) =
+                uint2{w0, w1};
+          }
+    } else {
+      float h[MT][NJ][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(h[mt][j][0]) | ((uint32_t)f32_to_bf16_rne(h[mt][j][1]) << 16);
-          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(h[mt][j][2]) | ((uint32_t)f32_to_bf16_rne(h[mt][j][3]) << 16);
-          *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * HW + 16 * j + 4 * g) * 2) = uint2{w0, w1};
-        }
-    } else {
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[mt][j][i] = swiglu_clamped<FAST>(acc[mt][j][i], acc[mt][j + NJ][i], c);
       // per-row amax over this wave's HW columns (4 values x NJ tiles in a lane,
       // then the 4 lanes g of the row), then over the waves sharing a
       // requantisation block (all of them for FP8's 128 columns, 32/HW of them
@@ -500,14 +561,29 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void ffn_gemm_kernel(GemmPar
     }
   } else {
     // down: bf16 rows scattered to their pair slots y[src_info[row]]
+    if constexpr (F == Fmt::BF16) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][0]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][1]) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][3]) << 16);
-        *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * 16 * NT + 16 * nt + 4 * g) * 2) = uint2{w0, w1};
-      }
+        for (int t = 0; t < NT32; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {  // rows 8q + 4*h32 + (0..3) of the tile
+            const f32x16& a = acc32[mt][t];
+            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(a[4 * q]) | ((uint32_t)f32_to_bf16_rne(a[4 * q + 1]) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(a[4 * q + 2]) | ((uint32_t)f32_to_bf16_rne(a[4 * q + 3]) << 16);
+            *(uint2*)(out_lds + (mt * 32 + r32) * TL::kOutStride + (wave * 16 * NT + 32 * t + 8 * q + 4 * h32) * 2) =
+                uint2{w0, w1};
+          }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][0]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][3]) << 16);
+          *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * 16 * NT + 16 * nt + 4 * g) * 2) = uint2{w0, w1};
+        }
+    }
     int* pair_lds = (int*)red_lds;  // [BM]
     if (tid < BM) pair_lds[tid] = pair_of_row;
     __syncthreads();
@@ -536,16 +612,16 @@ int ffn_max_m_tiles(int npairs, int E, int bm) {
   return (int)(((long long)npairs + act * (bm - 1)) / bm);
 }
 
-template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG>
+template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, int WGS>
 static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
   const int grid = gp.m_tiles_max * gp.n_tiles;
   if (grid <= 0) return;
   if (fast)
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, true>), dim3(grid), dim3(64 * WAVES), 0,
-                       s, gp);
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, true>), dim3(grid),
+                       dim3(64 * WAVES), 0, s, gp);
   else
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, false>), dim3(grid), dim3(64 * WAVES), 0,
-                       s, gp);
+    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, false>), dim3(grid),
+                       dim3(64 * WAVES), 0, s, gp);
 }
 
 // 8 waves x 32 weight rows; weight-ring depth per format and tile height, sized
@@ -555,17 +631,18 @@ static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
 // of the activations.  Chosen by measurement on the decode, prefill, Mixtral
 // BF16 and W4A8 shapes (deeper rings and stages cost registers and spill).
 struct LegConfig {
-  int waves, nt, depth, ksg;
+  int waves, nt, depth, ksg, wgs;  // wgs: workgroups per CU the registers must allow
 };
 template <Fmt F, bool GATEUP, int BM>
 constexpr LegConfig leg_config() {
   if (BM <= 96) {  // weight-bound tiles
-    if (GATEUP) return {4, 4, 2, 1};  // 4 waves x 64 weight rows, two workgroups per CU
-    return {8, 2, 2, F == Fmt::FP8 ? 2 : 1};
+    if (GATEUP) return {4, 4, 2, 1, 2};  // 4 waves x 64 weight rows, two workgroups per CU
+    return {8, 2, 2, F == Fmt::FP8 ? 2 : 1, 1};
   }
-  // MFMA-bound tiles
-  if (F == Fmt::MX) return {8, 2, 6, 2};
-  return {8, 2, 2, F == Fmt::BF16 ? 1 : 2};
+  // MFMA-bound tiles (BF16 fits two workgroups per CU in registers and LDS)
+  if (F == Fmt::MX) return {8, 2, 6, 2, 1};
+  if (F == Fmt::BF16) return {8, 2, 2, 1, 2};
+  return {8, 2, 2, 2, 1};
 }
 // output columns of a down tile
 constexpr int kDownBN = 256;
@@ -574,7 +651,7 @@ template <Fmt F, bool GATEUP, int BM>
 static void launch_leg(const GemmParams& gp, bool fast, hipStream_t s) {
   constexpr LegConfig c = leg_config<F, GATEUP, BM>();
   static_assert(GATEUP || c.waves * 16 * c.nt == kDownBN, "down tiles are kDownBN columns wide");
-  launch_one<F, GATEUP, BM, c.waves, c.nt, c.depth, c.ksg>(gp, fast, s);
+  launch_one<F, GATEUP, BM, c.waves, c.nt, c.depth, c.ksg, c.wgs>(gp, fast, s);
 }
 
 template <Fmt F, int BM>
@@ -595,7 +672,9 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.src_info = a.src_info;
   g1.E = a.E;
   g1.topk = a.topk;
-  g1.m_tiles_max = ffn_max_m_tiles(npairs, a.E, a.bm);
+  // BF16 weight-bound tiles are 96 rows (whole 32-token slices of its 32x32 MFMA)
+  const int bm = (a.fmt == Fmt::BF16 && a.bm <= 96) ? 96 : a.bm;
+  g1.m_tiles_max = ffn_max_m_tiles(npairs, a.E, bm);
   g1.n_tiles = (a.I + kHCols - 1) / kHCols;
   g1.K = a.H;
   g1.ksteps = (a.H + elem_k - 1) / elem_k;
@@ -646,8 +725,8 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
       else launch_pair<Fmt::FP8, 80>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::BF16:
-      if (a.bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::BF16, 80>(g1, g2, a.fast, s, stage);
+      if (bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::BF16, 96>(g1, g2, a.fast, s, stage);
       break;
     case Fmt::MX:
       if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage);

@@ -32,13 +32,14 @@ hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, vo
                                     float* w_out, bool fast, hipStream_t s);
 
 // Prepared weight layout: tiles of 16 rows x one K-step in MFMA lane order.
-size_t prepared_tile_bytes(Fmt f);                           // 2048 (FP8, BF16) or 1024 (MX)
+size_t prepared_tile_bytes(Fmt f);                           // 2048 (FP8), 4096 (BF16) or 1024 (MX)
 int prepared_ksteps(Fmt f, int K);                           // K-steps of 128 (64 for BF16) elements
 size_t prepared_expert_bytes(Fmt f, int rows, int K);        // one expert's weight tiles
 size_t prepared_scale_expert_bytes(Fmt f, int rows, int K);  // MX: one expert's scale tiles; else 0
 // Relayout E experts' [rows, K] weights (and MX scales; FP8 scales are copied).
-hipError_t launch_prepare(Fmt f, int E, int rows, int K, const void* w, const void* w_sf, void* out, void* out_sf,
-                          hipStream_t s);
+// gate_up: the matrix is the gate_up weight (BF16 interleaves its gate and up rows).
+hipError_t launch_prepare(Fmt f, int E, int rows, int K, bool gate_up, const void* w, const void* w_sf, void* out,
+                          void* out_sf, hipStream_t s);
 
 // Grouped GEMMs over prepared weights.  Tile rows per workgroup (BM) by regime.
 struct FfnArgs {

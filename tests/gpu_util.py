@@ -55,7 +55,7 @@ def prepared(moe: MoEFFN, d: dict) -> dict:
     return d["weights"]
 
 
-def prepared_layout_reference(fmt: str, w: np.ndarray, sf: np.ndarray | None, rows: int, K: int):
+def prepared_layout_reference(fmt: str, w: np.ndarray, sf: np.ndarray | None, rows: int, K: int, gate_up: bool):
     """The prepared layout written out from its definition in include/moe_ffn.h
     (numpy index arithmetic, independent of the library)."""
     E = w.shape[0]
@@ -73,6 +73,14 @@ def prepared_layout_reference(fmt: str, w: np.ndarray, sf: np.ndarray | None, ro
     row_bytes = K * (2 if fmt == "bf16" else 1)
     ks = row_bytes // 128
     wb = np.ascontiguousarray(w).view(np.uint8).reshape(E, rows, row_bytes)
+    if fmt == "bf16":
+        if gate_up:  # tile j: gate rows 16j..16j+15, then up rows 16j..16j+15
+            half = rows // 2
+            order = np.stack([np.arange(half).reshape(-1, 16), half + np.arange(half).reshape(-1, 16)], 1).reshape(-1)
+            wb = wb[:, order]
+        # [E, rb, r(32), ks, sub, h, b] -> [E, rb, ks, sub, h, r, b]
+        t = wb.reshape(E, rows // 32, 32, ks, 4, 2, 16).transpose(0, 1, 3, 4, 5, 2, 6)
+        return t.reshape(-1), None
     # [E, rb, r, ks, half, g, b] -> [E, rb, ks, half, g, r, b]
     t = wb.reshape(E, rb, 16, ks, 2, 4, 16).transpose(0, 1, 3, 4, 5, 2, 6)
     return t.reshape(-1), (None if sf is None else np.ascontiguousarray(sf).view(np.uint8).reshape(-1))

@@ -130,7 +130,7 @@ def test_prepare_weights_layout(fmt, H, I):
     torch.cuda.synchronize()
     sizes = moe.prepared_weights_size()
     for name, rows, K in (("w13", 2 * I, H), ("w2", H, I)):
-        want, want_sf = prepared_layout_reference(fmt, inp[name], inp[name + "_sf"], rows, K)
+        want, want_sf = prepared_layout_reference(fmt, inp[name], inp[name + "_sf"], rows, K, name == "w13")
         got = pw[name].cpu().numpy()
         assert got.size == sizes[name] == want.size
         assert np.array_equal(got, want), f"{name}: first mismatch at byte {int(np.argmax(got != want))}"
