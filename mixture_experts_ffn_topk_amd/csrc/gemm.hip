@@ -115,7 +115,9 @@ struct Tile {
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
   static constexpr int kSA = kThreads > BM ? kThreads : BM;  // A-scale slots per buffer (one per thread)
   static constexpr int kMaxKSteps = 256;  // FP8 weight scales of up to 256 K-steps staged in LDS
-  static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? 2 * kMaxKSteps * 4 : 0);
+  // FP8 weight-scale blocks (128 rows) a tile touches: gate and up block, or a down window of BN rows
+  static constexpr int kNB = GATEUP ? 2 : BN / 128 + 1;
+  static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? kNB * kMaxKSteps * 4 : 0);
 };
 
 // WAVES waves per workgroup and room for WGS workgroups per CU: the second
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   uint8_t* out_lds = lds;                                        // aliases a_lds after the K loop
   uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [2][KSG][kSA] (fp32 bits or 4 UE8M0 bytes)
   float* red_lds = (float*)(lds + TL::kUnion + 2 * KSG * TL::kSA * 4);  // [WAVES][BM]
-  float* sb_lds = red_lds + WAVES * BM;                      // FP8: [2][kMaxKSteps] weight scales
+  float* sb_lds = red_lds + WAVES * BM;                      // FP8: [kNB][kMaxKSteps] weight scales
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
 
@@ -217,20 +219,21 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       bsc_off[nt] = ok ? tiles0 * 64u + (uint32_t)lane : kOOB;
     }
     if (F == Fmt::FP8) {
-      // the tile's weight-scale rows, staged in LDS: [0] the gate block (gate_up) or
-      // the first 128-row block (down), [1] the up block or the second 128-row block
+      // the tile's weight-scale rows, staged in LDS: gate_up [0] the gate block,
+      // [1] the up block; down: the kNB 128-row blocks from the tile's first
       const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
-      const int blk0 = GATEUP ? n_tile : min(n_tile * BN / 128, p.n_rows / 128 - 1);
-      const int blk1 = GATEUP ? p.N / 128 + n_tile : min(n_tile * BN / 128 + 1, p.n_rows / 128 - 1);
-      for (int i = tid; i < 2 * p.ksteps; i += kThreads)
-        sb_lds[(i >= p.ksteps) * TL::kMaxKSteps + i % p.ksteps] =
-            sfe[(size_t)(i >= p.ksteps ? blk1 : blk0) * p.b_sf_row + i % p.ksteps];
+      const int nblk = p.n_rows / 128;
+      for (int i = tid; i < TL::kNB * p.ksteps; i += kThreads) {
+        const int j = i / p.ksteps, k = i - j * p.ksteps;
+        const int blk = GATEUP ? (j == 0 ? n_tile : p.N / 128 + n_tile) : min(n_tile * BN / 128 + j, nblk - 1);
+        sb_lds[j * TL::kMaxKSteps + k] = sfe[(size_t)blk * p.b_sf_row + k];
+      }
     }
   }
   // FP8: which staged scale row this wave's column tile nt uses
   auto sb_row = [&](int nt) {
     if (GATEUP) return nt >= NT / 2 ? 1 : 0;
-    return ((n_tile * BN) % 128 + wave * 16 * NT + 16 * nt) >= 128 ? 1 : 0;
+    return ((n_tile * BN) % 128 + wave * 16 * NT + 16 * nt) / 128;
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
     const uint32_t dead = oob_if(ks >= p.ksteps);  // (the prepared layout is zero past a row's end)
@@ -375,7 +378,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // one 16x16x128 FP8 MFMA per K-step (unit hardware scales) into a fresh
       // partial, then acc += (sa[token] * sb[block]) * partial
       const int kc = min(ks, KS - 1);  // a step past the end multiplies zeros
-      const float sbv0 = sb_lds[kc], sbv1 = sb_lds[TL::kMaxKSteps + kc];
+      float sbv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sbv[nt] = sb_lds[sb_row(nt) * TL::kMaxKSteps + kc];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (kSkipSlices && mt * 16 >= rows) break;  // wave-uniform: no token rows left
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
           const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
           const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                               0, 127, 0, 127);
-          acc[mt][nt] += part * (sa * (sb_row(nt) ? sbv1 : sbv0));
+          acc[mt][nt] += part * (sa * sbv[nt]);
         }
       }
     } else if constexpr (F == Fmt::BF16) {
@@ -637,27 +642,30 @@ template <Fmt F, bool GATEUP, int BM>
 constexpr LegConfig leg_config() {
   if (BM <= 96) {  // weight-bound tiles
     if (GATEUP) return {4, 4, 2, 1, 2};  // 4 waves x 64 weight rows, two workgroups per CU
-    return {8, 2, 2, F == Fmt::FP8 ? 2 : 1, 1};
+    if (F == Fmt::FP8) return {7, 4, 2, 1, 1};  // 448 columns: 7168 = 16 tiles (two even rounds of 256)
+    return {8, 2, 2, 1, 1};
   }
   // MFMA-bound tiles (BF16 fits two workgroups per CU in registers and LDS)
   if (F == Fmt::MX) return {8, 2, 6, 2, 1};
   if (F == Fmt::BF16) return {8, 2, 2, 1, 2};
   return {8, 2, 2, 2, 1};
 }
-// output columns of a down tile
-constexpr int kDownBN = 256;
-
 template <Fmt F, bool GATEUP, int BM>
 static void launch_leg(const GemmParams& gp, bool fast, hipStream_t s) {
   constexpr LegConfig c = leg_config<F, GATEUP, BM>();
-  static_assert(GATEUP || c.waves * 16 * c.nt == kDownBN, "down tiles are kDownBN columns wide");
   launch_one<F, GATEUP, BM, c.waves, c.nt, c.depth, c.ksg, c.wgs>(gp, fast, s);
 }
 
 template <Fmt F, int BM>
-static void launch_pair(const GemmParams& g1, const GemmParams& g2, bool fast, hipStream_t s, int stage) {
+static void launch_pair(const GemmParams& g1, const GemmParams& g2_in, bool fast, hipStream_t s, int stage) {
   if (stage != 2) launch_leg<F, true, BM>(g1, fast, s);
-  if (stage != 1) launch_leg<F, false, BM>(g2, fast, s);
+  if (stage != 1) {
+    constexpr LegConfig c = leg_config<F, false, BM>();
+    constexpr int bn = c.waves * 16 * c.nt;  // output columns of a down tile
+    GemmParams g2 = g2_in;
+    g2.n_tiles = (g2.N + bn - 1) / bn;
+    launch_leg<F, false, BM>(g2, fast, s);
+  }
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
@@ -699,7 +707,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.clamp = a.clamp;
   // down: A = h rows, B = w2 [E, H, I]
   g2 = g1;
-  g2.n_tiles = (a.H + kDownBN - 1) / kDownBN;
+  // (g2.n_tiles is set by the down leg's launch from its tile width)
   g2.K = a.I;
   g2.ksteps = (a.I + elem_k - 1) / elem_k;
   g2.N = a.H;
