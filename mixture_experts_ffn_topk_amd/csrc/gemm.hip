@@ -34,7 +34,6 @@
 
 namespace moe {
 
-constexpr int kHCols = 128;      // gate_up: h columns per workgroup tile (one FP8 requant block)
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
 
 // kOOB if dead, else 0: OR-ed into a lane offset below 2^31 it turns the load
@@ -103,20 +102,29 @@ struct Tile {
   static constexpr int kThreads = 64 * WAVES;
   static constexpr int BN = WAVES * 16 * NT;  // weight rows per workgroup tile
   static constexpr int MT = BM / 16;
-  static constexpr int kAStride = 128 * KSG + 16;  // LDS bytes per A row: KSG K-steps + bank padding
+  // A is staged per K-step as kARows rows.  FP8 / MX: rows of 128 bytes, the
+  // 16-byte chunk c of row r stored at chunk c ^ (r & 7), so that the 16 rows of
+  // an MFMA fragment read spread over all LDS banks (a padded row stride still
+  // halves the read rate).  BF16 keeps a padded 144-byte row: its 32-row
+  // fragments read well enough, and the swizzle's extra offsets do not fit the
+  // register budget of its 4-workgroup tiles.
+  static constexpr int kSwz = F == Fmt::BF16 ? 0 : 7;
+  static constexpr int kARowBytes = F == Fmt::BF16 ? 144 : 128;
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
   // A buffer rows: BM rounded up so that every thread stores every chunk it loads
   // (chunks past BM rows are zeros landing in spare rows): no divergent stores in the loop
   static constexpr int kARows = kAChunks * kThreads / 8;
   static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (F == Fmt::BF16 ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
-  static constexpr int kABytes = 2 * kARows * kAStride;
+  static constexpr int kAStepBytes = kARows * kARowBytes;
+  static constexpr int kABytes = 2 * KSG * kAStepBytes;
   static constexpr int kOutBytes = BM * kOutStride;
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
   static constexpr int kSA = kThreads > BM ? kThreads : BM;  // A-scale slots per buffer (one per thread)
   static constexpr int kMaxKSteps = 256;  // FP8 weight scales of up to 256 K-steps staged in LDS
   // FP8 weight-scale blocks (128 rows) a tile touches: gate and up block, or a down window of BN rows
-  static constexpr int kNB = GATEUP ? 2 : BN / 128 + 1;
+  static constexpr int kHB = BN / 2 / 128;  // gate_up: 128-column h blocks per tile
+  static constexpr int kNB = GATEUP ? 2 * kHB : BN / 128 + 1;
   static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? kNB * kMaxKSteps * 4 : 0);
 };
 
@@ -133,13 +141,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // smaller than the tile).  MFMA-bound tiles are almost always full, and the
   // branch would split the K-step into blocks the scheduler cannot interleave.
   constexpr bool kSkipSlices = BM <= 96 || F == Fmt::BF16;  // (BF16 measured faster with the skip)
+  constexpr bool kPrio = BM > 96 && F != Fmt::BF16;  // (measured: helps MFMA-bound FP8 / MX tiles only)
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
-  static_assert(!GATEUP || BN / 2 == kHCols, "a gate_up tile is one 128-column block of h");
+  constexpr int HC = BN / 2;  // gate_up: h columns per tile (gate and up rows, NT/2 tiles each per wave)
+  static_assert(!GATEUP || HC % 128 == 0, "a gate_up tile holds whole 128-column blocks of h");
   constexpr int MT = TL::MT;
   constexpr int kThreads = TL::kThreads;
   constexpr int HW = 8 * NT;  // gate_up: h columns per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kLds];
-  uint8_t* a_lds = lds;                                          // [2][kARows][kAStride]
+  uint8_t* a_lds = lds;                                          // [2][KSG][kARows][kARowBytes]
   uint8_t* out_lds = lds;                                        // aliases a_lds after the K loop
   uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [2][KSG][kSA] (fp32 bits or 4 UE8M0 bytes)
   float* red_lds = (float*)(lds + TL::kUnion + 2 * KSG * TL::kSA * 4);  // [WAVES][BM]
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     for (int nt = 0; nt < NT; ++nt) {
       int wrow0, col0;  // first weight row and first output column of the 16-row tile
       if (GATEUP) {
-        col0 = n_tile * kHCols + wave * HW + 16 * (nt % (NT / 2));  // h column
+        col0 = n_tile * HC + wave * HW + 16 * (nt % (NT / 2));  // h column
         wrow0 = (nt < NT / 2 ? 0 : p.N) + col0;                      // gate rows, then up rows
       } else {
         col0 = n_tile * BN + wave * 16 * NT + 16 * nt;
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         // 32-row tiles: gate_up tile j holds gate rows [16j, 16j+16) then the
         // matching up rows; down tile j holds rows [32j, 32j+32)
         const int t = nt < NT32 ? nt : 0;
-        col0 = GATEUP ? n_tile * kHCols + wave * HW + 16 * t : n_tile * BN + wave * 16 * NT + 32 * t;
+        col0 = GATEUP ? n_tile * HC + wave * HW + 16 * t : n_tile * BN + wave * 16 * NT + 32 * t;
         tiles0 = (uint32_t)(GATEUP ? col0 / 16 : col0 / 32) * (uint32_t)p.ksteps;
       }
       const bool ok = col0 < p.N;
@@ -219,20 +229,23 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       bsc_off[nt] = ok ? tiles0 * 64u + (uint32_t)lane : kOOB;
     }
     if (F == Fmt::FP8) {
-      // the tile's weight-scale rows, staged in LDS: gate_up [0] the gate block,
-      // [1] the up block; down: the kNB 128-row blocks from the tile's first
+      // the tile's weight-scale rows, staged in LDS: gate_up [0, kHB) the gate
+      // blocks, [kHB, 2 kHB) the up blocks; down: the kNB 128-row blocks from the
+      // tile's first (blocks past the last stand in for dead columns)
       const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
       const int nblk = p.n_rows / 128;
       for (int i = tid; i < TL::kNB * p.ksteps; i += kThreads) {
         const int j = i / p.ksteps, k = i - j * p.ksteps;
-        const int blk = GATEUP ? (j == 0 ? n_tile : p.N / 128 + n_tile) : min(n_tile * BN / 128 + j, nblk - 1);
+        const int hb = TL::kHB, hblk = p.N / 128;
+        const int blk = GATEUP ? (j < hb ? min(n_tile * hb + j, hblk - 1) : hblk + min(n_tile * hb + j - hb, hblk - 1))
+                               : min(n_tile * BN / 128 + j, nblk - 1);
         sb_lds[j * TL::kMaxKSteps + k] = sfe[(size_t)blk * p.b_sf_row + k];
       }
     }
   }
   // FP8: which staged scale row this wave's column tile nt uses
   auto sb_row = [&](int nt) {
-    if (GATEUP) return nt >= NT / 2 ? 1 : 0;
+    if (GATEUP) return (nt >= NT / 2 ? TL::kHB : 0) + (wave * HW + 16 * (nt % (NT / 2))) / 128;
     return ((n_tile * BN) % 128 + wave * 16 * NT + 16 * nt) / 128;
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
@@ -344,14 +357,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   };
   auto store_a = [&](const i32x4 (&v)[KSG][TL::kAChunks], const uint32_t (&s)[KSG], int buf) {
-    uint8_t* base = a_lds + buf * TL::kARows * TL::kAStride;
 #pragma unroll
-    for (int u = 0; u < KSG; ++u)
+    for (int u = 0; u < KSG; ++u) {
+      uint8_t* base = a_lds + (buf * KSG + u) * TL::kAStepBytes;
 #pragma unroll
       for (int i = 0; i < TL::kAChunks; ++i) {
-        const int c = tid + kThreads * i;
-        *(i32x4*)(base + (c >> 3) * TL::kAStride + u * 128 + (c & 7) * 16) = v[u][i];
+        const int c = tid + kThreads * i, r = c >> 3;
+        *(i32x4*)(base + r * TL::kARowBytes + (((c & 7) ^ (r & TL::kSwz)) * 16)) = v[u][i];
       }
+    }
     if (F != Fmt::BF16) {
 #pragma unroll
       for (int u = 0; u < KSG; ++u) sa_lds[(buf * KSG + u) * TL::kSA + tid] = s[u];
@@ -366,11 +380,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 
   // One K-step on the staged A of LDS buffer `buf` (K-step u of the stage) and B(ks) in `bq_`.
   auto kstep = [&](const BFrag<F, NT>& bq_, int buf, int u, int ks) {
-    const uint8_t* abuf = a_lds + buf * TL::kARows * TL::kAStride + u * 128;
+    const uint8_t* abuf = a_lds + (buf * KSG + u) * TL::kAStepBytes;
     const uint32_t* sbuf = sa_lds + (buf * KSG + u) * TL::kSA;
     // activation fragment of token slice mt: token row mt*16 + r16, bytes [16g, 16g+16) and [64+16g, 64+16g+16)
-    auto rd_lo = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * TL::kAStride + 16 * g); };
-    auto rd_hi = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * TL::kAStride + 64 + 16 * g); };
+    // (token row mt*16 + r16 has row & 7 == r16 & 7: the swizzled chunk offsets are per lane)
+    const int lo_off = 16 * (g ^ (r16 & TL::kSwz)), hi_off = lo_off ^ 64;
+    auto rd_lo = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * TL::kARowBytes + lo_off); };
+    auto rd_hi = [&](int mt) { return *(const i32x4*)(abuf + (mt * 16 + r16) * TL::kARowBytes + hi_off); };
     // The weights are the MFMA's first operand and the activations its second, so
     // a lane's outputs are 4 weight rows (16*nt + 4g + i) of one token (mt*16 + r16):
     // the activation scale of a lane is one value per token slice.
@@ -402,10 +418,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
       for (int mt = 0; mt < MT32; ++mt) {
         if (kSkipSlices && mt * 32 >= rows) break;  // wave-uniform: no token rows left
-        const uint8_t* arow = abuf + (mt * 32 + r32) * TL::kAStride + 16 * h32;
+        const uint8_t* arow = abuf + (mt * 32 + r32) * TL::kARowBytes;
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
-          const i32x4 a = *(const i32x4*)(arow + 32 * sub);
+          const i32x4 a = *(const i32x4*)(arow + 16 * ((2 * sub + h32) ^ (r32 & TL::kSwz)));
 #pragma unroll
           for (int t = 0; t < NT32; ++t) {
             const i32x4 b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
@@ -440,6 +456,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
                    i32x4 (&an)[KSG][TL::kAChunks], uint32_t (&sn)[KSG]) {
     load_a(ap, sp, st + 2);
     __syncthreads();
+    // The MFMA section runs at raised wave priority, so that while one wave of a
+    // SIMD feeds the matrix core the other's loads and LDS stores fill the gaps.
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
       const int ks = st * KSG + u;
@@ -457,6 +476,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
       load_b(slot, ks_next);
     }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     store_a(an, sn, (su + 1) & 1);
   };
 
@@ -510,9 +530,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
           for (int i = 0; i < 4; ++i) h[mt][j][i] = swiglu_clamped<FAST>(acc[mt][j][i], acc[mt][j + NJ][i], c);
       // per-row amax over this wave's HW columns (4 values x NJ tiles in a lane,
       // then the 4 lanes g of the row), then over the waves sharing a
-      // requantisation block (all of them for FP8's 128 columns, 32/HW of them
-      // for MX's 32)
-      constexpr int WPB = F == Fmt::FP8 ? WAVES : (32 / HW > 0 ? 32 / HW : 1);  // waves per block
+      // requantisation block (128/HW of them for FP8's 128 columns, 32/HW of
+      // them for MX's 32)
+      constexpr int WPB = F == Fmt::FP8 ? 128 / HW : (32 / HW > 0 ? 32 / HW : 1);  // waves per block
+      static_assert(!GATEUP || F != Fmt::FP8 || (128 % HW == 0 && WAVES % WPB == 0), "FP8 blocks span whole waves");
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         float m = 0.f;
@@ -526,7 +547,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       }
       __syncthreads();
       const int w0 = wave - wave % WPB;  // first wave of this wave's block
-      const int hcol_blk = n_tile * kHCols + w0 * HW;
+      const int hcol_blk = n_tile * HC + w0 * HW;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + r16;
@@ -538,7 +559,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         if (F == Fmt::FP8) {
           const float sc = a > 0.f ? a / 448.0f : 1.0f;
           q = 1.0f / sc;
-          if (writer) ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + n_tile] = sc;
+          if (writer) ((float*)p.C_sf)[(long long)(row0 + r) * p.c_sf_row + hcol_blk / 128] = sc;
         } else {
           const int e = mx_exponent_for_amax(a);
           q = exp2i(-e);
@@ -558,9 +579,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     constexpr int elem = F == Fmt::BF16 ? 2 : 1;
     for (int c = tid; c < BM * CPR; c += kThreads) {
       const int r = c / CPR, cc = c % CPR;
-      const int col = n_tile * kHCols + cc * 16 / elem;
+      const int col = n_tile * HC + cc * 16 / elem;
       if (r < rows && col < p.N) {
-        *(i32x4*)((uint8_t*)p.C + (long long)(row0 + r) * p.c_row_bytes + (long long)n_tile * kHCols * elem +
+        *(i32x4*)((uint8_t*)p.C + (long long)(row0 + r) * p.c_row_bytes + (long long)n_tile * HC * elem +
                   cc * 16) = *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
       }
     }
@@ -648,6 +669,7 @@ constexpr LegConfig leg_config() {
   // MFMA-bound tiles (BF16 fits two workgroups per CU in registers and LDS)
   if (F == Fmt::MX) return {8, 2, 6, 2, 1};
   if (F == Fmt::BF16) return {8, 2, 2, 1, 2};
+  if (F == Fmt::FP8) return {8, 4, 2, 1, 1};  // 512 weight rows (gate_up: 256 h columns)
   return {8, 2, 2, 2, 1};
 }
 template <Fmt F, bool GATEUP, int BM>
@@ -657,8 +679,14 @@ static void launch_leg(const GemmParams& gp, bool fast, hipStream_t s) {
 }
 
 template <Fmt F, int BM>
-static void launch_pair(const GemmParams& g1, const GemmParams& g2_in, bool fast, hipStream_t s, int stage) {
-  if (stage != 2) launch_leg<F, true, BM>(g1, fast, s);
+static void launch_pair(const GemmParams& g1_in, const GemmParams& g2_in, bool fast, hipStream_t s, int stage) {
+  if (stage != 2) {
+    constexpr LegConfig c = leg_config<F, true, BM>();
+    constexpr int hc = c.waves * 16 * c.nt / 2;  // h columns of a gate_up tile
+    GemmParams g1 = g1_in;
+    g1.n_tiles = (g1.N + hc - 1) / hc;
+    launch_leg<F, true, BM>(g1, fast, s);
+  }
   if (stage != 1) {
     constexpr LegConfig c = leg_config<F, false, BM>();
     constexpr int bn = c.waves * 16 * c.nt;  // output columns of a down tile
@@ -683,7 +711,6 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   // BF16 weight-bound tiles are 96 rows (whole 32-token slices of its 32x32 MFMA)
   const int bm = (a.fmt == Fmt::BF16 && a.bm <= 96) ? 96 : a.bm;
   g1.m_tiles_max = ffn_max_m_tiles(npairs, a.E, bm);
-  g1.n_tiles = (a.I + kHCols - 1) / kHCols;
   g1.K = a.H;
   g1.ksteps = (a.H + elem_k - 1) / elem_k;
   g1.N = a.I;
@@ -707,7 +734,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.clamp = a.clamp;
   // down: A = h rows, B = w2 [E, H, I]
   g2 = g1;
-  // (g2.n_tiles is set by the down leg's launch from its tile width)
+  // (n_tiles of both legs are set at launch from their tile widths)
   g2.K = a.I;
   g2.ksteps = (a.I + elem_k - 1) / elem_k;
   g2.N = a.H;
