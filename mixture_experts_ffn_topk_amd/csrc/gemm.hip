@@ -34,12 +34,27 @@
 
 namespace moe {
 
+#define LDS3 __attribute__((address_space(3)))  // LDS pointers of the direct-to-LDS loads
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
 
 // kOOB if dead, else 0: OR-ed into a lane offset below 2^31 it turns the load
 // into one that reads zeros, without a branch or a select (a uniform condition
 // would otherwise become a branch around the load)
 MOE_DEV uint32_t oob_if(bool dead) { return (uint32_t)dead << 31; }
+
+// Direct-to-LDS buffer loads: lane l's 16 (4) bytes land at lds + 16 l (4 l).
+// (Kept out of the kernel body: inline there, the host pass drops the kernel's
+// launch stub.)
+MOE_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS3 void*)lds, 16, voff, soff, 0, 0);
+}
+MOE_DEV void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS3 void*)lds, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding): VMEM count <= vm, LDS / scalar count 0,
+// export count not waited on.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) & 3) << 14 | 7 << 4; }
 
 struct GemmParams {
   const int* start;     // expert_start_indices [E+1]
@@ -117,7 +132,14 @@ struct Tile {
   static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (F == Fmt::BF16 ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
   static constexpr int kAStepBytes = kARows * kARowBytes;
-  static constexpr int kABytes = 2 * KSG * kAStepBytes;
+  // MFMA-bound FP8 tiles stage A with direct-to-LDS loads into three buffers
+  // (the load two stages ahead cannot land in the buffer being read): no staging
+  // registers.  The others load A into registers and store it, double-buffered
+  // (measured faster for the weight-bound tiles, whose weight stream then starts
+  // before the activation addresses are known).
+  static constexpr bool kDma = F == Fmt::FP8 && BM > 96;
+  static constexpr int kABufs = kDma ? 3 : 2;
+  static constexpr int kABytes = kABufs * KSG * kAStepBytes;
   static constexpr int kOutBytes = BM * kOutStride;
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
   static constexpr int kSA = kThreads > BM ? kThreads : BM;  // A-scale slots per buffer (one per thread)
@@ -125,7 +147,7 @@ struct Tile {
   // FP8 weight-scale blocks (128 rows) a tile touches: gate and up block, or a down window of BN rows
   static constexpr int kHB = BN / 2 / 128;  // gate_up: 128-column h blocks per tile
   static constexpr int kNB = GATEUP ? 2 * kHB : BN / 128 + 1;
-  static constexpr int kLds = kUnion + 2 * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? kNB * kMaxKSteps * 4 : 0);
+  static constexpr int kLds = kUnion + kABufs * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? kNB * kMaxKSteps * 4 : 0);
 };
 
 // WAVES waves per workgroup and room for WGS workgroups per CU: the second
@@ -149,10 +171,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   constexpr int kThreads = TL::kThreads;
   constexpr int HW = 8 * NT;  // gate_up: h columns per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kLds];
-  uint8_t* a_lds = lds;                                          // [2][KSG][kARows][kARowBytes]
+  uint8_t* a_lds = lds;                                          // [kABufs][KSG][kARows][kARowBytes]
   uint8_t* out_lds = lds;                                        // aliases a_lds after the K loop
-  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [2][KSG][kSA] (fp32 bits or 4 UE8M0 bytes)
-  float* red_lds = (float*)(lds + TL::kUnion + 2 * KSG * TL::kSA * 4);  // [WAVES][BM]
+  uint32_t* sa_lds = (uint32_t*)(lds + TL::kUnion);              // [kABufs][KSG][kSA] (fp32 bits or 4 UE8M0 bytes)
+  float* red_lds = (float*)(lds + TL::kUnion + TL::kABufs * KSG * TL::kSA * 4);  // [WAVES][BM]
   float* sb_lds = red_lds + WAVES * BM;                      // FP8: [kNB][kMaxKSteps] weight scales
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -278,8 +300,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // Issued first, before the activation rows' addresses are known.
   const int KS = p.ksteps;
   BFrag<F, NT> bq[DEPTH];
+  if constexpr (!TL::kDma) {
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_b(bq[d], d);
+    for (int d = 0; d < DEPTH; ++d) load_b(bq[d], d);
+  }
   // down: the pair slot of each tile row, for the epilogue's scatter (loaded early)
   const int pair_of_row = (!GATEUP && tid < rows) ? p.src_info[row0 + tid] : 0;
 
@@ -312,7 +336,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     if (r < rows) {
       const int grow = row0 + r;
       const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
-      a_off[i] = arow * p.a_row_bytes + (uint32_t)(c & 7) * 16u;
+      // direct-to-LDS: slot c of the K-step block holds row r's chunk (c & 7) ^ (r & 7)
+      const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ (r & 7)) : (uint32_t)(c & 7);
+      a_off[i] = arow * p.a_row_bytes + chunk * 16u;
     } else {
       a_off[i] = kOOB;
     }
@@ -372,11 +398,45 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   };
 
-  i32x4 av[2][KSG][TL::kAChunks];
-  uint32_t as[2][KSG] = {};
-  load_a(av[0], as[0], 0);
-  load_a(av[1], as[1], 1);
-  store_a(av[0], as[0], 0);
+  // FP8: A(st) and its scales go straight from HBM into LDS buffer `buf`.  Lane l
+  // of a wave's load lands at the instruction's LDS base + 16 l (4 l for the
+  // scale), so the lane loads the chunk that slot holds (swizzle in a_off).
+  auto dma_a = [&](int st, int buf) {
+#pragma unroll
+    for (int u = 0; u < KSG; ++u) {
+      const int ks = st * KSG + u;
+      const uint32_t dead = oob_if(ks >= p.ksteps);
+      uint8_t* base = a_lds + (buf * KSG + u) * TL::kAStepBytes;
+#pragma unroll
+      for (int i = 0; i < TL::kAChunks; ++i)
+        lds_load16(a_rs, base + (i * kThreads + wave * 64) * 16, a_off[i] | dead, (uint32_t)ks * 128u);
+      lds_load4(asf_rs, sa_lds + (buf * KSG + u) * TL::kSA + wave * 64, (asf_off + 4u * u) | dead,
+                (uint32_t)st * (KSG * 4u));
+    }
+  };
+  // VMEM instructions per stage: the A loads (D) and the weight-ring refills (R)
+  constexpr int kD = KSG * (TL::kAChunks + 1), kR = KSG * NT * 2;
+
+  i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
+  uint32_t as[TL::kDma ? 1 : 2][KSG] = {};
+  if constexpr (TL::kDma) {
+    // A(0), ring K-steps of stage 0, A(1), the rest of the ring: then at least
+    // 2 kR + kD VMEM instructions follow the loads of A(st) when stage st waits
+    // for them (exactly that many from stage 2 on; the surplus at stages 0 and 1
+    // is ring loads those stages need anyway), so one wait count serves every
+    // stage and the loop has no branches
+    static_assert(!TL::kDma || DEPTH >= 2 * KSG, "the direct-to-LDS pipeline keeps two stages of weights in flight");
+    dma_a(0, 0);
+#pragma unroll
+    for (int d = 0; d < KSG; ++d) load_b(bq[d], d);
+    dma_a(1, 1);
+#pragma unroll
+    for (int d = KSG; d < DEPTH; ++d) load_b(bq[d], d);
+  } else {
+    load_a(av[0], as[0], 0);
+    load_a(av[1], as[1], 1);
+    store_a(av[0], as[0], 0);
+  }
 
   // One K-step on the staged A of LDS buffer `buf` (K-step u of the stage) and B(ks) in `bq_`.
   auto kstep = [&](const BFrag<F, NT>& bq_, int buf, int u, int ks) {
@@ -480,18 +540,54 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     store_a(an, sn, (su + 1) & 1);
   };
 
+  // FP8 stage: A(st) was loaded into buffer st % 3 two stages ago.  Each wave
+  // waits for its own loads of A(st) (the VMEM counter retires in order, and
+  // at least 2 kR + kD instructions were issued after them), and its LDS reads; the
+  // barrier then publishes the buffer and frees buffer (st + 2) % 3, last read
+  // in stage st - 1, for A(st + 2).  A plain s_barrier: __syncthreads would wait
+  // for every outstanding load, weight ring included.
+  auto stage_dma = [&](int st, int su) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kR + kD));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(st + 2, (su + 2) % 3);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int u = 0; u < KSG; ++u) {
+      const int ks = st * KSG + u;
+      BFrag<F, NT>& slot = bq[(su * KSG + u) % DEPTH];
+      kstep(slot, su % 3, u, ks);
+      if (u + 1 < KSG) __builtin_amdgcn_sched_barrier(0);
+      int ks_next = ks + DEPTH;
+      asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
+      load_b(slot, ks_next);
+    }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // Unrolled so that both rings (DEPTH weight buffers, 2 activation stages)
   // index statically: U K-steps = SU stages per trip.  The trip count is rounded
   // up to the unroll: the extra steps load zeros and add zeros, and the loop has
   // no early exit (an exit per step would make the compiler drain every
   // outstanding load there).
-  constexpr int U = lcm_c(2 * KSG, DEPTH);
+  constexpr int U = lcm_c(TL::kABufs * KSG, DEPTH);
   constexpr int SU = U / KSG;
   const int KS_PAD = (KS + U - 1) / U * U;
-  for (int ks0 = 0; ks0 < KS_PAD; ks0 += U) {
+  if constexpr (TL::kDma) {
+    for (int ks0 = 0; ks0 < KS_PAD; ks0 += U) {
 #pragma unroll
-    for (int su = 0; su < SU; ++su)
-      stage(ks0 / KSG + su, su, av[su & 1], as[su & 1], av[(su + 1) & 1], as[(su + 1) & 1]);
+      for (int su = 0; su < SU; ++su) stage_dma(ks0 / KSG + su, su);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the trailing loads (zeros) have landed before the LDS is reused
+  } else {
+    for (int ks0 = 0; ks0 < KS_PAD; ks0 += U) {
+#pragma unroll
+      for (int su = 0; su < SU; ++su)
+        stage(ks0 / KSG + su, su, av[su & 1], as[su & 1], av[(su + 1) & 1], as[(su + 1) & 1]);
+    }
   }
   __syncthreads();  // every wave is done with the A buffers; the output tile reuses them
 
