@@ -148,6 +148,9 @@ SMALL = [
     ("fp8_tiny_config", dict(T=64, H=256, I=128, E=8, k=2, fmt="fp8_block128"), "auto"),
     ("fp8_decode_tiles", dict(T=100, H=512, I=256, E=8, k=4, fmt="fp8_block128"), "decode"),
     ("fp8_prefill_tiles", dict(T=300, H=512, I=384, E=4, k=2, fmt="fp8_block128"), "prefill"),
+    # several 128-row tiles per expert, K-step counts (7 and 5) that are not multiples of the
+    # 3-buffer activation pipeline, a ragged last gate_up column tile
+    ("fp8_prefill_ragged", dict(T=520, H=896, I=640, E=5, k=3, fmt="fp8_block128"), "prefill"),
     ("fp8_multi_mtile_decode", dict(T=300, H=384, I=256, E=4, k=2, fmt="fp8_block128"), "decode"),
     ("bf16_ragged_n", dict(T=96, H=512, I=320, E=4, k=2, fmt="bf16"), "decode"),
     ("bf16_prefill", dict(T=200, H=448, I=256, E=3, k=2, fmt="bf16"), "prefill"),
