@@ -117,14 +117,14 @@ struct Tile {
   static constexpr int kThreads = 64 * WAVES;
   static constexpr int BN = WAVES * 16 * NT;  // weight rows per workgroup tile
   static constexpr int MT = BM / 16;
-  // A is staged per K-step as kARows rows.  FP8 / MX: rows of 128 bytes, the
-  // 16-byte chunk c of row r stored at chunk c ^ (r & 7), so that the 16 rows of
-  // an MFMA fragment read spread over all LDS banks (a padded row stride still
-  // halves the read rate).  BF16 keeps a padded 144-byte row: its 32-row
-  // fragments read well enough, and the swizzle's extra offsets do not fit the
-  // register budget of its 4-workgroup tiles.
-  static constexpr int kSwz = F == Fmt::BF16 ? 0 : 7;
-  static constexpr int kARowBytes = F == Fmt::BF16 ? 144 : 128;
+  // A is staged per K-step as kARows rows of 128 bytes, the 16-byte chunk c of
+  // row r stored at chunk c ^ (r & 7), so that the rows of an MFMA fragment read
+  // spread over all LDS banks (a padded row stride still halves the read rate).
+  // Weight-bound BF16 tiles keep a padded 144-byte row instead: the swizzle's
+  // per-sub-step offsets do not fit their register budget.
+  static constexpr bool kDma = F != Fmt::MX && BM > 96;  // direct-to-LDS staging (below)
+  static constexpr int kSwz = F == Fmt::BF16 && !kDma ? 0 : 7;
+  static constexpr int kARowBytes = F == Fmt::BF16 && !kDma ? 144 : 128;
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
   // A buffer rows: BM rounded up so that every thread stores every chunk it loads
   // (chunks past BM rows are zeros landing in spare rows): no divergent stores in the loop
@@ -132,12 +132,12 @@ struct Tile {
   static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (F == Fmt::BF16 ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
   static constexpr int kAStepBytes = kARows * kARowBytes;
-  // MFMA-bound FP8 tiles stage A with direct-to-LDS loads into three buffers
-  // (the load two stages ahead cannot land in the buffer being read): no staging
-  // registers.  The others load A into registers and store it, double-buffered
-  // (measured faster for the weight-bound tiles, whose weight stream then starts
-  // before the activation addresses are known).
-  static constexpr bool kDma = F == Fmt::FP8 && BM > 96;
+  // MFMA-bound FP8 / BF16 tiles stage A with direct-to-LDS loads into three
+  // buffers (the load two stages ahead cannot land in the buffer being read): no
+  // staging registers, which also leaves BF16 room for the swizzled layout.  The
+  // others load A into registers and store it, double-buffered (measured faster
+  // for the weight-bound tiles, whose weight stream then starts before the
+  // activation addresses are known).
   static constexpr int kABufs = kDma ? 3 : 2;
   static constexpr int kABytes = kABufs * KSG * kAStepBytes;
   static constexpr int kOutBytes = BM * kOutStride;
@@ -410,12 +410,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
       for (int i = 0; i < TL::kAChunks; ++i)
         lds_load16(a_rs, base + (i * kThreads + wave * 64) * 16, a_off[i] | dead, (uint32_t)ks * 128u);
-      lds_load4(asf_rs, sa_lds + (buf * KSG + u) * TL::kSA + wave * 64, (asf_off + 4u * u) | dead,
-                (uint32_t)st * (KSG * 4u));
+      if constexpr (F == Fmt::FP8)
+        lds_load4(asf_rs, sa_lds + (buf * KSG + u) * TL::kSA + wave * 64, (asf_off + 4u * u) | dead,
+                  (uint32_t)st * (KSG * 4u));
     }
   };
   // VMEM instructions per stage: the A loads (D) and the weight-ring refills (R)
-  constexpr int kD = KSG * (TL::kAChunks + 1), kR = KSG * NT * 2;
+  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * NT * 2;
 
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
   uint32_t as[TL::kDma ? 1 : 2][KSG] = {};
@@ -561,7 +562,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       kstep(slot, su % 3, u, ks);
       if (u + 1 < KSG) __builtin_amdgcn_sched_barrier(0);
       int ks_next = ks + DEPTH;
-      asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
+      if constexpr (F == Fmt::BF16)
+        asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc32[MT32 - 1][NT32 - 1][15]));
+      else
+        asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
       load_b(slot, ks_next);
     }
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
@@ -760,6 +764,7 @@ constexpr LegConfig leg_config() {
   if (BM <= 96) {  // weight-bound tiles
     if (GATEUP) return {4, 4, 2, 1, 2};  // 4 waves x 64 weight rows, two workgroups per CU
     if (F == Fmt::FP8) return {7, 4, 2, 1, 1};  // 448 columns: 7168 = 16 tiles (two even rounds of 256)
+    if (F == Fmt::MX) return {4, 4, 2, 1, 2};   // 256 columns, two workgroups per CU
     return {8, 2, 2, 1, 1};
   }
   // MFMA-bound tiles (BF16 fits two workgroups per CU in registers and LDS)
