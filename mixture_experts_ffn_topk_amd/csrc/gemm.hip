@@ -750,8 +750,6 @@ static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
                        dim3(64 * WAVES), 0, s, gp);
 }
 
-// 8 waves x 32 weight rows; weight-ring depth per format and tile height, sized
-// to the registers of two waves per SIMD
 // Launch configuration per format, regime and leg: waves per workgroup, 16-row
 // column tiles per wave, weight-ring depth (K-steps) and K-steps per LDS stage
 // of the activations.  Chosen by measurement on the decode, prefill, Mixtral
