@@ -765,9 +765,9 @@ constexpr LegConfig leg_config() {
     if (F == Fmt::MX) return {4, 4, 2, 1, 2};   // 256 columns, two workgroups per CU
     return {8, 2, 2, 1, 1};
   }
-  // MFMA-bound tiles (BF16 fits two workgroups per CU in registers and LDS)
+  // MFMA-bound tiles
   if (F == Fmt::MX) return {8, 2, 6, 2, 1};
-  if (F == Fmt::BF16) return {8, 2, 2, 1, 2};
+  if (F == Fmt::BF16) return {8, 4, 2, 1, 1};  // 512 weight rows (gate_up: 256 h columns)
   if (F == Fmt::FP8) return {8, 4, 2, 1, 1};  // 512 weight rows (gate_up: 256 h columns)
   return {8, 2, 2, 2, 1};
 }
