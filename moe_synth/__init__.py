@@ -20,6 +20,11 @@ MegaMoESymmBuffer page):
 * ``w4a8_mx``       x: E4M3 [T, H] + UE8M0 bytes [T, H/32]; w13: packed E2M1
   [E, 2I, H/2] (element 2i in the low nibble of byte i) + UE8M0 [E, 2I, H/32];
   w2: packed E2M1 [E, H, I/2] + UE8M0 [E, H, I/32].
+* ``nvfp4_w4a16``   x [T, H] bf16 bit patterns, no scale (the page's NVFP4 x BF16
+  W4A16 pair); w13: packed E2M1 [E, 2I, H/2] + E4M3 block scales [E, 2I, H/16]
+  + one fp32 global scale per expert ``w13_gs`` [E]; w2: packed E2M1
+  [E, H, I/2] + E4M3 [E, H, I/16] + ``w2_gs`` [E].  A weight is
+  e2m1 * e4m3 block scale * global scale.
 
 Routing inputs: ``logits`` f32 [T, E] always; for precomputed routing the
 caller-side ``topk_idx`` (int64 [T, k]) and ``topk_weights`` (f32 [T, k]) are
@@ -38,6 +43,7 @@ import torch
 FP8_BLOCK128 = "fp8_block128"
 BF16 = "bf16"
 W4A8_MX = "w4a8_mx"
+NVFP4_W4A16 = "nvfp4_w4a16"
 
 PRECOMPUTED = "precomputed"
 FROM_LOGITS = "from_logits"
@@ -85,6 +91,9 @@ CONFIGS = {
     "w4a8_mx_logits": MoEShape("w4a8_mx_logits", 5, 2048, 2880, 2880, 128, 4, W4A8_MX, FROM_LOGITS),
 }
 CONFIG_ORDER = ["tiny_fp8", "decode_fp8", "prefill_fp8_zipf", "mixtral_bf16", "w4a8_mx_logits"]
+# The NVFP4 weight x BF16 activation variant at the decode shape (not one of the
+# five named workloads).
+CONFIGS["nvfp4_decode"] = MoEShape("nvfp4_decode", 6, 256, 7168, 2048, 32, 8, NVFP4_W4A16, PRECOMPUTED)
 
 
 def _rng(seed: int, stream: int, expert: int = 0) -> np.random.Generator:
@@ -170,6 +179,23 @@ def quant_mx_weight(v: np.ndarray):
     return _pack_nibbles(codes), (e + 127).astype(np.uint8)
 
 
+def quant_nvfp4_weight(v: np.ndarray):
+    """float32 [R, C] -> (packed E2M1 [R, C/2], E4M3 block scales [R, C/16], fp32 global scale).
+    The global scale puts the largest block scale at the E4M3 maximum; each block's
+    scale is its amax / 6 over the global scale, rounded to E4M3; the values are
+    the nearest E2M1 codes of v over (block scale * global scale)."""
+    r, c = v.shape
+    amax = float(np.abs(v).max())
+    gs = np.float32(amax / (6.0 * 448.0)) if amax > 0 else np.float32(1.0)
+    bamax = np.abs(v.reshape(r, c // 16, 16)).max(axis=2)
+    sc = _to_e4m3_codes((bamax / (6.0 * float(gs))).astype(np.float32))
+    sdec = torch.from_numpy(sc).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    denom = (sdec.astype(np.float64) * float(gs))[..., None]
+    q = np.where(denom > 0, v.reshape(r, c // 16, 16) / np.where(denom > 0, denom, 1.0), 0.0)
+    codes = _to_e2m1_codes(q.reshape(r, c).astype(np.float32))
+    return _pack_nibbles(codes), sc, gs
+
+
 # ---------------------------------------------------------------- draws
 def draw_logits(shape: MoEShape) -> np.ndarray:
     lg = _rng(shape.seed, _S_LOGITS).standard_normal((shape.tokens, shape.experts), dtype=np.float32)
@@ -200,6 +226,8 @@ def _weights_for_expert(shape: MoEShape, e: int):
         return _to_bf16_bits(w13), None, _to_bf16_bits(w2), None
     if shape.fmt == W4A8_MX:
         return quant_mx_weight(w13) + quant_mx_weight(w2)
+    if shape.fmt == NVFP4_W4A16:
+        return quant_nvfp4_weight(w13) + quant_nvfp4_weight(w2)
     raise ValueError(shape.fmt)
 
 
@@ -216,7 +244,7 @@ def make_inputs(shape: MoEShape, with_weights: bool = True) -> dict:
         x = x * np.float32(shape.x_scale)
     if shape.fmt == FP8_BLOCK128:
         out["x"], out["x_sf"] = quant_fp8_block(x, 1, 128)
-    elif shape.fmt == BF16:
+    elif shape.fmt in (BF16, NVFP4_W4A16):
         out["x"], out["x_sf"] = _to_bf16_bits(x), None
     else:
         out["x"], out["x_sf"] = quant_mx_act(x)
@@ -224,6 +252,10 @@ def make_inputs(shape: MoEShape, with_weights: bool = True) -> dict:
         return out
     with ThreadPoolExecutor(_threads()) as ex:
         parts = list(ex.map(lambda e: _weights_for_expert(shape, e), range(E)))
+    if shape.fmt == NVFP4_W4A16:  # (w13, sf, gs, w2, sf, gs) per expert
+        out["w13_gs"] = np.array([p[2] for p in parts], dtype=np.float32)
+        out["w2_gs"] = np.array([p[5] for p in parts], dtype=np.float32)
+        parts = [(p[0], p[1], p[3], p[4]) for p in parts]
     out["w13"] = np.stack([p[0] for p in parts])
     out["w13_sf"] = None if parts[0][1] is None else np.stack([p[1] for p in parts])
     out["w2"] = np.stack([p[2] for p in parts])

@@ -12,14 +12,14 @@ parity unpinned.
 """
 from .codecs import (bf16_decode, e2m1_decode_nibbles, e2m1_unpack, e4m3_decode, round_bf16,
                      round_e4m3_sat, round_to_grid, ue8m0_decode)
-from .moe import (BF16, FP8_BLOCK128, W4A8_MX, Geometry, build_plan, combine, dequant_activations,
-                  dequant_expert, dequant_fp8_block, dequant_mx, expert_rows, forward, forward_tokens,
+from .moe import (BF16, FP8_BLOCK128, NVFP4_W4A16, W4A8_MX, Geometry, build_plan, combine, dequant_activations,
+                  dequant_expert, dequant_fp8_block, dequant_mx, dequant_nvfp4, expert_rows, forward, forward_tokens,
                   mx_exponent, requant, requant_fp8_block128, requant_mx, route_from_logits,
                   route_from_logits_fast, silu, swiglu_clamped)
 
 __all__ = [
-    "BF16", "FP8_BLOCK128", "W4A8_MX", "Geometry", "bf16_decode", "build_plan", "combine",
-    "dequant_activations", "dequant_expert", "dequant_fp8_block", "dequant_mx", "e2m1_decode_nibbles",
+    "BF16", "FP8_BLOCK128", "NVFP4_W4A16", "W4A8_MX", "Geometry", "bf16_decode", "build_plan", "combine",
+    "dequant_activations", "dequant_expert", "dequant_fp8_block", "dequant_mx", "dequant_nvfp4", "e2m1_decode_nibbles",
     "e2m1_unpack", "e4m3_decode", "expert_rows", "forward", "forward_tokens", "mx_exponent", "requant",
     "requant_fp8_block128", "requant_mx", "round_bf16", "round_e4m3_sat", "round_to_grid",
     "route_from_logits", "route_from_logits_fast", "silu", "swiglu_clamped", "ue8m0_decode",

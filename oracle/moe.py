@@ -33,7 +33,7 @@ values, so each step states which reading it takes):
   dispatch metadata), ``num_active_experts``, and ``clamp_activation``
   (selects the clamped L1 activation).
 * flashinfer.fused_moe.MoEActivationPack: the operand encodings (DeepSeek FP8,
-  MXFP8, MXFP4 x MXFP8, BF16) and the routing input modes (precomputed
+  MXFP8, MXFP4 x MXFP8, BF16, NVFP4 x BF16) and the routing input modes (precomputed
   ``topk_ids``/``topk_weights``; ``FromLogits`` with in-kernel top-k).
 * DistributedEPCombine (max ep): ``router_weights`` scale each expert's
   contribution; ``input_tokens`` are the expert outputs; ``src_info`` records
@@ -45,7 +45,10 @@ silu(min(g, c)) * clamp(u, -c, c); the FP8 intermediate is requantised per
 (row, 128 columns) with scale fp32(amax / 448) (1.0 for an all-zero block) and
 E4M3 round-to-nearest-even with saturation; the MX intermediate uses per
 (row, 32 columns) the smallest power of two 2**e with 448 * 2**e >= amax;
-the BF16 intermediate is rounded to bf16; rows inside an expert keep pair order
+the BF16 intermediate is rounded to bf16; an NVFP4 weight is e2m1 * e4m3 block
+scale (one per 16 along K) * the expert's fp32 global scale (the per-expert
+scales of the max mega_ffn arguments), and the NVFP4 x BF16 intermediate is
+rounded to bf16 like BF16's; rows inside an expert keep pair order
 p = t * k + j; ``src_info[row] = p``; the combine sums valid slots in slot order;
 ids outside [0, E) are masked slots that contribute nothing.
 
@@ -66,6 +69,7 @@ from .codecs import (bf16_decode, e2m1_decode_nibbles, e2m1_unpack, e4m3_decode,
 FP8_BLOCK128 = "fp8_block128"
 BF16 = "bf16"
 W4A8_MX = "w4a8_mx"
+NVFP4_W4A16 = "nvfp4_w4a16"
 
 
 @dataclass(frozen=True)
@@ -103,18 +107,29 @@ def dequant_mx(values: np.ndarray, scale_bytes: np.ndarray, is_fp4: bool) -> np.
     return v * s
 
 
+def dequant_nvfp4(values: np.ndarray, block_scales: np.ndarray, global_scale: float) -> np.ndarray:
+    """NVFP4 operand: packed E2M1 [R, K/2] with E4M3 block scales [R, K/16] and one
+    fp32 global scale -> float64 values (MoEActivationPack page, "NVFP4": packed
+    uint8 values with float8_e4m3fn [., K/16] block scales; the max mega_ffn
+    arguments carry one fp32 scale per expert)."""
+    v = e2m1_decode_nibbles(e2m1_unpack(values))
+    s = np.repeat(e4m3_decode(block_scales), 16, axis=-1)
+    return v * s * float(global_scale)
+
+
 def dequant_activations(geo: Geometry, x: np.ndarray, x_sf) -> np.ndarray:
     if geo.fmt == FP8_BLOCK128:
         return dequant_fp8_block(x, x_sf, 1, 128)
-    if geo.fmt == BF16:
+    if geo.fmt in (BF16, NVFP4_W4A16):
         return bf16_decode(x)
     if geo.fmt == W4A8_MX:
         return dequant_mx(x, x_sf, is_fp4=False)
     raise ValueError(geo.fmt)
 
 
-def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int):
-    """Expert e's gate/up weights [2I, H] and down weights [H, I] in float64."""
+def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int, w13_gs=None, w2_gs=None):
+    """Expert e's gate/up weights [2I, H] and down weights [H, I] in float64
+    (``w13_gs``/``w2_gs``: the NVFP4 per-expert global scales)."""
     if geo.fmt == FP8_BLOCK128:
         return (dequant_fp8_block(w13[e], w13_sf[e], 128, 128),
                 dequant_fp8_block(w2[e], w2_sf[e], 128, 128))
@@ -122,6 +137,8 @@ def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int):
         return bf16_decode(w13[e]), bf16_decode(w2[e])
     if geo.fmt == W4A8_MX:
         return dequant_mx(w13[e], w13_sf[e], True), dequant_mx(w2[e], w2_sf[e], True)
+    if geo.fmt == NVFP4_W4A16:
+        return dequant_nvfp4(w13[e], w13_sf[e], w13_gs[e]), dequant_nvfp4(w2[e], w2_sf[e], w2_gs[e])
     raise ValueError(geo.fmt)
 
 
@@ -264,7 +281,7 @@ def requant_mx(h: np.ndarray):
 def requant(geo: Geometry, h: np.ndarray) -> np.ndarray:
     if geo.fmt == FP8_BLOCK128:
         return requant_fp8_block128(h)[0]
-    if geo.fmt == BF16:
+    if geo.fmt in (BF16, NVFP4_W4A16):
         return round_bf16(h)
     if geo.fmt == W4A8_MX:
         return requant_mx(h)[0]
@@ -298,7 +315,7 @@ def combine(y_rows: np.ndarray, topk_weights: np.ndarray, pair_row: np.ndarray, 
 
 # ------------------------------------------------------------------ forward
 def forward(geo: Geometry, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx=None, topk_weights=None,
-            logits=None) -> dict:
+            logits=None, w13_gs=None, w2_gs=None) -> dict:
     """Whole path over all tokens.  Routing is taken from ``topk_idx``/``topk_weights``
     when given, else computed from ``logits``."""
     if topk_idx is None:
@@ -311,14 +328,15 @@ def forward(geo: Geometry, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx=None, topk_
         r0, r1 = int(start[e]), int(start[e + 1])
         if r1 == r0:
             continue
-        w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e)
+        w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e, w13_gs, w2_gs)
         y[r0:r1] = expert_rows(geo, xd[src[r0:r1] // geo.topk], w13d, w2d)
     out = combine(y, topk_weights, plan["pair_row"], geo.hidden)
     return {"out": out, "plan": plan, "y_rows": y, "topk_idx": np.asarray(topk_idx),
             "topk_weights": np.asarray(topk_weights, dtype=np.float64)}
 
 
-def forward_tokens(geo: Geometry, tokens, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx, topk_weights) -> np.ndarray:
+def forward_tokens(geo: Geometry, tokens, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx, topk_weights,
+                   w13_gs=None, w2_gs=None) -> np.ndarray:
     """Outputs of selected tokens only, each computed on its own (the requantisation
     blocks lie inside one row, so a pair's result depends only on its token and
     expert).  Used to check full-size runs on a sample of tokens."""
@@ -335,7 +353,7 @@ def forward_tokens(geo: Geometry, tokens, x, x_sf, w13, w13_sf, w2, w2_sf, topk_
     out = np.zeros((len(tokens), geo.hidden), dtype=np.float64)
     contrib = np.zeros((len(tokens), geo.topk, geo.hidden), dtype=np.float64)
     for e, lst in need.items():
-        w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e)
+        w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e, w13_gs, w2_gs)
         rows = np.array([n for n, _ in lst])
         y = expert_rows(geo, xd[rows], w13d, w2d)
         for (n, j), yr in zip(lst, y):

@@ -157,20 +157,25 @@ def _ops(inp):
     return inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"]
 
 
-@pytest.mark.parametrize("fmt", ["fp8_block128", "bf16", "w4a8_mx"])
+def _gs(inp):
+    """The NVFP4 per-expert global scales as forward()/dequant_expert() keywords."""
+    return {"w13_gs": inp["w13_gs"], "w2_gs": inp["w2_gs"]} if "w13_gs" in inp else {}
+
+
+@pytest.mark.parametrize("fmt", ["fp8_block128", "bf16", "w4a8_mx", "nvfp4_w4a16"])
 def test_dense_equivalence_topk_equals_E(fmt):
     sh, inp = _small_inputs(fmt, E=3, k=3)
     geo = Geometry(sh.hidden, sh.inter, sh.experts, sh.topk, fmt)
     T = sh.tokens
     ids = np.tile(np.arange(3), (T, 1))
     w = np.full((T, 3), 1.0 / 3)
-    res = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w)
+    res = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w, **_gs(inp))
     # no routing code: every expert over every token, averaged
     from oracle import dequant_activations, dequant_expert
     xd = dequant_activations(geo, inp["x"], inp["x_sf"])
     dense = np.zeros((T, sh.hidden))
     for e in range(3):
-        w13d, w2d = dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e)
+        w13d, w2d = dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e, **_gs(inp))
         dense += expert_rows(geo, xd, w13d, w2d) / 3
     assert np.allclose(res["out"], dense, rtol=1e-12, atol=1e-12 * np.abs(dense).max())
 
@@ -196,8 +201,15 @@ def _torch_deq(fmt, codes, scales, br=1, bc=128, fp4=False):
     return v * s.repeat_interleave(32, 1)
 
 
+def _torch_nvfp4(packed, block_scales, gs):
+    c = torch.from_numpy(np.ascontiguousarray(packed))
+    v = torch.stack([_E2M1[(c & 15).long()], _E2M1[(c >> 4).long()]], dim=-1).reshape(c.shape[0], -1)
+    s = torch.from_numpy(np.ascontiguousarray(block_scales)).view(torch.float8_e4m3fn).to(torch.float64)
+    return v * s.repeat_interleave(16, 1) * float(gs)
+
+
 def _torch_requant(fmt, h):
-    if fmt == "bf16":
+    if fmt in ("bf16", "nvfp4_w4a16"):
         return h.to(torch.bfloat16).to(torch.float64)
     R, C = h.shape
     if fmt == "fp8_block128":
@@ -217,15 +229,20 @@ def _torch_requant(fmt, h):
 
 
 @pytest.mark.parametrize("fmt,x_scale", [("fp8_block128", 1.0), ("fp8_block128", 20.0), ("bf16", 1.0),
-                                         ("bf16", 20.0), ("w4a8_mx", 1.0)])
+                                         ("bf16", 20.0), ("w4a8_mx", 1.0), ("nvfp4_w4a16", 1.0),
+                                         ("nvfp4_w4a16", 20.0)])
 def test_single_expert_matches_torch_chain(fmt, x_scale):
     sh, inp = _small_inputs(fmt, T=16, E=1, k=1, x_scale=x_scale, H=256, I=256)
     geo = Geometry(sh.hidden, sh.inter, 1, 1, fmt)
     ids = np.zeros((sh.tokens, 1), np.int64)
     w = np.ones((sh.tokens, 1), np.float32)
-    out = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w)["out"]
+    out = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w, **_gs(inp))["out"]
     H, I = sh.hidden, sh.inter
-    if fmt == "w4a8_mx":
+    if fmt == "nvfp4_w4a16":
+        x = _torch_deq("bf16", inp["x"], None)
+        w13 = _torch_nvfp4(inp["w13"][0], inp["w13_sf"][0], inp["w13_gs"][0])
+        w2 = _torch_nvfp4(inp["w2"][0], inp["w2_sf"][0], inp["w2_gs"][0])
+    elif fmt == "w4a8_mx":
         x = _torch_deq(fmt, inp["x"], inp["x_sf"])
         w13 = _torch_deq(fmt, inp["w13"][0], inp["w13_sf"][0], fp4=True)
         w2 = _torch_deq(fmt, inp["w2"][0], inp["w2_sf"][0], fp4=True)
@@ -293,3 +310,45 @@ def test_combine_masked_token_is_zero():
     assert out[1].tolist() == [0, 0, 0, 0]
     assert np.allclose(out[0], 0.5 * y[0])
     assert np.allclose(out[2], 0.25 * y[2] + 2.0 * y[1])
+
+
+# ---- NVFP4 (E2M1 values, E4M3 scale per 16 along K, fp32 global scale per expert)
+def test_nvfp4_dequant_hand_values():
+    from oracle import dequant_nvfp4
+    # one row of 32 elements: bytes 0x21, 0xF7 then zeros; block scales 1.5 (E4M3 0x3C) and 0.25 (0x28)
+    packed = np.zeros((1, 16), np.uint8)
+    packed[0, 0], packed[0, 1] = 0x21, 0xF7   # nibbles 1, 2, 7, 15 -> 0.5, 1.0, 6.0, -6.0
+    packed[0, 8] = 0x3B                       # elements 16, 17: nibbles 11, 3 -> -1.5, 1.5
+    scales = np.array([[0x3C, 0x28]], np.uint8)
+    v = dequant_nvfp4(packed, scales, 0.5)
+    want = np.zeros(32)
+    want[:4] = np.array([0.5, 1.0, 6.0, -6.0]) * 1.5 * 0.5
+    want[16:18] = np.array([-1.5, 1.5]) * 0.25 * 0.5
+    assert np.array_equal(v[0], want)
+
+
+def test_nvfp4_forward_equals_bf16_forward_on_exact_weights():
+    """With a power-of-two global scale every NVFP4 weight is a bf16 value; the
+    NVFP4 path must then give exactly the BF16 path's result on those weights."""
+    from oracle import dequant_nvfp4
+    sh, inp = _small_inputs("nvfp4_w4a16", E=3, k=2)
+    inp["w13_gs"] = np.full(3, 2.0 ** -5, np.float32)
+    inp["w2_gs"] = np.full(3, 2.0 ** -4, np.float32)
+    to_bf16 = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    w13b = np.stack([to_bf16(dequant_nvfp4(inp["w13"][e], inp["w13_sf"][e], inp["w13_gs"][e])) for e in range(3)])
+    w2b = np.stack([to_bf16(dequant_nvfp4(inp["w2"][e], inp["w2_sf"][e], inp["w2_gs"][e])) for e in range(3)])
+    geo_n = Geometry(sh.hidden, sh.inter, 3, 2, "nvfp4_w4a16")
+    geo_b = Geometry(sh.hidden, sh.inter, 3, 2, "bf16")
+    a = forward(geo_n, *_ops(inp), topk_idx=inp["topk_idx"], topk_weights=inp["topk_weights"], **_gs(inp))["out"]
+    b = forward(geo_b, inp["x"], None, w13b, None, w2b, None, topk_idx=inp["topk_idx"],
+                topk_weights=inp["topk_weights"])["out"]
+    assert np.array_equal(a, b)
+
+
+def test_nvfp4_down_global_scale_is_linear():
+    sh, inp = _small_inputs("nvfp4_w4a16", E=3, k=2)
+    geo = Geometry(sh.hidden, sh.inter, 3, 2, "nvfp4_w4a16")
+    kw = dict(topk_idx=inp["topk_idx"], topk_weights=inp["topk_weights"])
+    a = forward(geo, *_ops(inp), w13_gs=inp["w13_gs"], w2_gs=inp["w2_gs"], **kw)["out"]
+    b = forward(geo, *_ops(inp), w13_gs=inp["w13_gs"], w2_gs=inp["w2_gs"] * 4, **kw)["out"]
+    assert np.array_equal(b, 4 * a)

@@ -42,3 +42,19 @@ def test_decode_load_is_uniform():
     a = moe_synth.make_inputs(sh, with_weights=False)
     counts = np.bincount(a["topk_idx"].reshape(-1), minlength=sh.experts)
     assert counts.min() > 0 and counts.max() < 2 * sh.pairs / sh.experts
+
+
+def test_nvfp4_shapes_and_quantisation_error():
+    from oracle import dequant_nvfp4
+    sh = moe_synth.CONFIGS["nvfp4_decode"].with_(tokens=16, hidden=256, inter=128, experts=3, topk=2)
+    inp = moe_synth.make_inputs(sh)
+    assert inp["x"].dtype == np.uint16 and inp["x_sf"] is None
+    assert inp["w13"].shape == (3, 256, 128) and inp["w13_sf"].shape == (3, 256, 16)
+    assert inp["w2"].shape == (3, 256, 64) and inp["w2_sf"].shape == (3, 256, 8)
+    assert inp["w13_gs"].shape == (3,) and inp["w2_gs"].dtype == np.float32
+    # the draws behind the codes: redraw expert 1's w13 and compare with its dequantisation
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sh.seed, 3, 1])))
+    w = rng.standard_normal((256, 256), dtype=np.float32) * np.float32(1.0 / 16.0)
+    deq = dequant_nvfp4(inp["w13"][1], inp["w13_sf"][1], inp["w13_gs"][1])
+    step = np.repeat(np.abs(w).reshape(256, 16, 16).max(axis=2) / 6.0, 16, axis=1)  # block amax / 6
+    assert np.all(np.abs(deq - w) <= 1.07 * step + 1e-12)
