@@ -30,8 +30,9 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"fp8_block128": 5000.0, "bf16": 2500.0, "w4a8_mx": 5000.0}  # MX: f8 x f4 MFMA runs at the FP8 rate
-DTYPE = {"fp8_block128": "fp8_e4m3", "bf16": "bf16", "w4a8_mx": "mxfp4xmxfp8"}
+# MX: the f8 x f4 MFMA runs at the FP8 rate; NVFP4 x BF16 decodes its weights to bf16 for the bf16 MFMA
+PEAK_TFLOPS = {"fp8_block128": 5000.0, "bf16": 2500.0, "w4a8_mx": 5000.0, "nvfp4_w4a16": 2500.0}
+DTYPE = {"fp8_block128": "fp8_e4m3", "bf16": "bf16", "w4a8_mx": "mxfp4xmxfp8", "nvfp4_w4a16": "nvfp4xbf16"}
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "device.h", "prepare.hip")]
 
@@ -55,6 +56,8 @@ def weight_bytes_per_expert(sh) -> tuple[int, int]:
         return 2 * I * H + (2 * I // 128) * (H // 128) * 4, H * I + (H // 128) * (I // 128) * 4
     if sh.fmt == "bf16":
         return 2 * I * H * 2, H * I * 2
+    if sh.fmt == "nvfp4_w4a16":  # E2M1 values, one E4M3 scale per 16, one fp32 global scale
+        return 2 * I * H // 2 + 2 * I * (H // 16) + 4, H * I // 2 + H * (I // 16) + 4
     return 2 * I * H // 2 + 2 * I * (H // 32), H * I // 2 + H * (I // 32)
 
 
@@ -62,7 +65,7 @@ def act_bytes(sh) -> int:
     T, H = sh.tokens, sh.hidden
     if sh.fmt == "fp8_block128":
         return T * H + T * (H // 128) * 4
-    if sh.fmt == "bf16":
+    if sh.fmt in ("bf16", "nvfp4_w4a16"):
         return T * H * 2
     return T * H + T * (H // 32)
 
@@ -88,7 +91,8 @@ def cpu_baseline(sh, inp, ids, w, budget_s: float) -> dict:
         r0, r1 = int(start[e]), int(start[e + 1])
         if r1 == r0:
             continue
-        w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e)
+        w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e,
+                                          inp.get("w13_gs"), inp.get("w2_gs"))
         oracle.expert_rows(geo, xd[src[r0:r1] // sh.topk], w13d, w2d)
         done_rows += r1 - r0
         n_exp += 1
@@ -187,7 +191,8 @@ def main() -> int:
         return torch.from_numpy(a).cuda()
 
     x, x_sf = dev(inp["x"]), dev(inp["x_sf"])
-    weights = {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]), "w2": dev(inp["w2"]), "w2_sf": dev(inp["w2_sf"])}
+    weights = {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]), "w2": dev(inp["w2"]), "w2_sf": dev(inp["w2_sf"]),
+               "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs"))}
     logits = dev(inp["logits"])
     if sh.routing == "precomputed":
         topk_idx, topk_w = dev(inp["topk_idx"]), dev(inp["topk_weights"])

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 2
+#define MOE_FFN_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -63,13 +63,20 @@ typedef enum {
      [SymmBuffer] x_sf view); w13 E4M3 [E,2I,H] + fp32 [E,2I/128,H/128];
      w2 E4M3 [E,H,I] + fp32 [E,H/128,I/128].  H and I multiples of 128. */
   MOE_FMT_FP8_BLOCK128 = 0,
-  /* "BF16": x [T,H], w13 [E,2I,H], w2 [E,H,I] bf16, no scales.  H, I multiples of 128. */
+  /* "BF16": x [T,H], w13 [E,2I,H], w2 [E,H,I] bf16, no scales.  H, I multiples of 64. */
   MOE_FMT_BF16 = 1,
   /* "MXFP4 x MXFP8 (W4A8)": x E4M3 [T,H] + UE8M0 bytes [T,H/32] (token-major);
      w13 packed E2M1 [E,2I,H/2] + UE8M0 [E,2I,H/32]; w2 packed E2M1 [E,H,I/2]
      + UE8M0 [E,H,I/32].  Element 2i is the low nibble of byte i.
      H and I multiples of 32. */
-  MOE_FMT_W4A8_MX = 2
+  MOE_FMT_W4A8_MX = 2,
+  /* "NVFP4 x BF16 (W4A16)": x bf16 [T,H], no activation scale; w13 packed
+     E2M1 [E,2I,H/2] + E4M3 block scales [E,2I,H/16] + one fp32 global scale
+     per expert (moe_weights.w13_gs [E]); w2 packed E2M1 [E,H,I/2] + E4M3
+     [E,H,I/16] + w2_gs [E].  A weight is e2m1 * block scale * global scale
+     ([MegaFFN] gate_up_expert_scales / down_expert_scales carry the per-expert
+     scale).  The intermediate is bf16.  H and I multiples of 64. */
+  MOE_FMT_NVFP4_W4A16 = 3
 } moe_format;
 
 /* Routing input modes ([ActPack] routing_input_mode). */
@@ -107,6 +114,10 @@ typedef struct moe_weights {
   const void* w13_sf;  /* its scales (NULL for BF16) */
   const void* w2;      /* down_weight */
   const void* w2_sf;   /* its scales (NULL for BF16) */
+  const float* w13_gs; /* NVFP4: fp32 global scale per expert [E], read as given
+                          (no relayout; a prepared struct points at the same
+                          buffer); NULL for the other formats */
+  const float* w2_gs;  /* NVFP4: likewise for down_weight */
 } moe_weights;
 
 /* (host struct of device pointers) Routing plan, int32 each ([MegaFFN] Args). */
@@ -153,7 +164,12 @@ void moe_destroy(moe_handle* h);
            (sub < 4, l = 32*h + r, h < 2, r < 32) holds byte ks*128 + 32*sub + 16*h + b
            of tile row 32*rb + r; for w13 tile row 32*j + q is gate row 16*j + q
            (q < 16) or up row 16*j + q - 16 (q >= 16), for w2 it is row 32*j + q
-     FP8 scales unchanged.
+     NVFP4 RT 32, K-step 64, 1024-byte tile: byte 16*l + 4*sub + b (l = 32*h + r,
+           sub < 4, b < 4) holds byte ks*32 + 8*sub + 4*h + b of packed E2M1 tile
+           row r (rows mapped as for BF16), zero past the row's end
+     NVFP4 scales: 128-byte tile: byte 4*r + sub holds the E4M3 scale of
+           K-block (16 elements) 4*ks + sub of tile row r, zero past the end
+     FP8 scales unchanged; NVFP4 global scales are not part of the layout.
    moe_prepared_weights_size gives the sizes; moe_prepare_weights writes them. */
 moe_status moe_prepared_weights_size(const moe_handle* h, moe_prepared_sizes* out /* host */);
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
-FORMATS = {"fp8_block128": 0, "bf16": 1, "w4a8_mx": 2}
+FORMATS = {"fp8_block128": 0, "bf16": 1, "w4a8_mx": 2, "nvfp4_w4a16": 3}
 ROUTE_MODES = {"precomputed": 0, "from_logits": 1}
 TILE_REGIMES = {"auto": 0, "decode": 1, "prefill": 2}
 
@@ -43,7 +43,8 @@ class _Config(ctypes.Structure):
 
 class _Weights(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_sf", ctypes.c_void_p),
-                ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p)]
+                ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p),
+                ("w13_gs", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p)]
 
 
 class _Plan(ctypes.Structure):
@@ -178,6 +179,9 @@ class MoEFFN:
             dev = weights["w13"].device
             out = {n: (torch.empty(b, dtype=torch.uint8, device=dev) if b else None)
                    for n, b in self.prepared_weights_size().items()}
+        for g in ("w13_gs", "w2_gs"):  # NVFP4 global scales: read as given, no relayout
+            if weights.get(g) is not None:
+                out.setdefault(g, weights[g])
         cw, pw = self._weights_struct(weights), self._weights_struct(out)
         _check(self.lib.moe_prepare_weights(self._h, ctypes.byref(cw), ctypes.byref(pw), _stream(stream)),
                "moe_prepare_weights")
@@ -196,7 +200,8 @@ class MoEFFN:
 
     @staticmethod
     def _weights_struct(w: dict) -> _Weights:
-        return _Weights(_ptr(w["w13"]), _ptr(w.get("w13_sf")), _ptr(w["w2"]), _ptr(w.get("w2_sf")))
+        return _Weights(_ptr(w["w13"]), _ptr(w.get("w13_sf")), _ptr(w["w2"]), _ptr(w.get("w2_sf")),
+                        _ptr(w.get("w13_gs")), _ptr(w.get("w2_gs")))
 
     @staticmethod
     def _nbytes(t) -> int:
@@ -220,7 +225,7 @@ class MoEFFN:
         """(h, h_sf) buffers for moe_ffn_gate_up / moe_ffn_down."""
         import torch
         n = max(1, num_tokens * self.topk)
-        if self.fmt == "bf16":
+        if self.fmt in ("bf16", "nvfp4_w4a16"):
             return torch.empty((n, self.inter), dtype=torch.bfloat16, device=device), None
         h = torch.empty((n, self.inter), dtype=torch.uint8, device=device)
         if self.fmt == "fp8_block128":

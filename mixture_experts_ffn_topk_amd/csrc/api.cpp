@@ -26,7 +26,16 @@ struct Layout {
   size_t h_off, hsf_off, ffn_bytes, plan_scratch_bytes, total;
 };
 
-moe::Fmt to_fmt(int f) { return f == MOE_FMT_FP8_BLOCK128 ? moe::Fmt::FP8 : (f == MOE_FMT_BF16 ? moe::Fmt::BF16 : moe::Fmt::MX); }
+moe::Fmt to_fmt(int f) {
+  switch (f) {
+    case MOE_FMT_FP8_BLOCK128: return moe::Fmt::FP8;
+    case MOE_FMT_BF16: return moe::Fmt::BF16;
+    case MOE_FMT_NVFP4_W4A16: return moe::Fmt::NV4;
+    default: return moe::Fmt::MX;
+  }
+}
+// bf16 activations and intermediate, no activation scales
+bool bf16_acts(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_NVFP4_W4A16; }
 
 Layout layout_for(const moe_config& c, int T) {
   Layout L{};
@@ -111,6 +120,8 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
   a.w13_sf = w->w13_sf;
   a.w2 = w->w2;
   a.w2_sf = w->w2_sf;
+  a.w13_gs = w->w13_gs;
+  a.w2_gs = w->w2_gs;
   a.h = hbuf;
   a.h_sf = hsf;
   a.y = y;
@@ -120,11 +131,12 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
 bool weights_ok(const moe_config& c, const moe_weights* w) {
   if (!w || !w->w13 || !w->w2) return false;
   if (c.format != MOE_FMT_BF16 && (!w->w13_sf || !w->w2_sf)) return false;
+  if (c.format == MOE_FMT_NVFP4_W4A16 && (!w->w13_gs || !w->w2_gs)) return false;
   return true;
 }
 
 bool x_ok(const moe_config& c, const void* x, const void* x_sf) {
-  return x && (c.format == MOE_FMT_BF16 || x_sf);
+  return x && (bf16_acts(c.format) || x_sf);
 }
 
 // The GEMM kernels address every operand through buffer resources with 32-bit
@@ -134,7 +146,7 @@ bool sizes_supported(const moe_config& c) {
   constexpr unsigned long long kMaxBytes = 0x7FFFFFFFull;
   const unsigned long long T = (unsigned long long)c.max_num_tokens, H = (unsigned long long)c.hidden,
                            I = (unsigned long long)c.intermediate_hidden, k = (unsigned long long)c.num_topk;
-  const unsigned long long act = c.format == MOE_FMT_BF16 ? 2 : 1;  // bytes per activation element
+  const unsigned long long act = bf16_acts(c.format) ? 2 : 1;  // bytes per activation element
   if (T * H * act > kMaxBytes || T * k * I * act > kMaxBytes) return false;
   // prepared weight bytes per expert
   const moe::Fmt f = to_fmt(c.format);
@@ -182,6 +194,9 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
       break;
     case MOE_FMT_W4A8_MX:
       if (c.hidden % 32 || c.intermediate_hidden % 32) return MOE_ERR_INVALID_ARGUMENT;
+      break;
+    case MOE_FMT_NVFP4_W4A16:
+      if (c.hidden % 64 || c.intermediate_hidden % 64) return MOE_ERR_INVALID_ARGUMENT;
       break;
     default:
       return MOE_ERR_INVALID_ARGUMENT;
@@ -266,7 +281,7 @@ moe_status moe_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_
 moe_status moe_ffn_gate_up(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
                            const moe_plan_buffers* plan, void* h_out, void* h_sf_out, hipStream_t stream) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (h->cfg.format != MOE_FMT_BF16 && !h_sf_out)))
+  if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (!bf16_acts(h->cfg.format) && !h_sf_out)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1);
@@ -275,7 +290,7 @@ moe_status moe_ffn_gate_up(const moe_handle* h, int32_t T, const void* x, const 
 moe_status moe_ffn_down(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in, const moe_weights* w,
                         const moe_plan_buffers* plan, void* y, hipStream_t stream) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!h_in || !y || (h->cfg.format != MOE_FMT_BF16 && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!h_in || !y || (!bf16_acts(h->cfg.format) && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2);
 }

@@ -77,6 +77,7 @@ struct GemmParams {
   uint32_t bsc_expert_bytes;  // MX: prepared scale bytes per expert
   const void* B_sf;
   int b_sf_row;  // FP8: K/128 floats per 128-row block
+  const float* B_gs;  // NV4: global weight scale per expert
   void* C;
   long long c_row_bytes;
   void* C_sf;
@@ -94,6 +95,26 @@ MOE_DEV i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
+// Formats whose MFMA runs on bf16 operands (32x32x16): BF16, and NV4, whose
+// E2M1 weights are decoded to bf16 in registers.  Both take bf16 activations.
+constexpr bool bf16_mma(Fmt f) { return f == Fmt::BF16 || f == Fmt::NV4; }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Two fp32 values -> packed bf16 (round to nearest even; NV4 products are exact in bf16)
+MOE_DEV int pack_bf16x2(f32x2 v) { return __builtin_bit_cast(int, __builtin_convertvector(v, bf16x2v)); }
+// NV4: 8 E2M1 values (a 32-bit word, element 2i in the low nibble of byte i) times
+// their E4M3 block scale s, as 8 bf16.  The product of a 2-bit and a 4-bit
+// significand is exact in bf16; the hardware conversion is exact (unit scale).
+MOE_DEV i32x4 nv4_bf16x8(uint32_t d, float s) {
+  i32x4 r;
+  r[0] = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0) * s);
+  r[1] = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1) * s);
+  r[2] = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2) * s);
+  r[3] = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3) * s);
+  return r;
+}
+
 MOE_DEV int xcd_remap(int bid, int G) {
   // Work-groups are dealt round-robin over the 8 XCDs; give each XCD a
   // contiguous range of logical tiles so neighbours share its L2.
@@ -105,7 +126,8 @@ template <Fmt F, int NT>
 struct BFrag {
   // 16-byte pieces of the lane's weight K-step segment: FP8 / BF16 use bytes
   // [16g, 16g+16) (lo) and [64+16g, 64+16g+16) (hi); MX uses lo (32 E2M1 values)
-  // and a scale byte.  Kept as separate 4-register values so that each load
+  // and a scale byte; NV4 uses lo[t] (32 E2M1 values of 32-row tile t) and sc[t]
+  // (its four E4M3 block scales).  Kept as separate 4-register values so that each load
   // lands in the registers the MFMA reads.
   i32x4 lo[NT], hi[NT];
   int sc[NT];
@@ -123,13 +145,13 @@ struct Tile {
   // Weight-bound BF16 tiles keep a padded 144-byte row instead: the swizzle's
   // per-sub-step offsets do not fit their register budget.
   static constexpr bool kDma = F != Fmt::MX && BM > 96;  // direct-to-LDS staging (below)
-  static constexpr int kSwz = F == Fmt::BF16 && !kDma ? 0 : 7;
-  static constexpr int kARowBytes = F == Fmt::BF16 && !kDma ? 144 : 128;
+  static constexpr int kSwz = bf16_mma(F) && !kDma ? 0 : 7;
+  static constexpr int kARowBytes = bf16_mma(F) && !kDma ? 144 : 128;
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
   // A buffer rows: BM rounded up so that every thread stores every chunk it loads
   // (chunks past BM rows are zeros landing in spare rows): no divergent stores in the loop
   static constexpr int kARows = kAChunks * kThreads / 8;
-  static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (F == Fmt::BF16 ? 2 : 1) : BN * 2;
+  static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (bf16_mma(F) ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
   static constexpr int kAStepBytes = kARows * kARowBytes;
   // MFMA-bound FP8 / BF16 tiles stage A with direct-to-LDS loads into three
@@ -158,12 +180,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
   constexpr int BN = TL::BN;
   constexpr int MT32 = BM / 32, NT32 = NT / 2;  // BF16: 32-row token slices and weight tiles
-  static_assert(F != Fmt::BF16 || BM % 32 == 0, "BF16 tiles hold whole 32-token slices");
+  static_assert(!bf16_mma(F) || BM % 32 == 0, "bf16-operand tiles hold whole 32-token slices");
   // Weight-bound tiles skip the 16-row token slices past the tile's rows (experts
   // smaller than the tile).  MFMA-bound tiles are almost always full, and the
   // branch would split the K-step into blocks the scheduler cannot interleave.
-  constexpr bool kSkipSlices = BM <= 96 || F == Fmt::BF16;  // (BF16 measured faster with the skip)
-  constexpr bool kPrio = BM > 96 && F != Fmt::BF16;  // (measured: helps MFMA-bound FP8 / MX tiles only)
+  constexpr bool kSkipSlices = BM <= 96 || bf16_mma(F);  // (BF16 measured faster with the skip)
+  constexpr bool kPrio = BM > 96 && !bf16_mma(F);  // (measured: helps MFMA-bound FP8 / MX tiles only)
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
   constexpr int HC = BN / 2;  // gate_up: h columns per tile (gate and up rows, NT/2 tiles each per wave)
   static_assert(!GATEUP || HC % 128 == 0, "a gate_up tile holds whole 128-column blocks of h");
@@ -226,7 +248,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   __amdgpu_buffer_rsrc_t bsc_rs = b_rs;
   uint32_t b_off[NT], bsc_off[NT];
   {
-    if (F == Fmt::MX)
+    if (F == Fmt::MX || F == Fmt::NV4)
       bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         wrow0 = col0;
       }
       uint32_t tiles0 = (uint32_t)(wrow0 / 16) * (uint32_t)p.ksteps;  // first tile of the row block
-      if (F == Fmt::BF16) {
+      if (bf16_mma(F)) {
         // 32-row tiles: gate_up tile j holds gate rows [16j, 16j+16) then the
         // matching up rows; down tile j holds rows [32j, 32j+32)
         const int t = nt < NT32 ? nt : 0;
@@ -248,7 +270,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       }
       const bool ok = col0 < p.N;
       b_off[nt] = ok ? tiles0 * p.b_tile + (uint32_t)lane * 16u : kOOB;
-      bsc_off[nt] = ok ? tiles0 * 64u + (uint32_t)lane : kOOB;
+      // MX: the lane's scale byte; NV4: the four scale bytes of the lane's tile row
+      bsc_off[nt] = ok ? (F == Fmt::NV4 ? tiles0 * 128u + (uint32_t)(lane & 31) * 4u : tiles0 * 64u + (uint32_t)lane)
+                       : kOOB;
     }
     if (F == Fmt::FP8) {
       // the tile's weight-scale rows, staged in LDS: gate_up [0, kHB) the gate
@@ -284,6 +308,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       }
       return;
     }
+    if constexpr (F == Fmt::NV4) {
+      // 32-row tile t: one 1 KB load of E2M1 data and the lanes' block scales
+#pragma unroll
+      for (int t = 0; t < NT32; ++t) {
+        b.lo[t] = bload16(b_rs, b_off[t] | dead, (uint32_t)ks * p.b_tile);
+        b.sc[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(bsc_rs, bsc_off[t] | dead, (uint32_t)ks * 128u, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint32_t o = b_off[nt] | dead;
@@ -310,9 +343,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // ---------------------------------------------------------------- main loop
   // FP8, MX: 16x16 tiles acc[token slice][weight tile]; BF16: 32x32 tiles
   // acc32[32-token slice][32-row weight tile] (v_mfma_f32_32x32x16_bf16)
-  f32x4 acc[F == Fmt::BF16 ? 1 : MT][F == Fmt::BF16 ? 1 : NT];
-  f32x16 acc32[F == Fmt::BF16 ? MT32 : 1][F == Fmt::BF16 ? NT32 : 1];
-  if constexpr (F == Fmt::BF16) {
+  f32x4 acc[bf16_mma(F) ? 1 : MT][bf16_mma(F) ? 1 : NT];
+  f32x16 acc32[bf16_mma(F) ? MT32 : 1][bf16_mma(F) ? NT32 : 1];
+  if constexpr (bf16_mma(F)) {
 #pragma unroll
     for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
@@ -346,7 +379,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step)
   const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
   uint32_t asf_off = kOOB;  // threads past the tile's rows load zeros
-  if (F != Fmt::BF16 && tid < rows) {
+  if (!bf16_mma(F) && tid < rows) {
     const int grow = row0 + tid;
     const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
     asf_off = arow * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u);
@@ -392,7 +425,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         *(i32x4*)(base + r * TL::kARowBytes + (((c & 7) ^ (r & TL::kSwz)) * 16)) = v[u][i];
       }
     }
-    if (F != Fmt::BF16) {
+    if (!bf16_mma(F)) {
 #pragma unroll
       for (int u = 0; u < KSG; ++u) sa_lds[(buf * KSG + u) * TL::kSA + tid] = s[u];
     }
@@ -416,7 +449,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   };
   // VMEM instructions per stage: the A loads (D) and the weight-ring refills (R)
-  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * NT * 2;
+  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * (F == Fmt::NV4 ? NT : NT * 2);
 
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
   uint32_t as[TL::kDma ? 1 : 2][KSG] = {};
@@ -471,11 +504,23 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
           acc[mt][nt] += part * (sa * sbv[nt]);
         }
       }
-    } else if constexpr (F == Fmt::BF16) {
+    } else if constexpr (bf16_mma(F)) {
       // 32x32x16 MFMAs: lane l = 32*h + r holds token mt*32 + r and bytes
       // [32*sub + 16*h, +16) of the K-step segment; weight sub-step fragments
-      // are bq_.lo[2t], lo[2t+1], hi[2t], hi[2t+1] for sub = 0..3
+      // are bq_.lo[2t], lo[2t+1], hi[2t], hi[2t+1] for sub = 0..3 (BF16), or
+      // decoded from word sub of bq_.lo[t] with block scale byte sub of bq_.sc[t] (NV4)
       const int r32 = lane & 31, h32 = lane >> 5;
+      i32x4 bop[F == Fmt::NV4 ? NT32 : 1][4];
+      if constexpr (F == Fmt::NV4) {
+#pragma unroll
+        for (int t = 0; t < NT32; ++t) {
+          const int sw = bq_.sc[t];
+          bop[t][0] = nv4_bf16x8((uint32_t)bq_.lo[t][0], __builtin_amdgcn_cvt_f32_fp8(sw, 0));
+          bop[t][1] = nv4_bf16x8((uint32_t)bq_.lo[t][1], __builtin_amdgcn_cvt_f32_fp8(sw, 1));
+          bop[t][2] = nv4_bf16x8((uint32_t)bq_.lo[t][2], __builtin_amdgcn_cvt_f32_fp8(sw, 2));
+          bop[t][3] = nv4_bf16x8((uint32_t)bq_.lo[t][3], __builtin_amdgcn_cvt_f32_fp8(sw, 3));
+        }
+      }
 #pragma unroll
       for (int mt = 0; mt < MT32; ++mt) {
         if (kSkipSlices && mt * 32 >= rows) break;  // wave-uniform: no token rows left
@@ -485,7 +530,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
           const i32x4 a = *(const i32x4*)(arow + 16 * ((2 * sub + h32) ^ (r32 & TL::kSwz)));
 #pragma unroll
           for (int t = 0; t < NT32; ++t) {
-            const i32x4 b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
+            i32x4 b;
+            if constexpr (F == Fmt::NV4)
+              b = bop[t][sub];
+            else
+              b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
             acc32[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
                                                                    __builtin_bit_cast(bf16x8, a), acc32[mt][t], 0, 0, 0);
           }
@@ -531,7 +580,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // its previous contents (the two values would then both be live): tie the
       // load's scalar offset to the step's last accumulator update.
       int ks_next = ks + DEPTH;
-      if constexpr (F == Fmt::BF16)
+      if constexpr (bf16_mma(F))
         asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc32[MT32 - 1][NT32 - 1][15]));
       else
         asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
@@ -562,7 +611,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       kstep(slot, su % 3, u, ks);
       if (u + 1 < KSG) __builtin_amdgcn_sched_barrier(0);
       int ks_next = ks + DEPTH;
-      if constexpr (F == Fmt::BF16)
+      if constexpr (bf16_mma(F))
         asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc32[MT32 - 1][NT32 - 1][15]));
       else
         asm volatile("; ring refill after step" : "+s"(ks_next) : "v"(acc[MT - 1][NT - 1][3]));
@@ -602,10 +651,18 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // tile's rows 8*(i/4) + 4*h32 + i%4 (i < 16); in a gate_up tile rows < 16 are
   // gate rows and row 16 + j the up row of gate row j, so acc32[..][i] pairs with [i + 8].
   const int r32 = lane & 31, h32 = lane >> 5;
+  if constexpr (F == Fmt::NV4) {
+    // the expert's global weight scale multiplies every output of the leg
+    const float gsc = p.B_gs[expert];
+#pragma unroll
+    for (int mt = 0; mt < MT32; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT32; ++t) acc32[mt][t] *= gsc;
+  }
   if (GATEUP) {
     constexpr int NJ = NT / 2;  // gate (and up) column tiles per wave
     const float c = p.clamp;
-    if constexpr (F == Fmt::BF16) {
+    if constexpr (bf16_mma(F)) {
 #pragma unroll
       for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
@@ -676,7 +733,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     __syncthreads();
     // coalesced copy of the tile's h rows: 16-byte chunks
     constexpr int CPR = TL::kOutRowBytes / 16;  // chunks per row
-    constexpr int elem = F == Fmt::BF16 ? 2 : 1;
+    constexpr int elem = bf16_mma(F) ? 2 : 1;
     for (int c = tid; c < BM * CPR; c += kThreads) {
       const int r = c / CPR, cc = c % CPR;
       const int col = n_tile * HC + cc * 16 / elem;
@@ -687,7 +744,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   } else {
     // down: bf16 rows scattered to their pair slots y[src_info[row]]
-    if constexpr (F == Fmt::BF16) {
+    if constexpr (bf16_mma(F)) {
 #pragma unroll
       for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
@@ -727,7 +784,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 }
 
 // ------------------------------------------------------------------ host side
-size_t ffn_h_bytes(Fmt f, int rows, int I) { return (size_t)rows * I * (f == Fmt::BF16 ? 2 : 1); }
+size_t ffn_h_bytes(Fmt f, int rows, int I) { return (size_t)rows * I * (bf16_mma(f) ? 2 : 1); }
 size_t ffn_hsf_bytes(Fmt f, int rows, int I) {
   if (f == Fmt::FP8) return (size_t)rows * (I / 128) * 4;
   if (f == Fmt::MX) return (size_t)rows * (I / 32);
@@ -767,7 +824,7 @@ constexpr LegConfig leg_config() {
   }
   // MFMA-bound tiles
   if (F == Fmt::MX) return {8, 2, 6, 2, 1};
-  if (F == Fmt::BF16) return {8, 4, 2, 1, 1};  // 512 weight rows (gate_up: 256 h columns)
+  if (bf16_mma(F)) return {8, 4, 2, 1, 1};  // 512 weight rows (gate_up: 256 h columns)
   if (F == Fmt::FP8) return {8, 4, 2, 1, 1};  // 512 weight rows (gate_up: 256 h columns)
   return {8, 2, 2, 2, 1};
 }
@@ -798,8 +855,8 @@ static void launch_pair(const GemmParams& g1_in, const GemmParams& g2_in, bool f
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   const int npairs = a.T * a.topk;
   if (npairs == 0) return hipSuccess;
-  const int elem_k = a.fmt == Fmt::BF16 ? 64 : 128;
-  const uint32_t esz = a.fmt == Fmt::BF16 ? 2 : 1;
+  const int elem_k = bf16_mma(a.fmt) ? 64 : 128;
+  const uint32_t esz = bf16_mma(a.fmt) ? 2 : 1;
   const int sf_div = a.fmt == Fmt::FP8 ? 128 : 32;
   GemmParams g1{}, g2{};
   // gate_up: A = x rows gathered through src_info, B = w13 [E, 2I, H]
@@ -808,7 +865,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.E = a.E;
   g1.topk = a.topk;
   // BF16 weight-bound tiles are 96 rows (whole 32-token slices of its 32x32 MFMA)
-  const int bm = (a.fmt == Fmt::BF16 && a.bm <= 96) ? 96 : a.bm;
+  const int bm = (bf16_mma(a.fmt) && a.bm <= 96) ? 96 : a.bm;
   g1.m_tiles_max = ffn_max_m_tiles(npairs, a.E, bm);
   g1.K = a.H;
   g1.ksteps = (a.H + elem_k - 1) / elem_k;
@@ -826,6 +883,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(a.fmt, 2 * a.I, a.H));
   g1.B_sf = a.w13_sf;
   g1.b_sf_row = a.H / sf_div;
+  g1.B_gs = a.w13_gs;
   g1.C = a.h;
   g1.c_row_bytes = (long long)a.I * esz;
   g1.C_sf = a.h_sf;
@@ -849,6 +907,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g2.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(a.fmt, a.H, a.I));
   g2.B_sf = a.w2_sf;
   g2.b_sf_row = a.I / sf_div;
+  g2.B_gs = a.w2_gs;
   g2.C = a.y;
   g2.c_row_bytes = (long long)a.H * 2;
   g2.C_sf = nullptr;
@@ -865,6 +924,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
     case Fmt::MX:
       if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage);
       else launch_pair<Fmt::MX, 80>(g1, g2, a.fast, s, stage);
+      break;
+    case Fmt::NV4:
+      if (bm == 128) launch_pair<Fmt::NV4, 128>(g1, g2, a.fast, s, stage);
+      else launch_pair<Fmt::NV4, 96>(g1, g2, a.fast, s, stage);
       break;
   }
   return hipGetLastError();

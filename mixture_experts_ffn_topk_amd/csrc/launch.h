@@ -7,7 +7,7 @@
 
 namespace moe {
 
-enum class Fmt : int { FP8 = 0, BF16 = 1, MX = 2 };
+enum class Fmt : int { FP8 = 0, BF16 = 1, MX = 2, NV4 = 3 };  // NV4: NVFP4 weights x bf16 activations
 
 struct PlanPtrs {
   int* expert_counts;
@@ -32,12 +32,12 @@ hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, vo
                                     float* w_out, bool fast, hipStream_t s);
 
 // Prepared weight layout: tiles of 16 rows x one K-step in MFMA lane order.
-size_t prepared_tile_bytes(Fmt f);                           // 2048 (FP8), 4096 (BF16) or 1024 (MX)
-int prepared_ksteps(Fmt f, int K);                           // K-steps of 128 (64 for BF16) elements
+size_t prepared_tile_bytes(Fmt f);                           // 2048 (FP8), 4096 (BF16), 1024 (MX, NV4)
+int prepared_ksteps(Fmt f, int K);                           // K-steps of 128 (64 for BF16, NV4) elements
 size_t prepared_expert_bytes(Fmt f, int rows, int K);        // one expert's weight tiles
-size_t prepared_scale_expert_bytes(Fmt f, int rows, int K);  // MX: one expert's scale tiles; else 0
-// Relayout E experts' [rows, K] weights (and MX scales; FP8 scales are copied).
-// gate_up: the matrix is the gate_up weight (BF16 interleaves its gate and up rows).
+size_t prepared_scale_expert_bytes(Fmt f, int rows, int K);  // MX, NV4: one expert's scale tiles; else 0
+// Relayout E experts' [rows, K] weights (and MX / NV4 scales; FP8 scales are copied).
+// gate_up: the matrix is the gate_up weight (BF16 and NV4 interleave its gate and up rows).
 hipError_t launch_prepare(Fmt f, int E, int rows, int K, bool gate_up, const void* w, const void* w_sf, void* out,
                           void* out_sf, hipStream_t s);
 
@@ -47,7 +47,7 @@ struct FfnArgs {
   int T, E, topk, H, I;
   float clamp;
   bool fast;
-  int bm;  // 80 (weight-bound tiles) or 128 (MFMA-bound tiles)
+  int bm;  // 80 (weight-bound tiles; 96 for bf16 operands) or 128 (MFMA-bound tiles)
   const int* start;     // expert_start_indices [E+1]
   const int* src_info;  // [T*k]
   const void* x;
@@ -56,6 +56,8 @@ struct FfnArgs {
   const void* w13_sf;
   const void* w2;
   const void* w2_sf;
+  const float* w13_gs;  // NV4: fp32 global scale per expert [E]
+  const float* w2_gs;
   void* h;     // intermediate [T*k, I] (E4M3 or bf16)
   void* h_sf;  // its scales: fp32 [T*k, I/128] (FP8) or UE8M0 [T*k, I/32] (MX)
   void* y;     // [T*k, H] bf16, row p = src_info[row]

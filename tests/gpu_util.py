@@ -34,7 +34,8 @@ def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.i
     sh = inp["shape"]
     d = {"x": dev(inp["x"]), "x_sf": dev(inp["x_sf"]),
          "weights": {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]),
-                     "w2": dev(inp["w2"]), "w2_sf": dev(inp["w2_sf"])},
+                     "w2": dev(inp["w2"]), "w2_sf": dev(inp["w2_sf"]),
+                     "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs"))},
          "logits": dev(inp["logits"])}
     if sh.routing == "precomputed":
         ids = inp["topk_idx"] if topk_idx is None else topk_idx
@@ -45,6 +46,11 @@ def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.i
         d["topk_idx"] = torch.full((sh.tokens, sh.topk), -7, dtype=idx_dtype, device="cuda")
         d["topk_weights"] = torch.full((sh.tokens, sh.topk), -1.0, dtype=torch.float32, device="cuda")
     return d
+
+
+def gs_kwargs(inp: dict) -> dict:
+    """The NVFP4 per-expert global scales as oracle keywords (empty for the other formats)."""
+    return {"w13_gs": inp["w13_gs"], "w2_gs": inp["w2_gs"]} if "w13_gs" in inp else {}
 
 
 def prepared(moe: MoEFFN, d: dict) -> dict:
@@ -60,6 +66,19 @@ def prepared_layout_reference(fmt: str, w: np.ndarray, sf: np.ndarray | None, ro
     (numpy index arithmetic, independent of the library)."""
     E = w.shape[0]
     rb = rows // 16
+    if fmt == "nvfp4_w4a16":
+        ks = K // 64
+        wb = np.ascontiguousarray(w).reshape(E, rows, K // 2)
+        sb = np.ascontiguousarray(sf).reshape(E, rows, K // 16)
+        if gate_up:  # tile j: gate rows 16j..16j+15, then up rows 16j..16j+15
+            half = rows // 2
+            order = np.stack([np.arange(half).reshape(-1, 16), half + np.arange(half).reshape(-1, 16)], 1).reshape(-1)
+            wb, sb = wb[:, order], sb[:, order]
+        # [E, rb, r(32), ks, sub, h, b] -> [E, rb, ks, h, r, sub, b]  (lane l = 32*h + r)
+        t = wb.reshape(E, rows // 32, 32, ks, 4, 2, 4).transpose(0, 1, 3, 5, 2, 4, 6)
+        # [E, rb, r(32), ks, sub] -> [E, rb, ks, r, sub]
+        ts = sb.reshape(E, rows // 32, 32, ks, 4).transpose(0, 1, 3, 2, 4)
+        return t.reshape(-1), ts.reshape(-1)
     if fmt == "w4a8_mx":
         ks = -(-K // 128)
         wb = np.zeros((E, rows, ks * 64), np.uint8)
@@ -150,7 +169,7 @@ def run_ffn_intermediates(moe: MoEFFN, d: dict, T: int):
     torch.cuda.synchronize()
     n = T * moe.topk
     hc = h[:n].cpu()
-    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt == "bf16" else hc.numpy()
+    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt in ("bf16", "nvfp4_w4a16") else hc.numpy()
     hs = None if hsf is None else hsf[:n].cpu().numpy()
     return out[:T], plan, y, hc, hs
 
@@ -168,7 +187,7 @@ def check_intermediate(fmt, hx, codes, hsf, I):
     """Check the GPU's requantised intermediate rows (codes, scales) against the
     oracle's requantisation of the exact rows hx.  Returns (GPU values, flips)."""
     R = hx.shape[0]
-    if fmt == "bf16":
+    if fmt in ("bf16", "nvfp4_w4a16"):
         hr = oracle.round_bf16(hx)
         hg = oracle.bf16_decode(codes)
         bad = hr != hg
@@ -229,7 +248,8 @@ def staged_check(shape, inp: dict, res: dict, ref_plan: dict, topk_idx, topk_wei
         r0, r1 = int(start[e]), int(start[e + 1])
         if r1 == r0:
             continue
-        w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e)
+        w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e,
+                                          **gs_kwargs(inp))
         X = xd[src[r0:r1] // k]
         hx = oracle.swiglu_clamped(X @ w13d[:I].T, X @ w13d[I:].T, geo.clamp)
         hg, f = check_intermediate(shape.fmt, hx, h_g[r0:r1], None if hsf_g is None else hsf_g[r0:r1], I)

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -65,6 +65,8 @@ def _cfg(**kw):
     ({"format": 2, "hidden": 2880, "intermediate_hidden": 2880, "num_experts": 128, "num_topk": 4,
       "route_mode": 1}, 0),                    # MX: multiples of 32, logits routing
     ({"format": 2, "hidden": 2880 + 16, "intermediate_hidden": 2880}, 1),
+    ({"format": 3}, 0),                                          # NVFP4: multiples of 64
+    ({"format": 3, "hidden": 7168 + 32}, 1),
     ({"route_mode": 1, "num_experts": 600, "num_topk": 4}, 2),   # FromLogits over > 512 experts
     ({"max_num_tokens": -1}, 1),
     ({"hidden": 32768 + 128}, 2),                # FP8 weight scales of > 256 K-steps
@@ -122,6 +124,9 @@ def test_prepared_weight_sizes_and_validation():
         # MX: K = 2880 -> 23 K-steps of 128 (the last one half empty, zero-padded)
         (dict(format=2, hidden=2880, intermediate_hidden=2880, num_experts=128, num_topk=4),
          (128 * 360 * 23 * 1024, 128 * 360 * 23 * 64, 128 * 180 * 23 * 1024, 128 * 180 * 23 * 64)),
+        # NVFP4: 32-row tiles, K-steps of 64 -> 1024-byte data tiles and 128-byte scale tiles
+        (dict(format=3, hidden=7168, intermediate_hidden=2048, num_experts=32, num_topk=8),
+         (32 * 128 * 112 * 1024, 32 * 128 * 112 * 128, 32 * 224 * 32 * 1024, 32 * 224 * 32 * 128)),
     ]
     for kw, want in cases:
         h = ctypes.c_void_p()
@@ -137,6 +142,16 @@ def test_prepared_weight_sizes_and_validation():
     assert lib.moe_prepare_weights(h, ctypes.byref(canon), ctypes.byref(mx._Weights(None, 1, 1, 1)), None) == 1
     assert lib.moe_prepare_weights(h, ctypes.byref(canon), ctypes.byref(mx._Weights(4104, 16, 8192, 16)), None) == 1
     assert lib.moe_prepare_weights(h, ctypes.byref(canon), ctypes.byref(mx._Weights(256, 16, 8192, 16)), None) == 1
+    lib.moe_destroy(h)
+    # NVFP4 needs both per-expert global scales
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(format=3)), ctypes.byref(h)) == 0
+    no_gs = mx._Weights(256, 512, 768, 1024)
+    with_gs = mx._Weights(256, 512, 768, 1024, 2048, 4096)
+    out = mx._Weights(8192, 16384, 32768, 65536, 2048, 4096)
+    assert lib.moe_prepare_weights(h, ctypes.byref(no_gs), ctypes.byref(out), None) == 1
+    assert lib.moe_prepare_weights(h, ctypes.byref(with_gs), ctypes.byref(mx._Weights(8192, 16384, 32768, 65536)),
+                                   None) == 1
     lib.moe_destroy(h)
 
 

@@ -9,7 +9,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import (compare_out, device_inputs, geometry, make_moe, prepared_layout_reference, run_ffn_intermediates,
+from gpu_util import (compare_out, device_inputs, geometry, gs_kwargs, make_moe, prepared_layout_reference, run_ffn_intermediates,
                       run_forward, run_split,
                       staged_check)
 
@@ -120,7 +120,8 @@ def test_combine_against_oracle():
 
 
 # ------------------------------------------------------------------ prepared weight layout (bit-exact)
-@pytest.mark.parametrize("fmt,H,I", [("fp8_block128", 512, 384), ("bf16", 448, 320), ("w4a8_mx", 576, 352)])
+@pytest.mark.parametrize("fmt,H,I", [("fp8_block128", 512, 384), ("bf16", 448, 320), ("w4a8_mx", 576, 352),
+                                     ("nvfp4_w4a16", 448, 320)])
 def test_prepare_weights_layout(fmt, H, I):
     sh = small("prep_" + fmt, 7, 16, H, I, 3, 2, fmt)
     inp = moe_synth.make_inputs(sh)
@@ -156,6 +157,9 @@ SMALL = [
     ("bf16_prefill", dict(T=200, H=448, I=256, E=3, k=2, fmt="bf16"), "prefill"),
     ("mx_tails_logits", dict(T=80, H=576, I=352, E=6, k=3, fmt="w4a8_mx", routing="from_logits"), "decode"),
     ("mx_prefill_logits", dict(T=150, H=320, I=224, E=3, k=2, fmt="w4a8_mx", routing="from_logits"), "prefill"),
+    ("nvfp4_decode_tiles", dict(T=100, H=512, I=320, E=8, k=4, fmt="nvfp4_w4a16"), "decode"),
+    ("nvfp4_prefill_tiles", dict(T=300, H=448, I=384, E=4, k=2, fmt="nvfp4_w4a16"), "prefill"),
+    ("nvfp4_clamp_fires", dict(T=48, H=256, I=128, E=4, k=2, fmt="nvfp4_w4a16", x_scale=20.0), "auto"),
     ("fp8_clamp_fires", dict(T=48, H=256, I=256, E=4, k=2, fmt="fp8_block128", x_scale=20.0), "auto"),
     ("bf16_clamp_fires", dict(T=48, H=256, I=128, E=4, k=2, fmt="bf16", x_scale=20.0), "auto"),
 ]
@@ -179,7 +183,7 @@ def test_ffn_small_against_oracle(name, kw, regime):
         np.testing.assert_allclose(d["topk_weights"].cpu().numpy(), w, rtol=1e-5, atol=1e-7)
         w = d["topk_weights"].cpu().numpy()  # the combine uses the GPU's fp32 weights
     ref = oracle.forward(geo, inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
-                         topk_idx=ids, topk_weights=w)
+                         topk_idx=ids, topk_weights=w, **gs_kwargs(inp))
     # end to end: relative L2 against the pure oracle
     compare_out(out, ref["out"], rel_l2=1e-2, max_rms=np.inf)
     # stage by stage, with rounding-tie flips of the requantised intermediate accounted for

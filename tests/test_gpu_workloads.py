@@ -12,7 +12,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import check_intermediate, check_y_rows, compare_out, device_inputs, geometry, make_moe, prepared
+from gpu_util import check_intermediate, check_y_rows, compare_out, device_inputs, geometry, gs_kwargs, make_moe, prepared
 
 pytestmark = pytest.mark.gpu
 
@@ -38,12 +38,12 @@ def _gather_intermediate(moe, d, T, rows):
     torch.cuda.synchronize()
     ridx = torch.as_tensor(rows, dtype=torch.int64, device="cuda")
     hc = h.index_select(0, ridx).cpu()
-    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt == "bf16" else hc.numpy()
+    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt in ("bf16", "nvfp4_w4a16") else hc.numpy()
     hs = None if hsf is None else hsf.index_select(0, ridx).cpu().numpy()
     return plan, y, hc, hs
 
 
-@pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER)
+@pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER + ["nvfp4_decode"])
 def test_named_workload_full_size(name):
     sh = moe_synth.CONFIGS[name]
     print(f"[fullsize] {name}: generating inputs", flush=True)
@@ -91,7 +91,8 @@ def test_named_workload_full_size(name):
     y_ref2 = np.zeros((len(pairs), H))
     flips = 0
     for e, lst in by_e.items():
-        w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e)
+        w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e,
+                                          **gs_kwargs(inp))
         X = xd[[tpos[pairs[n][0]] for n in lst]]
         hx = oracle.swiglu_clamped(X @ w13d[:I].T, X @ w13d[I:].T, geo.clamp)
         hg, f = check_intermediate(sh.fmt, hx, h_g[lst], None if hsf_g is None else hsf_g[lst], I)
@@ -106,6 +107,6 @@ def test_named_workload_full_size(name):
     compare_out(torch.from_numpy(out_np[toks]), out_ref2)
     # and the pure oracle on the sample, relative L2
     ref = oracle.forward_tokens(geo, toks, inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
-                                ids, w)
+                                ids, w, **gs_kwargs(inp))
     compare_out(torch.from_numpy(out_np[toks]), ref, rel_l2=1e-2, max_rms=np.inf)
     print(f"[fullsize] {name}: ok ({len(pairs)} pairs sampled, {flips} rounding-tie flips)", flush=True)
