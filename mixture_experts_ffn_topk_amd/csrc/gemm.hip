@@ -9,26 +9,33 @@
 //
 // Workgroup: WAVES wavefronts, BM rows x BN = WAVES*16*NT weight rows per tile.
 //   * A (activation rows, gathered through src_info for gate_up) is staged in
-//     LDS, double buffered, one 128-byte K-step segment per row.
-//   * B (weights) streams from HBM straight into VGPRs in MFMA operand order,
-//     DEPTH K-steps deep, each wave owning 16*NT weight rows.  Every weight byte
-//     of a tile is read once.
+//     LDS, KSG K-steps per stage, rows XOR-swizzled in 16-byte chunks; MFMA-bound
+//     FP8 / bf16-operand tiles load it with direct-to-LDS buffer loads.
+//   * B (weights) streams from HBM straight into VGPRs from the prepared tiles
+//     (MFMA operand order, one 1 KB run per wave load), DEPTH K-steps deep,
+//     each wave owning 16*NT weight rows.  Every weight byte of a tile is read once.
 // All global loads are buffer loads: a uniform base, a loop-invariant 32-bit
 // lane offset and the K-step offset in a scalar register; a lane offset past
 // the end of the resource reads zeros, which masks rows and columns outside
 // the problem.
-// MFMA per format, weights as the first operand and activations as the second
-// (16x16 output tiles, 4 f32 per lane: token l%16, weight rows 4*(l/16)+i):
+// MFMA per format, weights as the first operand and activations as the second:
 //   FP8 block-128: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales per
 //                  K-step of 128 into a partial, then acc += (sa[token] * sb) *
 //                  partial with the fp32 block scales of the DeepSeek FP8 encoding.
-//   BF16:          2 x v_mfma_f32_16x16x32_bf16 per K-step of 64.
+//   BF16:          v_mfma_f32_32x32x16_bf16, four per 32-row tile and K-step of 64.
+//   NV4 (NVFP4 x BF16): the same bf16 MFMAs on weights decoded in registers:
+//                  E2M1 -> fp32 (exact) times the E4M3 block scale of its 16
+//                  elements (exact in bf16); the expert's global scale
+//                  multiplies the accumulators in the epilogue.
 //   MX (W4A8):     v_mfma_scale_f32_16x16x128_f8f6f4, weights E2M1 + UE8M0,
 //                  activations E4M3 + UE8M0, the block scales applied by the hardware.
-// Operand lane layout (lane l, g = l/16): an FP8/BF16 row segment of 128 bytes
-// is fed as bytes [16g, 16g+16) and [64+16g, 64+16g+16); an E2M1 segment of
-// 64 bytes as bytes [16g, 16g+16); the scale byte of lane l belongs to
-// K-block g (32 elements) of row l%16.
+// 16x16 output tiles hold 4 f32 per lane (token l%16, weight rows 4*(l/16)+i);
+// 32x32 tiles 16 (token l%32, weight rows 8*(i/4)+4*(l/32)+i%4).
+// Operand lane layout (lane l, g = l/16): an FP8 row segment of 128 bytes is fed
+// as bytes [16g, 16g+16) and [64+16g, 64+16g+16); an E2M1 segment of 64 bytes
+// as bytes [16g, 16g+16); the scale byte of lane l belongs to K-block g (32
+// elements) of row l%16; a bf16 32x32x16 operand gives lane l = 32h + r the
+// K elements [8h, 8h+8) of its 16-element sub-step, row r.
 #include "device.h"
 #include "launch.h"
 
