@@ -161,13 +161,15 @@ struct Tile {
   static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (bf16_mma(F) ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
   static constexpr int kAStepBytes = kARows * kARowBytes;
-  // MFMA-bound FP8 / BF16 tiles stage A with direct-to-LDS loads into three
-  // buffers (the load two stages ahead cannot land in the buffer being read): no
-  // staging registers, which also leaves BF16 room for the swizzled layout.  The
-  // others load A into registers and store it, double-buffered (measured faster
-  // for the weight-bound tiles, whose weight stream then starts before the
-  // activation addresses are known).
-  static constexpr int kABufs = kDma ? 3 : 2;
+  // MFMA-bound FP8 / BF16 tiles stage A with direct-to-LDS loads, two stages
+  // ahead, into four buffers (at least three: the load two stages ahead cannot
+  // land in the buffer being read; four keep the unrolled K loop a divisor of the
+  // usual K-step counts, so that it runs no padding steps): no staging
+  // registers, which also leaves BF16 room for the swizzled layout.  The others
+  // load A into registers and store it, double-buffered (measured faster for the
+  // weight-bound tiles, whose weight stream then starts before the activation
+  // addresses are known).
+  static constexpr int kABufs = kDma ? 4 : 2;
   static constexpr int kABytes = kABufs * KSG * kAStepBytes;
   static constexpr int kOutBytes = BM * kOutStride;
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
@@ -498,6 +500,43 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       float sbv[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) sbv[nt] = sb_lds[sb_row(nt) * TL::kMaxKSteps + kc];
+      if constexpr (!kSkipSlices) {
+        // MFMA-bound tiles: software-pipelined.  The scale update of MFMA i is
+        // issued after MFMA i+1 (two partials in flight), and the activation
+        // fragment of the next token slice is read one slice ahead, so that the
+        // matrix core never waits on the VALU or on LDS within a wave.
+        auto rd8 = [&](int mt) { return (i32x8)__builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7); };
+        auto rd_sa = [&](int mt) { return __builtin_bit_cast(float, sbuf[mt * 16 + r16]); };
+        i32x8 a_cur = rd8(0), a_nxt = rd8(MT > 1 ? 1 : 0);
+        float sa_cur = rd_sa(0), sa_nxt = rd_sa(MT > 1 ? 1 : 0);
+        f32x4 prev = {};
+        float s_prev = 0.f;
+#pragma unroll
+        for (int i = 0; i < MT * NT; ++i) {
+          const int mt = i / NT, nt = i % NT;
+          const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
+          const f32x4 cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a_cur, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                             0, 0, 127, 0, 127);
+          const float s_cur = sa_cur * sbv[nt];
+          if (i > 0) acc[(i - 1) / NT][(i - 1) % NT] += prev * s_prev;
+          if (nt == NT - 1 && mt + 1 < MT) {
+            a_cur = a_nxt;
+            sa_cur = sa_nxt;
+            if (mt + 2 < MT) {
+              a_nxt = rd8(mt + 2);
+              sa_nxt = rd_sa(mt + 2);
+            }
+          }
+          prev = cur;
+          s_prev = s_cur;
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then the previous one's scale update
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the LDS reads of the slice after next
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[MT - 1][NT - 1] += prev * s_prev;
+        return;
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (kSkipSlices && mt * 16 >= rows) break;  // wave-uniform: no token rows left
@@ -597,25 +636,25 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     store_a(an, sn, (su + 1) & 1);
   };
 
-  // FP8 stage: A(st) was loaded into buffer st % 3 two stages ago.  Each wave
+  // Direct-to-LDS stage: A(st) was loaded into buffer st % kABufs two stages ago.  Each wave
   // waits for its own loads of A(st) (the VMEM counter retires in order, and
   // at least 2 kR + kD instructions were issued after them), and its LDS reads; the
-  // barrier then publishes the buffer and frees buffer (st + 2) % 3, last read
-  // in stage st - 1, for A(st + 2).  A plain s_barrier: __syncthreads would wait
+  // barrier then publishes the buffer and frees buffer (st + 2) % kABufs, last
+  // read in stage st - 2, for A(st + 2).  A plain s_barrier: __syncthreads would wait
   // for every outstanding load, weight ring included.
   auto stage_dma = [&](int st, int su) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kR + kD));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    dma_a(st + 2, (su + 2) % 3);
+    dma_a(st + 2, (su + 2) % TL::kABufs);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
       const int ks = st * KSG + u;
       BFrag<F, NT>& slot = bq[(su * KSG + u) % DEPTH];
-      kstep(slot, su % 3, u, ks);
+      kstep(slot, su % TL::kABufs, u, ks);
       if (u + 1 < KSG) __builtin_amdgcn_sched_barrier(0);
       int ks_next = ks + DEPTH;
       if constexpr (bf16_mma(F))
