@@ -254,6 +254,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // (lane l's 16 bytes at 16*l, FP8/BF16 second halves 1 KB further), so one
   // load instruction of a wave reads 1 KB of consecutive bytes.
   const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + (size_t)expert * p.b_expert_bytes, p.b_expert_bytes);
+  // FP8 weight scales of the tile, per thread (kNB rows of at most kMaxKSteps)
+  constexpr int kSbPer = F == Fmt::FP8 ? (TL::kNB * TL::kMaxKSteps + kThreads - 1) / kThreads : 1;
+  float sb_pre[kSbPer];
   __amdgpu_buffer_rsrc_t bsc_rs = b_rs;
   uint32_t b_off[NT], bsc_off[NT];
   {
@@ -286,15 +289,22 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     if (F == Fmt::FP8) {
       // the tile's weight-scale rows, staged in LDS: gate_up [0, kHB) the gate
       // blocks, [kHB, 2 kHB) the up blocks; down: the kNB 128-row blocks from the
-      // tile's first (blocks past the last stand in for dead columns)
+      // tile's first (blocks past the last stand in for dead columns).  Loaded
+      // here, stored to LDS after the prologue's weight and activation loads are
+      // issued, so that their round trip overlaps those loads.
       const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
       const int nblk = p.n_rows / 128;
-      for (int i = tid; i < TL::kNB * p.ksteps; i += kThreads) {
-        const int j = i / p.ksteps, k = i - j * p.ksteps;
-        const int hb = TL::kHB, hblk = p.N / 128;
-        const int blk = GATEUP ? (j < hb ? min(n_tile * hb + j, hblk - 1) : hblk + min(n_tile * hb + j - hb, hblk - 1))
-                               : min(n_tile * BN / 128 + j, nblk - 1);
-        sb_lds[j * TL::kMaxKSteps + k] = sfe[(size_t)blk * p.b_sf_row + k];
+#pragma unroll
+      for (int q = 0; q < kSbPer; ++q) {
+        const int i = tid + q * kThreads;
+        sb_pre[q] = 0.f;
+        if (i < TL::kNB * p.ksteps) {
+          const int j = i / p.ksteps, k = i - j * p.ksteps;
+          const int hb = TL::kHB, hblk = p.N / 128;
+          const int blk = GATEUP ? (j < hb ? min(n_tile * hb + j, hblk - 1) : hblk + min(n_tile * hb + j - hb, hblk - 1))
+                                 : min(n_tile * BN / 128 + j, nblk - 1);
+          sb_pre[q] = sfe[(size_t)blk * p.b_sf_row + k];
+        }
       }
     }
   }
@@ -338,14 +348,45 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   };
 
+  // ---------------------------------------------------------------- A (activation) addressing
+  // A is staged KSG K-steps at a time.  For each K-step of a stage, thread tid
+  // loads 16-byte chunks c = tid + threads*i of the BM x 128-byte tile: row c/8, chunk c%8.
+  // The gathered rows' src_info entries are loaded here, without branches (rows
+  // past the tile's read its last entry and are then masked), before the weight
+  // ring is issued, and used after it: their round trip then overlaps the
+  // weights' instead of preceding it.
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
+  int a_src[TL::kAChunks];
+#pragma unroll
+  for (int i = 0; i < TL::kAChunks; ++i)
+    a_src[i] = GATEUP ? p.src_info[row0 + min((tid + kThreads * i) >> 3, rows - 1)] : 0;
+  const int asf_src = GATEUP && !bf16_mma(F) ? p.src_info[row0 + min(tid, rows - 1)] : 0;
   // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed.
-  // Issued first, before the activation rows' addresses are known.
+  // Issued first, before the activation rows' addresses are known (direct-to-LDS
+  // tiles: the first stage's K-steps here, the rest after the first activation stage).
   const int KS = p.ksteps;
   BFrag<F, NT> bq[DEPTH];
-  if constexpr (!TL::kDma) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_b(bq[d], d);
+  for (int d = 0; d < (TL::kDma ? KSG : DEPTH); ++d) load_b(bq[d], d);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t a_off[TL::kAChunks];
+#pragma unroll
+  for (int i = 0; i < TL::kAChunks; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 3;
+    const uint32_t arow = GATEUP ? (uint32_t)(a_src[i] / p.topk) : (uint32_t)(row0 + r);
+    // direct-to-LDS: slot c of the K-step block holds row r's chunk (c & 7) ^ (r & 7)
+    const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ (r & 7)) : (uint32_t)(c & 7);
+    a_off[i] = r < rows ? arow * p.a_row_bytes + chunk * 16u : kOOB;
   }
+  // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step);
+  // threads past the tile's rows load zeros
+  const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
+  const uint32_t asf_off =
+      (!bf16_mma(F) && tid < rows)
+          ? (GATEUP ? (uint32_t)(asf_src / p.topk) : (uint32_t)(row0 + tid)) * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u)
+          : kOOB;
+
   // down: the pair slot of each tile row, for the epilogue's scatter (loaded early)
   const int pair_of_row = (!GATEUP && tid < rows) ? p.src_info[row0 + tid] : 0;
 
@@ -364,34 +405,6 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // ---------------------------------------------------------------- A (activation) addressing
-  // A is staged KSG K-steps at a time.  For each K-step of a stage, thread tid
-  // loads 16-byte chunks c = tid + threads*i of the BM x 128-byte tile: row c/8, chunk c%8.
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
-  uint32_t a_off[TL::kAChunks];
-#pragma unroll
-  for (int i = 0; i < TL::kAChunks; ++i) {
-    const int c = tid + kThreads * i;
-    const int r = c >> 3;
-    if (r < rows) {
-      const int grow = row0 + r;
-      const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
-      // direct-to-LDS: slot c of the K-step block holds row r's chunk (c & 7) ^ (r & 7)
-      const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ (r & 7)) : (uint32_t)(c & 7);
-      a_off[i] = arow * p.a_row_bytes + chunk * 16u;
-    } else {
-      a_off[i] = kOOB;
-    }
-  }
-  // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step)
-  const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
-  uint32_t asf_off = kOOB;  // threads past the tile's rows load zeros
-  if (!bf16_mma(F) && tid < rows) {
-    const int grow = row0 + tid;
-    const uint32_t arow = GATEUP ? (uint32_t)(p.src_info[grow] / p.topk) : (uint32_t)grow;
-    asf_off = arow * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u);
   }
 
   // Loads past the last K-step read zeros (no branch, so the register rings stay static).
@@ -463,22 +476,36 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
   uint32_t as[TL::kDma ? 1 : 2][KSG] = {};
   if constexpr (TL::kDma) {
-    // A(0), ring K-steps of stage 0, A(1), the rest of the ring: then at least
-    // 2 kR + kD VMEM instructions follow the loads of A(st) when stage st waits
-    // for them (exactly that many from stage 2 on; the surplus at stages 0 and 1
-    // is ring loads those stages need anyway), so one wait count serves every
-    // stage and the loop has no branches
-    static_assert(!TL::kDma || DEPTH >= 2 * KSG, "the direct-to-LDS pipeline keeps two stages of weights in flight");
+    // Ring K-steps of stage 0 (above), A(0), the ring K-steps of stage 1, A(1),
+    // in this order (the scheduling barriers keep it).  When stage st waits for
+    // A(st), the VMEM instructions issued after A(st) are first this stage's
+    // ring loads (kR: the prologue's stage-1 loads, or the refills issued in
+    // stage st - 2, since DEPTH = 2 KSG), then A(st + 1) and the later refills.
+    // Waiting down to kR + kD outstanding therefore lands A(st) and this stage's
+    // weights and nothing later: one wait count for every stage, no branches.
+    static_assert(!TL::kDma || DEPTH == 2 * KSG, "the direct-to-LDS pipeline keeps two stages of weights in flight");
+    __builtin_amdgcn_sched_barrier(0);
     dma_a(0, 0);
-#pragma unroll
-    for (int d = 0; d < KSG; ++d) load_b(bq[d], d);
-    dma_a(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = KSG; d < DEPTH; ++d) load_b(bq[d], d);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
   } else {
     load_a(av[0], as[0], 0);
     load_a(av[1], as[1], 1);
     store_a(av[0], as[0], 0);
+  }
+  if (F == Fmt::FP8) {
+#pragma unroll
+    for (int q = 0; q < kSbPer; ++q) {
+      const int i = tid + q * kThreads;
+      if (i < TL::kNB * p.ksteps) {
+        const int j = i / p.ksteps;
+        sb_lds[j * TL::kMaxKSteps + (i - j * p.ksteps)] = sb_pre[q];
+      }
+    }
   }
 
   // One K-step on the staged A of LDS buffer `buf` (K-step u of the stage) and B(ks) in `bq_`.
@@ -637,14 +664,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   };
 
   // Direct-to-LDS stage: A(st) was loaded into buffer st % kABufs two stages ago.  Each wave
-  // waits for its own loads of A(st) (the VMEM counter retires in order, and
-  // at least 2 kR + kD instructions were issued after them), and its LDS reads; the
-  // barrier then publishes the buffer and frees buffer (st + 2) % kABufs, last
-  // read in stage st - 2, for A(st + 2).  A plain s_barrier: __syncthreads would wait
-  // for every outstanding load, weight ring included.
+  // waits for its own loads of A(st) and of this stage's weights (the VMEM
+  // counter retires in order; see the prologue for the count), and its LDS
+  // accesses; the barrier then publishes the buffer and frees buffer
+  // (st + 2) % kABufs, last read in stage st - 2, for A(st + 2).  A plain
+  // s_barrier: __syncthreads would wait for every outstanding load.
   auto stage_dma = [&](int st, int su) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kR + kD));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kR + kD));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     dma_a(st + 2, (su + 2) % TL::kABufs);
