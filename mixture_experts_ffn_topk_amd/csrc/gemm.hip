@@ -190,10 +190,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   constexpr int BN = TL::BN;
   constexpr int MT32 = BM / 32, NT32 = NT / 2;  // BF16: 32-row token slices and weight tiles
   static_assert(!bf16_mma(F) || BM % 32 == 0, "bf16-operand tiles hold whole 32-token slices");
-  // Weight-bound tiles skip the 16-row token slices past the tile's rows (experts
-  // smaller than the tile).  MFMA-bound tiles are almost always full, and the
-  // branch would split the K-step into blocks the scheduler cannot interleave.
-  constexpr bool kSkipSlices = BM <= 96 || bf16_mma(F);  // (BF16 measured faster with the skip)
+  // bf16-operand tiles skip the 32-row token slices past the tile's rows (experts
+  // smaller than the tile; measured faster).  The FP8 and MX K-steps compute every
+  // slice: a branch would split the software-pipelined K-step into blocks the
+  // scheduler cannot interleave.
+  constexpr bool kSkipSlices = bf16_mma(F);
   constexpr bool kPrio = BM > 96 && !bf16_mma(F);  // (measured: helps MFMA-bound FP8 / MX tiles only)
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
   constexpr int HC = BN / 2;  // gate_up: h columns per tile (gate and up rows, NT/2 tiles each per wave)
@@ -527,56 +528,41 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       float sbv[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) sbv[nt] = sb_lds[sb_row(nt) * TL::kMaxKSteps + kc];
-      if constexpr (!kSkipSlices) {
-        // MFMA-bound tiles: software-pipelined.  The scale update of MFMA i is
-        // issued after MFMA i+1 (two partials in flight), and the activation
-        // fragment of the next token slice is read one slice ahead, so that the
-        // matrix core never waits on the VALU or on LDS within a wave.
-        auto rd8 = [&](int mt) { return (i32x8)__builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7); };
-        auto rd_sa = [&](int mt) { return __builtin_bit_cast(float, sbuf[mt * 16 + r16]); };
-        i32x8 a_cur = rd8(0), a_nxt = rd8(MT > 1 ? 1 : 0);
-        float sa_cur = rd_sa(0), sa_nxt = rd_sa(MT > 1 ? 1 : 0);
-        f32x4 prev = {};
-        float s_prev = 0.f;
+      // Software-pipelined: the scale update of MFMA i is issued after MFMA i+1
+      // (two partials in flight), and the activation fragment of the next token
+      // slice is read one slice ahead, so that the matrix core never waits on the
+      // VALU or on LDS within a wave.  Every token slice is computed (slices past
+      // the tile's rows multiply zeros).
+      auto rd8 = [&](int mt) { return (i32x8)__builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7); };
+      auto rd_sa = [&](int mt) { return __builtin_bit_cast(float, sbuf[mt * 16 + r16]); };
+      i32x8 a_cur = rd8(0), a_nxt = rd8(MT > 1 ? 1 : 0);
+      float sa_cur = rd_sa(0), sa_nxt = rd_sa(MT > 1 ? 1 : 0);
+      f32x4 prev = {};
+      float s_prev = 0.f;
 #pragma unroll
-        for (int i = 0; i < MT * NT; ++i) {
-          const int mt = i / NT, nt = i % NT;
-          const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
-          const f32x4 cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a_cur, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
-                                                                             0, 0, 127, 0, 127);
-          const float s_cur = sa_cur * sbv[nt];
-          if (i > 0) acc[(i - 1) / NT][(i - 1) % NT] += prev * s_prev;
-          if (nt == NT - 1 && mt + 1 < MT) {
-            a_cur = a_nxt;
-            sa_cur = sa_nxt;
-            if (mt + 2 < MT) {
-              a_nxt = rd8(mt + 2);
-              sa_nxt = rd_sa(mt + 2);
-            }
+      for (int i = 0; i < MT * NT; ++i) {
+        const int mt = i / NT, nt = i % NT;
+        const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x4 cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a_cur, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                           0, 0, 127, 0, 127);
+        const float s_cur = sa_cur * sbv[nt];
+        if (i > 0) acc[(i - 1) / NT][(i - 1) % NT] += prev * s_prev;
+        if (nt == NT - 1 && mt + 1 < MT) {
+          a_cur = a_nxt;
+          sa_cur = sa_nxt;
+          if (mt + 2 < MT) {
+            a_nxt = rd8(mt + 2);
+            sa_nxt = rd_sa(mt + 2);
           }
-          prev = cur;
-          s_prev = s_cur;
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then the previous one's scale update
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the LDS reads of the slice after next
-          __builtin_amdgcn_sched_barrier(0);
         }
-        acc[MT - 1][NT - 1] += prev * s_prev;
-        return;
+        prev = cur;
+        s_prev = s_cur;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then the previous one's scale update
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the LDS reads of the slice after next
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (kSkipSlices && mt * 16 >= rows) break;  // wave-uniform: no token rows left
-        const i32x8 a8 = __builtin_shufflevector(rd_lo(mt), rd_hi(mt), 0, 1, 2, 3, 4, 5, 6, 7);
-        const float sa = __builtin_bit_cast(float, sbuf[mt * 16 + r16]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                              0, 127, 0, 127);
-          acc[mt][nt] += part * (sa * sbv[nt]);
-        }
-      }
+      acc[MT - 1][NT - 1] += prev * s_prev;
     } else if constexpr (bf16_mma(F)) {
       // 32x32x16 MFMAs: lane l = 32*h + r holds token mt*32 + r and bytes
       // [32*sub + 16*h, +16) of the K-step segment; weight sub-step fragments
