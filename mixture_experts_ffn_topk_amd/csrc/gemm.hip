@@ -212,9 +212,27 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
 
   // ---------------------------------------------------------------- tile decode
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int n_tile = L / p.m_tiles_max;
-  const int m_tile = L - n_tile * p.m_tiles_max;
+  // The grid is sized for the worst case; the real m-tile count (per-expert tile
+  // counts summed) sends the surplus workgroups home at once, so that the
+  // XCD-aware mapping spreads real tiles only.
+  int total_m = 0;
+  for (int e0 = 0; e0 < p.E; e0 += 64) {
+    const int e = e0 + lane;
+    int t = e < p.E ? (p.start[e + 1] - p.start[e] + BM - 1) / BM : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
+    total_m += t;
+  }
+  total_m = __builtin_amdgcn_readfirstlane(total_m);
+  const int G = total_m * p.n_tiles;
+  if ((int)blockIdx.x >= G) return;
+  const int L = xcd_remap(blockIdx.x, G);
+  // Weight-bound tiles (about one m-tile per expert: no weight reuse between
+  // m-tiles) run expert-major, so that an expert's activation rows stay in the
+  // XCD's L2 across its column tiles.  MFMA-bound tiles run column-tile-major, so
+  // that an XCD's consecutive tiles share weights.
+  const int m_tile = BM <= 96 ? L / p.n_tiles : L % total_m;
+  const int n_tile = BM <= 96 ? L % p.n_tiles : L / total_m;
   int expert = -1, tile_in_e = 0, e_start = 0, e_count = 0;
   {
     int base = 0;
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   }
   expert = __builtin_amdgcn_readfirstlane(expert);
   tile_in_e = __builtin_amdgcn_readfirstlane(tile_in_e);
-  if (expert < 0) return;  // beyond the real tile count (grid is sized for the worst case)
+  if (expert < 0) return;  // (not reached: L < G)
   const int row0 = __builtin_amdgcn_readfirstlane(e_start) + tile_in_e * BM;
   const int rows = min(BM, __builtin_amdgcn_readfirstlane(e_count) - tile_in_e * BM);
 
