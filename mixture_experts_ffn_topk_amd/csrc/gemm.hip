@@ -587,33 +587,62 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // are bq_.lo[2t], lo[2t+1], hi[2t], hi[2t+1] for sub = 0..3 (BF16), or
       // decoded from word sub of bq_.lo[t] with block scale byte sub of bq_.sc[t] (NV4)
       const int r32 = lane & 31, h32 = lane >> 5;
-      i32x4 bop[F == Fmt::NV4 ? NT32 : 1][4];
+      auto rd_a = [&](int mt, int sub) {
+        return *(const i32x4*)(abuf + (mt * 32 + r32) * TL::kARowBytes + 16 * ((2 * sub + h32) ^ (r32 & TL::kSwz)));
+      };
       if constexpr (F == Fmt::NV4) {
+        // Sub-step outer: the weights of sub-step sub + 1 are decoded (VALU) while
+        // the MFMAs of sub-step sub, issued just before, run on the matrix core.
+        // Every token slice but the last is computed unconditionally (slices past
+        // the tile's rows multiply zeros); the last only when it holds rows.
+        float scf[NT32][4];  // the four E4M3 block scales of each tile row, as fp32
 #pragma unroll
         for (int t = 0; t < NT32; ++t) {
-          const int sw = bq_.sc[t];
-          bop[t][0] = nv4_bf16x8((uint32_t)bq_.lo[t][0], __builtin_amdgcn_cvt_f32_fp8(sw, 0));
-          bop[t][1] = nv4_bf16x8((uint32_t)bq_.lo[t][1], __builtin_amdgcn_cvt_f32_fp8(sw, 1));
-          bop[t][2] = nv4_bf16x8((uint32_t)bq_.lo[t][2], __builtin_amdgcn_cvt_f32_fp8(sw, 2));
-          bop[t][3] = nv4_bf16x8((uint32_t)bq_.lo[t][3], __builtin_amdgcn_cvt_f32_fp8(sw, 3));
+          scf[t][0] = __builtin_amdgcn_cvt_f32_fp8(bq_.sc[t], 0);
+          scf[t][1] = __builtin_amdgcn_cvt_f32_fp8(bq_.sc[t], 1);
+          scf[t][2] = __builtin_amdgcn_cvt_f32_fp8(bq_.sc[t], 2);
+          scf[t][3] = __builtin_amdgcn_cvt_f32_fp8(bq_.sc[t], 3);
         }
-      }
+        auto dec = [&](int t, int sub) { return nv4_bf16x8((uint32_t)bq_.lo[t][sub], scf[t][sub]); };
+        const bool last_live = (MT32 - 1) * 32 < rows;
+        i32x4 cur[NT32];
 #pragma unroll
-      for (int mt = 0; mt < MT32; ++mt) {
-        if (kSkipSlices && mt * 32 >= rows) break;  // wave-uniform: no token rows left
-        const uint8_t* arow = abuf + (mt * 32 + r32) * TL::kARowBytes;
+        for (int t = 0; t < NT32; ++t) cur[t] = dec(t, 0);
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
-          const i32x4 a = *(const i32x4*)(arow + 16 * ((2 * sub + h32) ^ (r32 & TL::kSwz)));
+          i32x4 nxt[NT32];
+          if (sub < 3) {
 #pragma unroll
-          for (int t = 0; t < NT32; ++t) {
-            i32x4 b;
-            if constexpr (F == Fmt::NV4)
-              b = bop[t][sub];
-            else
-              b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
-            acc32[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
-                                                                   __builtin_bit_cast(bf16x8, a), acc32[mt][t], 0, 0, 0);
+            for (int t = 0; t < NT32; ++t) nxt[t] = dec(t, sub + 1);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT32; ++mt) {
+            if (mt == MT32 - 1 && !last_live) break;  // wave-uniform
+            const i32x4 a = rd_a(mt, sub);
+#pragma unroll
+            for (int t = 0; t < NT32; ++t)
+              acc32[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[t]),
+                                                                     __builtin_bit_cast(bf16x8, a), acc32[mt][t], 0, 0, 0);
+          }
+          if (sub < 3) {
+#pragma unroll
+            for (int t = 0; t < NT32; ++t) cur[t] = nxt[t];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT32; ++mt) {
+          if (kSkipSlices && mt * 32 >= rows) break;  // wave-uniform: no token rows left
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) {
+            const i32x4 a = rd_a(mt, sub);
+#pragma unroll
+            for (int t = 0; t < NT32; ++t) {
+              const i32x4 b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
+              acc32[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
+                                                                     __builtin_bit_cast(bf16x8, a), acc32[mt][t], 0, 0, 0);
+            }
           }
         }
       }
