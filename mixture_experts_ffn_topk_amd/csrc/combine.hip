@@ -20,15 +20,30 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   if (col >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const long long p0 = (long long)t * topk;
-  for (int j = 0; j < topk; ++j) {
-    if (pair_row[p0 + j] < 0) continue;  // masked slot
-    const float wj = w[p0 + j];
-    const i32x4 v = *(const i32x4*)(y + (p0 + j) * H + col);
+  // Slots in groups of 8 with every row load issued before the first is used (a
+  // masked slot's row, never written, is read but not added).  The rows are read
+  // once: non-temporal loads.
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    i32x4 v[8];
+    bool ok[8];
+    float wj[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t u = (uint32_t)v[q];
-      acc[2 * q] = fmaf(wj, bf16_to_f32((uint16_t)(u & 0xFFFFu)), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(wj, bf16_to_f32((uint16_t)(u >> 16)), acc[2 * q + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      ok[u] = j < topk && pair_row[p0 + j] >= 0;
+      wj[u] = ok[u] ? w[p0 + j] : 0.f;
+      const long long row = p0 + (j < topk ? j : 0);
+      v[u] = __builtin_bit_cast(i32x4, __builtin_nontemporal_load((const i32x4*)(y + row * H + col)));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t e = (uint32_t)v[u][q];
+        acc[2 * q] = fmaf(wj[u], bf16_to_f32((uint16_t)(e & 0xFFFFu)), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wj[u], bf16_to_f32((uint16_t)(e >> 16)), acc[2 * q + 1]);
+      }
     }
   }
   i32x4 o;
