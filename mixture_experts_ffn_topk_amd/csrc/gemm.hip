@@ -644,6 +644,27 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      } else if constexpr (BM > 96) {
+        // MFMA-bound BF16: (sub-step, token slice) pairs, sub-step outer, so that
+        // consecutive MFMAs update different accumulators; every slice computed
+        // (no branch), each activation fragment read from LDS one pair ahead.
+        constexpr int NP = 4 * MT32;
+        i32x4 a_cur = rd_a(0, 0), a_nxt = rd_a(NP > 1 ? 1 % MT32 : 0, NP > 1 ? 1 / MT32 : 0);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int sub = i / MT32, mt = i % MT32;
+#pragma unroll
+          for (int t = 0; t < NT32; ++t) {
+            const i32x4 b = sub < 2 ? bq_.lo[2 * t + sub] : bq_.hi[2 * t + sub - 2];
+            acc32[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
+                                                                   __builtin_bit_cast(bf16x8, a_cur), acc32[mt][t], 0, 0, 0);
+          }
+          a_cur = a_nxt;
+          if (i + 2 < NP) a_nxt = rd_a((i + 2) % MT32, (i + 2) / MT32);
+          __builtin_amdgcn_sched_group_barrier(0x008, NT32, 0);  // this pair's MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // then the read two pairs ahead
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT32; ++mt) {
