@@ -196,10 +196,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   constexpr int BN = TL::BN;
   constexpr int MT32 = BM / 32, NT32 = NT / 2;  // BF16: 32-row token slices and weight tiles
   static_assert(!bf16_mma(F) || BM % 32 == 0, "bf16-operand tiles hold whole 32-token slices");
-  // bf16-operand tiles skip the 32-row token slices past the tile's rows (experts
-  // smaller than the tile; measured faster).  The FP8 and MX K-steps compute every
-  // slice: a branch would split the software-pipelined K-step into blocks the
-  // scheduler cannot interleave.
+  // Weight-bound BF16 tiles skip the 32-row token slices past the tile's rows
+  // (experts smaller than the tile; measured faster).  The other K-steps compute
+  // every slice (NVFP4: all but the last): a branch would split the
+  // software-pipelined K-step into blocks the scheduler cannot interleave.
   constexpr bool kSkipSlices = bf16_mma(F);
   constexpr bool kPrio = BM > 96 && !bf16_mma(F);  // (measured: helps MFMA-bound FP8 / MX tiles only)
   static_assert(!GATEUP || NT % 2 == 0, "gate_up pairs a gate tile with an up tile");
@@ -762,8 +762,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Unrolled so that both rings (DEPTH weight buffers, 2 activation stages)
-  // index statically: U K-steps = SU stages per trip.  The trip count is rounded
+  // Unrolled so that both rings (DEPTH weight buffers, kABufs activation
+  // buffers) index statically: U K-steps = SU stages per trip.  The trip count is rounded
   // up to the unroll: the extra steps load zeros and add zeros, and the loop has
   // no early exit (an exit per step would make the compiler drain every
   // outstanding load there).
