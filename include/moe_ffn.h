@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 3
+#define MOE_FFN_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -197,6 +197,17 @@ moe_status moe_plan(const moe_handle* h, int32_t num_tokens, const void* topk_id
                     const moe_plan_buffers* plan /* host struct */, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* moe_plan with bias-aware FROM_LOGITS routing ([ActPack] routing_bias of the
+   bias-aware routing methods).  routing_bias [E] fp32 (device; NULL = none)
+   ranks the experts by routing_logits[t,e] + routing_bias[e] (fp32 sum; ties ->
+   lower expert id); the weights stay a softmax over the k selected experts'
+   unbiased logits.  A non-NULL routing_bias in PRECOMPUTED mode is
+   MOE_ERR_INVALID_ARGUMENT.  moe_plan(...) is moe_plan_ex(..., NULL, ...). */
+moe_status moe_plan_ex(const moe_handle* h, int32_t num_tokens, const void* topk_idx_in,
+                       const float* routing_logits, const float* routing_bias, void* topk_idx_out,
+                       float* topk_weights_out, const moe_plan_buffers* plan /* host struct */, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
 /* Expert FFN over the plan's rows ([MegaFFN]: gate/up GEMM -> clamped SwiGLU ->
    intermediate requantisation -> down GEMM).  x, x_sf per the format; y [T,k,H]
    bf16 receives each row's result at its pair slot p = src_info[row]; slots of
@@ -226,6 +237,20 @@ moe_status moe_ffn_down(const moe_handle* h, int32_t num_tokens, const void* h_i
 moe_status moe_combine(const moe_handle* h, int32_t num_tokens, const void* y, const float* topk_weights,
                        const moe_plan_buffers* plan /* host struct */, void* out, hipStream_t stream);
 
+/* moe_combine with fused addends (MAX mega_ffn / EP pages: fused_shared_expert,
+   "a shared expert is fused into the combine kernel", and has_epilogue_fusion,
+   "the combine output is fused with a downstream elementwise epilogue"):
+     out[t] = bf16( sum over valid slots j of topk_weights[t,j] * y[t,j,:]
+                    + shared[t,:] + residual[t,:] ),
+   accumulated in fp32 in that order.  shared and residual are bf16 [T,H]
+   (device, 16-byte aligned; NULL = absent).  A shared expert's output comes from
+   moe_ffn of a handle with num_experts = 1, num_topk = 1 and every token routed
+   to expert 0: its y [T,1,H] is [T,H] in token order.  moe_combine(...) is
+   moe_combine_ex(..., NULL, NULL, ...). */
+moe_status moe_combine_ex(const moe_handle* h, int32_t num_tokens, const void* y, const float* topk_weights,
+                          const moe_plan_buffers* plan /* host struct */, const void* shared, const void* residual,
+                          void* out, hipStream_t stream);
+
 /* The whole path in one call: plan (into ws), FFN (y in ws), combine into out
    [T,H] bf16.  PRECOMPUTED: topk_idx / topk_weights are inputs and are not
    modified.  FROM_LOGITS: routing_logits is the input and topk_idx / topk_weights
@@ -234,6 +259,13 @@ moe_status moe_forward(const moe_handle* h, int32_t num_tokens, const void* x, c
                        void* topk_idx, float* topk_weights, const float* routing_logits,
                        const moe_weights* w /* host struct */, void* out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* moe_forward with the routing bias of moe_plan_ex and the combine addends of
+   moe_combine_ex (each NULL = absent). */
+moe_status moe_forward_ex(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
+                          void* topk_idx, float* topk_weights, const float* routing_logits,
+                          const float* routing_bias, const moe_weights* w /* host struct */, const void* shared,
+                          const void* residual, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 const char* moe_status_string(moe_status s);
 int32_t moe_abi_version(void);

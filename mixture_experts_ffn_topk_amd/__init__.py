@@ -59,7 +59,7 @@ class _PreparedSizes(ctypes.Structure):
 PLAN_FIELDS = [f for f, _ in _Plan._fields_]
 EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
-            "moe_status_string", "moe_abi_version"]
+            "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_status_string", "moe_abi_version"]
 
 _lib = None
 
@@ -95,6 +95,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_combine.restype = i32
     lib.moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, sz, vp]
     lib.moe_forward.restype = i32
+    lib.moe_plan_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Plan), vp, sz, vp]
+    lib.moe_plan_ex.restype = i32
+    lib.moe_combine_ex.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp, vp]
+    lib.moe_combine_ex.restype = i32
+    lib.moe_forward_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, vp, vp, sz, vp]
+    lib.moe_forward_ex.restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_abi_version.argtypes = []
@@ -209,11 +215,16 @@ class MoEFFN:
 
     # ---------------------------------------------------------------- entry points
     def plan(self, num_tokens, plan: dict, topk_idx=None, routing_logits=None, topk_idx_out=None,
-             topk_weights_out=None, ws=None, stream=None):
+             topk_weights_out=None, ws=None, stream=None, routing_bias=None):
         ps = self._plan_struct(plan)
-        _check(self.lib.moe_plan(self._h, num_tokens, _ptr(topk_idx), _ptr(routing_logits), _ptr(topk_idx_out),
-                                 _ptr(topk_weights_out), ctypes.byref(ps), _ptr(ws), self._nbytes(ws),
-                                 _stream(stream)), "moe_plan")
+        if routing_bias is None:
+            _check(self.lib.moe_plan(self._h, num_tokens, _ptr(topk_idx), _ptr(routing_logits), _ptr(topk_idx_out),
+                                     _ptr(topk_weights_out), ctypes.byref(ps), _ptr(ws), self._nbytes(ws),
+                                     _stream(stream)), "moe_plan")
+        else:
+            _check(self.lib.moe_plan_ex(self._h, num_tokens, _ptr(topk_idx), _ptr(routing_logits), _ptr(routing_bias),
+                                        _ptr(topk_idx_out), _ptr(topk_weights_out), ctypes.byref(ps), _ptr(ws),
+                                        self._nbytes(ws), _stream(stream)), "moe_plan_ex")
 
     def ffn(self, num_tokens, x, x_sf, weights: dict, plan: dict, y, ws, stream=None):
         ws_ = self._weights_struct(weights)
@@ -244,17 +255,27 @@ class MoEFFN:
         _check(self.lib.moe_ffn_down(self._h, num_tokens, _ptr(h), _ptr(h_sf), ctypes.byref(ws_), ctypes.byref(ps),
                                      _ptr(y), _stream(stream)), "moe_ffn_down")
 
-    def combine(self, num_tokens, y, topk_weights, plan: dict, out, stream=None):
+    def combine(self, num_tokens, y, topk_weights, plan: dict, out, stream=None, shared=None, residual=None):
         ps = self._plan_struct(plan)
-        _check(self.lib.moe_combine(self._h, num_tokens, _ptr(y), _ptr(topk_weights), ctypes.byref(ps), _ptr(out),
-                                    _stream(stream)), "moe_combine")
+        if shared is None and residual is None:
+            _check(self.lib.moe_combine(self._h, num_tokens, _ptr(y), _ptr(topk_weights), ctypes.byref(ps), _ptr(out),
+                                        _stream(stream)), "moe_combine")
+        else:
+            _check(self.lib.moe_combine_ex(self._h, num_tokens, _ptr(y), _ptr(topk_weights), ctypes.byref(ps),
+                                           _ptr(shared), _ptr(residual), _ptr(out), _stream(stream)), "moe_combine_ex")
 
     def forward(self, num_tokens, x, x_sf, topk_idx, topk_weights, routing_logits, weights: dict, out, ws,
-                stream=None):
+                stream=None, routing_bias=None, shared=None, residual=None):
         ws_ = self._weights_struct(weights)
-        _check(self.lib.moe_forward(self._h, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
-                                    _ptr(routing_logits), ctypes.byref(ws_), _ptr(out), _ptr(ws), self._nbytes(ws),
-                                    _stream(stream)), "moe_forward")
+        if routing_bias is None and shared is None and residual is None:
+            _check(self.lib.moe_forward(self._h, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
+                                        _ptr(routing_logits), ctypes.byref(ws_), _ptr(out), _ptr(ws),
+                                        self._nbytes(ws), _stream(stream)), "moe_forward")
+        else:
+            _check(self.lib.moe_forward_ex(self._h, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx),
+                                           _ptr(topk_weights), _ptr(routing_logits), _ptr(routing_bias),
+                                           ctypes.byref(ws_), _ptr(shared), _ptr(residual), _ptr(out), _ptr(ws),
+                                           self._nbytes(ws), _stream(stream)), "moe_forward_ex")
 
 
 __all__ = ["MoEFFN", "MoEError", "load_library", "LIB_PATH", "EXPORTED", "FORMATS", "ROUTE_MODES", "TILE_REGIMES"]

@@ -85,13 +85,13 @@ int choose_bm(const moe_config& c, int T) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const float* logits, void* idx_out,
-                   float* w_out, const moe_plan_buffers* plan, void* scratch, hipStream_t s) {
+moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const float* logits, const float* bias,
+                   void* idx_out, float* w_out, const moe_plan_buffers* plan, void* scratch, hipStream_t s) {
   const moe_config& c = h->cfg;
   const bool idx64 = c.topk_idx_bits == 64;
   const void* ids = idx_in;
   if (c.route_mode == MOE_ROUTE_FROM_LOGITS) {
-    hipError_t e = moe::launch_route_logits_topk(logits, T, c.num_experts, c.num_topk, idx_out, idx64, w_out,
+    hipError_t e = moe::launch_route_logits_topk(logits, bias, T, c.num_experts, c.num_topk, idx_out, idx64, w_out,
                                                  c.fast_math != 0, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     ids = idx_out;
@@ -252,19 +252,26 @@ size_t moe_workspace_size(const moe_handle* h, int32_t T) {
   return layout_for(h->cfg, T).total;
 }
 
-moe_status moe_plan(const moe_handle* h, int32_t T, const void* topk_idx_in, const float* routing_logits,
-                    void* topk_idx_out, float* topk_weights_out, const moe_plan_buffers* plan, void* ws,
-                    size_t ws_bytes, hipStream_t stream) {
+moe_status moe_plan_ex(const moe_handle* h, int32_t T, const void* topk_idx_in, const float* routing_logits,
+                       const float* routing_bias, void* topk_idx_out, float* topk_weights_out,
+                       const moe_plan_buffers* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_T(h, T) || !plan_complete(plan)) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = h->cfg;
   if (c.route_mode == MOE_ROUTE_PRECOMPUTED) {
-    if (T > 0 && !topk_idx_in) return MOE_ERR_INVALID_ARGUMENT;
+    if ((T > 0 && !topk_idx_in) || routing_bias) return MOE_ERR_INVALID_ARGUMENT;
   } else if (T > 0 && (!routing_logits || !topk_idx_out || !topk_weights_out)) {
     return MOE_ERR_INVALID_ARGUMENT;
   }
   const size_t need = layout_for(c, T).plan_scratch_bytes;
   if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  return do_plan(h, T, topk_idx_in, routing_logits, topk_idx_out, topk_weights_out, plan, ws, stream);
+  return do_plan(h, T, topk_idx_in, routing_logits, routing_bias, topk_idx_out, topk_weights_out, plan, ws, stream);
+}
+
+moe_status moe_plan(const moe_handle* h, int32_t T, const void* topk_idx_in, const float* routing_logits,
+                    void* topk_idx_out, float* topk_weights_out, const moe_plan_buffers* plan, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  return moe_plan_ex(h, T, topk_idx_in, routing_logits, nullptr, topk_idx_out, topk_weights_out, plan, ws, ws_bytes,
+                     stream);
 }
 
 moe_status moe_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
@@ -295,35 +302,56 @@ moe_status moe_ffn_down(const moe_handle* h, int32_t T, const void* h_in, const 
   return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2);
 }
 
-moe_status moe_combine(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
-                       const moe_plan_buffers* plan, void* out, hipStream_t stream) {
+moe_status moe_combine_ex(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
+                          const moe_plan_buffers* plan, const void* shared, const void* residual, void* out,
+                          hipStream_t stream) {
   if (!valid_T(h, T) || !plan || !plan->pair_row) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!y || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(moe::launch_combine(y, topk_weights, plan->pair_row, T, h->cfg.num_topk, h->cfg.hidden, out,
-                                        stream));
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (!aligned(shared) || !aligned(residual)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_combine(y, topk_weights, plan->pair_row, T, h->cfg.num_topk, h->cfg.hidden, shared,
+                                        residual, out, stream));
 }
 
-moe_status moe_forward(const moe_handle* h, int32_t T, const void* x, const void* x_sf, void* topk_idx,
-                       float* topk_weights, const float* routing_logits, const moe_weights* w, void* out, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+moe_status moe_combine(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
+                       const moe_plan_buffers* plan, void* out, hipStream_t stream) {
+  return moe_combine_ex(h, T, y, topk_weights, plan, nullptr, nullptr, out, stream);
+}
+
+moe_status moe_forward_ex(const moe_handle* h, int32_t T, const void* x, const void* x_sf, void* topk_idx,
+                          float* topk_weights, const float* routing_logits, const float* routing_bias,
+                          const moe_weights* w, const void* shared, const void* residual, void* out, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   if (!valid_T(h, T) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = h->cfg;
   if (T > 0) {
     if (!x_ok(c, x, x_sf) || !out || !topk_idx || !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
     if (c.route_mode == MOE_ROUTE_FROM_LOGITS && !routing_logits) return MOE_ERR_INVALID_ARGUMENT;
   }
+  if (c.route_mode == MOE_ROUTE_PRECOMPUTED && routing_bias) return MOE_ERR_INVALID_ARGUMENT;
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (!aligned(shared) || !aligned(residual)) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout_for(c, T);
   if (ws_bytes < L.total || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
   char* base = (char*)ws;
   moe_plan_buffers plan{(int32_t*)(base + L.counts), (int32_t*)(base + L.start), (int32_t*)(base + L.ids),
                         (int32_t*)(base + L.nact),   (int32_t*)(base + L.src),   (int32_t*)(base + L.prow),
                         (int32_t*)(base + L.status)};
-  moe_status st = do_plan(h, T, topk_idx, routing_logits, topk_idx, topk_weights, &plan, base + L.scratch, stream);
+  moe_status st =
+      do_plan(h, T, topk_idx, routing_logits, routing_bias, topk_idx, topk_weights, &plan, base + L.scratch, stream);
   if (st != MOE_OK || T == 0) return st;
   void* y = base + L.y;
   st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, out, stream));
+  return hip_status(
+      moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, shared, residual, out, stream));
+}
+
+moe_status moe_forward(const moe_handle* h, int32_t T, const void* x, const void* x_sf, void* topk_idx,
+                       float* topk_weights, const float* routing_logits, const moe_weights* w, void* out, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  return moe_forward_ex(h, T, x, x_sf, topk_idx, topk_weights, routing_logits, nullptr, w, nullptr, nullptr, out, ws,
+                        ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,6 +1,9 @@
 // Router-weighted combine: out[t, :] = sum over valid slots j (ascending) of
 // w[t, j] * y[t, j, :] (DistributedEPCombine page: router_weights scale each
-// expert's contribution; the per-pair rows y are the expert outputs).
+// expert's contribution; the per-pair rows y are the expert outputs), then,
+// when given, + shared[t, :] (a shared expert's output fused into the combine:
+// the fused_shared_expert option of the MAX mega_ffn / EP pages) and
+// + residual[t, :] (a downstream elementwise epilogue: has_epilogue_fusion).
 // HBM-bound gather-reduce: each thread owns 8 consecutive bf16 columns and reads
 // the k slot rows with 16-byte loads; fp32 accumulation; bf16 store.
 #include "device.h"
@@ -14,6 +17,8 @@ constexpr int kCombineCols = kCombineThreads * 8;  // columns per workgroup
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                                   const float* __restrict__ w,
                                                                   const int* __restrict__ pair_row, int topk, int H,
+                                                                  const uint16_t* __restrict__ shared,
+                                                                  const uint16_t* __restrict__ residual,
                                                                   uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
   const int col = blockIdx.y * kCombineCols + threadIdx.x * 8;
@@ -46,6 +51,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
       }
     }
   }
+  // the addends, in this order, after the slots
+  const uint16_t* add[2] = {shared, residual};
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if (add[a] == nullptr) continue;  // uniform
+    const i32x4 v = *(const i32x4*)(add[a] + (long long)t * H + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t e = (uint32_t)v[q];
+      acc[2 * q] += bf16_to_f32((uint16_t)(e & 0xFFFFu));
+      acc[2 * q + 1] += bf16_to_f32((uint16_t)(e >> 16));
+    }
+  }
   i32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -53,12 +71,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   *(i32x4*)(out + (long long)t * H + col) = o;
 }
 
-hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H, void* out,
-                          hipStream_t s) {
+hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H,
+                          const void* shared, const void* residual, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid(T, (H + kCombineCols - 1) / kCombineCols);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row, topk, H,
-                     (uint16_t*)out);
+                     (const uint16_t*)shared, (const uint16_t*)residual, (uint16_t*)out);
   return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@ int plan_num_blocks(int npairs);
 size_t plan_workspace_bytes(int npairs, int E);
 hipError_t launch_plan(const void* ids, bool idx64, int npairs, int E, const PlanPtrs& out, int* ws,
                        hipStream_t s);
-hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, void* idx_out, bool idx64,
-                                    float* w_out, bool fast, hipStream_t s);
+// bias: per-expert selection bias [E] or nullptr
+hipError_t launch_route_logits_topk(const float* logits, const float* bias, int T, int E, int k, void* idx_out,
+                                    bool idx64, float* w_out, bool fast, hipStream_t s);
 
 // Prepared weight layout: tiles of 16 rows x one K-step in MFMA lane order.
 size_t prepared_tile_bytes(Fmt f);                           // 2048 (FP8), 4096 (BF16), 1024 (MX, NV4)
@@ -68,7 +69,8 @@ int ffn_max_m_tiles(int npairs, int E, int bm);
 // stage: 0 = both legs, 1 = gate_up only, 2 = down only
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage = 0);
 
-hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H, void* out,
-                          hipStream_t s);
+// shared, residual: bf16 [T,H] addends or nullptr
+hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H,
+                          const void* shared, const void* residual, void* out, hipStream_t s);
 
 }  // namespace moe

@@ -22,43 +22,50 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 
 // ------------------------------------------------------------------ top-k
 // One wavefront per token.  Each lane holds logits e = lane + 64*i (i < 8),
-// k rounds of wave-wide argmax with key (logit desc, index asc), then a
-// softmax over the k selected logits.
+// k rounds of wave-wide argmax with key (logit + bias desc, index asc), then a
+// softmax over the k selected logits.  The optional per-expert bias (the
+// routing_bias of bias-aware methods on the MoEActivationPack page) only ranks
+// the experts: the weights come from the logits themselves.
 template <typename IdxT, bool FAST>
-__global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                                int k, IdxT* __restrict__ idx_out,
+__global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __restrict__ logits,
+                                                                const float* __restrict__ bias, int T, int E, int k,
+                                                                IdxT* __restrict__ idx_out,
                                                                 float* __restrict__ w_out) {
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float v[8];
+  float v[8], key[8];
   const float* row = logits + (size_t)t * E;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int e = lane + 64 * i;
     float x = e < E ? row[e] : -INFINITY;
     v[i] = (x != x) ? -INFINITY : x;  // NaN ranks as -inf
+    const float kb = (bias != nullptr && e < E) ? v[i] + bias[e] : v[i];
+    key[i] = (kb != kb) ? -INFINITY : kb;
   }
   unsigned taken = 0;
   float my_v = -INFINITY;
   int my_i = 0;
   for (int s = 0; s < k; ++s) {
-    float bv = -INFINITY;
+    float bk = -INFINITY, bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int e = lane + 64 * i;
       bool ok = e < E && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) {
+      if (ok && (key[i] > bk || (key[i] == bk && e < bi))) {
+        bk = key[i];
         bv = v[i];
         bi = e;
       }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-      float ov = __shfl_xor(bv, m);
+      float ok_ = __shfl_xor(bk, m), ov = __shfl_xor(bv, m);
       int oi = __shfl_xor(bi, m);
-      if (ov > bv || (ov == bv && oi < bi)) {
+      if (ok_ > bk || (ok_ == bk && oi < bi)) {
+        bk = ok_;
         bv = ov;
         bi = oi;
       }
@@ -69,7 +76,10 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __r
       my_i = bi;
     }
   }
-  const float vmax = __shfl(my_v, 0);  // the first selected logit is the largest
+  // the largest selected logit (the first one when there is no bias)
+  float vmax = lane < k ? my_v : -INFINITY;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, m));
   float ex = 0.0f;
   if (lane < k) ex = FAST ? __builtin_amdgcn_exp2f((my_v - vmax) * 1.4426950408889634f) : expf(my_v - vmax);
   float sum = ex;
@@ -288,23 +298,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(const IdxT* 
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t launch_route_logits_topk(const float* logits, int T, int E, int k, void* idx_out, bool idx64,
-                                    float* w_out, bool fast, hipStream_t s) {
+hipError_t launch_route_logits_topk(const float* logits, const float* bias, int T, int E, int k, void* idx_out,
+                                    bool idx64, float* w_out, bool fast, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + 3) / 4), block(256);
   if (idx64) {
     if (fast)
-      hipLaunchKernelGGL((route_logits_topk_kernel<long long, true>), grid, block, 0, s, logits, T, E, k,
+      hipLaunchKernelGGL((route_logits_topk_kernel<long long, true>), grid, block, 0, s, logits, bias, T, E, k,
                          (long long*)idx_out, w_out);
     else
-      hipLaunchKernelGGL((route_logits_topk_kernel<long long, false>), grid, block, 0, s, logits, T, E, k,
+      hipLaunchKernelGGL((route_logits_topk_kernel<long long, false>), grid, block, 0, s, logits, bias, T, E, k,
                          (long long*)idx_out, w_out);
   } else {
     if (fast)
-      hipLaunchKernelGGL((route_logits_topk_kernel<int, true>), grid, block, 0, s, logits, T, E, k,
+      hipLaunchKernelGGL((route_logits_topk_kernel<int, true>), grid, block, 0, s, logits, bias, T, E, k,
                          (int*)idx_out, w_out);
     else
-      hipLaunchKernelGGL((route_logits_topk_kernel<int, false>), grid, block, 0, s, logits, T, E, k,
+      hipLaunchKernelGGL((route_logits_topk_kernel<int, false>), grid, block, 0, s, logits, bias, T, E, k,
                          (int*)idx_out, w_out);
   }
   return hipGetLastError();

@@ -8,7 +8,8 @@ It computes, one expert at a time, in float64:
 
 1. exact dequantisation of the block-scaled operands  (``dequant_*``)
 2. routing: the caller's precomputed top-k, or top-k from router logits
-   followed by a softmax over the selected k                (``route_from_logits``)
+   (optionally ranked with a per-expert routing bias) followed by a softmax
+   over the selected k                                      (``route_from_logits``)
 3. the routing plan: per-expert counts, prefix-sum start offsets, the active
    expert list, and the stable (token, slot) -> row permutation  (``build_plan``)
 4. the gate/up projection of each expert's rows             (``expert_rows``)
@@ -16,7 +17,8 @@ It computes, one expert at a time, in float64:
 6. the intermediate requantisation, by the same stated rule as the GPU path
                                                              (``requant_*``)
 7. the down projection
-8. the router-weighted combine back into token order        (``combine``)
+8. the router-weighted combine back into token order, plus optional
+   addends (a shared expert's output, a residual)            (``combine``)
 
 Sources, by page (the pages are API documentation; none prints formulas or
 values, so each step states which reading it takes):
@@ -143,11 +145,22 @@ def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int, w13_gs=None, w
 
 
 # ------------------------------------------------------------------ routing
-def route_from_logits(logits: np.ndarray, k: int):
+def _selection_keys(lg: np.ndarray, bias) -> np.ndarray:
+    """Ranking keys of FromLogits routing: the logits, plus the per-expert
+    routing_bias of bias-aware methods when given (an fp32 sum, as the kernel
+    forms it); NaN ranks lowest."""
+    key = lg if bias is None else (lg + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    return np.where(np.isnan(key), np.float32(-np.inf), key)
+
+
+def route_from_logits(logits: np.ndarray, k: int, bias=None):
     """FromLogits routing (MoEActivationPack page, routing_input_mode): per token
     the k experts with the largest logit, ties to the lower expert index, in that
-    order; weights are a softmax over the k selected logits (float64)."""
+    order; weights are a softmax over the k selected logits (float64).  With a
+    routing_bias (bias-aware methods on the same page) the experts are ranked by
+    logit + bias, and the weights still come from the unbiased logits."""
     lg = np.asarray(logits, dtype=np.float32)
+    key = _selection_keys(lg, bias)
     T, E = lg.shape
     idx = np.empty((T, k), dtype=np.int64)
     w = np.empty((T, k), dtype=np.float64)
@@ -158,7 +171,7 @@ def route_from_logits(logits: np.ndarray, k: int):
             for e in range(E):
                 if e in chosen:
                     continue
-                if best < 0 or lg[t, e] > lg[t, best]:
+                if best < 0 or key[t, e] > key[t, best]:
                     best = e
             chosen.append(best)
         sel = lg[t, chosen].astype(np.float64)
@@ -168,10 +181,10 @@ def route_from_logits(logits: np.ndarray, k: int):
     return idx, w
 
 
-def route_from_logits_fast(logits: np.ndarray, k: int):
+def route_from_logits_fast(logits: np.ndarray, k: int, bias=None):
     """Same selection as ``route_from_logits`` through a stable sort (for large T)."""
     lg = np.asarray(logits, dtype=np.float32)
-    order = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    order = np.argsort(-_selection_keys(lg, bias), axis=1, kind="stable")[:, :k]
     sel = np.take_along_axis(lg, order, axis=1).astype(np.float64)
     ex = np.exp(sel - sel.max(axis=1, keepdims=True))
     return order.astype(np.int64), ex / ex.sum(axis=1, keepdims=True)
@@ -299,9 +312,13 @@ def expert_rows(geo: Geometry, xd_rows: np.ndarray, w13d: np.ndarray, w2d: np.nd
     return hd @ w2d.T
 
 
-def combine(y_rows: np.ndarray, topk_weights: np.ndarray, pair_row: np.ndarray, hidden: int) -> np.ndarray:
+def combine(y_rows: np.ndarray, topk_weights: np.ndarray, pair_row: np.ndarray, hidden: int,
+            addends=()) -> np.ndarray:
     """Router-weighted combine (DistributedEPCombine page, ``router_weights``):
-    out[t] = sum over valid slots j, ascending, of w[t, j] * y[row of (t, j)]."""
+    out[t] = sum over valid slots j, ascending, of w[t, j] * y[row of (t, j)],
+    then + each [T, H] addend (a shared expert's output fused into the combine,
+    fused_shared_expert; a downstream elementwise epilogue such as a residual,
+    has_epilogue_fusion: MAX mega_ffn / EP pages)."""
     w = np.asarray(topk_weights, dtype=np.float64)
     T, k = w.shape
     out = np.zeros((T, hidden), dtype=np.float64)
@@ -310,16 +327,20 @@ def combine(y_rows: np.ndarray, topk_weights: np.ndarray, pair_row: np.ndarray, 
             r = pair_row[t * k + j]
             if r >= 0:
                 out[t] += w[t, j] * y_rows[r]
+    for a in addends:
+        if a is not None:
+            out += np.asarray(a, dtype=np.float64).reshape(T, hidden)
     return out
 
 
 # ------------------------------------------------------------------ forward
 def forward(geo: Geometry, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx=None, topk_weights=None,
-            logits=None, w13_gs=None, w2_gs=None) -> dict:
+            logits=None, w13_gs=None, w2_gs=None, routing_bias=None, shared=None, residual=None) -> dict:
     """Whole path over all tokens.  Routing is taken from ``topk_idx``/``topk_weights``
-    when given, else computed from ``logits``."""
+    when given, else computed from ``logits`` (and ``routing_bias``).  ``shared`` and
+    ``residual`` ([T, H]) are added after the routed experts' weighted sum."""
     if topk_idx is None:
-        topk_idx, topk_weights = route_from_logits_fast(logits, geo.topk)
+        topk_idx, topk_weights = route_from_logits_fast(logits, geo.topk, routing_bias)
     plan = build_plan(topk_idx, geo.experts)
     xd = dequant_activations(geo, x, x_sf)
     start, src = plan["expert_start_indices"], plan["src_info"]
@@ -330,7 +351,7 @@ def forward(geo: Geometry, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx=None, topk_
             continue
         w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e, w13_gs, w2_gs)
         y[r0:r1] = expert_rows(geo, xd[src[r0:r1] // geo.topk], w13d, w2d)
-    out = combine(y, topk_weights, plan["pair_row"], geo.hidden)
+    out = combine(y, topk_weights, plan["pair_row"], geo.hidden, (shared, residual))
     return {"out": out, "plan": plan, "y_rows": y, "topk_idx": np.asarray(topk_idx),
             "topk_weights": np.asarray(topk_weights, dtype=np.float64)}
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     assert lib.moe_status_string(0) == b"ok"
 
 

@@ -1,0 +1,106 @@
+"""GPU parity of the optional pieces around the routed path: bias-aware FromLogits
+routing (moe_plan_ex), the combine's fused addends (moe_combine_ex: a shared
+expert's output and a residual), and the whole path with all of them
+(moe_forward_ex), each against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from gpu_util import compare_out, device_inputs, geometry, make_moe, prepared
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, seed, T, H, I, E, k, fmt, routing="precomputed"):
+    return moe_synth.MoEShape(name, seed, T, H, I, E, k, fmt, routing)
+
+
+def _bias(E, seed):
+    rng = np.random.default_rng(seed)
+    b = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    b[E // 3] = 8.0  # one expert the bias always selects
+    return b
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (300, 128, 4), (37, 512, 8)])
+def test_route_from_logits_biased(T, E, k):
+    rng = np.random.default_rng(100 + T)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = _bias(E, T)
+    lg[0, :] = 0.0                          # ties among the biased keys of equal bias
+    bias_t = bias.copy()
+    bias_t[: min(E, 6)] = 1.0               # ... e.g. experts 0..5 tie at key 1.0 on token 0
+    sh = small("route_bias", 1, T, 256, 128, E, k, "fp8_block128", "from_logits")
+    moe = make_moe(sh)
+    plan = moe.alloc_plan(T)
+    ws = moe.alloc_workspace(T)
+    ids = torch.empty((T, k), dtype=torch.int64, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.plan(T, plan, routing_logits=torch.from_numpy(lg).cuda(), topk_idx_out=ids, topk_weights_out=w, ws=ws,
+             routing_bias=torch.from_numpy(bias_t).cuda())
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route_from_logits(lg, k, bias_t)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-5, atol=1e-7)
+    # the bias changed the selection somewhere (else the test proves nothing)
+    assert not np.array_equal(ref_ids, oracle.route_from_logits(lg, k)[0])
+
+
+def test_combine_addends():
+    rng = np.random.default_rng(9)
+    T, k, E, H = 77, 3, 6, 4096
+    ids = rng.integers(-1, E, size=(T, k))
+    ids[5, :] = -1                                   # a token with no valid slot: the addends only
+    w = rng.random((T, k)).astype(np.float32)
+    sh = small("comb_add", 1, T, H, 128, E, k, "fp8_block128")
+    moe = make_moe(sh)
+    plan = moe.alloc_plan(T)
+    ws = moe.alloc_workspace(T)
+    moe.plan(T, plan, topk_idx=torch.from_numpy(ids).cuda(), ws=ws)
+    y = torch.randn((T * k, H), device="cuda").to(torch.bfloat16)
+    shared = torch.randn((T, H), device="cuda").to(torch.bfloat16)
+    residual = torch.randn((T, H), device="cuda").to(torch.bfloat16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.combine(T, y, torch.from_numpy(w).cuda(), plan, out, shared=shared, residual=residual)
+    torch.cuda.synchronize()
+    ref_plan = oracle.build_plan(ids, E)
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    ref = oracle.combine(f64(y), w, np.where(ref_plan["pair_row"] >= 0, np.arange(T * k), -1), H,
+                         (f64(shared), f64(residual)))
+    np.testing.assert_allclose(out.float().cpu().numpy(), ref, rtol=2 ** -7, atol=1e-5)
+
+
+@pytest.mark.parametrize("fmt", ["fp8_block128", "bf16"])
+def test_forward_with_bias_shared_expert_and_residual(fmt):
+    T, H, I, E, k = 96, 512, 256, 8, 2
+    sh = small("ext_" + fmt, 31, T, H, I, E, k, fmt, "from_logits")
+    inp = moe_synth.make_inputs(sh)
+    bias = _bias(E, 3)
+    # the shared expert: one more expert of the same format that every token visits with weight 1
+    sh1 = small("ext_shared_" + fmt, 32, T, H, I, 1, 1, fmt)
+    inp1 = moe_synth.make_inputs(sh1)
+    moe1 = make_moe(sh1)
+    d1 = device_inputs(inp1, topk_idx=np.zeros((T, 1), np.int64), topk_weights=np.ones((T, 1), np.float32))
+    d = device_inputs(inp)
+    plan1 = moe1.alloc_plan(T)
+    ws1 = moe1.alloc_workspace(T)
+    moe1.plan(T, plan1, topk_idx=d1["topk_idx"], ws=ws1)
+    y_shared = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")  # [T, 1, H]: token order
+    moe1.ffn(T, d["x"], d["x_sf"], prepared(moe1, d1), plan1, y_shared, ws1)
+    residual = torch.randn((T, H), device="cuda").to(torch.bfloat16)
+    moe = make_moe(sh)
+    out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = moe.alloc_workspace(T)
+    moe.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], prepared(moe, d), out, ws,
+                routing_bias=torch.from_numpy(bias).cuda(), shared=y_shared, residual=residual)
+    torch.cuda.synchronize()
+    geo1 = geometry(sh1)
+    shared_ref = oracle.forward(geo1, inp["x"], inp["x_sf"], inp1["w13"], inp1["w13_sf"], inp1["w2"], inp1["w2_sf"],
+                                topk_idx=np.zeros((T, 1), np.int64), topk_weights=np.ones((T, 1)))["y_rows"]
+    ref = oracle.forward(geometry(sh), inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
+                         logits=inp["logits"], routing_bias=bias, shared=shared_ref,
+                         residual=residual.float().cpu().numpy().astype(np.float64))
+    assert np.array_equal(d["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    compare_out(out, ref["out"])

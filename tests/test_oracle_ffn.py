@@ -312,6 +312,20 @@ def test_combine_masked_token_is_zero():
     assert np.allclose(out[2], 0.25 * y[2] + 2.0 * y[1])
 
 
+def test_combine_addends_hand_case():
+    # out[t] = sum of the weighted slot rows, then + shared[t] + residual[t]
+    y = np.arange(12.0).reshape(3, 4)
+    pr = np.array([0, -1, -1, -1, 2, 1])
+    w = np.array([[0.5, 9.0], [1.0, 1.0], [0.25, 2.0]])
+    shared = np.array([[1.0, 0, 0, 0], [0, 2.0, 0, 0], [0, 0, 3.0, 0]])
+    residual = np.full((3, 4), -0.5)
+    out = combine(y, w, pr, 4, (shared, residual))
+    assert out[1].tolist() == [-0.5, 1.5, -0.5, -0.5]   # masked token: the addends only
+    assert out[0].tolist() == (0.5 * y[0] + shared[0] - 0.5).tolist()
+    assert out[2].tolist() == (0.25 * y[2] + 2.0 * y[1] + shared[2] - 0.5).tolist()
+    assert np.array_equal(combine(y, w, pr, 4, (None, None)), combine(y, w, pr, 4))
+
+
 # ---- NVFP4 (E2M1 values, E4M3 scale per 16 along K, fp32 global scale per expert)
 def test_nvfp4_dequant_hand_values():
     from oracle import dequant_nvfp4

@@ -31,6 +31,37 @@ def test_topk_ties_go_to_lower_index():
     assert np.allclose(w, 1.0 / 3, rtol=0, atol=1e-15)
 
 
+def test_bias_hand_case():
+    # a large bias on expert 0 ranks it first although its logit is the smallest;
+    # the weights are the softmax of the two selected *unbiased* logits (1 and 4)
+    lg = np.array([[1, 2, 3, 4]], dtype=np.float32)
+    bias = np.array([10, 0, 0, 0], dtype=np.float32)
+    idx, w = route_from_logits(lg, 2, bias)
+    assert idx.tolist() == [[0, 3]]
+    e1, e4 = np.exp(1.0), np.exp(4.0)
+    assert np.allclose(w[0], [e1 / (e1 + e4), e4 / (e1 + e4)], rtol=0, atol=1e-15)
+
+
+def test_bias_zero_is_unbiased_and_bias_only_ranks():
+    rng = np.random.default_rng(11)
+    lg = rng.standard_normal((9, 24)).astype(np.float32)
+    idx0, w0 = route_from_logits(lg, 4)
+    idx1, w1 = route_from_logits(lg, 4, np.zeros(24, dtype=np.float32))
+    assert np.array_equal(idx0, idx1) and np.array_equal(w0, w1)
+    # with a random bias: the selection is the brute-force top-k of the fp32 sum,
+    # and the weights are a softmax over the selected raw logits
+    bias = rng.standard_normal(24).astype(np.float32)
+    idx, w = route_from_logits(lg, 4, bias)
+    key = (lg + bias[None, :]).astype(np.float32)
+    for t in range(9):
+        assert idx[t].tolist() == _brute_topk(key[t], 4)
+        sel = lg[t, idx[t]].astype(np.float64)
+        assert np.allclose(w[t], np.exp(sel) / np.exp(sel).sum(), rtol=0, atol=1e-14)
+    idx2, w2 = route_from_logits_fast(lg, 4, bias)
+    assert np.array_equal(idx, idx2)
+    assert np.allclose(w, w2, rtol=0, atol=1e-15)
+
+
 def test_softmax_over_topk_equals_renormalised_full_softmax():
     rng = np.random.default_rng(5)
     lg = rng.standard_normal((6, 10)).astype(np.float32)
