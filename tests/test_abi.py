@@ -112,6 +112,24 @@ def test_workspace_size_and_host_validation():
     lib.moe_destroy(h)
 
 
+def test_extended_entry_points_validate_on_host():
+    """moe_plan_ex / moe_combine_ex / moe_forward_ex reject, before any launch: a
+    routing bias with precomputed routing, and addends that are not 16-byte aligned."""
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg()), ctypes.byref(h)) == 0  # PRECOMPUTED
+    plan = mx._Plan(*([16] * 7))
+    assert lib.moe_plan_ex(h, 10, 16, None, 16, None, None, ctypes.byref(plan), None, 0, None) == 1  # bias, precomputed
+    assert lib.moe_combine_ex(h, 10, 16, 16, ctypes.byref(plan), 8, None, 16, None) == 1  # shared misaligned
+    assert lib.moe_combine_ex(h, 10, 16, 16, ctypes.byref(plan), None, 24, 16, None) == 1  # residual misaligned
+    w = mx._Weights(16, 16, 16, 16)
+    assert lib.moe_forward_ex(h, 10, 16, 16, 16, 16, None, 16, ctypes.byref(w), None, None, 16, 16, 1 << 40,
+                              None) == 1  # bias, precomputed
+    assert lib.moe_forward_ex(h, 10, 16, 16, 16, 16, None, None, ctypes.byref(w), 4, None, 16, 16, 1 << 40,
+                              None) == 1  # shared misaligned
+    lib.moe_destroy(h)
+
+
 def test_prepared_weight_sizes_and_validation():
     """Sizes follow the header's prepared layout: per expert, rows/16 row blocks x
     K-steps (128 elements; 64 for BF16) x 2048-byte tiles (1024 for MX), MX scale
