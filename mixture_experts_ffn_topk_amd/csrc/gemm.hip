@@ -13,7 +13,11 @@
 //     FP8 / bf16-operand tiles load it with direct-to-LDS buffer loads.
 //   * B (weights) streams from HBM straight into VGPRs from the prepared tiles
 //     (MFMA operand order, one 1 KB run per wave load), DEPTH K-steps deep,
-//     each wave owning 16*NT weight rows.  Every weight byte of a tile is read once.
+//     each wave owning 16*NT weight rows.  Every weight byte of a tile is read
+//     once; weight-bound tiles stream it with the non-temporal cache policy.
+// Tiles map to the 8 XCDs in contiguous ranges: column-tile major for the
+// MFMA-bound regime (an XCD's tiles share an expert's weights in its L2),
+// expert major for the weight-bound one (an expert's activation rows stay in L2).
 // All global loads are buffer loads: a uniform base, a loop-invariant 32-bit
 // lane offset and the K-step offset in a scalar register; a lane offset past
 // the end of the resource reads zeros, which masks rows and columns outside
