@@ -1,0 +1,60 @@
+"""The entry points allocate nothing and never synchronise, so a step can be
+captured into a HIP graph.  Each replay, with eager work and synchronisations
+between them, must reproduce the eager step bit for bit (every kernel of the path
+is deterministic)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from gpu_util import device_inputs, make_moe, prepared
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fmt,routing", [("fp8_block128", "precomputed"), ("w4a8_mx", "from_logits"),
+                                         ("nvfp4_w4a16", "precomputed")])
+def test_graph_replays_match_eager(fmt, routing):
+    sh = moe_synth.MoEShape("graph_" + fmt, 41, 96, 512, 256, 8, 2, fmt, routing)
+    inp = moe_synth.make_inputs(sh)
+    moe = make_moe(sh)
+    d = device_inputs(inp)
+    w = prepared(moe, d)
+    T, k = sh.tokens, sh.topk
+    plan = moe.alloc_plan(T)
+    ws = moe.alloc_workspace(T)
+    h, hsf = moe.alloc_intermediate(T)
+    y = torch.zeros((T * k, sh.hidden), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((T, sh.hidden), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+
+    def step():
+        if routing == "precomputed":
+            moe.plan(T, plan, topk_idx=d["topk_idx"], ws=ws, stream=s)
+        else:
+            moe.plan(T, plan, routing_logits=d["logits"], topk_idx_out=d["topk_idx"],
+                     topk_weights_out=d["topk_weights"], ws=ws, stream=s)
+        moe.ffn_gate_up(T, d["x"], d["x_sf"], w, plan, h, hsf, stream=s)
+        moe.ffn_down(T, h, hsf, w, plan, y, stream=s)
+        moe.combine(T, y, d["topk_weights"], plan, out, stream=s)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager step"
+        with torch.cuda.stream(s):  # eager work between replays
+            step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    assert not torch.isnan(eager.float()).any()
