@@ -48,6 +48,31 @@ def test_route_from_logits_biased(T, E, k):
     assert not np.array_equal(ref_ids, oracle.route_from_logits(lg, k)[0])
 
 
+def test_route_biased_nan_and_ragged_expert_count():
+    """E not a multiple of the wave width; NaN logits and a NaN bias entry rank lowest."""
+    T, E, k = 50, 100, 4
+    rng = np.random.default_rng(77)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[::5, 3] = np.nan
+    lg[2, :10] = np.nan
+    bias = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    bias[7] = np.nan
+    bias[99] = 4.0
+    sh = small("route_bias_nan", 1, T, 256, 128, E, k, "fp8_block128", "from_logits")
+    moe = make_moe(sh)
+    plan = moe.alloc_plan(T)
+    ws = moe.alloc_workspace(T)
+    ids = torch.empty((T, k), dtype=torch.int64, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.plan(T, plan, routing_logits=torch.from_numpy(lg).cuda(), topk_idx_out=ids, topk_weights_out=w, ws=ws,
+             routing_bias=torch.from_numpy(bias).cuda())
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route_from_logits(lg, k, bias)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-5, atol=1e-7)
+    assert not np.isin(ref_ids, [7]).any()  # the NaN-biased expert is never chosen
+
+
 def test_combine_addends():
     rng = np.random.default_rng(9)
     T, k, E, H = 77, 3, 6, 4096
