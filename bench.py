@@ -9,8 +9,8 @@ moe_prepare_weights before timing): routing plan (and top-k from logits where th
 workload routes from logits), gate_up grouped GEMM with the fused clamped
 SwiGLU and requantisation, down grouped GEMM, router-weighted combine — the
 same kernels moe_forward launches, called through the C ABI's stage entry
-points so that HIP events can bracket the two GEMM launches on the stream they
-run on.  K steps run back to back between two device synchronisations.
+points so that the two GEMM launches can carry HIP timing events (the timed
+variants of the leg entry points) on the stream they run on.  K steps run back to back between two device synchronisations.
 
 Prints one JSON line with tokens/s, the dominant kernel's roofline fraction
 (from its live HIP-event duration) and the CPU oracle timed on a bounded sample
@@ -212,13 +212,17 @@ def main() -> int:
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # Per-kernel durations come from HIP events recorded around the two GEMM legs in
-    # a sample of the timed steps (every stride-th step): an event in the stream
-    # costs a few microseconds between kernels, which would otherwise be counted
-    # in every step's time.
+    # Per-kernel durations come from HIP events that the two GEMM legs' kernel
+    # launches carry themselves (moe_ffn_gate_up_timed / moe_ffn_down_timed), in a
+    # sample of the timed steps (every stride-th step): the events hold each
+    # kernel's own start and end, with no marker commands between the kernels.
+    # torch creates an event at its first record, done here, before the timing.
     stride = max(1, args.steps // 10)
     sampled = list(range(0, args.steps, stride))
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    for e4 in ev.values():
+        for e in e4:
+            e.record(stream)
 
     def step(e=None):
         if sh.routing == "precomputed":
@@ -226,14 +230,8 @@ def main() -> int:
         else:
             moe.plan(T, plan, routing_logits=logits, topk_idx_out=topk_idx, topk_weights_out=topk_w, ws=ws,
                      stream=stream)
-        if e is not None:
-            e[0].record(stream)
-        moe.ffn_gate_up(T, x, x_sf, weights, plan, h, hsf, stream=stream)
-        if e is not None:
-            e[1].record(stream)
-        moe.ffn_down(T, h, hsf, weights, plan, y, stream=stream)
-        if e is not None:
-            e[2].record(stream)
+        moe.ffn_gate_up(T, x, x_sf, weights, plan, h, hsf, stream=stream, events=None if e is None else e[:2])
+        moe.ffn_down(T, h, hsf, weights, plan, y, stream=stream, events=None if e is None else e[2:])
         moe.combine(T, y, topk_w, plan, out, stream=stream)
 
     log(f"warmup {args.warmup} steps")
@@ -252,7 +250,7 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gate_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev.values()]))
-    down_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev.values()]))
+    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev.values()]))
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 4
+#define MOE_FFN_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -230,6 +230,21 @@ moe_status moe_ffn_gate_up(const moe_handle* h, int32_t num_tokens, const void* 
 moe_status moe_ffn_down(const moe_handle* h, int32_t num_tokens, const void* h_in, const void* h_sf_in,
                         const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
                         void* y, hipStream_t stream);
+
+/* moe_ffn_gate_up / moe_ffn_down with timing: start and stop are hipEvent_t
+   handles owned by the caller (created with timing enabled; either may be NULL).
+   They travel with the leg's GEMM kernel launch itself (hipExtLaunchKernel), so
+   hipEventElapsedTime(start, stop) is that kernel's own execution time, with no
+   separate marker commands between kernels of the stream.  Nothing is recorded
+   when no kernel is launched (num_tokens = 0).  Same validation and errors as
+   the untimed calls; the events are not checked. */
+moe_status moe_ffn_gate_up_timed(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
+                                 const moe_weights* w /* host struct */,
+                                 const moe_plan_buffers* plan /* host struct */, void* h_out, void* h_sf_out,
+                                 hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+moe_status moe_ffn_down_timed(const moe_handle* h, int32_t num_tokens, const void* h_in, const void* h_sf_in,
+                              const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
+                              void* y, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 /* Router-weighted combine ([EPCombine] router_weights): out[t] = sum over valid
    slots j in ascending order of topk_weights[t,j] * y[t,j,:], accumulated in

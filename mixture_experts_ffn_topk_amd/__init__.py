@@ -59,7 +59,8 @@ class _PreparedSizes(ctypes.Structure):
 PLAN_FIELDS = [f for f, _ in _Plan._fields_]
 EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
-            "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_status_string", "moe_abi_version"]
+            "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_ffn_gate_up_timed", "moe_ffn_down_timed",
+            "moe_status_string", "moe_abi_version"]
 
 _lib = None
 
@@ -91,6 +92,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_gate_up.restype = i32
     lib.moe_ffn_down.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp]
     lib.moe_ffn_down.restype = i32
+    lib.moe_ffn_gate_up_timed.argtypes = lib.moe_ffn_gate_up.argtypes + [vp, vp]
+    lib.moe_ffn_gate_up_timed.restype = i32
+    lib.moe_ffn_down_timed.argtypes = lib.moe_ffn_down.argtypes + [vp, vp]
+    lib.moe_ffn_down_timed.restype = i32
     lib.moe_combine.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Plan), vp, vp]
     lib.moe_combine.restype = i32
     lib.moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, sz, vp]
@@ -115,6 +120,18 @@ def _ptr(t) -> int | None:
     if isinstance(t, int):
         return t
     return t.data_ptr()
+
+
+def _event_handles(events):
+    """hipEvent_t handles of a (start, stop) pair of torch.cuda.Event; torch creates
+    an event at its first record, so an event never recorded has no handle yet."""
+    hs = []
+    for e in events:
+        hv = int(e.cuda_event)
+        if hv == 0:
+            raise ValueError("a timing event must be created (recorded once) before it is passed to a launch")
+        hs.append(ctypes.c_void_p(hv))
+    return hs
 
 
 def _stream(stream) -> int | None:
@@ -243,17 +260,29 @@ class MoEFFN:
             return h, torch.empty((n, self.inter // 128), dtype=torch.float32, device=device)
         return h, torch.empty((n, self.inter // 32), dtype=torch.uint8, device=device)
 
-    def ffn_gate_up(self, num_tokens, x, x_sf, weights: dict, plan: dict, h, h_sf, stream=None):
+    def ffn_gate_up(self, num_tokens, x, x_sf, weights: dict, plan: dict, h, h_sf, stream=None, events=None):
+        """events: optional (start, stop) torch.cuda.Event pair (timing enabled, already
+        created by one record) that the GEMM kernel's own launch updates
+        (moe_ffn_gate_up_timed)."""
         ws_ = self._weights_struct(weights)
         ps = self._plan_struct(plan)
-        _check(self.lib.moe_ffn_gate_up(self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps),
-                                        _ptr(h), _ptr(h_sf), _stream(stream)), "moe_ffn_gate_up")
+        args = (self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps), _ptr(h), _ptr(h_sf),
+                _stream(stream))
+        if events is None:
+            _check(self.lib.moe_ffn_gate_up(*args), "moe_ffn_gate_up")
+        else:
+            _check(self.lib.moe_ffn_gate_up_timed(*args, *_event_handles(events)), "moe_ffn_gate_up_timed")
 
-    def ffn_down(self, num_tokens, h, h_sf, weights: dict, plan: dict, y, stream=None):
+    def ffn_down(self, num_tokens, h, h_sf, weights: dict, plan: dict, y, stream=None, events=None):
+        """events: as for ffn_gate_up (moe_ffn_down_timed)."""
         ws_ = self._weights_struct(weights)
         ps = self._plan_struct(plan)
-        _check(self.lib.moe_ffn_down(self._h, num_tokens, _ptr(h), _ptr(h_sf), ctypes.byref(ws_), ctypes.byref(ps),
-                                     _ptr(y), _stream(stream)), "moe_ffn_down")
+        args = (self._h, num_tokens, _ptr(h), _ptr(h_sf), ctypes.byref(ws_), ctypes.byref(ps), _ptr(y),
+                _stream(stream))
+        if events is None:
+            _check(self.lib.moe_ffn_down(*args), "moe_ffn_down")
+        else:
+            _check(self.lib.moe_ffn_down_timed(*args, *_event_handles(events)), "moe_ffn_down_timed")
 
     def combine(self, num_tokens, y, topk_weights, plan: dict, out, stream=None, shared=None, residual=None):
         ps = self._plan_struct(plan)

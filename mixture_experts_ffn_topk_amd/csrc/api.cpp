@@ -100,7 +100,8 @@ moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const flo
 }
 
 moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
-                  const moe_plan_buffers* plan, void* y, void* hbuf, void* hsf, hipStream_t s, int stage) {
+                  const moe_plan_buffers* plan, void* y, void* hbuf, void* hsf, hipStream_t s, int stage,
+                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const moe_config& c = h->cfg;
   moe::FfnArgs a{};
   a.fmt = to_fmt(c.format);
@@ -125,6 +126,8 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
   a.h = hbuf;
   a.h_sf = hsf;
   a.y = y;
+  if (stage == 1) a.ev[0] = e0, a.ev[1] = e1;
+  if (stage == 2) a.ev[2] = e0, a.ev[3] = e1;
   return hip_status(moe::launch_ffn(a, s, stage));
 }
 
@@ -285,21 +288,34 @@ moe_status moe_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_
   return do_ffn(h, T, x, x_sf, w, plan, y, (char*)ws + L.h_off, (char*)ws + L.hsf_off, stream, 0);
 }
 
-moe_status moe_ffn_gate_up(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
-                           const moe_plan_buffers* plan, void* h_out, void* h_sf_out, hipStream_t stream) {
+moe_status moe_ffn_gate_up_timed(const moe_handle* h, int32_t T, const void* x, const void* x_sf,
+                                 const moe_weights* w, const moe_plan_buffers* plan, void* h_out, void* h_sf_out,
+                                 hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (!bf16_acts(h->cfg.format) && !h_sf_out)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
-  return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1);
+  return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1, start, stop);
+}
+
+moe_status moe_ffn_gate_up(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
+                           const moe_plan_buffers* plan, void* h_out, void* h_sf_out, hipStream_t stream) {
+  return moe_ffn_gate_up_timed(h, T, x, x_sf, w, plan, h_out, h_sf_out, stream, nullptr, nullptr);
+}
+
+moe_status moe_ffn_down_timed(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in,
+                              const moe_weights* w, const moe_plan_buffers* plan, void* y, hipStream_t stream,
+                              hipEvent_t start, hipEvent_t stop) {
+  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!h_in || !y || (!bf16_acts(h->cfg.format) && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2,
+                start, stop);
 }
 
 moe_status moe_ffn_down(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in, const moe_weights* w,
                         const moe_plan_buffers* plan, void* y, hipStream_t stream) {
-  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!h_in || !y || (!bf16_acts(h->cfg.format) && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
-  if (T == 0) return MOE_OK;
-  return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2);
+  return moe_ffn_down_timed(h, T, h_in, h_sf_in, w, plan, y, stream, nullptr, nullptr);
 }
 
 moe_status moe_combine_ex(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,

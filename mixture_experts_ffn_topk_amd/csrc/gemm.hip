@@ -40,6 +40,8 @@
 // as bytes [16g, 16g+16); the scale byte of lane l belongs to K-block g (32
 // elements) of row l%16; a bf16 32x32x16 operand gives lane l = 32h + r the
 // K elements [8h, 8h+8) of its 16-element sub-step, row r.
+#include <hip/hip_ext.h>
+
 #include "device.h"
 #include "launch.h"
 
@@ -943,15 +945,17 @@ int ffn_max_m_tiles(int npairs, int E, int bm) {
 }
 
 template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, int WGS>
-static void launch_one(const GemmParams& gp, bool fast, hipStream_t s) {
+// With timing events the launch carries them in its own dispatch, so they hold the
+// kernel's start and end, not those of separate marker commands in the stream.
+static void launch_one(const GemmParams& gp, bool fast, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int grid = gp.m_tiles_max * gp.n_tiles;
   if (grid <= 0) return;
   if (fast)
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, true>), dim3(grid),
-                       dim3(64 * WAVES), 0, s, gp);
+    hipExtLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, true>), dim3(grid),
+                          dim3(64 * WAVES), 0, s, e0, e1, 0, gp);
   else
-    hipLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, false>), dim3(grid),
-                       dim3(64 * WAVES), 0, s, gp);
+    hipExtLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, false>), dim3(grid),
+                          dim3(64 * WAVES), 0, s, e0, e1, 0, gp);
 }
 
 // Launch configuration per format, regime and leg: waves per workgroup, 16-row
@@ -976,26 +980,27 @@ constexpr LegConfig leg_config() {
   return {8, 2, 2, 2, 1};
 }
 template <Fmt F, bool GATEUP, int BM>
-static void launch_leg(const GemmParams& gp, bool fast, hipStream_t s) {
+static void launch_leg(const GemmParams& gp, bool fast, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr LegConfig c = leg_config<F, GATEUP, BM>();
-  launch_one<F, GATEUP, BM, c.waves, c.nt, c.depth, c.ksg, c.wgs>(gp, fast, s);
+  launch_one<F, GATEUP, BM, c.waves, c.nt, c.depth, c.ksg, c.wgs>(gp, fast, s, e0, e1);
 }
 
 template <Fmt F, int BM>
-static void launch_pair(const GemmParams& g1_in, const GemmParams& g2_in, bool fast, hipStream_t s, int stage) {
+static void launch_pair(const GemmParams& g1_in, const GemmParams& g2_in, bool fast, hipStream_t s, int stage,
+                        const hipEvent_t (&ev)[4]) {
   if (stage != 2) {
     constexpr LegConfig c = leg_config<F, true, BM>();
     constexpr int hc = c.waves * 16 * c.nt / 2;  // h columns of a gate_up tile
     GemmParams g1 = g1_in;
     g1.n_tiles = (g1.N + hc - 1) / hc;
-    launch_leg<F, true, BM>(g1, fast, s);
+    launch_leg<F, true, BM>(g1, fast, s, ev[0], ev[1]);
   }
   if (stage != 1) {
     constexpr LegConfig c = leg_config<F, false, BM>();
     constexpr int bn = c.waves * 16 * c.nt;  // output columns of a down tile
     GemmParams g2 = g2_in;
     g2.n_tiles = (g2.N + bn - 1) / bn;
-    launch_leg<F, false, BM>(g2, fast, s);
+    launch_leg<F, false, BM>(g2, fast, s, ev[2], ev[3]);
   }
 }
 
@@ -1061,20 +1066,20 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g2.c_sf_row = 0;
   switch (a.fmt) {
     case Fmt::FP8:
-      if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::FP8, 80>(g1, g2, a.fast, s, stage);
+      if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s, stage, a.ev);
+      else launch_pair<Fmt::FP8, 80>(g1, g2, a.fast, s, stage, a.ev);
       break;
     case Fmt::BF16:
-      if (bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::BF16, 96>(g1, g2, a.fast, s, stage);
+      if (bm == 128) launch_pair<Fmt::BF16, 128>(g1, g2, a.fast, s, stage, a.ev);
+      else launch_pair<Fmt::BF16, 96>(g1, g2, a.fast, s, stage, a.ev);
       break;
     case Fmt::MX:
-      if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::MX, 80>(g1, g2, a.fast, s, stage);
+      if (a.bm == 128) launch_pair<Fmt::MX, 128>(g1, g2, a.fast, s, stage, a.ev);
+      else launch_pair<Fmt::MX, 80>(g1, g2, a.fast, s, stage, a.ev);
       break;
     case Fmt::NV4:
-      if (bm == 128) launch_pair<Fmt::NV4, 128>(g1, g2, a.fast, s, stage);
-      else launch_pair<Fmt::NV4, 96>(g1, g2, a.fast, s, stage);
+      if (bm == 128) launch_pair<Fmt::NV4, 128>(g1, g2, a.fast, s, stage, a.ev);
+      else launch_pair<Fmt::NV4, 96>(g1, g2, a.fast, s, stage, a.ev);
       break;
   }
   return hipGetLastError();

@@ -62,6 +62,9 @@ struct FfnArgs {
   void* h;     // intermediate [T*k, I] (E4M3 or bf16)
   void* h_sf;  // its scales: fp32 [T*k, I/128] (FP8) or UE8M0 [T*k, I/32] (MX)
   void* y;     // [T*k, H] bf16, row p = src_info[row]
+  // optional timing events (hipEvent_t or null) carried by the launch of each leg's
+  // kernel: gate_up start/stop, down start/stop
+  hipEvent_t ev[4];
 };
 size_t ffn_h_bytes(Fmt f, int rows, int I);
 size_t ffn_hsf_bytes(Fmt f, int rows, int I);

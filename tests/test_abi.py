@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -114,7 +114,8 @@ def test_workspace_size_and_host_validation():
 
 def test_extended_entry_points_validate_on_host():
     """moe_plan_ex / moe_combine_ex / moe_forward_ex reject, before any launch: a
-    routing bias with precomputed routing, and addends that are not 16-byte aligned."""
+    routing bias with precomputed routing, and addends that are not 16-byte aligned;
+    the timed legs reject what the untimed ones do."""
     lib = _lib()
     h = ctypes.c_void_p()
     assert lib.moe_create(ctypes.byref(_cfg()), ctypes.byref(h)) == 0  # PRECOMPUTED
@@ -127,6 +128,13 @@ def test_extended_entry_points_validate_on_host():
                               None) == 1  # bias, precomputed
     assert lib.moe_forward_ex(h, 10, 16, 16, 16, 16, None, None, ctypes.byref(w), 4, None, 16, 16, 1 << 40,
                               None) == 1  # shared misaligned
+    # the timed legs validate like the untimed ones; T = 0 launches nothing and records nothing
+    assert lib.moe_ffn_gate_up_timed(h, 10, None, None, ctypes.byref(w), ctypes.byref(plan), 16, 16, None, None,
+                                     None) == 1  # x missing
+    assert lib.moe_ffn_down_timed(h, 10, 16, 16, ctypes.byref(w), ctypes.byref(plan), None, None, None,
+                                  None) == 1  # y missing
+    assert lib.moe_ffn_down_timed(h, 0, None, None, ctypes.byref(w), ctypes.byref(plan), None, None, None,
+                                  None) == 0
     lib.moe_destroy(h)
 
 

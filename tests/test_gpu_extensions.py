@@ -1,7 +1,8 @@
 """GPU parity of the optional pieces around the routed path: bias-aware FromLogits
 routing (moe_plan_ex), the combine's fused addends (moe_combine_ex: a shared
 expert's output and a residual), and the whole path with all of them
-(moe_forward_ex), each against the oracle."""
+(moe_forward_ex), each against the oracle; and the timed GEMM legs, whose
+events carry the kernels' own start and end."""
 import numpy as np
 import pytest
 import torch
@@ -129,3 +130,38 @@ def test_forward_with_bias_shared_expert_and_residual(fmt):
                          residual=residual.float().cpu().numpy().astype(np.float64))
     assert np.array_equal(d["topk_idx"].cpu().numpy(), ref["topk_idx"])
     compare_out(out, ref["out"])
+
+
+@pytest.mark.parametrize("fmt", ["fp8_block128", "w4a8_mx"])
+def test_timed_legs_match_untimed(fmt):
+    """moe_ffn_gate_up_timed / moe_ffn_down_timed write what the untimed legs write,
+    and their events enclose a positive kernel time shorter than the two events
+    recorded around the launch in the stream."""
+    sh = small("timed_" + fmt, 51, 200, 512, 256, 8, 2, fmt)
+    inp = moe_synth.make_inputs(sh)
+    moe = make_moe(sh)
+    d = device_inputs(inp)
+    w = prepared(moe, d)
+    T = sh.tokens
+    plan = moe.alloc_plan(T)
+    ws = moe.alloc_workspace(T)
+    moe.plan(T, plan, topk_idx=d["topk_idx"], ws=ws)
+    outs = []
+    for timed in (False, True):
+        h, hsf = moe.alloc_intermediate(T)
+        y = torch.zeros((T * sh.topk, sh.hidden), dtype=torch.bfloat16, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if timed else None
+        if timed:
+            for e in ev[:4]:
+                e.record()  # creates the events
+            ev[4].record()
+        moe.ffn_gate_up(T, d["x"], d["x_sf"], w, plan, h, hsf, events=ev[0:2] if timed else None)
+        moe.ffn_down(T, h, hsf, w, plan, y, events=ev[2:4] if timed else None)
+        if timed:
+            ev[5].record()
+        torch.cuda.synchronize()
+        outs.append((h.clone(), y.clone()))
+        if timed:
+            g, dn, around = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3]), ev[4].elapsed_time(ev[5])
+            assert 0 < g and 0 < dn and g + dn <= around, (g, dn, around)
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
