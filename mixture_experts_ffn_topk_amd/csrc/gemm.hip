@@ -399,7 +399,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
   for (int i = 0; i < TL::kAChunks; ++i)
     a_src[i] = GATEUP ? p.src_info[row0 + min((tid + kThreads * i) >> 3, rows - 1)] : 0;
-  const int asf_src = GATEUP && !bf16_mma(F) ? p.src_info[row0 + min(tid, rows - 1)] : 0;
+  const int asf_src = GATEUP && F == Fmt::FP8 ? p.src_info[row0 + min(tid, rows - 1)] : 0;
+  // MX activation scales per stage: the BM x 4 UE8M0 bytes of each of its KSG
+  // K-steps, loaded densely, one byte per lane and load (entry e: K-step e / (4 BM),
+  // tile row (e % (4 BM)) / 4, K-block e % 4), so that a wave issues one or two
+  // loads per stage instead of one per K-block (a scale row of H/32 bytes need not
+  // be 4-byte aligned, so wider loads do not apply).
+  constexpr int kSfTotal = BM * 4 * KSG;
+  constexpr int kSfQ = F == Fmt::MX ? (kSfTotal + kThreads - 1) / kThreads : 1;
+  constexpr int kSfN = F == Fmt::MX ? kSfQ : KSG;  // scale registers per stage
+  // the K-step of entry tid + kThreads q, known at compile time for every MX tiling
+  static_assert(F != Fmt::MX || KSG == 1 || (BM * 4) % kThreads == 0, "MX scale entries: K-step per load");
+  auto sf_u = [](int q) { return KSG == 1 ? 0 : kThreads * q / (BM * 4); };
+  int asf_srcq[kSfQ];
+#pragma unroll
+  for (int q = 0; q < kSfQ; ++q) {
+    const int row = ((tid + kThreads * q) % (BM * 4)) >> 2;
+    asf_srcq[q] = GATEUP && F == Fmt::MX ? p.src_info[row0 + min(row, rows - 1)] : 0;
+  }
   // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed.
   // Issued first, before the activation rows' addresses are known (direct-to-LDS
   // tiles: the first stage's K-steps here, the rest after the first activation stage).
@@ -418,13 +435,20 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ (r & 7)) : (uint32_t)(c & 7);
     a_off[i] = r < rows ? arow * p.a_row_bytes + chunk * 16u : kOOB;
   }
-  // A scale of row tid (FP8: fp32 per K-step; MX: 4 UE8M0 bytes per K-step);
-  // threads past the tile's rows load zeros
+  // FP8: the fp32 A scale of row tid per K-step; threads past the tile's rows load zeros
   const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
   const uint32_t asf_off =
-      (!bf16_mma(F) && tid < rows)
+      (F == Fmt::FP8 && tid < rows)
           ? (GATEUP ? (uint32_t)(asf_src / p.topk) : (uint32_t)(row0 + tid)) * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u)
           : kOOB;
+  uint32_t asf_offq[kSfQ];  // MX: entry tid + kThreads q
+#pragma unroll
+  for (int q = 0; q < kSfQ; ++q) {
+    const int e = tid + kThreads * q, u = sf_u(q), rem = e - u * (BM * 4), row = rem >> 2;
+    const uint32_t rt = GATEUP ? (uint32_t)(asf_srcq[q] / p.topk) : (uint32_t)(row0 + row);
+    asf_offq[q] = (F == Fmt::MX && e < kSfTotal && row < rows) ? rt * (uint32_t)p.a_sf_row + (uint32_t)(4 * u + (rem & 3))
+                                                                : kOOB;
+  }
 
   // down: the pair slot of each tile row, for the epilogue's scatter (loaded early)
   const int pair_of_row = (!GATEUP && tid < rows) ? p.src_info[row0 + tid] : 0;
@@ -447,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   }
 
   // Loads past the last K-step read zeros (no branch, so the register rings stay static).
-  auto load_a = [&](i32x4 (&v)[KSG][TL::kAChunks], uint32_t (&s)[KSG], int st) {
+  auto load_a = [&](i32x4 (&v)[KSG][TL::kAChunks], uint32_t (&s)[kSfN], int st) {
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
       const int ks = st * KSG + u;
@@ -459,24 +483,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         v[u][i] = bload16(a_rs, o, (uint32_t)ks * 128u);
       }
     }
+    if constexpr (F == Fmt::FP8) {
 #pragma unroll
-    for (int u = 0; u < KSG; ++u) {
-      const int ks = st * KSG + u;
-      if (F == Fmt::FP8) {
+      for (int u = 0; u < KSG; ++u) {
+        const int ks = st * KSG + u;
         s[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, (asf_off + 4u * u) | oob_if(ks >= p.ksteps),
                                                               (uint32_t)st * (KSG * 4u), 0);
-      } else if (F == Fmt::MX) {
-        uint32_t w = 0;
+      }
+    } else if constexpr (F == Fmt::MX) {
+      // byte 4 ks + (e % 4) of the row; K-blocks past the row's end and entries past
+      // the stage's read zeros (no branch in the main loop)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t o = (asf_off + (uint32_t)(4 * u + j)) | oob_if(ks * 4 + j >= p.a_sf_row);
-          w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, o, (uint32_t)st * (KSG * 4u), 0) << (8 * j);
-        }
-        s[u] = w;
+      for (int q = 0; q < kSfQ; ++q) {
+        const uint32_t o = asf_offq[q] | oob_if(st * KSG * 4 + 4 * sf_u(q) + (tid & 3) >= p.a_sf_row);
+        s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, o, (uint32_t)st * (KSG * 4u), 0);
       }
     }
   };
-  auto store_a = [&](const i32x4 (&v)[KSG][TL::kAChunks], const uint32_t (&s)[KSG], int buf) {
+  auto store_a = [&](const i32x4 (&v)[KSG][TL::kAChunks], const uint32_t (&s)[kSfN], int buf) {
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
       uint8_t* base = a_lds + (buf * KSG + u) * TL::kAStepBytes;
@@ -486,9 +510,26 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         *(i32x4*)(base + r * TL::kARowBytes + (((c & 7) ^ (r & TL::kSwz)) * 16)) = v[u][i];
       }
     }
-    if (!bf16_mma(F)) {
+    if constexpr (F == Fmt::FP8) {
 #pragma unroll
       for (int u = 0; u < KSG; ++u) sa_lds[(buf * KSG + u) * TL::kSA + tid] = s[u];
+    } else if constexpr (F == Fmt::MX) {
+      // the four lanes of a quad hold the four bytes of one row's scale word (entry
+      // e = 4 row + block): the quad's first lane gathers them (DPP quad
+      // permutations) and stores the word
+#pragma unroll
+      for (int q = 0; q < kSfQ; ++q) {
+        const int v = (int)s[q];
+        const uint32_t w = (uint32_t)v | (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false) << 8 |
+                           (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false) << 16 |
+                           (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false) << 24;
+        const int e = tid + kThreads * q, u = sf_u(q);
+        // every lane stores (a branch here costs registers across the main loop): the
+        // other lanes write a spare slot past the tile's rows, which no K-step reads
+        static_assert(F != Fmt::MX || TL::kSA > BM, "a spare scale slot");
+        const int slot = ((tid & 3) == 0 && e < kSfTotal) ? (e - u * (BM * 4)) >> 2 : TL::kSA - 1;
+        sa_lds[(buf * KSG + u) * TL::kSA + slot] = w;
+      }
     }
   };
 
@@ -513,7 +554,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * (F == Fmt::NV4 ? NT : NT * 2);
 
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
-  uint32_t as[TL::kDma ? 1 : 2][KSG] = {};
+  uint32_t as[TL::kDma ? 1 : 2][kSfN] = {};
   if constexpr (TL::kDma) {
     // Ring K-steps of stage 0 (above), A(0), the ring K-steps of stage 1, A(1),
     // in this order (the scheduling barriers keep it).  When stage st waits for
@@ -709,8 +750,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 
   // One stage of KSG K-steps: A(st) is in LDS buffer st&1 and A(st+1) in flight in
   // `an`; issues A(st+2) into `ap`, and refills each consumed weight-ring slot.
-  auto stage = [&](int st, int su, i32x4 (&ap)[KSG][TL::kAChunks], uint32_t (&sp)[KSG],
-                   i32x4 (&an)[KSG][TL::kAChunks], uint32_t (&sn)[KSG]) {
+  auto stage = [&](int st, int su, i32x4 (&ap)[KSG][TL::kAChunks], uint32_t (&sp)[kSfN],
+                   i32x4 (&an)[KSG][TL::kAChunks], uint32_t (&sn)[kSfN]) {
     load_a(ap, sp, st + 2);
     __syncthreads();
     // The MFMA section runs at raised wave priority, so that while one wave of a
