@@ -290,6 +290,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   float sb_pre[kSbPer];
   __amdgpu_buffer_rsrc_t bsc_rs = b_rs;
   uint32_t b_off[NT], bsc_off[NT];
+  // MX with four 16-row tiles per wave: the wave's 4 x 64 scale bytes of a K-step are
+  // one dword per lane (lane l: dword l % 16 of tile l / 16), handed to the lanes
+  // that use them with ds_bpermute: one load per K-step instead of one per tile.
+  constexpr bool kMxDenseSc = F == Fmt::MX && NT == 4;
+  uint32_t bsc_dense = kOOB;
   {
     if (F == Fmt::MX || F == Fmt::NV4)
       bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);
@@ -316,6 +321,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // MX: the lane's scale byte; NV4: the four scale bytes of the lane's tile row
       bsc_off[nt] = ok ? (F == Fmt::NV4 ? tiles0 * 128u + (uint32_t)(lane & 31) * 4u : tiles0 * 64u + (uint32_t)lane)
                        : kOOB;
+      if (kMxDenseSc && (lane >> 4) == nt) bsc_dense = ok ? tiles0 * 64u + (uint32_t)(lane & 15) * 4u : kOOB;
     }
     if (F == Fmt::FP8) {
       // the tile's weight-scale rows, staged in LDS: gate_up [0, kHB) the gate
@@ -380,7 +386,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       const uint32_t o = b_off[nt] | dead;
       b.lo[nt] = bload_w(o, (uint32_t)ks * p.b_tile);
       if (F == Fmt::MX) {
-        b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, bsc_off[nt] | dead, (uint32_t)ks * 64u, 0);
+        if constexpr (kMxDenseSc) {
+          if (nt == 0) b.sc[0] = (int)__builtin_amdgcn_raw_buffer_load_b32(bsc_rs, bsc_dense | dead, (uint32_t)ks * 64u, 0);
+        } else {
+          b.sc[nt] = (int)__builtin_amdgcn_raw_buffer_load_b8(bsc_rs, bsc_off[nt] | dead, (uint32_t)ks * 64u, 0);
+        }
       } else {
         b.hi[nt] = bload_w(o + 1024u, (uint32_t)ks * p.b_tile);
       }
@@ -729,6 +739,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         }
       }
     } else {
+      // the lane's scale byte of each tile: byte l of the tile's 64 (dense: held by
+      // lane 16 nt + l / 4, byte l % 4; the MFMA reads the operand's low byte)
+      int scb[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        scb[nt] = kMxDenseSc ? __builtin_amdgcn_ds_bpermute((16 * nt + (lane >> 2)) * 4, bq_.sc[0]) >> (8 * (lane & 3))
+                             : bq_.sc[nt];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const i32x4 alo = rd_lo(mt), ahi = rd_hi(mt);
@@ -740,7 +757,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             const i32x8 b8 = {bq_.lo[nt][0], bq_.lo[nt][1], bq_.lo[nt][2], bq_.lo[nt][3], 0, 0, 0, 0};
-            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[mt][nt], 4, 0, 0, bq_.sc[nt], 0,
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[mt][nt], 4, 0, 0, scb[nt], 0,
                                                                            sa);
           }
         }
