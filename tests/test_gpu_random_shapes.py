@@ -35,7 +35,7 @@ def _shape(fmt, seed):
 
 
 @pytest.mark.parametrize("regime", ["decode", "prefill"])
-@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("fmt", list(_GRAIN))
 def test_random_shape_forward(fmt, seed, regime):
     sh = _shape(fmt, 1000 * seed + len(fmt))
