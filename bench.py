@@ -180,7 +180,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    sh = moe_synth.CONFIGS[args.workload]
+    sh = moe_synth.WORKLOADS[args.workload]
     log(f"workload {sh.name}: generating seeded inputs")
     inp = moe_synth.make_inputs(sh)
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter

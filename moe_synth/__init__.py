@@ -82,7 +82,7 @@ class MoEShape:
 # The five named workloads.  Sizes follow the problem statement of the
 # MegaMoESymmBuffer page (hidden, intermediate_hidden, num_experts, num_topk)
 # at the shapes of common MoE layers.
-CONFIGS = {
+WORKLOADS = {
     "tiny_fp8": MoEShape("tiny_fp8", 1, 64, 256, 128, 8, 2, FP8_BLOCK128, PRECOMPUTED),
     "decode_fp8": MoEShape("decode_fp8", 2, 256, 7168, 2048, 32, 8, FP8_BLOCK128, PRECOMPUTED),
     "prefill_fp8_zipf": MoEShape("prefill_fp8_zipf", 3, 8192, 7168, 2048, 32, 8, FP8_BLOCK128,
@@ -93,7 +93,7 @@ CONFIGS = {
 CONFIG_ORDER = ["tiny_fp8", "decode_fp8", "prefill_fp8_zipf", "mixtral_bf16", "w4a8_mx_logits"]
 # The NVFP4 weight x BF16 activation variant at the decode shape (not one of the
 # five named workloads).
-CONFIGS["nvfp4_decode"] = MoEShape("nvfp4_decode", 6, 256, 7168, 2048, 32, 8, NVFP4_W4A16, PRECOMPUTED)
+WORKLOADS["nvfp4_decode"] = MoEShape("nvfp4_decode", 6, 256, 7168, 2048, 32, 8, NVFP4_W4A16, PRECOMPUTED)
 
 
 def _rng(seed: int, stream: int, expert: int = 0) -> np.random.Generator:

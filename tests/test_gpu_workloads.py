@@ -45,7 +45,7 @@ def _gather_intermediate(moe, d, T, rows):
 
 @pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER + ["nvfp4_decode"])
 def test_named_workload_full_size(name):
-    sh = moe_synth.CONFIGS[name]
+    sh = moe_synth.WORKLOADS[name]
     print(f"[fullsize] {name}: generating inputs", flush=True)
     inp = moe_synth.make_inputs(sh)
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter

@@ -3,11 +3,11 @@ each named workload is meant to have (CPU only)."""
 import numpy as np
 
 import moe_synth
-from moe_synth import CONFIGS
+from moe_synth import WORKLOADS
 
 
 def test_deterministic_and_shaped():
-    sh = CONFIGS["tiny_fp8"]
+    sh = WORKLOADS["tiny_fp8"]
     a = moe_synth.make_inputs(sh)
     b = moe_synth.make_inputs(sh)
     for key in ("x", "x_sf", "w13", "w13_sf", "w2", "w2_sf", "topk_idx", "topk_weights", "logits"):
@@ -20,7 +20,7 @@ def test_deterministic_and_shaped():
 
 
 def test_mx_shapes():
-    sh = CONFIGS["w4a8_mx_logits"].with_(tokens=8, experts=2)
+    sh = WORKLOADS["w4a8_mx_logits"].with_(tokens=8, experts=2)
     a = moe_synth.make_inputs(sh)
     assert a["x"].shape == (8, 2880) and a["x_sf"].shape == (8, 90) and a["x_sf"].dtype == np.uint8
     assert a["w13"].shape == (2, 5760, 1440) and a["w13_sf"].shape == (2, 5760, 90)
@@ -29,7 +29,7 @@ def test_mx_shapes():
 
 
 def test_prefill_zipf_load_is_skewed():
-    sh = CONFIGS["prefill_fp8_zipf"]
+    sh = WORKLOADS["prefill_fp8_zipf"]
     a = moe_synth.make_inputs(sh, with_weights=False)
     counts = np.bincount(a["topk_idx"].reshape(-1), minlength=sh.experts)
     mean = sh.pairs / sh.experts
@@ -38,7 +38,7 @@ def test_prefill_zipf_load_is_skewed():
 
 
 def test_decode_load_is_uniform():
-    sh = CONFIGS["decode_fp8"]
+    sh = WORKLOADS["decode_fp8"]
     a = moe_synth.make_inputs(sh, with_weights=False)
     counts = np.bincount(a["topk_idx"].reshape(-1), minlength=sh.experts)
     assert counts.min() > 0 and counts.max() < 2 * sh.pairs / sh.experts
@@ -46,7 +46,7 @@ def test_decode_load_is_uniform():
 
 def test_nvfp4_shapes_and_quantisation_error():
     from oracle import dequant_nvfp4
-    sh = moe_synth.CONFIGS["nvfp4_decode"].with_(tokens=16, hidden=256, inter=128, experts=3, topk=2)
+    sh = moe_synth.WORKLOADS["nvfp4_decode"].with_(tokens=16, hidden=256, inter=128, experts=3, topk=2)
     inp = moe_synth.make_inputs(sh)
     assert inp["x"].dtype == np.uint16 and inp["x_sf"] is None
     assert inp["w13"].shape == (3, 256, 128) and inp["w13_sf"].shape == (3, 256, 16)
