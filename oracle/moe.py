@@ -145,18 +145,36 @@ def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int, w13_gs=None, w
 
 
 # ------------------------------------------------------------------ routing
+def _nan_as_neg_inf(v: np.ndarray) -> np.ndarray:
+    """A NaN router logit (or NaN ranking key) reads as -inf: it ranks below every
+    number, and inside the softmax over the selected logits its term exp(-inf - m)
+    is 0, so a NaN expert that is selected (k larger than the token's non-NaN
+    logits) gets weight 0.  If every selected logit is -inf the softmax is 0/0 and
+    the weights are NaN."""
+    return np.where(np.isnan(v), -np.inf, v).astype(v.dtype)
+
+
 def _selection_keys(lg: np.ndarray, bias) -> np.ndarray:
     """Ranking keys of FromLogits routing: the logits, plus the per-expert
-    routing_bias of bias-aware methods when given (an fp32 sum, as the kernel
-    forms it); NaN ranks lowest."""
+    routing_bias of bias-aware methods when given (the sum is formed in fp32,
+    the logits' precision); NaN ranks lowest."""
     key = lg if bias is None else (lg + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
-    return np.where(np.isnan(key), np.float32(-np.inf), key)
+    return _nan_as_neg_inf(key)
+
+
+def _softmax_selected(sel: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis of the selected logits in float64, NaN read as -inf."""
+    sel = _nan_as_neg_inf(np.asarray(sel, dtype=np.float64))
+    with np.errstate(invalid="ignore"):
+        ex = np.exp(sel - sel.max(axis=-1, keepdims=True))
+        return ex / ex.sum(axis=-1, keepdims=True)
 
 
 def route_from_logits(logits: np.ndarray, k: int, bias=None):
     """FromLogits routing (MoEActivationPack page, routing_input_mode): per token
     the k experts with the largest logit, ties to the lower expert index, in that
-    order; weights are a softmax over the k selected logits (float64).  With a
+    order; weights are a softmax over the k selected logits (float64), a NaN
+    logit reading as -inf in both steps.  With a
     routing_bias (bias-aware methods on the same page) the experts are ranked by
     logit + bias, and the weights still come from the unbiased logits."""
     lg = np.asarray(logits, dtype=np.float32)
@@ -174,10 +192,8 @@ def route_from_logits(logits: np.ndarray, k: int, bias=None):
                 if best < 0 or key[t, e] > key[t, best]:
                     best = e
             chosen.append(best)
-        sel = lg[t, chosen].astype(np.float64)
-        ex = np.exp(sel - sel.max())
         idx[t] = chosen
-        w[t] = ex / ex.sum()
+        w[t] = _softmax_selected(lg[t, chosen])
     return idx, w
 
 
@@ -185,9 +201,7 @@ def route_from_logits_fast(logits: np.ndarray, k: int, bias=None):
     """Same selection as ``route_from_logits`` through a stable sort (for large T)."""
     lg = np.asarray(logits, dtype=np.float32)
     order = np.argsort(-_selection_keys(lg, bias), axis=1, kind="stable")[:, :k]
-    sel = np.take_along_axis(lg, order, axis=1).astype(np.float64)
-    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
-    return order.astype(np.int64), ex / ex.sum(axis=1, keepdims=True)
+    return order.astype(np.int64), _softmax_selected(np.take_along_axis(lg, order, axis=1))
 
 
 def build_plan(topk_idx: np.ndarray, num_experts: int) -> dict:

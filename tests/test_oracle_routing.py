@@ -139,3 +139,36 @@ def test_plan_exhaustive_tiny():
     for combo in itertools.product([-1, 0, 1, 2], repeat=4):
         ids = np.array(combo).reshape(2, 2)
         _check_plan_invariants(ids, 3, build_plan(ids, 3))
+
+
+def test_nan_logit_ranks_last_and_gets_weight_zero():
+    # MoEActivationPack page, routing_input_mode FromLogits; the pages say nothing of
+    # NaN logits.  Reading: a NaN logit is -inf, for the ranking and in the softmax.
+    # Token 0 has two real logits and k = 3, so one NaN expert is selected (the lower
+    # index among the tied -inf keys) and its weight is exp(-inf) / sum = 0.
+    nan = np.float32("nan")
+    lg = np.array([[nan, 1, 2, nan], [0.5, nan, -1, 3]], dtype=np.float32)
+    e1, e2 = np.exp(1.0), np.exp(2.0)
+    for fn in (route_from_logits, route_from_logits_fast):
+        idx, w = fn(lg, 3)
+        assert idx.tolist() == [[2, 1, 0], [3, 0, 2]]
+        assert np.allclose(w[0], [e2 / (e1 + e2), e1 / (e1 + e2), 0.0], rtol=0, atol=1e-15)
+        assert w[0, 2] == 0.0
+        ex = np.exp(np.array([3.0, 0.5, -1.0]))
+        assert np.allclose(w[1], ex / ex.sum(), rtol=0, atol=1e-15)
+
+
+def test_nan_logit_with_bias_and_all_nan_row():
+    nan = np.float32("nan")
+    # a bias cannot lift a NaN logit: logit + bias is NaN, which ranks last
+    lg = np.array([[nan, 0, 1]], dtype=np.float32)
+    bias = np.array([100, 0, 0], dtype=np.float32)
+    for fn in (route_from_logits, route_from_logits_fast):
+        idx, w = fn(lg, 2, bias)
+        assert idx.tolist() == [[2, 1]]
+        assert np.allclose(w[0], [np.exp(1) / (np.exp(1) + 1), 1 / (np.exp(1) + 1)], rtol=0, atol=1e-15)
+    # every selected logit -inf: ids by index, the softmax is 0/0 (NaN weights)
+    for fn in (route_from_logits, route_from_logits_fast):
+        idx, w = fn(np.full((1, 4), nan, np.float32), 2)
+        assert idx.tolist() == [[0, 1]]
+        assert np.isnan(w).all()
