@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the routed MoE expert-FFN path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_fp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_fp8_zipf]
 
 One step is one pass of the whole path over one batch of synthetic, seeded
 inputs already resident in HBM (weights in the prepared layout, written once by
@@ -10,11 +10,22 @@ workload routes from logits), gate_up grouped GEMM with the fused clamped
 SwiGLU and requantisation, down grouped GEMM, router-weighted combine — the
 same kernels moe_forward launches, called through the C ABI's stage entry
 points so that the two GEMM launches can carry HIP timing events (the timed
-variants of the leg entry points) on the stream they run on.  K steps run back to back between two device synchronisations.
+variants of the leg entry points) on the stream they run on.
+
+The timed workload (default: the prefill shape, T = 8192, the largest one-GPU
+configuration) runs W warm-up steps, then exactly K steps back to back between
+two device synchronisations: `value` is T * K / that wall time.  An event pair
+around each step gives the median and minimum step time.  A weight-bound
+workload rewrites a 512 MB scrub buffer before each step, outside the step's
+events, so that no weight byte stays in the memory-side cache between steps.
+
+The weight-bound decode shape is measured beside it in the same run (the
+`decode` object): its own W warm-up steps, K steps back to back, then K steps
+with the scrub between them (median and minimum).
 
 Prints one JSON line with tokens/s, the dominant kernel's roofline fraction
-(from its live HIP-event duration) and the CPU oracle timed on a bounded sample
-of the same workload.
+(from its live HIP-event duration), whole-step roofline fractions, and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -145,15 +156,165 @@ def write_counters(workload: str, fetch_dir: str, write_dir: str, command: str) 
     return 0
 
 
+class Leg:
+    """The step's kernels on one workload: inputs resident in HBM, weights in the
+    prepared layout (written once, untimed), caller-owned plan, intermediate and y."""
+
+    def __init__(self, name: str):
+        import numpy as np
+        import torch
+
+        import moe_synth
+        from mixture_experts_ffn_topk_amd import MoEFFN
+
+        sh = moe_synth.WORKLOADS[name]
+        log(f"workload {sh.name}: generating seeded inputs")
+        inp = moe_synth.make_inputs(sh)
+        T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter
+
+        def dev(a):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).cuda()
+
+        self.sh, self.inp = sh, inp
+        self.x, self.x_sf = dev(inp["x"]), dev(inp["x_sf"])
+        canonical = {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]), "w2": dev(inp["w2"]),
+                     "w2_sf": dev(inp["w2_sf"]), "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs"))}
+        self.logits = dev(inp["logits"])
+        if sh.routing == "precomputed":
+            self.topk_idx, self.topk_w = dev(inp["topk_idx"]), dev(inp["topk_weights"])
+        else:
+            self.topk_idx = torch.empty((T, k), dtype=torch.int64, device="cuda")
+            self.topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        self.moe = MoEFFN(H, I, E, k, T, fmt=sh.fmt, route_mode=sh.routing, activation_clamp=sh.clamp)
+        # one-time weight relayout (the pages' pre-permuted weights); outside every timed region
+        self.weights = self.moe.prepare_weights(canonical)
+        torch.cuda.synchronize()
+        del canonical
+        self.plan = self.moe.alloc_plan(T)
+        self.ws = self.moe.alloc_workspace(T)
+        self.h, self.hsf = self.moe.alloc_intermediate(T)
+        self.y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, legs=None):
+        """One pass of the whole path.  legs: optional 4 events (gate_up start/stop,
+        down start/stop) that the two GEMM launches carry themselves."""
+        m, T, s = self.moe, self.sh.tokens, self.stream
+        if self.sh.routing == "precomputed":
+            m.plan(T, self.plan, topk_idx=self.topk_idx, ws=self.ws, stream=s)
+        else:
+            m.plan(T, self.plan, routing_logits=self.logits, topk_idx_out=self.topk_idx, topk_weights_out=self.topk_w,
+                   ws=self.ws, stream=s)
+        m.ffn_gate_up(T, self.x, self.x_sf, self.weights, self.plan, self.h, self.hsf, stream=s,
+                      events=None if legs is None else legs[:2])
+        m.ffn_down(T, self.h, self.hsf, self.weights, self.plan, self.y, stream=s,
+                   events=None if legs is None else legs[2:])
+        m.combine(T, self.y, self.topk_w, self.plan, self.out, stream=s)
+
+    def counts(self):
+        c = self.plan["expert_counts"].cpu().numpy()
+        return int((c > 0).sum()), int(c.sum())
+
+    def algorithmic(self):
+        """(gate_up bytes, down bytes, whole-step bytes, gate_up flops, down flops) of one step."""
+        sh = self.sh
+        active, pairs = self.counts()
+        wb_gu, wb_dn = weight_bytes_per_expert(sh)
+        gu_bytes = active * wb_gu + act_bytes(sh)
+        dn_bytes = active * wb_dn
+        step_bytes = active * (wb_gu + wb_dn) + act_bytes(sh) + sh.tokens * sh.hidden * 2 + sh.tokens * sh.topk * 8
+        return gu_bytes, dn_bytes, step_bytes, 4.0 * pairs * sh.hidden * sh.inter, 2.0 * pairs * sh.hidden * sh.inter
+
+
+def _events(n):
+    """n timing events, each recorded once so that torch creates its HIP event."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()
+    return ev
+
+
+def timed_steps(leg: Leg, steps: int, step_markers: bool, scrub=None):
+    """`steps` steps between two device synchronisations.  The two GEMM launches of
+    every (steps/10)-th step carry timing events.  step_markers: an event pair around
+    every step (median and minimum step time).  scrub: a buffer rewritten before each
+    step, outside the step's events, so that no weight byte is still cached from the
+    previous step.  Returns (elapsed s, per-step ms list or None, gate_up ms, down ms)."""
+    import numpy as np
+    import torch
+    stride = max(1, steps // 10)
+    legs = {i: _events(4) for i in range(0, steps, stride)}
+    marks = [_events(2) for _ in range(steps)] if step_markers else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if scrub is not None:
+            torch.add(scrub, 1, out=scrub)
+        if marks:
+            marks[i][0].record(leg.stream)
+        leg.step(legs.get(i))
+        if marks:
+            marks[i][1].record(leg.stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in marks] if marks else None
+    gu = float(np.mean([e[0].elapsed_time(e[1]) for e in legs.values()]))
+    dn = float(np.mean([e[2].elapsed_time(e[3]) for e in legs.values()]))
+    return elapsed, per, gu, dn
+
+
+def roofline(leg: Leg, gate_ms: float, down_ms: float) -> dict:
+    """The dominant kernel (the gate_up GEMM) against its binding roof; the down leg beside it."""
+    sh = leg.sh
+    gu_bytes, dn_bytes, _, gu_flops, dn_flops = leg.algorithmic()
+    peak_f = PEAK_TFLOPS[sh.fmt]
+    t_mem, t_mma = gu_bytes / (PEAK_HBM_GBS * 1e9), gu_flops / (peak_f * 1e12)
+    bound = "hbm" if t_mem >= t_mma else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = gu_bytes / (gate_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = gu_flops / (gate_ms * 1e-3) / 1e12, peak_f, "TFLOP/s"
+    traffic = None
+    if os.path.exists(COUNTERS):
+        try:
+            c = json.load(open(COUNTERS))
+            if c.get("workload") == sh.name and c.get("kernel_source_sha") == kernel_source_hash():
+                traffic = c["traffic_bytes_per_launch"]
+        except Exception:
+            traffic = None
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": "ffn_gemm_kernel gate_up (FFN leg 1)",
+            "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops, "avg_launch_ms": round(gate_ms, 4),
+            "down_leg": {"avg_launch_ms": round(down_ms, 4),
+                         "hbm_frac": round(dn_bytes / (down_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "mfma_frac": round(dn_flops / (down_ms * 1e-3) / 1e12 / peak_f, 4)}}
+
+
+def step_fracs(leg: Leg, ms: float) -> dict:
+    """Whole-step roofline fractions at a step time of `ms`."""
+    _, _, step_bytes, gu_flops, dn_flops = leg.algorithmic()
+    return {"step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "step_mfma_frac": round((gu_flops + dn_flops) / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[leg.sh.fmt], 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the first few dozen steps after start-up run several percent slower (measured: the
-    # decode step 0.263 ms over steps 6-55, 0.246-0.248 ms from then on), so the
-    # default warm-up reaches the steady state
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode_fp8")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_fp8_zipf",
+                    help="the timed workload (default: the largest one-GPU configuration, the prefill shape)")
+    ap.add_argument("--decode-workload", default="decode_fp8",
+                    help="the weight-bound workload measured beside it (with a cache scrub); 'none' to skip")
+    ap.add_argument("--scrub-mb", type=int, default=512, help="cache scrub between the weight-bound steps (MB)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -174,86 +335,28 @@ def main() -> int:
     import numpy as np
     import torch
 
-    import moe_synth
-    from mixture_experts_ffn_topk_amd import MoEFFN
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    sh = moe_synth.WORKLOADS[args.workload]
-    log(f"workload {sh.name}: generating seeded inputs")
-    inp = moe_synth.make_inputs(sh)
+
+    leg = Leg(args.workload)
+    sh = leg.sh
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter
-
-    def dev(a):
-        if a is None:
-            return None
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            a = a.view(np.int16)
-        return torch.from_numpy(a).cuda()
-
-    x, x_sf = dev(inp["x"]), dev(inp["x_sf"])
-    weights = {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]), "w2": dev(inp["w2"]), "w2_sf": dev(inp["w2_sf"]),
-               "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs"))}
-    logits = dev(inp["logits"])
-    if sh.routing == "precomputed":
-        topk_idx, topk_w = dev(inp["topk_idx"]), dev(inp["topk_weights"])
-    else:
-        topk_idx = torch.empty((T, k), dtype=torch.int64, device="cuda")
-        topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    moe = MoEFFN(H, I, E, k, T, fmt=sh.fmt, route_mode=sh.routing, activation_clamp=sh.clamp)
-    # one-time weight relayout (the pages' pre-permuted weights); outside the timed region
-    canonical = weights
-    weights = moe.prepare_weights(canonical)
-    torch.cuda.synchronize()
-    del canonical
-    plan = moe.alloc_plan(T)
-    ws = moe.alloc_workspace(T)
-    h, hsf = moe.alloc_intermediate(T)
-    y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    # Per-kernel durations come from HIP events that the two GEMM legs' kernel
-    # launches carry themselves (moe_ffn_gate_up_timed / moe_ffn_down_timed), in a
-    # sample of the timed steps (every stride-th step): the events hold each
-    # kernel's own start and end, with no marker commands between the kernels.
-    # torch creates an event at its first record, done here, before the timing.
-    stride = max(1, args.steps // 10)
-    sampled = list(range(0, args.steps, stride))
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
-    for e4 in ev.values():
-        for e in e4:
-            e.record(stream)
-
-    def step(e=None):
-        if sh.routing == "precomputed":
-            moe.plan(T, plan, topk_idx=topk_idx, ws=ws, stream=stream)
-        else:
-            moe.plan(T, plan, routing_logits=logits, topk_idx_out=topk_idx, topk_weights_out=topk_w, ws=ws,
-                     stream=stream)
-        moe.ffn_gate_up(T, x, x_sf, weights, plan, h, hsf, stream=stream, events=None if e is None else e[:2])
-        moe.ffn_down(T, h, hsf, weights, plan, y, stream=stream, events=None if e is None else e[2:])
-        moe.combine(T, y, topk_w, plan, out, stream=stream)
+    scrub = torch.zeros(args.scrub_mb << 18, dtype=torch.float32, device="cuda") if args.scrub_mb > 0 else None
 
     log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
+    leg.step()  # (at least one step, so that the plan's counts exist)
+    for _ in range(args.warmup - 1):
+        leg.step()
     torch.cuda.synchronize()
-    counts = plan["expert_counts"].cpu().numpy()
-    active = int((counts > 0).sum())
-    pairs = int(counts.sum())
+    active, pairs = leg.counts()
+    weight_bound = roofline(leg, 1.0, 1.0)["bound"] == "hbm"
 
+    # The timed region: exactly `steps` steps back to back; an event pair around every
+    # step gives the median and minimum (the weight-bound shapes also rewrite the
+    # scrub buffer before each step, outside the step's events).
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev.get(i))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gate_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev.values()]))
-    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev.values()]))
+    elapsed, per, gate_ms, down_ms = timed_steps(leg, args.steps, True, scrub if weight_bound else None)
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -264,39 +367,9 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    # ---------------------------------------------------------------- roofline of the dominant kernel (gate_up)
-    wb_gu, wb_dn = weight_bytes_per_expert(sh)
-    gu_bytes = active * wb_gu + act_bytes(sh)
-    dn_bytes = active * wb_dn
-    gu_flops = 4.0 * pairs * H * I
-    dn_flops = 2.0 * pairs * H * I
-    peak_f = PEAK_TFLOPS[sh.fmt]
-    t_mem, t_mma = gu_bytes / (PEAK_HBM_GBS * 1e9), gu_flops / (peak_f * 1e12)
-    bound = "hbm" if t_mem >= t_mma else "mfma"
-    if bound == "hbm":
-        achieved, peak, unit = gu_bytes / (gate_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-    else:
-        achieved, peak, unit = gu_flops / (gate_ms * 1e-3) / 1e12, peak_f, "TFLOP/s"
-    traffic = None
-    if os.path.exists(COUNTERS):
-        try:
-            c = json.load(open(COUNTERS))
-            if c.get("workload") == sh.name and c.get("kernel_source_sha") == kernel_source_hash():
-                traffic = c["traffic_bytes_per_launch"]
-        except Exception:
-            traffic = None
-    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": "ffn_gemm_kernel gate_up (FFN leg 1)",
-                "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops, "avg_launch_ms": round(gate_ms, 4),
-                "event_timed_steps": len(ev),
-                "down_leg": {"avg_launch_ms": round(down_ms, 4),
-                             "hbm_frac": round(dn_bytes / (down_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "mfma_frac": round(dn_flops / (down_ms * 1e-3) / 1e12 / peak_f, 4)}}
-
     ms_per_step = elapsed * 1e3 / args.steps
     tok_s = T * args.steps / elapsed
-    total_bytes = active * (wb_gu + wb_dn) + act_bytes(sh) + T * H * 2 + T * k * 8
+    _, _, step_bytes, gu_flops, dn_flops = leg.algorithmic()
     result = {
         "metric": "MoE FFN tokens/s + achieved TFLOP/s & HBM GB/s vs MI355X peak",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -305,15 +378,41 @@ def main() -> int:
         "config": {"workload": sh.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "topk": k,
                    "format": sh.fmt, "routing": sh.routing, "active_experts": active, "routed_pairs": pairs,
                    "parallelism": "single GPU"},
+        "step_ms_median": round(float(np.median(per)), 4), "step_ms_min": round(float(np.min(per)), 4),
         "step_tflops": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
-        "step_hbm_gbs": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": roofline,
+        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        **step_fracs(leg, ms_per_step),
+        "scrubbed": bool(weight_bound and scrub is not None),
+        "roofline": roofline(leg, gate_ms, down_ms),
     }
+
+    # The weight-bound decode shape beside it: its own warm-up, then the same number of
+    # steps back to back, then as many with the cache scrub between steps.
+    if args.decode_workload != "none" and args.decode_workload != args.workload:
+        dec = Leg(args.decode_workload)
+        for _ in range(max(1, args.warmup)):
+            dec.step()
+        el, _, gu, dn = timed_steps(dec, args.steps, False)
+        _, per_s, gu_s, dn_s = timed_steps(dec, args.steps, True, scrub)
+        ms_b2b = el * 1e3 / args.steps
+        med = float(np.median(per_s))
+        result["decode"] = {
+            "workload": dec.sh.name, "tokens": dec.sh.tokens, "ms_per_step": round(ms_b2b, 4),
+            "tokens_per_s": round(dec.sh.tokens / (ms_b2b * 1e-3), 1), **step_fracs(dec, ms_b2b),
+            "scrubbed": {"scrub_mb": args.scrub_mb, "step_ms_median": round(med, 4),
+                         "step_ms_min": round(float(np.min(per_s)), 4),
+                         "step_hbm_frac_median": step_fracs(dec, med)["step_hbm_frac"],
+                         "gate_up": roofline(dec, gu_s, dn_s)},
+            "roofline": roofline(dec, gu, dn)}
+        for r in (result["decode"]["roofline"], result["decode"]["scrubbed"]["gate_up"]):
+            r.pop("algorithmic_flops", None)
+        del dec
+
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
-        ids = inp["topk_idx"] if sh.routing == "precomputed" else topk_idx.cpu().numpy()
-        w = inp["topk_weights"] if sh.routing == "precomputed" else topk_w.cpu().numpy()
-        result["cpu_baseline"] = cpu_baseline(sh, inp, ids, w, args.cpu_budget)
+        ids = leg.inp["topk_idx"] if sh.routing == "precomputed" else leg.topk_idx.cpu().numpy()
+        w = leg.inp["topk_weights"] if sh.routing == "precomputed" else leg.topk_w.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(sh, leg.inp, ids, w, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -29,6 +29,9 @@
  *     sequence of calls can be captured into a HIP graph.
  *   - Arguments are validated on the host before anything is launched; a
  *     failed validation launches nothing and returns a status != MOE_OK.
+ *   - Alignment: activation, intermediate, y and output buffers (x, h, y, out,
+ *     shared, residual) 16 bytes; scale buffers 4 bytes; workspaces 256 bytes.
+ *     A misaligned pointer is MOE_ERR_INVALID_ARGUMENT.
  *   - Data errors found on the device (an expert id outside [0, E) that is not
  *     -1) never trap: that slot is treated as masked and counted in
  *     plan->status[0].
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 5
+#define MOE_FFN_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -104,6 +107,9 @@ typedef struct moe_config {
   int32_t topk_idx_bits;        /* 64 (INT64 ids, [SymmBuffer]) or 32 (int32 ids, [ActPack]) */
   int32_t fast_math;            /* 1: hardware exp/reciprocal in SiLU and softmax ([SymmBuffer]) */
   int32_t tile_regime;          /* moe_tile_regime */
+  int32_t out_fp32;             /* dtype of the combine output ([EPConfig] combine_dtype and the
+                                   mega_ffn combine_dtype parameter leave it open): 0 = bf16
+                                   [T,H] (one rounding of the fp32 sum), 1 = fp32 [T,H] */
 } moe_config;
 
 /* (host struct of device pointers) Expert weights of this GPU: the canonical
@@ -146,6 +152,10 @@ typedef struct moe_prepared_sizes {
    intermediate_hidden (intermediate) or one expert's gate_up weight reaches
    2^31 bytes. */
 moe_status moe_create(const moe_config* cfg /* host */, moe_handle** out /* host */);
+/* Release the host handle ([SymmBuffer] destroy(): release what the object
+   holds).  The handle owns no device memory, so nothing on the device is freed
+   and no stream is touched; NULL is a no-op.  The caller must not pass the
+   handle to any call afterwards. */
 void moe_destroy(moe_handle* h);
 
 /* Prepared weight layout ([MegaFFN] takes its gate_up weight pre-permuted; here
@@ -182,8 +192,10 @@ moe_status moe_prepare_weights(const moe_handle* h, const moe_weights* canonical
                                const moe_weights* prepared /* host struct */, hipStream_t stream);
 
 /* Bytes of workspace moe_plan / moe_ffn / moe_forward need for num_tokens tokens
-   (0 if num_tokens is out of range).  The workspace is caller-owned device memory,
-   256-byte aligned; one workspace per concurrently running stream. */
+   ([EPConfig] estimate_memory_usage(): the bytes a configuration needs per device,
+   known before anything runs), 0 if num_tokens is out of range.  The workspace
+   is caller-owned device memory, 256-byte aligned (a misaligned workspace is
+   MOE_ERR_INVALID_ARGUMENT); one workspace per concurrently running stream. */
 size_t moe_workspace_size(const moe_handle* h, int32_t num_tokens);
 
 /* Routing plan ([MegaFFN] expert_start_indices, expert_ids, num_active_experts,
@@ -248,7 +260,8 @@ moe_status moe_ffn_down_timed(const moe_handle* h, int32_t num_tokens, const voi
 
 /* Router-weighted combine ([EPCombine] router_weights): out[t] = sum over valid
    slots j in ascending order of topk_weights[t,j] * y[t,j,:], accumulated in
-   fp32, written as bf16 [T,H].  A token with no valid slot gets zeros. */
+   fp32, written as bf16 [T,H] (fp32 [T,H] when moe_config.out_fp32).  A token with
+   no valid slot gets zeros. */
 moe_status moe_combine(const moe_handle* h, int32_t num_tokens, const void* y, const float* topk_weights,
                        const moe_plan_buffers* plan /* host struct */, void* out, hipStream_t stream);
 

@@ -38,7 +38,7 @@ class _Config(ctypes.Structure):
                 ("max_num_tokens", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
                 ("format", ctypes.c_int32), ("route_mode", ctypes.c_int32),
                 ("topk_idx_bits", ctypes.c_int32), ("fast_math", ctypes.c_int32),
-                ("tile_regime", ctypes.c_int32)]
+                ("tile_regime", ctypes.c_int32), ("out_fp32", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -146,21 +146,56 @@ def _check(st: int, what: str):
         raise MoEError(st, what)
 
 
+def _need(t, what: str, nbytes: int, dtypes=None, elem: int | None = None, required: bool = True):
+    """Check a tensor argument before its address crosses the C ABI, which cannot:
+    of an allowed dtype (or element size), contiguous, and holding at least
+    `nbytes` (its device is checked by _on_gpu).  A raw device address (int) is
+    passed through unchecked."""
+    if t is None:
+        if required and nbytes > 0:
+            raise ValueError(f"{what} is required")
+        return
+    if isinstance(t, int):
+        return
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{what} must have dtype {' or '.join(str(d) for d in dtypes)} (got {t.dtype})")
+    if elem is not None and t.element_size() != elem:
+        raise TypeError(f"{what} must have {elem}-byte elements (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes; {nbytes} are needed")
+
+
+def _on_gpu(**tensors):
+    """Every tensor given (None and raw addresses aside) lives on the GPU; checked
+    after the dtype and size checks of the same call."""
+    for what, t in tensors.items():
+        if isinstance(t, dict):
+            _on_gpu(**{f"{what}['{k}']": v for k, v in t.items()})
+        elif t is not None and not isinstance(t, int) and t.device.type != "cuda":
+            raise ValueError(f"{what} must be a GPU tensor (got {t.device})")
+
+
 class MoEFFN:
     """One GPU's share of experts with a fixed geometry (moe_create / moe_destroy).
 
     Tensors are torch tensors on the GPU (or raw device addresses as ints); their
-    dtype and layout must match include/moe_ffn.h — the binding only forwards
-    pointers."""
+    dtype and layout must match include/moe_ffn.h.  The binding checks each tensor
+    it is given (device, contiguity, dtype where it decides how the kernels read
+    it, size in bytes) and forwards its address; raw addresses are forwarded as
+    they are."""
 
     def __init__(self, hidden: int, intermediate_hidden: int, num_experts: int, num_topk: int,
                  max_num_tokens: int, fmt: str = "fp8_block128", route_mode: str = "precomputed",
                  activation_clamp: float = 10.0, topk_idx_bits: int = 64, fast_math: bool = True,
-                 tile_regime: str = "auto"):
+                 tile_regime: str = "auto", out_fp32: bool = False):
         self.lib = load_library()
         self.cfg = _Config(hidden, intermediate_hidden, num_experts, num_topk, max_num_tokens,
                            float(activation_clamp), FORMATS[fmt], ROUTE_MODES[route_mode], topk_idx_bits,
-                           int(bool(fast_math)), TILE_REGIMES[tile_regime])
+                           int(bool(fast_math)), TILE_REGIMES[tile_regime], int(bool(out_fp32)))
+        self.out_fp32 = bool(out_fp32)
         self.fmt, self.route_mode = fmt, route_mode
         self.hidden, self.inter, self.experts, self.topk = hidden, intermediate_hidden, num_experts, num_topk
         self.max_num_tokens = max_num_tokens
@@ -179,6 +214,49 @@ class MoEFFN:
             self.close()
         except Exception:
             pass
+
+    # ---------------------------------------------------------------- argument checks
+    def _esz(self) -> int:
+        """Bytes per activation / intermediate element."""
+        return 2 if self.fmt in ("bf16", "nvfp4_w4a16") else 1
+
+    def _sf_row(self, n: int) -> int:
+        """Bytes of activation scales per row of n elements."""
+        return {"fp8_block128": n // 128 * 4, "w4a8_mx": n // 32}.get(self.fmt, 0)
+
+    def _idx_dtypes(self):
+        import torch
+        return (torch.int64,) if self.topk_idx_bits == 64 else (torch.int32,)
+
+    def _check_plan(self, plan: dict, T: int):
+        import torch
+        E, n = self.experts, T * self.topk
+        sizes = {"expert_counts": E, "expert_start_indices": E + 1, "expert_ids": E, "num_active_experts": 1,
+                 "src_info": n, "pair_row": n, "status": 1}
+        for f in PLAN_FIELDS:
+            _need(plan.get(f), f"plan['{f}']", 4 * sizes[f], (torch.int32,))
+
+    def _check_x(self, x, x_sf, T: int):
+        _need(x, "x", T * self.hidden * self._esz())
+        _need(x_sf, "x_sf", T * self._sf_row(self.hidden), required=self._sf_row(self.hidden) > 0)
+
+    def _check_weights(self, w: dict):
+        import torch
+        if not hasattr(self, "_psizes"):
+            self._psizes = self.prepared_weights_size()
+        for n, b in self._psizes.items():
+            _need(w.get(n), f"weights['{n}']", b, required=b > 0)
+        if self.fmt == "nvfp4_w4a16":
+            for g in ("w13_gs", "w2_gs"):
+                _need(w.get(g), f"weights['{g}']", 4 * self.experts, (torch.float32,))
+
+    def _check_routing_in(self, T: int, topk_idx, routing_logits, routing_bias):
+        import torch
+        if self.route_mode == "precomputed":
+            _need(topk_idx, "topk_idx", T * self.topk * self.topk_idx_bits // 8, self._idx_dtypes())
+        else:
+            _need(routing_logits, "routing_logits", T * self.experts * 4, (torch.float32,))
+            _need(routing_bias, "routing_bias", self.experts * 4, (torch.float32,), required=False)
 
     # ---------------------------------------------------------------- helpers (torch allocation)
     def workspace_size(self, num_tokens: int) -> int:
@@ -233,6 +311,16 @@ class MoEFFN:
     # ---------------------------------------------------------------- entry points
     def plan(self, num_tokens, plan: dict, topk_idx=None, routing_logits=None, topk_idx_out=None,
              topk_weights_out=None, ws=None, stream=None, routing_bias=None):
+        import torch
+        T = num_tokens
+        self._check_plan(plan, T)
+        self._check_routing_in(T, topk_idx, routing_logits, routing_bias)
+        if self.route_mode == "from_logits":
+            _need(topk_idx_out, "topk_idx_out", T * self.topk * self.topk_idx_bits // 8, self._idx_dtypes())
+            _need(topk_weights_out, "topk_weights_out", T * self.topk * 4, (torch.float32,))
+        _need(ws, "ws", 0, required=False)
+        _on_gpu(plan=plan, topk_idx=topk_idx, routing_logits=routing_logits, topk_idx_out=topk_idx_out,
+                topk_weights_out=topk_weights_out, ws=ws, routing_bias=routing_bias)
         ps = self._plan_struct(plan)
         if routing_bias is None:
             _check(self.lib.moe_plan(self._h, num_tokens, _ptr(topk_idx), _ptr(routing_logits), _ptr(topk_idx_out),
@@ -244,6 +332,13 @@ class MoEFFN:
                                         self._nbytes(ws), _stream(stream)), "moe_plan_ex")
 
     def ffn(self, num_tokens, x, x_sf, weights: dict, plan: dict, y, ws, stream=None):
+        T = num_tokens
+        self._check_x(x, x_sf, T)
+        self._check_weights(weights)
+        self._check_plan(plan, T)
+        _need(y, "y", T * self.topk * self.hidden * 2, elem=2)
+        _need(ws, "ws", 0, required=False)
+        _on_gpu(x=x, x_sf=x_sf, weights=weights, plan=plan, y=y, ws=ws)
         ws_ = self._weights_struct(weights)
         ps = self._plan_struct(plan)
         _check(self.lib.moe_ffn(self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps),
@@ -264,6 +359,13 @@ class MoEFFN:
         """events: optional (start, stop) torch.cuda.Event pair (timing enabled, already
         created by one record) that the GEMM kernel's own launch updates
         (moe_ffn_gate_up_timed)."""
+        T = num_tokens
+        self._check_x(x, x_sf, T)
+        self._check_weights(weights)
+        self._check_plan(plan, T)
+        _need(h, "h", T * self.topk * self.inter * self._esz())
+        _need(h_sf, "h_sf", T * self.topk * self._sf_row(self.inter), required=self._sf_row(self.inter) > 0)
+        _on_gpu(x=x, x_sf=x_sf, weights=weights, plan=plan, h=h, h_sf=h_sf)
         ws_ = self._weights_struct(weights)
         ps = self._plan_struct(plan)
         args = (self._h, num_tokens, _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps), _ptr(h), _ptr(h_sf),
@@ -275,6 +377,13 @@ class MoEFFN:
 
     def ffn_down(self, num_tokens, h, h_sf, weights: dict, plan: dict, y, stream=None, events=None):
         """events: as for ffn_gate_up (moe_ffn_down_timed)."""
+        T = num_tokens
+        _need(h, "h", T * self.topk * self.inter * self._esz())
+        _need(h_sf, "h_sf", T * self.topk * self._sf_row(self.inter), required=self._sf_row(self.inter) > 0)
+        self._check_weights(weights)
+        self._check_plan(plan, T)
+        _need(y, "y", T * self.topk * self.hidden * 2, elem=2)
+        _on_gpu(h=h, h_sf=h_sf, weights=weights, plan=plan, y=y)
         ws_ = self._weights_struct(weights)
         ps = self._plan_struct(plan)
         args = (self._h, num_tokens, _ptr(h), _ptr(h_sf), ctypes.byref(ws_), ctypes.byref(ps), _ptr(y),
@@ -284,7 +393,20 @@ class MoEFFN:
         else:
             _check(self.lib.moe_ffn_down_timed(*args, *_event_handles(events)), "moe_ffn_down_timed")
 
+    def _check_out(self, T, out, shared, residual):
+        _need(out, "out", T * self.hidden * (4 if self.out_fp32 else 2), elem=4 if self.out_fp32 else 2)
+        _need(shared, "shared", T * self.hidden * 2, elem=2, required=False)
+        _need(residual, "residual", T * self.hidden * 2, elem=2, required=False)
+
     def combine(self, num_tokens, y, topk_weights, plan: dict, out, stream=None, shared=None, residual=None):
+        import torch
+        T = num_tokens
+        _need(y, "y", T * self.topk * self.hidden * 2, elem=2)
+        _need(topk_weights, "topk_weights", T * self.topk * 4, (torch.float32,))
+        _need(plan.get("pair_row"), "plan['pair_row']", T * self.topk * 4, (torch.int32,))
+        self._check_out(T, out, shared, residual)
+        _on_gpu(y=y, topk_weights=topk_weights, pair_row=plan.get("pair_row"), out=out, shared=shared,
+                residual=residual)
         ps = self._plan_struct(plan)
         if shared is None and residual is None:
             _check(self.lib.moe_combine(self._h, num_tokens, _ptr(y), _ptr(topk_weights), ctypes.byref(ps), _ptr(out),
@@ -295,6 +417,18 @@ class MoEFFN:
 
     def forward(self, num_tokens, x, x_sf, topk_idx, topk_weights, routing_logits, weights: dict, out, ws,
                 stream=None, routing_bias=None, shared=None, residual=None):
+        import torch
+        T = num_tokens
+        self._check_x(x, x_sf, T)
+        self._check_weights(weights)
+        self._check_routing_in(T, topk_idx, routing_logits, routing_bias)
+        _need(topk_idx, "topk_idx", T * self.topk * self.topk_idx_bits // 8, self._idx_dtypes())
+        _need(topk_weights, "topk_weights", T * self.topk * 4, (torch.float32,))
+        self._check_out(T, out, shared, residual)
+        _need(ws, "ws", 0, required=False)
+        _on_gpu(x=x, x_sf=x_sf, weights=weights, topk_idx=topk_idx, topk_weights=topk_weights,
+                routing_logits=routing_logits, routing_bias=routing_bias, out=out, ws=ws, shared=shared,
+                residual=residual)
         ws_ = self._weights_struct(weights)
         if routing_bias is None and shared is None and residual is None:
             _check(self.lib.moe_forward(self._h, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),

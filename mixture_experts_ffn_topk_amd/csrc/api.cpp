@@ -85,6 +85,11 @@ int choose_bm(const moe_config& c, int T) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Alignment the kernels rely on: 16-byte vector loads and stores of activation,
+// intermediate and output rows, 4-byte scale loads, and the 256-byte workspace
+// carving.  A null pointer passes (presence is checked separately).
+bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const float* logits, const float* bias,
                    void* idx_out, float* w_out, const moe_plan_buffers* plan, void* scratch, hipStream_t s) {
   const moe_config& c = h->cfg;
@@ -188,6 +193,7 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
   if (c.topk_idx_bits != 32 && c.topk_idx_bits != 64) return MOE_ERR_INVALID_ARGUMENT;
   if (c.route_mode != MOE_ROUTE_PRECOMPUTED && c.route_mode != MOE_ROUTE_FROM_LOGITS) return MOE_ERR_INVALID_ARGUMENT;
   if (c.tile_regime < MOE_TILES_AUTO || c.tile_regime > MOE_TILES_PREFILL) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.out_fp32 != 0 && c.out_fp32 != 1) return MOE_ERR_INVALID_ARGUMENT;
   switch (c.format) {
     case MOE_FMT_FP8_BLOCK128:
       if (c.hidden % 128 || c.intermediate_hidden % 128) return MOE_ERR_INVALID_ARGUMENT;
@@ -267,6 +273,7 @@ moe_status moe_plan_ex(const moe_handle* h, int32_t T, const void* topk_idx_in, 
   }
   const size_t need = layout_for(c, T).plan_scratch_bytes;
   if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!al(ws, 256)) return MOE_ERR_INVALID_ARGUMENT;
   return do_plan(h, T, topk_idx_in, routing_logits, routing_bias, topk_idx_out, topk_weights_out, plan, ws, stream);
 }
 
@@ -281,6 +288,7 @@ moe_status moe_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_
                    const moe_plan_buffers* plan, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !y)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(x, 16) || !al(x_sf, 4) || !al(y, 16) || !al(ws, 256)) return MOE_ERR_INVALID_ARGUMENT;
   const size_t need = layout_for(h->cfg, T).ffn_bytes;
   if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (T == 0) return MOE_OK;
@@ -294,6 +302,7 @@ moe_status moe_ffn_gate_up_timed(const moe_handle* h, int32_t T, const void* x, 
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (!bf16_acts(h->cfg.format) && !h_sf_out)))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(x, 16) || !al(x_sf, 4) || !al(h_out, 16) || !al(h_sf_out, 4)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1, start, stop);
 }
@@ -308,6 +317,7 @@ moe_status moe_ffn_down_timed(const moe_handle* h, int32_t T, const void* h_in, 
                               hipEvent_t start, hipEvent_t stop) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!h_in || !y || (!bf16_acts(h->cfg.format) && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(h_in, 16) || !al(h_sf_in, 4) || !al(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2,
                 start, stop);
@@ -323,10 +333,9 @@ moe_status moe_combine_ex(const moe_handle* h, int32_t T, const void* y, const f
                           hipStream_t stream) {
   if (!valid_T(h, T) || !plan || !plan->pair_row) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!y || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
-  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
-  if (!aligned(shared) || !aligned(residual)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(y, 16) || !al(out, 16) || !al(shared, 16) || !al(residual, 16)) return MOE_ERR_INVALID_ARGUMENT;
   return hip_status(moe::launch_combine(y, topk_weights, plan->pair_row, T, h->cfg.num_topk, h->cfg.hidden, shared,
-                                        residual, out, stream));
+                                        residual, out, h->cfg.out_fp32 != 0, stream));
 }
 
 moe_status moe_combine(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
@@ -345,8 +354,8 @@ moe_status moe_forward_ex(const moe_handle* h, int32_t T, const void* x, const v
     if (c.route_mode == MOE_ROUTE_FROM_LOGITS && !routing_logits) return MOE_ERR_INVALID_ARGUMENT;
   }
   if (c.route_mode == MOE_ROUTE_PRECOMPUTED && routing_bias) return MOE_ERR_INVALID_ARGUMENT;
-  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
-  if (!aligned(shared) || !aligned(residual)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(x, 16) || !al(x_sf, 4) || !al(out, 16) || !al(shared, 16) || !al(residual, 16) || !al(ws, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout_for(c, T);
   if (ws_bytes < L.total || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
   char* base = (char*)ws;
@@ -359,8 +368,8 @@ moe_status moe_forward_ex(const moe_handle* h, int32_t T, const void* x, const v
   void* y = base + L.y;
   st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0);
   if (st != MOE_OK) return st;
-  return hip_status(
-      moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, shared, residual, out, stream));
+  return hip_status(moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, shared, residual, out,
+                                        c.out_fp32 != 0, stream));
 }
 
 moe_status moe_forward(const moe_handle* h, int32_t T, const void* x, const void* x_sf, void* topk_idx,

@@ -5,7 +5,9 @@
 // the fused_shared_expert option of the MAX mega_ffn / EP pages) and
 // + residual[t, :] (a downstream elementwise epilogue: has_epilogue_fusion).
 // HBM-bound gather-reduce: each thread owns 8 consecutive bf16 columns and reads
-// the k slot rows with 16-byte loads; fp32 accumulation; bf16 store.
+// the k slot rows with 16-byte loads; fp32 accumulation; one bf16 rounding at
+// the store, or an fp32 store (the combine dtype is a choice on the EPConfig and
+// DistributedEPCombine pages).
 #include "device.h"
 #include "launch.h"
 
@@ -14,12 +16,13 @@ namespace moe {
 constexpr int kCombineThreads = 256;
 constexpr int kCombineCols = kCombineThreads * 8;  // columns per workgroup
 
+template <bool OUT_F32>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                                   const float* __restrict__ w,
                                                                   const int* __restrict__ pair_row, int topk, int H,
                                                                   const uint16_t* __restrict__ shared,
                                                                   const uint16_t* __restrict__ residual,
-                                                                  uint16_t* __restrict__ out) {
+                                                                  void* __restrict__ out) {
   const int t = blockIdx.x;
   const int col = blockIdx.y * kCombineCols + threadIdx.x * 8;
   if (col >= H) return;
@@ -64,19 +67,29 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
       acc[2 * q + 1] += bf16_to_f32((uint16_t)(e >> 16));
     }
   }
-  i32x4 o;
+  if constexpr (OUT_F32) {
+    f32x4* o = (f32x4*)((float*)out + (long long)t * H + col);
+    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    i32x4 o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
-  *(i32x4*)(out + (long long)t * H + col) = o;
+    for (int q = 0; q < 4; ++q)
+      o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
+    *(i32x4*)((uint16_t*)out + (long long)t * H + col) = o;
+  }
 }
 
 hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H,
-                          const void* shared, const void* residual, void* out, hipStream_t s) {
+                          const void* shared, const void* residual, void* out, bool out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid(T, (H + kCombineCols - 1) / kCombineCols);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row, topk, H,
-                     (const uint16_t*)shared, (const uint16_t*)residual, (uint16_t*)out);
+  if (out_f32)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row, topk,
+                       H, (const uint16_t*)shared, (const uint16_t*)residual, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row,
+                       topk, H, (const uint16_t*)shared, (const uint16_t*)residual, out);
   return hipGetLastError();
 }
 

@@ -72,8 +72,8 @@ int ffn_max_m_tiles(int npairs, int E, int bm);
 // stage: 0 = both legs, 1 = gate_up only, 2 = down only
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage = 0);
 
-// shared, residual: bf16 [T,H] addends or nullptr
+// shared, residual: bf16 [T,H] addends or nullptr; out: bf16 [T,H], or fp32 when out_f32
 hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H,
-                          const void* shared, const void* residual, void* out, hipStream_t s);
+                          const void* shared, const void* residual, void* out, bool out_f32, hipStream_t s);
 
 }  // namespace moe

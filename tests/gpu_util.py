@@ -23,11 +23,11 @@ def geometry(shape) -> "oracle.Geometry":
     return oracle.Geometry(shape.hidden, shape.inter, shape.experts, shape.topk, shape.fmt, shape.clamp)
 
 
-def make_moe(shape, max_tokens=None, tile_regime="auto", topk_idx_bits=64, fast_math=True) -> MoEFFN:
+def make_moe(shape, max_tokens=None, tile_regime="auto", topk_idx_bits=64, fast_math=True, out_fp32=False) -> MoEFFN:
     return MoEFFN(shape.hidden, shape.inter, shape.experts, shape.topk,
                   max_tokens if max_tokens is not None else shape.tokens, fmt=shape.fmt,
                   route_mode=shape.routing, activation_clamp=shape.clamp, topk_idx_bits=topk_idx_bits,
-                  fast_math=fast_math, tile_regime=tile_regime)
+                  fast_math=fast_math, tile_regime=tile_regime, out_fp32=out_fp32)
 
 
 def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.int64) -> dict:
@@ -131,7 +131,8 @@ def run_split(moe: MoEFFN, d: dict, T: int):
 
 
 def compare_out(got: torch.Tensor, ref: np.ndarray, rel_l2=1e-2, max_rms=5e-2):
-    """FFN output tolerance: relative L2 <= 1e-2 and max-abs <= 5e-2 * RMS(ref)."""
+    """FFN output tolerance: relative L2 <= 1e-2 and max-abs <= 5e-2 * RMS(ref).
+    Returns (relative L2, max-abs / RMS)."""
     g = got.float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(g)), "non-finite output"
     diff = g - ref
@@ -260,5 +261,21 @@ def staged_check(shape, inp: dict, res: dict, ref_plan: dict, topk_idx, topk_wei
     w = np.asarray(topk_weights, dtype=np.float64)
     pr = ref_plan["pair_row"]
     compare_out(out_g, oracle.combine(y_ref2, w, pr, H))
-    compare_out(out_g, oracle.combine(y_ref, w, pr, H), rel_l2=1e-2, max_rms=np.inf)
     return flips
+
+
+def check_against_oracle(shape, inp, out, ref, res, ids, w, name):
+    """The output contract against the pure oracle: relative L2 <= 1e-2 always, and
+    max-abs <= 5e-2 * RMS unless the GPU's requantised intermediate took the other
+    rounding at a tie somewhere (a code whose exact value lies within 2e-4 of its
+    block maximum from a rounding midpoint, so both codes are correct roundings): then
+    the max-abs bound must hold against the oracle that takes the GPU's rounding at
+    those ties, and every differing code must be such a tie (staged_check).  With a
+    small intermediate width one tie flip moves an output by a few percent of its
+    RMS, so the bound cannot hold outright at every small shape."""
+    rl2, mr = compare_out(out, ref["out"], max_rms=np.inf)
+    flips = staged_check(shape, inp, res, ref["plan"], ids, w)
+    print(f"[parity] {name}: rel-L2 {rl2:.2e}, max-abs/RMS {mr:.2e} against the pure oracle, "
+          f"{flips} rounding-tie flips", flush=True)
+    assert mr <= 5e-2 or flips > 0, f"max abs {mr:.3e} * RMS without any rounding-tie flip"
+    return rl2, mr, flips

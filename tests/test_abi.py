@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -105,9 +105,9 @@ def test_workspace_size_and_host_validation():
     assert lib.moe_plan(h, 10, None, None, None, None, ctypes.byref(plan), None, 0, None) == 1   # null plan bufs
     w = mx._Weights(None, None, None, None)
     assert lib.moe_forward(h, 10, None, None, None, None, None, ctypes.byref(w), None, None, 0, None) == 1
-    w = mx._Weights(1, 1, 1, 1)
-    assert lib.moe_forward(h, 10, 1, 1, 1, 1, None, ctypes.byref(w), 1, 1, 16, None) == 3  # workspace too small
-    assert lib.moe_forward(h, 10, 1, None, 1, 1, None, ctypes.byref(w), 1, 1, ws, None) == 1  # FP8 needs x_sf
+    w = mx._Weights(256, 256, 256, 256)
+    assert lib.moe_forward(h, 10, 256, 256, 256, 256, None, ctypes.byref(w), 256, 256, 16, None) == 3  # ws too small
+    assert lib.moe_forward(h, 10, 256, None, 256, 256, None, ctypes.byref(w), 256, 256, ws, None) == 1  # needs x_sf
     assert lib.moe_combine(h, 10, None, None, ctypes.byref(plan), None, None) == 1
     lib.moe_destroy(h)
 
@@ -184,3 +184,79 @@ def test_prepared_weight_sizes_and_validation():
 def test_binding_raises_on_bad_config():
     with pytest.raises(mx.MoEError):
         mx.MoEFFN(7168 + 64, 2048, 32, 8, 256)
+
+
+def test_misaligned_buffers_are_rejected_before_any_launch():
+    """The kernels move activation, intermediate, y and output rows in 16-byte
+    vectors, scales in 4-byte words, and carve the workspace at 256 bytes: a
+    pointer off those alignments is MOE_ERR_INVALID_ARGUMENT (fake addresses;
+    nothing is launched)."""
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg()), ctypes.byref(h)) == 0
+    A = 1 << 20  # an aligned fake address
+    plan = mx._Plan(*([A] * 7))
+    w = mx._Weights(A, A, A, A)
+    big = 1 << 40
+    # combine: y, out
+    assert lib.moe_combine(h, 10, A + 8, A, ctypes.byref(plan), A, None) == 1
+    assert lib.moe_combine(h, 10, A, A, ctypes.byref(plan), A + 2, None) == 1
+    # ffn: x, x_sf, y, workspace
+    assert lib.moe_ffn(h, 10, A + 4, A, ctypes.byref(w), ctypes.byref(plan), A, A, big, None) == 1
+    assert lib.moe_ffn(h, 10, A, A + 2, ctypes.byref(w), ctypes.byref(plan), A, A, big, None) == 1
+    assert lib.moe_ffn(h, 10, A, A, ctypes.byref(w), ctypes.byref(plan), A + 8, A, big, None) == 1
+    assert lib.moe_ffn(h, 10, A, A, ctypes.byref(w), ctypes.byref(plan), A, A + 128, big, None) == 1
+    # legs: h, h_sf
+    assert lib.moe_ffn_gate_up(h, 10, A, A, ctypes.byref(w), ctypes.byref(plan), A + 8, A, None) == 1
+    assert lib.moe_ffn_gate_up(h, 10, A, A, ctypes.byref(w), ctypes.byref(plan), A, A + 1, None) == 1
+    assert lib.moe_ffn_down(h, 10, A + 8, A, ctypes.byref(w), ctypes.byref(plan), A, None) == 1
+    assert lib.moe_ffn_down(h, 10, A, A, ctypes.byref(w), ctypes.byref(plan), A + 8, None) == 1
+    # plan and forward workspaces
+    assert lib.moe_plan(h, 10, A, None, None, None, ctypes.byref(plan), A + 64, big, None) == 1
+    assert lib.moe_forward(h, 10, A, A, A, A, None, ctypes.byref(w), A, A + 16, big, None) == 1
+    assert lib.moe_forward(h, 10, A, A, A, A, None, ctypes.byref(w), A + 8, A, big, None) == 1  # out
+    lib.moe_destroy(h)
+
+
+def test_out_fp32_config_is_validated():
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(out_fp32=1)), ctypes.byref(h)) == 0
+    lib.moe_destroy(h)
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(out_fp32=2)), ctypes.byref(h)) == 1
+
+
+def test_binding_checks_tensors_before_the_call():
+    """The binding refuses, before any address crosses the C ABI: an id tensor of the
+    wrong width for topk_idx_bits (the plan kernels would read past it), weights of
+    the wrong dtype, buffers that are too small, non-contiguous views, and host
+    tensors."""
+    import torch
+    moe = mx.MoEFFN(256, 128, 8, 2, 64)  # FP8, 64-bit ids
+    plan = {f: torch.zeros(n, dtype=torch.int32) for f, n in
+            (("expert_counts", 8), ("expert_start_indices", 9), ("expert_ids", 8), ("num_active_experts", 1),
+             ("src_info", 128), ("pair_row", 128), ("status", 1))}
+    with pytest.raises(TypeError, match="topk_idx"):
+        moe.plan(64, plan, topk_idx=torch.zeros((64, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match="topk_idx holds"):
+        moe.plan(64, plan, topk_idx=torch.zeros((32, 2), dtype=torch.int64))
+    with pytest.raises(ValueError, match="contiguous"):
+        moe.plan(64, plan, topk_idx=torch.zeros((2, 64), dtype=torch.int64).t())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.plan(64, plan, topk_idx=torch.zeros((64, 2), dtype=torch.int64))
+    bad_plan = dict(plan, src_info=torch.zeros(128, dtype=torch.int64))
+    with pytest.raises(TypeError, match="src_info"):
+        moe.plan(64, bad_plan, topk_idx=torch.zeros((64, 2), dtype=torch.int64))
+    y = torch.zeros((128, 256), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="topk_weights"):
+        moe.combine(64, y, torch.zeros((64, 2), dtype=torch.float64), plan, torch.zeros((64, 256), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="out"):
+        moe.combine(64, y, torch.zeros((64, 2)), plan, torch.zeros((64, 256), dtype=torch.float32))
+    moe32 = mx.MoEFFN(256, 128, 8, 2, 64, topk_idx_bits=32, out_fp32=True)
+    with pytest.raises(TypeError, match="topk_idx"):
+        moe32.plan(64, plan, topk_idx=torch.zeros((64, 2), dtype=torch.int64))
+    with pytest.raises(TypeError, match="out"):
+        moe32.combine(64, y, torch.zeros((64, 2)), plan, torch.zeros((64, 256), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="x holds"):
+        moe.ffn_gate_up(64, torch.zeros(100, dtype=torch.uint8), torch.zeros((64, 2)), {}, plan, None, None)

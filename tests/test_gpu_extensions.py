@@ -74,6 +74,38 @@ def test_route_biased_nan_and_ragged_expert_count():
     assert not np.isin(ref_ids, [7]).any()  # the NaN-biased expert is never chosen
 
 
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_route_nan_expert_selected(with_bias):
+    """NaN logits among the k selected (a token with fewer non-NaN logits than k): a NaN
+    logit reads as -inf, so the NaN expert is chosen last (lowest index among the
+    tied) and gets weight 0; a token whose logits are all NaN gets NaN weights."""
+    T, E, k = 40, 64, 4
+    rng = np.random.default_rng(91)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[1, :] = np.nan
+    lg[1, [5, 40]] = [0.25, 1.5]        # two real logits, k = 4: two NaN experts selected
+    lg[3, :] = np.nan
+    lg[3, 63] = -2.0                   # one real logit
+    lg[6, :] = np.nan                  # all NaN: 0/0 weights
+    lg[9, ::2] = np.nan                # half NaN: none selected
+    bias = (rng.standard_normal(E) * 0.3).astype(np.float32) if with_bias else None
+    sh = small("route_nan_sel", 1, T, 256, 128, E, k, "fp8_block128", "from_logits")
+    moe = make_moe(sh)
+    plan = moe.alloc_plan(T)
+    ws = moe.alloc_workspace(T)
+    ids = torch.empty((T, k), dtype=torch.int64, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.plan(T, plan, routing_logits=torch.from_numpy(lg).cuda(), topk_idx_out=ids, topk_weights_out=w, ws=ws,
+             routing_bias=None if bias is None else torch.from_numpy(bias).cuda())
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route_from_logits(lg, k, bias)
+    got_ids, got_w = ids.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(got_ids, ref_ids)
+    np.testing.assert_allclose(got_w, ref_w, rtol=1e-5, atol=1e-7, equal_nan=True)
+    assert (ref_w[1, 2:] == 0).all() and (ref_w[3, 1:] == 0).all() and np.isnan(ref_w[6]).all()
+    assert (got_w[1, 2:] == 0).all() and (got_w[3, 1:] == 0).all()
+
+
 def test_combine_addends():
     rng = np.random.default_rng(9)
     T, k, E, H = 77, 3, 6, 4096
@@ -165,3 +197,25 @@ def test_timed_legs_match_untimed(fmt):
             g, dn, around = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3]), ev[4].elapsed_time(ev[5])
             assert 0 < g and 0 < dn and g + dn <= around, (g, dn, around)
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_out_fp32_combine():
+    """moe_config.out_fp32: the combine writes its fp32 sum unrounded; rounding it to
+    bf16 (RNE) gives the bf16 output bit for bit, and it meets the output contract
+    against the oracle."""
+    sh = small("out_f32", 41, 90, 512, 256, 8, 3, "fp8_block128")
+    inp = moe_synth.make_inputs(sh)
+    d = device_inputs(inp)
+    m16 = make_moe(sh)
+    m32 = make_moe(sh, out_fp32=True)
+    w = prepared(m16, d)
+    T = sh.tokens
+    o16 = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device="cuda")
+    o32 = torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda")
+    m16.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], None, w, o16, m16.alloc_workspace(T))
+    m32.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], None, w, o32, m32.alloc_workspace(T))
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+    ref = oracle.forward(geometry(sh), inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
+                         topk_idx=inp["topk_idx"], topk_weights=inp["topk_weights"])
+    compare_out(o32, ref["out"])

@@ -1,11 +1,14 @@
 """GPU parity at the five named workloads' full sizes, in the launch
 configuration the benchmark times (moe_forward, automatic tile regime).
 
-The routing plan is compared in full (bit-exact).  The FFN output is compared
-on a seeded sample of tokens that the oracle computes one by one, stage by
-stage: requantised intermediate codes (rounding ties allowed), the down
-projection of the GPU's own intermediate, and the combined output within
-relative L2 <= 1e-2 and max-abs <= 5e-2 * RMS."""
+The routing plan is compared in full (bit-exact).  Every row of the heaviest
+and of the lightest active expert (the heaviest spans all of its m-tiles) is
+compared against the pure oracle at its pair slot of y, within relative L2
+<= 1e-2 and max-abs <= 5e-2 * RMS, and stage by stage (requantised intermediate
+codes with rounding ties allowed; the down projection of the GPU's own
+intermediate).  The combined output is compared on a seeded sample of tokens
+that the oracle computes one by one, within the same two bounds against the
+pure oracle."""
 import numpy as np
 import pytest
 import torch
@@ -22,8 +25,37 @@ if not torch.cuda.is_available():  # pragma: no cover
 SAMPLE = 24
 
 
+def _rows_of(h, hsf, rows, fmt):
+    ridx = torch.as_tensor(rows, dtype=torch.int64, device="cuda")
+    hc = h.index_select(0, ridx).cpu()
+    hc = hc.view(torch.int16).numpy().view(np.uint16) if fmt in ("bf16", "nvfp4_w4a16") else hc.numpy()
+    hs = None if hsf is None else hsf.index_select(0, ridx).cpu().numpy()
+    return hc, hs
+
+
+def _check_whole_expert(sh, inp, geo, e, ref_plan, y, h, hsf):
+    """Every row of expert e: y at the rows' pair slots against the pure oracle
+    (both output bounds), and stage by stage.  Returns (rows, rel-L2, max-abs/RMS, flips)."""
+    k, I = sh.topk, sh.inter
+    r0, r1 = int(ref_plan["expert_start_indices"][e]), int(ref_plan["expert_start_indices"][e + 1])
+    src = ref_plan["src_info"][r0:r1]
+    toks = src // k
+    X = oracle.dequant_activations(geo, inp["x"][toks], None if inp["x_sf"] is None else inp["x_sf"][toks])
+    w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e, **gs_kwargs(inp))
+    hx = oracle.swiglu_clamped(X @ w13d[:I].T, X @ w13d[I:].T, geo.clamp)
+    del X
+    y_pure = oracle.requant(geo, hx) @ w2d.T
+    y_gpu = y.index_select(0, torch.as_tensor(src, dtype=torch.int64, device="cuda")).float().cpu()
+    rl2, mr = compare_out(y_gpu, y_pure)
+    hc, hs = _rows_of(h, hsf, np.arange(r0, r1), sh.fmt)
+    hg, flips = check_intermediate(sh.fmt, hx, hc, hs, I)
+    check_y_rows(y_gpu.numpy().astype(np.float64), hg @ w2d.T)
+    return r1 - r0, rl2, mr, flips
+
+
 def _gather_intermediate(moe, d, T, rows):
-    """moe_plan, moe_ffn_gate_up, moe_ffn_down; return (plan, y, h codes, h scales) of the given rows."""
+    """moe_plan, moe_ffn_gate_up, moe_ffn_down; return (plan, y, h codes, h scales) of the
+    given rows, and the whole h and h_sf buffers."""
     plan = moe.alloc_plan(T)
     ws = moe.alloc_workspace(T)
     if moe.route_mode == "precomputed":
@@ -36,11 +68,8 @@ def _gather_intermediate(moe, d, T, rows):
     y = torch.zeros((T * moe.topk, moe.hidden), dtype=torch.bfloat16, device="cuda")
     moe.ffn_down(T, h, hsf, prepared(moe, d), plan, y)
     torch.cuda.synchronize()
-    ridx = torch.as_tensor(rows, dtype=torch.int64, device="cuda")
-    hc = h.index_select(0, ridx).cpu()
-    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt in ("bf16", "nvfp4_w4a16") else hc.numpy()
-    hs = None if hsf is None else hsf.index_select(0, ridx).cpu().numpy()
-    return plan, y, hc, hs
+    hc, hs = _rows_of(h, hsf, rows, moe.fmt)
+    return plan, y, hc, hs, h, hsf
 
 
 @pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER + ["nvfp4_decode"])
@@ -75,7 +104,7 @@ def test_named_workload_full_size(name):
     toks = np.sort(rng.choice(T, size=min(SAMPLE, T), replace=False))
     pairs = [(t, j) for t in toks for j in range(k) if ref_plan["pair_row"][t * k + j] >= 0]
     rows = [int(ref_plan["pair_row"][t * k + j]) for t, j in pairs]
-    plan, y, h_g, hsf_g = _gather_intermediate(moe, d, T, rows)
+    plan, y, h_g, hsf_g, h_all, hsf_all = _gather_intermediate(moe, d, T, rows)
     for f, key in (("expert_counts", "expert_counts"), ("expert_start_indices", "expert_start_indices"),
                    ("expert_ids", "expert_ids"), ("pair_row", "pair_row")):
         assert np.array_equal(plan[f].cpu().numpy()[: ref_plan[key].size], ref_plan[key]), f
@@ -108,5 +137,14 @@ def test_named_workload_full_size(name):
     # and the pure oracle on the sample, relative L2
     ref = oracle.forward_tokens(geo, toks, inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
                                 ids, w, **gs_kwargs(inp))
-    compare_out(torch.from_numpy(out_np[toks]), ref, rel_l2=1e-2, max_rms=np.inf)
-    print(f"[fullsize] {name}: ok ({len(pairs)} pairs sampled, {flips} rounding-tie flips)", flush=True)
+    rl2, mr = compare_out(torch.from_numpy(out_np[toks]), ref)
+    print(f"[fullsize] {name}: sampled tokens: rel-L2 {rl2:.2e}, max-abs/RMS {mr:.2e} against the pure oracle "
+          f"({len(pairs)} pairs, {flips} rounding-tie flips)", flush=True)
+
+    # every row of the heaviest and of the lightest active expert
+    counts = ref_plan["expert_counts"]
+    act = np.flatnonzero(counts > 0)
+    for e in sorted({int(act[np.argmax(counts[act])]), int(act[np.argmin(counts[act])])}):
+        n, rl2, mr, fl = _check_whole_expert(sh, inp, geo, e, ref_plan, y, h_all, hsf_all)
+        print(f"[fullsize] {name}: expert {e}, all {n} rows: rel-L2 {rl2:.2e}, max-abs/RMS {mr:.2e} against the "
+              f"pure oracle ({fl} rounding-tie flips)", flush=True)

@@ -229,7 +229,7 @@ def _torch_requant(fmt, h):
 
 
 @pytest.mark.parametrize("fmt,x_scale", [("fp8_block128", 1.0), ("fp8_block128", 20.0), ("bf16", 1.0),
-                                         ("bf16", 20.0), ("w4a8_mx", 1.0), ("nvfp4_w4a16", 1.0),
+                                         ("bf16", 20.0), ("w4a8_mx", 1.0), ("w4a8_mx", 20.0), ("nvfp4_w4a16", 1.0),
                                          ("nvfp4_w4a16", 20.0)])
 def test_single_expert_matches_torch_chain(fmt, x_scale):
     sh, inp = _small_inputs(fmt, T=16, E=1, k=1, x_scale=x_scale, H=256, I=256)
