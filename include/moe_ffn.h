@@ -295,6 +295,26 @@ moe_status moe_forward_ex(const moe_handle* h, int32_t num_tokens, const void* x
                           const float* routing_bias, const moe_weights* w /* host struct */, const void* shared,
                           const void* residual, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the scratch array moe_forward_static uses as its workspace, one array
+   per device. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+   graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+   arguments and results as moe_forward without ws / ws_bytes: the workspace is a
+   scratch array of MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on
+   each device it runs on until the process ends; the call itself allocates
+   nothing.  Its address on the current device is resolved at the first call on
+   that device.  Limit: num_tokens whose moe_workspace_size exceeds 64 MiB gets
+   MOE_ERR_WORKSPACE_TOO_SMALL before any launch (at the decode shape H = 7168,
+   I = 2048, k = 8, up to 456 tokens).  Every call on one device shares that
+   device's array, which keeps the last call's contents (nothing in it needs to
+   start at zero); calls that overlap on one device (other streams, other
+   threads) race on it and must be serialised by the caller. */
+moe_status moe_forward_static(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
+                              void* topk_idx, float* topk_weights, const float* routing_logits,
+                              const moe_weights* w /* host struct */, void* out, hipStream_t stream);
+
 const char* moe_status_string(moe_status s);
 int32_t moe_abi_version(void);
 

@@ -60,7 +60,8 @@ PLAN_FIELDS = [f for f, _ in _Plan._fields_]
 EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
             "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_ffn_gate_up_timed", "moe_ffn_down_timed",
-            "moe_status_string", "moe_abi_version"]
+            "moe_forward_static", "moe_status_string", "moe_abi_version"]
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 
 _lib = None
 
@@ -106,6 +107,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_combine_ex.restype = i32
     lib.moe_forward_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, vp, vp, sz, vp]
     lib.moe_forward_ex.restype = i32
+    lib.moe_forward_static.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp]
+    lib.moe_forward_static.restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_abi_version.argtypes = []
@@ -439,6 +442,25 @@ class MoEFFN:
                                            _ptr(topk_weights), _ptr(routing_logits), _ptr(routing_bias),
                                            ctypes.byref(ws_), _ptr(shared), _ptr(residual), _ptr(out), _ptr(ws),
                                            self._nbytes(ws), _stream(stream)), "moe_forward_ex")
+
+    def forward_static(self, num_tokens, x, x_sf, topk_idx, topk_weights, routing_logits, weights: dict, out,
+                       stream=None):
+        """moe_forward_static: moe_forward with the library's per-device static scratch
+        as its workspace (no allocation; calls on one device share that scratch)."""
+        import torch
+        T = num_tokens
+        self._check_x(x, x_sf, T)
+        self._check_weights(weights)
+        self._check_routing_in(T, topk_idx, routing_logits, None)
+        _need(topk_idx, "topk_idx", T * self.topk * self.topk_idx_bits // 8, self._idx_dtypes())
+        _need(topk_weights, "topk_weights", T * self.topk * 4, (torch.float32,))
+        self._check_out(T, out, None, None)
+        _on_gpu(x=x, x_sf=x_sf, weights=weights, topk_idx=topk_idx, topk_weights=topk_weights,
+                routing_logits=routing_logits, out=out)
+        ws_ = self._weights_struct(weights)
+        _check(self.lib.moe_forward_static(self._h, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx),
+                                           _ptr(topk_weights), _ptr(routing_logits), ctypes.byref(ws_), _ptr(out),
+                                           _stream(stream)), "moe_forward_static")
 
 
 __all__ = ["MoEFFN", "MoEError", "load_library", "LIB_PATH", "EXPORTED", "FORMATS", "ROUTE_MODES", "TILE_REGIMES"]

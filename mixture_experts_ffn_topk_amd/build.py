@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
-SOURCES = ["api.cpp", "route.hip", "gemm.hip", "combine.hip", "prepare.hip"]
+SOURCES = ["api.cpp", "route.hip", "gemm.hip", "combine.hip", "prepare.hip", "static_ws.hip"]
 ARCH = os.environ.get("MOE_FFN_ARCH", "gfx950")
 
 
