@@ -25,6 +25,15 @@ MegaMoESymmBuffer page):
   + one fp32 global scale per expert ``w13_gs`` [E]; w2: packed E2M1
   [E, H, I/2] + E4M3 [E, H, I/16] + ``w2_gs`` [E].  A weight is
   e2m1 * e4m3 block scale * global scale.
+* ``nvfp4``         x: packed E2M1 [T, H/2] + E4M3 block scales [T, H/16] (the
+  page's NVFP4 x NVFP4 activations) against one global scale for the whole
+  tensor; weights as ``nvfp4_w4a16``.  The per-expert scales handed to the FFN
+  are those of the max mega_ffn arguments: ``w13_gs`` = gate_up_expert_scales
+  (the activations' global scale times the gate_up weight's), ``c_scales`` =
+  c_input_scales (the global scale the intermediate is requantised against: a
+  static calibration value, drawn here around 16 / (6 * 448) per expert) and
+  ``w2_gs`` = down_expert_scales (that input scale times the down weight's
+  global scale).
 
 Routing inputs: ``logits`` f32 [T, E] always; for precomputed routing the
 caller-side ``topk_idx`` (int64 [T, k]) and ``topk_weights`` (f32 [T, k]) are
@@ -44,12 +53,13 @@ FP8_BLOCK128 = "fp8_block128"
 BF16 = "bf16"
 W4A8_MX = "w4a8_mx"
 NVFP4_W4A16 = "nvfp4_w4a16"
+NVFP4 = "nvfp4"  # NVFP4 weights x NVFP4 activations
 
 PRECOMPUTED = "precomputed"
 FROM_LOGITS = "from_logits"
 
 # generator stream ids
-_S_LOGITS, _S_RANKS, _S_X, _S_W13, _S_W2 = 0, 1, 2, 3, 4
+_S_LOGITS, _S_RANKS, _S_X, _S_W13, _S_W2, _S_CSCALE = 0, 1, 2, 3, 4, 5
 
 
 @dataclass(frozen=True)
@@ -94,6 +104,8 @@ CONFIG_ORDER = ["tiny_fp8", "decode_fp8", "prefill_fp8_zipf", "mixtral_bf16", "w
 # The NVFP4 weight x BF16 activation variant at the decode shape (not one of the
 # five named workloads).
 WORKLOADS["nvfp4_decode"] = MoEShape("nvfp4_decode", 6, 256, 7168, 2048, 32, 8, NVFP4_W4A16, PRECOMPUTED)
+# NVFP4 weights x NVFP4 activations at the decode shape
+WORKLOADS["nvfp4x4_decode"] = MoEShape("nvfp4x4_decode", 7, 256, 7168, 2048, 32, 8, NVFP4, PRECOMPUTED)
 
 
 def _rng(seed: int, stream: int, expert: int = 0) -> np.random.Generator:
@@ -226,7 +238,7 @@ def _weights_for_expert(shape: MoEShape, e: int):
         return _to_bf16_bits(w13), None, _to_bf16_bits(w2), None
     if shape.fmt == W4A8_MX:
         return quant_mx_weight(w13) + quant_mx_weight(w2)
-    if shape.fmt == NVFP4_W4A16:
+    if shape.fmt in (NVFP4_W4A16, NVFP4):
         return quant_nvfp4_weight(w13) + quant_nvfp4_weight(w2)
     raise ValueError(shape.fmt)
 
@@ -246,6 +258,8 @@ def make_inputs(shape: MoEShape, with_weights: bool = True) -> dict:
         out["x"], out["x_sf"] = quant_fp8_block(x, 1, 128)
     elif shape.fmt in (BF16, NVFP4_W4A16):
         out["x"], out["x_sf"] = _to_bf16_bits(x), None
+    elif shape.fmt == NVFP4:
+        out["x"], out["x_sf"], out["x_gs"] = quant_nvfp4_weight(x)
     else:
         out["x"], out["x_sf"] = quant_mx_act(x)
     if not with_weights:
@@ -255,6 +269,13 @@ def make_inputs(shape: MoEShape, with_weights: bool = True) -> dict:
     if shape.fmt == NVFP4_W4A16:  # (w13, sf, gs, w2, sf, gs) per expert
         out["w13_gs"] = np.array([p[2] for p in parts], dtype=np.float32)
         out["w2_gs"] = np.array([p[5] for p in parts], dtype=np.float32)
+        parts = [(p[0], p[1], p[3], p[4]) for p in parts]
+    elif shape.fmt == NVFP4:
+        # the legs' per-expert output scales and the intermediate's per-expert input scale
+        c = (shape.x_scale * (12.0 + 8.0 * _rng(shape.seed, _S_CSCALE).random(E)) / (6.0 * 448.0)).astype(np.float32)
+        out["c_scales"] = c
+        out["w13_gs"] = (np.float32(out["x_gs"]) * np.array([p[2] for p in parts], dtype=np.float32)).astype(np.float32)
+        out["w2_gs"] = (c * np.array([p[5] for p in parts], dtype=np.float32)).astype(np.float32)
         parts = [(p[0], p[1], p[3], p[4]) for p in parts]
     out["w13"] = np.stack([p[0] for p in parts])
     out["w13_sf"] = None if parts[0][1] is None else np.stack([p[1] for p in parts])

@@ -9,12 +9,12 @@ float64 values already rounded onto the target grid (rounders).  Nothing here
 is shared with the GPU code.
 
 Formats (operand encodings of the flashinfer.fused_moe MoEActivationPack page:
-"DeepSeek FP8", "MXFP8", "MXFP4 x MXFP8 (W4A8)", "BF16"):
+"DeepSeek FP8", "MXFP8", "MXFP4 x MXFP8 (W4A8)", "BF16", "NVFP4"):
 
 * E4M3 (float8_e4m3fn): sign, 4 exponent bits (bias 7), 3 mantissa bits.
   Exponent field 0 is subnormal (m/8 * 2**-6); field 15 with mantissa 7 is
   NaN; there is no infinity, so the largest finite magnitude is 448.
-* E2M1 (MXFP4 element): sign, 2 exponent bits (bias 1), 1 mantissa bit.
+* E2M1 (MXFP4 / NVFP4 element): sign, 2 exponent bits (bias 1), 1 mantissa bit.
   Exponent field 0 is subnormal (m/2 * 2**0).  Magnitudes 0 .. 6.
 * UE8M0 (MX block scale): unsigned 8-bit exponent, value 2**(b - 127); the
   byte 255 is NaN.
@@ -92,6 +92,12 @@ def round_to_grid(v: np.ndarray, mant_bits: int, emin: int, maxval: float, satur
 def round_e4m3_sat(v: np.ndarray) -> np.ndarray:
     """Value of E4M3FN round-to-nearest-even with saturation to +-448."""
     return round_to_grid(v, 3, -6, E4M3_MAX, saturate=True)
+
+
+def round_e2m1_sat(v: np.ndarray) -> np.ndarray:
+    """Value of E2M1 round-to-nearest-even with saturation to +-6 (1 mantissa bit,
+    minimum normal exponent 0, subnormal step 0.5)."""
+    return round_to_grid(v, 1, 0, 6.0, saturate=True)
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:

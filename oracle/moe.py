@@ -50,7 +50,10 @@ E4M3 round-to-nearest-even with saturation; the MX intermediate uses per
 the BF16 intermediate is rounded to bf16; an NVFP4 weight is e2m1 * e4m3 block
 scale (one per 16 along K) * the expert's fp32 global scale (the per-expert
 scales of the max mega_ffn arguments), and the NVFP4 x BF16 intermediate is
-rounded to bf16 like BF16's; rows inside an expert keep pair order
+rounded to bf16 like BF16's; NVFP4 x NVFP4 takes E2M1 activations with E4M3
+block scales per 16, multiplies each leg by its per-expert output scale, and
+requantises the intermediate per (row, 16 columns) to E2M1 with an E4M3 block
+scale chosen against the expert's c_input_scales entry; rows inside an expert keep pair order
 p = t * k + j; ``src_info[row] = p``; the combine sums valid slots in slot order;
 ids outside [0, E) are masked slots that contribute nothing.
 
@@ -65,13 +68,14 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .codecs import (bf16_decode, e2m1_decode_nibbles, e2m1_unpack, e4m3_decode, round_bf16,
+from .codecs import (bf16_decode, e2m1_decode_nibbles, e2m1_unpack, e4m3_decode, round_bf16, round_e2m1_sat,
                      round_e4m3_sat, ue8m0_decode)
 
 FP8_BLOCK128 = "fp8_block128"
 BF16 = "bf16"
 W4A8_MX = "w4a8_mx"
 NVFP4_W4A16 = "nvfp4_w4a16"
+NVFP4 = "nvfp4"  # NVFP4 weights x NVFP4 activations
 
 
 @dataclass(frozen=True)
@@ -120,8 +124,14 @@ def dequant_nvfp4(values: np.ndarray, block_scales: np.ndarray, global_scale: fl
 
 
 def dequant_activations(geo: Geometry, x: np.ndarray, x_sf) -> np.ndarray:
+    """Activations in float64.  NVFP4: codes times their E4M3 block scales; the
+    activations' own global scale is not an operand of the FFN (it is part of the
+    gate_up leg's per-expert output scale, the gate_up_expert_scales argument of the
+    max mega_ffn page)."""
     if geo.fmt == FP8_BLOCK128:
         return dequant_fp8_block(x, x_sf, 1, 128)
+    if geo.fmt == NVFP4:
+        return dequant_nvfp4(x, x_sf, 1.0)
     if geo.fmt in (BF16, NVFP4_W4A16):
         return bf16_decode(x)
     if geo.fmt == W4A8_MX:
@@ -130,8 +140,12 @@ def dequant_activations(geo: Geometry, x: np.ndarray, x_sf) -> np.ndarray:
 
 
 def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int, w13_gs=None, w2_gs=None):
-    """Expert e's gate/up weights [2I, H] and down weights [H, I] in float64
-    (``w13_gs``/``w2_gs``: the NVFP4 per-expert global scales)."""
+    """Expert e's gate/up weights [2I, H] and down weights [H, I] in float64.
+    ``w13_gs``/``w2_gs`` are the per-expert scales of the NVFP4 formats: the weights'
+    global scales (NVFP4 x BF16), or the legs' per-expert output scales (NVFP4 x
+    NVFP4: gate_up_expert_scales and down_expert_scales of the max mega_ffn page).
+    Either way the scale multiplies every product of the leg, so it is applied to
+    the weights here."""
     if geo.fmt == FP8_BLOCK128:
         return (dequant_fp8_block(w13[e], w13_sf[e], 128, 128),
                 dequant_fp8_block(w2[e], w2_sf[e], 128, 128))
@@ -139,7 +153,7 @@ def dequant_expert(geo: Geometry, w13, w13_sf, w2, w2_sf, e: int, w13_gs=None, w
         return bf16_decode(w13[e]), bf16_decode(w2[e])
     if geo.fmt == W4A8_MX:
         return dequant_mx(w13[e], w13_sf[e], True), dequant_mx(w2[e], w2_sf[e], True)
-    if geo.fmt == NVFP4_W4A16:
+    if geo.fmt in (NVFP4_W4A16, NVFP4):
         return dequant_nvfp4(w13[e], w13_sf[e], w13_gs[e]), dequant_nvfp4(w2[e], w2_sf[e], w2_gs[e])
     raise ValueError(geo.fmt)
 
@@ -305,24 +319,45 @@ def requant_mx(h: np.ndarray):
     return (q * sc[..., None]).reshape(R, C), (e + 127).astype(np.uint8)
 
 
-def requant(geo: Geometry, h: np.ndarray) -> np.ndarray:
+def requant_nvfp4(h: np.ndarray, c: float):
+    """NVFP4 intermediate (the NVFP4 re-quant of the max mega_ffn page, with the
+    expert's c_input_scales entry c as the global scale): per (row, 16 columns)
+    a = amax, block scale s = E4M3 RNE-saturated(a / (6 c)), codes
+    q = E2M1 RNE-saturated(h / (s c)) (all zero where s = 0).  Returns (q * s,
+    block scales [R, C/16]): the values the down projection consumes; c itself
+    reaches the output through the down leg's per-expert output scale
+    (down_expert_scales)."""
+    R, C = h.shape
+    hb = h.reshape(R, C // 16, 16)
+    a = np.abs(hb).max(axis=2)
+    s = round_e4m3_sat(a / (6.0 * float(c)))
+    den = (s * float(c))[..., None]
+    q = np.where(den > 0, round_e2m1_sat(hb / np.where(den > 0, den, 1.0)), 0.0)
+    return (q * s[..., None]).reshape(R, C), s
+
+
+def requant(geo: Geometry, h: np.ndarray, c_scale=None) -> np.ndarray:
+    """The intermediate after its requantisation (c_scale: NVFP4's per-expert
+    input scale)."""
     if geo.fmt == FP8_BLOCK128:
         return requant_fp8_block128(h)[0]
     if geo.fmt in (BF16, NVFP4_W4A16):
         return round_bf16(h)
     if geo.fmt == W4A8_MX:
         return requant_mx(h)[0]
+    if geo.fmt == NVFP4:
+        return requant_nvfp4(h, c_scale)[0]
     raise ValueError(geo.fmt)
 
 
-def expert_rows(geo: Geometry, xd_rows: np.ndarray, w13d: np.ndarray, w2d: np.ndarray) -> np.ndarray:
+def expert_rows(geo: Geometry, xd_rows: np.ndarray, w13d: np.ndarray, w2d: np.ndarray, c_scale=None) -> np.ndarray:
     """One expert's FFN over its rows: gate/up projection, clamped SwiGLU,
     intermediate requantisation, down projection (float64)."""
     I = geo.inter
     g = xd_rows @ w13d[:I].T
     u = xd_rows @ w13d[I:].T
     h = swiglu_clamped(g, u, geo.clamp)
-    hd = requant(geo, h)
+    hd = requant(geo, h, c_scale)
     return hd @ w2d.T
 
 
@@ -349,7 +384,8 @@ def combine(y_rows: np.ndarray, topk_weights: np.ndarray, pair_row: np.ndarray, 
 
 # ------------------------------------------------------------------ forward
 def forward(geo: Geometry, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx=None, topk_weights=None,
-            logits=None, w13_gs=None, w2_gs=None, routing_bias=None, shared=None, residual=None) -> dict:
+            logits=None, w13_gs=None, w2_gs=None, routing_bias=None, shared=None, residual=None,
+            c_scales=None) -> dict:
     """Whole path over all tokens.  Routing is taken from ``topk_idx``/``topk_weights``
     when given, else computed from ``logits`` (and ``routing_bias``).  ``shared`` and
     ``residual`` ([T, H]) are added after the routed experts' weighted sum."""
@@ -364,14 +400,14 @@ def forward(geo: Geometry, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx=None, topk_
         if r1 == r0:
             continue
         w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e, w13_gs, w2_gs)
-        y[r0:r1] = expert_rows(geo, xd[src[r0:r1] // geo.topk], w13d, w2d)
+        y[r0:r1] = expert_rows(geo, xd[src[r0:r1] // geo.topk], w13d, w2d, None if c_scales is None else c_scales[e])
     out = combine(y, topk_weights, plan["pair_row"], geo.hidden, (shared, residual))
     return {"out": out, "plan": plan, "y_rows": y, "topk_idx": np.asarray(topk_idx),
             "topk_weights": np.asarray(topk_weights, dtype=np.float64)}
 
 
 def forward_tokens(geo: Geometry, tokens, x, x_sf, w13, w13_sf, w2, w2_sf, topk_idx, topk_weights,
-                   w13_gs=None, w2_gs=None) -> np.ndarray:
+                   w13_gs=None, w2_gs=None, c_scales=None) -> np.ndarray:
     """Outputs of selected tokens only, each computed on its own (the requantisation
     blocks lie inside one row, so a pair's result depends only on its token and
     expert).  Used to check full-size runs on a sample of tokens."""
@@ -390,7 +426,7 @@ def forward_tokens(geo: Geometry, tokens, x, x_sf, w13, w13_sf, w2, w2_sf, topk_
     for e, lst in need.items():
         w13d, w2d = dequant_expert(geo, w13, w13_sf, w2, w2_sf, e, w13_gs, w2_gs)
         rows = np.array([n for n, _ in lst])
-        y = expert_rows(geo, xd[rows], w13d, w2d)
+        y = expert_rows(geo, xd[rows], w13d, w2d, None if c_scales is None else c_scales[e])
         for (n, j), yr in zip(lst, y):
             contrib[n, j] = w[tokens[n], j] * yr
     for j in range(geo.topk):  # slot order

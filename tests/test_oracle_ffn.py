@@ -10,7 +10,7 @@ import torch
 
 import moe_synth
 from oracle import (Geometry, build_plan, combine, expert_rows, forward, forward_tokens, mx_exponent,
-                    requant_fp8_block128, requant_mx, silu, swiglu_clamped)
+                    requant_fp8_block128, requant_mx, requant_nvfp4, silu, swiglu_clamped)
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
 
@@ -162,21 +162,28 @@ def _gs(inp):
     return {"w13_gs": inp["w13_gs"], "w2_gs": inp["w2_gs"]} if "w13_gs" in inp else {}
 
 
-@pytest.mark.parametrize("fmt", ["fp8_block128", "bf16", "w4a8_mx", "nvfp4_w4a16"])
+def _cs(inp, e=None):
+    """NVFP4 x NVFP4: the per-expert input scales of the intermediate (all, or expert e's)."""
+    if "c_scales" not in inp:
+        return None
+    return inp["c_scales"] if e is None else inp["c_scales"][e]
+
+
+@pytest.mark.parametrize("fmt", ["fp8_block128", "bf16", "w4a8_mx", "nvfp4_w4a16", "nvfp4"])
 def test_dense_equivalence_topk_equals_E(fmt):
     sh, inp = _small_inputs(fmt, E=3, k=3)
     geo = Geometry(sh.hidden, sh.inter, sh.experts, sh.topk, fmt)
     T = sh.tokens
     ids = np.tile(np.arange(3), (T, 1))
     w = np.full((T, 3), 1.0 / 3)
-    res = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w, **_gs(inp))
+    res = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w, c_scales=_cs(inp), **_gs(inp))
     # no routing code: every expert over every token, averaged
     from oracle import dequant_activations, dequant_expert
     xd = dequant_activations(geo, inp["x"], inp["x_sf"])
     dense = np.zeros((T, sh.hidden))
     for e in range(3):
         w13d, w2d = dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e, **_gs(inp))
-        dense += expert_rows(geo, xd, w13d, w2d) / 3
+        dense += expert_rows(geo, xd, w13d, w2d, _cs(inp, e)) / 3
     assert np.allclose(res["out"], dense, rtol=1e-12, atol=1e-12 * np.abs(dense).max())
 
 
@@ -208,9 +215,30 @@ def _torch_nvfp4(packed, block_scales, gs):
     return v * s.repeat_interleave(16, 1) * float(gs)
 
 
-def _torch_requant(fmt, h):
+def _torch_e2m1_round(v):
+    """Nearest signed E2M1 value, ties to the even code, saturated at 6 (torch)."""
+    mags = _E2M1[:8]
+    a = v.abs().clamp(max=6.0)
+    d = (a.unsqueeze(-1) - mags).abs()
+    best = d.min(-1, keepdim=True).values
+    cand = d == best
+    code = torch.where(cand.sum(-1) > 1, torch.argmax((cand & (torch.arange(8) % 2 == 0)).to(torch.int64), -1),
+                       torch.argmax(cand.to(torch.int64), -1))
+    return torch.copysign(mags[code], v)
+
+
+def _torch_requant(fmt, h, c=None):
     if fmt in ("bf16", "nvfp4_w4a16"):
         return h.to(torch.bfloat16).to(torch.float64)
+    if fmt == "nvfp4":  # per 16: E4M3 block scale of amax / (6 c), E2M1 codes of h / (s c); returns codes * s
+        R, C = h.shape
+        hb = h.reshape(R, C // 16, 16)
+        s = (hb.abs().amax(-1, keepdim=True) / (6 * c)).clamp(max=448).to(torch.float32).to(
+            torch.float8_e4m3fn).to(torch.float64)
+        den = s * c
+        q = torch.where(den > 0, _torch_e2m1_round(hb / torch.where(den > 0, den, torch.ones_like(den))),
+                        torch.zeros_like(hb))
+        return (q * s).reshape(R, C)
     R, C = h.shape
     if fmt == "fp8_block128":
         hb = h.reshape(R, C // 128, 128)
@@ -230,15 +258,19 @@ def _torch_requant(fmt, h):
 
 @pytest.mark.parametrize("fmt,x_scale", [("fp8_block128", 1.0), ("fp8_block128", 20.0), ("bf16", 1.0),
                                          ("bf16", 20.0), ("w4a8_mx", 1.0), ("w4a8_mx", 20.0), ("nvfp4_w4a16", 1.0),
-                                         ("nvfp4_w4a16", 20.0)])
+                                         ("nvfp4_w4a16", 20.0), ("nvfp4", 1.0), ("nvfp4", 20.0)])
 def test_single_expert_matches_torch_chain(fmt, x_scale):
     sh, inp = _small_inputs(fmt, T=16, E=1, k=1, x_scale=x_scale, H=256, I=256)
     geo = Geometry(sh.hidden, sh.inter, 1, 1, fmt)
     ids = np.zeros((sh.tokens, 1), np.int64)
     w = np.ones((sh.tokens, 1), np.float32)
-    out = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w, **_gs(inp))["out"]
+    out = forward(geo, *_ops(inp), topk_idx=ids, topk_weights=w, c_scales=_cs(inp), **_gs(inp))["out"]
     H, I = sh.hidden, sh.inter
-    if fmt == "nvfp4_w4a16":
+    if fmt == "nvfp4":  # both operands E2M1 x E4M3 per 16; each leg times its per-expert output scale
+        x = _torch_nvfp4(inp["x"], inp["x_sf"], 1.0)
+        w13 = _torch_nvfp4(inp["w13"][0], inp["w13_sf"][0], 1.0) * float(inp["w13_gs"][0])
+        w2 = _torch_nvfp4(inp["w2"][0], inp["w2_sf"][0], 1.0) * float(inp["w2_gs"][0])
+    elif fmt == "nvfp4_w4a16":
         x = _torch_deq("bf16", inp["x"], None)
         w13 = _torch_nvfp4(inp["w13"][0], inp["w13_sf"][0], inp["w13_gs"][0])
         w2 = _torch_nvfp4(inp["w2"][0], inp["w2_sf"][0], inp["w2_gs"][0])
@@ -255,7 +287,7 @@ def test_single_expert_matches_torch_chain(fmt, x_scale):
     if x_scale > 1:
         assert (g > 10).any() and (u.abs() > 10).any()  # the clamp fires
     h = torch.nn.functional.silu(torch.clamp(g, max=10.0)) * torch.clamp(u, -10.0, 10.0)
-    ref = (_torch_requant(fmt, h) @ w2.T).numpy()
+    ref = (_torch_requant(fmt, h, None if fmt != "nvfp4" else float(inp["c_scales"][0])) @ w2.T).numpy()
     err = np.abs(out - ref).max() / np.abs(ref).max()
     assert err < 1e-9, err
 
@@ -366,3 +398,54 @@ def test_nvfp4_down_global_scale_is_linear():
     a = forward(geo, *_ops(inp), w13_gs=inp["w13_gs"], w2_gs=inp["w2_gs"], **kw)["out"]
     b = forward(geo, *_ops(inp), w13_gs=inp["w13_gs"], w2_gs=inp["w2_gs"] * 4, **kw)["out"]
     assert np.array_equal(b, 4 * a)
+
+
+# ---- NVFP4 x NVFP4: E2M1 rounding and the requantisation against c_input_scales
+def test_round_e2m1_brute_force():
+    """RNE onto the signed E2M1 values with saturation, against a nearest-value
+    search that breaks ties toward the even code (mantissa bit 0)."""
+    from oracle import round_e2m1_sat
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # codes 0..7; the mantissa bit is the code's low bit
+    rng = np.random.default_rng(8)
+    vals = np.concatenate([rng.uniform(-8, 8, 4000), [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 100.0],
+                           -np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0])])
+    got = round_e2m1_sat(vals)
+    for v, g in zip(vals, got):
+        a = min(abs(v), 6.0)
+        d = [abs(a - m) for m in mags]
+        best = min(d)
+        cands = [c for c in range(8) if d[c] == best]
+        c = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        assert g == np.copysign(mags[c], v), (v, g)
+
+
+def test_requant_nvfp4_hand_case():
+    gold = GOLD["requant_nvfp4_block"]
+    h = np.array([gold["h"] + [0.0] * 16])  # two blocks: the hand block and an all-zero block
+    hq, s = requant_nvfp4(h, gold["c"])
+    assert s[0, 0] == gold["scale"] and s[0, 1] == 0.0
+    assert hq[0, :16].tolist() == gold["q_times_s"]
+    assert np.all(hq[0, 16:] == 0)
+
+
+def test_requant_nvfp4_grid_saturation_and_underflow():
+    from oracle import e4m3_decode
+    rng = np.random.default_rng(9)
+    c = 0.01
+    # values already on the grid (E2M1 codes times an E4M3 block scale whose block
+    # reaches 6 * s * c) come back unchanged
+    e4 = e4m3_decode(np.arange(0x08, 0x78, dtype=np.uint8))  # normal E4M3 values 2^-6 .. 240
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for _ in range(20):
+        s = rng.choice(e4)
+        q = rng.choice(mags, 16) * rng.choice([-1, 1], 16)
+        q[rng.integers(16)] = 6.0
+        hq, sc = requant_nvfp4((q * s * c)[None, :], c)
+        assert sc[0, 0] == s and np.array_equal(hq[0], q * s)
+    # a block whose scale would exceed 448 saturates the scale at 448 and the codes at 6
+    h = np.full((1, 16), 6.0 * 1000.0 * c)
+    hq, sc = requant_nvfp4(h, c)
+    assert sc[0, 0] == 448.0 and np.all(hq == 6.0 * 448.0)
+    # a block too small for the smallest E4M3 scale becomes zero
+    hq, sc = requant_nvfp4(np.full((1, 16), 1e-9), c)
+    assert sc[0, 0] == 0.0 and np.all(hq == 0)
