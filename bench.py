@@ -42,8 +42,10 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
 # MX: the f8 x f4 MFMA runs at the FP8 rate; NVFP4 x BF16 decodes its weights to bf16 for the bf16 MFMA
-PEAK_TFLOPS = {"fp8_block128": 5000.0, "bf16": 2500.0, "w4a8_mx": 5000.0, "nvfp4_w4a16": 2500.0}
-DTYPE = {"fp8_block128": "fp8_e4m3", "bf16": "bf16", "w4a8_mx": "mxfp4xmxfp8", "nvfp4_w4a16": "nvfp4xbf16"}
+# NVFP4 x NVFP4 decodes both operands to bf16 (exactly) for the bf16 MFMA
+PEAK_TFLOPS = {"fp8_block128": 5000.0, "bf16": 2500.0, "w4a8_mx": 5000.0, "nvfp4_w4a16": 2500.0, "nvfp4": 2500.0}
+DTYPE = {"fp8_block128": "fp8_e4m3", "bf16": "bf16", "w4a8_mx": "mxfp4xmxfp8", "nvfp4_w4a16": "nvfp4xbf16",
+         "nvfp4": "nvfp4xnvfp4"}
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "device.h", "prepare.hip")]
 
@@ -69,6 +71,8 @@ def weight_bytes_per_expert(sh) -> tuple[int, int]:
         return 2 * I * H * 2, H * I * 2
     if sh.fmt == "nvfp4_w4a16":  # E2M1 values, one E4M3 scale per 16, one fp32 global scale
         return 2 * I * H // 2 + 2 * I * (H // 16) + 4, H * I // 2 + H * (I // 16) + 4
+    if sh.fmt == "nvfp4":  # as above, plus the intermediate's per-expert scale
+        return 2 * I * H // 2 + 2 * I * (H // 16) + 8, H * I // 2 + H * (I // 16) + 4
     return 2 * I * H // 2 + 2 * I * (H // 32), H * I // 2 + H * (I // 32)
 
 
@@ -78,6 +82,8 @@ def act_bytes(sh) -> int:
         return T * H + T * (H // 128) * 4
     if sh.fmt in ("bf16", "nvfp4_w4a16"):
         return T * H * 2
+    if sh.fmt == "nvfp4":
+        return T * H // 2 + T * (H // 16)
     return T * H + T * (H // 32)
 
 
@@ -104,7 +110,8 @@ def cpu_baseline(sh, inp, ids, w, budget_s: float) -> dict:
             continue
         w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e,
                                           inp.get("w13_gs"), inp.get("w2_gs"))
-        oracle.expert_rows(geo, xd[src[r0:r1] // sh.topk], w13d, w2d)
+        oracle.expert_rows(geo, xd[src[r0:r1] // sh.topk], w13d, w2d,
+                           None if "c_scales" not in inp else float(inp["c_scales"][e]))
         done_rows += r1 - r0
         n_exp += 1
         if time.perf_counter() - t0 > budget_s:
@@ -156,11 +163,110 @@ def write_counters(workload: str, fetch_dir: str, write_dir: str, command: str) 
     return 0
 
 
+def counter_summary(workload: str, out_md: str, dirs: list, command: str) -> int:
+    """Summarise rocprofv3 --pmc runs of this script (one folder per pass) into a
+    markdown table per kernel of the step: each counter's mean per launch, and the
+    derived figures -- MFMA busy fraction and effective clock (SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE and the launches' own timestamps), issued MFMA work against the
+    algorithmic flops, HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by what they
+    read for the plain 1 GiB copy (--copy-calibration), and the L2 hit rate."""
+    import csv
+    import glob
+
+    import numpy as np
+
+    import moe_synth
+    sh = moe_synth.WORKLOADS[workload]
+    inp = moe_synth.make_inputs(sh, with_weights=False)
+    ids = np.asarray(inp["topk_idx"]).reshape(-1) if "topk_idx" in inp else None
+    if ids is None:  # from-logits routing: the same top-k the kernel takes (ties to the lower index)
+        ids = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :sh.topk].reshape(-1)
+    cnt = np.bincount(ids[(ids >= 0) & (ids < sh.experts)], minlength=sh.experts)
+    active, pairs = int((cnt > 0).sum()), int(cnt.sum())
+    wb_gu, wb_dn = weight_bytes_per_expert(sh)
+    algo = {"gate_up": (4.0 * pairs * sh.hidden * sh.inter, active * wb_gu + act_bytes(sh)),
+            "down": (2.0 * pairs * sh.hidden * sh.inter, active * wb_dn)}
+
+    def kind(name):
+        if "ffn_gemm_kernel" in name:
+            return "gate_up" if ", true, " in name.split(">")[0] else "down"
+        for k in ("combine", "plan_", "route_"):
+            if k in name:
+                return k.strip("_")
+        if "elementwise_kernel" in name:
+            return "copy"
+        return None
+
+    vals, durs = {}, {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = kind(r["Kernel_Name"])
+                if k is None:
+                    continue
+                vals.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                durs.setdefault(k, {})[(f, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    gib_kb = float(1 << 20)
+
+    def mean(k, c, pred=None):
+        v = [x for x in vals.get((k, c), []) if pred is None or pred(x)]
+        return sum(v) / len(v) if v else None
+
+    f_copy = mean("copy", "FETCH_SIZE", lambda x: x > 0.25 * gib_kb)
+    w_copy = mean("copy", "WRITE_SIZE", lambda x: x > 0.25 * gib_kb)
+    f_fac = gib_kb / f_copy if f_copy else None
+    w_fac = gib_kb / w_copy if w_copy else None
+    lines = [f"# Counters: {workload} (T={sh.tokens}, hidden {sh.hidden}, intermediate {sh.inter}, {sh.experts} experts, "
+             f"top-{sh.topk}, {sh.fmt})", "", "One rocprofv3 `--pmc` pass per counter group, each its own run:", "",
+             "```", command, "```", "",
+             f"Routing: {active} active experts, {pairs} routed pairs.  Copy calibration: FETCH_SIZE factor "
+             f"{f_fac if f_fac is None else round(f_fac, 3)}, WRITE_SIZE factor {w_fac if w_fac is None else round(w_fac, 3)} "
+             "(1 GiB read and written by a plain elementwise copy in the same process).", ""]
+    counters = sorted({c for (_, c) in vals})
+    for k in ("gate_up", "down", "combine", "plan"):
+        if not any(kk == k for (kk, _) in vals):
+            continue
+        dur = float(np.mean(list(durs[k].values())))
+        lines += [f"## {k}", "", f"Mean launch duration under the profiler: {dur:.1f} us "
+                  f"({len(durs[k])} profiled launches over all passes).", "", "| counter | mean per launch |", "|---|---|"]
+        for c in counters:
+            m = mean(k, c)
+            if m is not None:
+                lines.append(f"| {c} | {m:,.0f} |")
+        lines += ["", "| derived | value |", "|---|---|"]
+        busy, grbm = mean(k, "SQ_VALU_MFMA_BUSY_CYCLES"), mean(k, "GRBM_GUI_ACTIVE")
+        if busy is not None and grbm is not None:
+            per_xcd = grbm / 8.0
+            lines.append(f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs)) | "
+                         f"{busy / 1024.0 / per_xcd:.3f} |")
+            lines.append(f"| effective clock (GRBM_GUI_ACTIVE / 8 / launch duration) | {per_xcd / dur / 1e3:.2f} GHz |")
+        mops = mean(k, "SQ_INSTS_VALU_MFMA_MOPS_F8") or mean(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16") or \
+            mean(k, "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+        if mops is not None and k in algo:
+            lines.append(f"| issued MFMA flops (MOPS x 512) / algorithmic flops | {mops * 512 / algo[k][0]:.3f} |")
+        fetch, write = mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")
+        if fetch is not None and f_fac:
+            lines.append(f"| HBM fetch (FETCH_SIZE x {f_fac:.3f}) | {fetch * f_fac * 1024 / 1e6:,.1f} MB |")
+        if write is not None and w_fac:
+            lines.append(f"| HBM write (WRITE_SIZE x {w_fac:.3f}) | {write * w_fac * 1024 / 1e6:,.1f} MB |")
+        if fetch is not None and write is not None and f_fac and w_fac and k in algo:
+            t = (fetch * f_fac + write * w_fac) * 1024
+            lines.append(f"| traffic / algorithmic bytes ({algo[k][1] / 1e6:,.1f} MB) | {t / algo[k][1]:.2f} |")
+        hit, miss = mean(k, "TCC_HIT_sum"), mean(k, "TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            lines.append(f"| L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) | {hit / (hit + miss):.3f} |")
+        lines.append("")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 class Leg:
     """The step's kernels on one workload: inputs resident in HBM, weights in the
     prepared layout (written once, untimed), caller-owned plan, intermediate and y."""
 
-    def __init__(self, name: str):
+    def __init__(self, name: str, fuse_combine: bool = False):
         import numpy as np
         import torch
 
@@ -181,16 +287,19 @@ class Leg:
             return torch.from_numpy(a).cuda()
 
         self.sh, self.inp = sh, inp
+        self.fuse = fuse_combine
         self.x, self.x_sf = dev(inp["x"]), dev(inp["x_sf"])
         canonical = {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]), "w2": dev(inp["w2"]),
-                     "w2_sf": dev(inp["w2_sf"]), "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs"))}
+                     "w2_sf": dev(inp["w2_sf"]), "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs")),
+                     "c_input_scales": dev(inp.get("c_scales"))}
         self.logits = dev(inp["logits"])
         if sh.routing == "precomputed":
             self.topk_idx, self.topk_w = dev(inp["topk_idx"]), dev(inp["topk_weights"])
         else:
             self.topk_idx = torch.empty((T, k), dtype=torch.int64, device="cuda")
             self.topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-        self.moe = MoEFFN(H, I, E, k, T, fmt=sh.fmt, route_mode=sh.routing, activation_clamp=sh.clamp)
+        self.moe = MoEFFN(H, I, E, k, T, fmt=sh.fmt, route_mode=sh.routing, activation_clamp=sh.clamp,
+                          fuse_combine=fuse_combine)
         # one-time weight relayout (the pages' pre-permuted weights); outside every timed region
         self.weights = self.moe.prepare_weights(canonical)
         torch.cuda.synchronize()
@@ -201,21 +310,67 @@ class Leg:
         self.y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         self.stream = torch.cuda.current_stream()
+        self._calls = None
 
-    def step(self, legs=None):
-        """One pass of the whole path.  legs: optional 4 events (gate_up start/stop,
-        down start/stop) that the two GEMM launches carry themselves."""
+    def checked_step(self):
+        """One step through the binding's methods, which check every tensor argument."""
         m, T, s = self.moe, self.sh.tokens, self.stream
         if self.sh.routing == "precomputed":
             m.plan(T, self.plan, topk_idx=self.topk_idx, ws=self.ws, stream=s)
         else:
             m.plan(T, self.plan, routing_logits=self.logits, topk_idx_out=self.topk_idx, topk_weights_out=self.topk_w,
                    ws=self.ws, stream=s)
-        m.ffn_gate_up(T, self.x, self.x_sf, self.weights, self.plan, self.h, self.hsf, stream=s,
-                      events=None if legs is None else legs[:2])
-        m.ffn_down(T, self.h, self.hsf, self.weights, self.plan, self.y, stream=s,
-                   events=None if legs is None else legs[2:])
-        m.combine(T, self.y, self.topk_w, self.plan, self.out, stream=s)
+        m.ffn_gate_up(T, self.x, self.x_sf, self.weights, self.plan, self.h, self.hsf, stream=s)
+        if self.fuse:
+            m.ffn_down_combine(T, self.h, self.hsf, self.weights, self.plan, self.topk_w, self.y, self.out, stream=s)
+        else:
+            m.ffn_down(T, self.h, self.hsf, self.weights, self.plan, self.y, stream=s)
+            m.combine(T, self.y, self.topk_w, self.plan, self.out, stream=s)
+
+    def _build_calls(self):
+        """The C ABI calls of one step with their arguments marshalled once (the same
+        buffers every step, already checked by checked_step), so that issuing a step
+        costs the host a few microseconds and the GPU never waits for it."""
+        import ctypes
+        m, T, sh = self.moe, self.sh.tokens, self.sh
+        lib, h, s = m.lib, m._h, self.stream.cuda_stream
+        self._ws_s, self._ps = m._weights_struct(self.weights), m._plan_struct(self.plan)
+        W, P = ctypes.byref(self._ws_s), ctypes.byref(self._ps)
+        nb = self.ws.numel() * self.ws.element_size()
+        hsf = None if self.hsf is None else self.hsf.data_ptr()
+        x_sf = None if self.x_sf is None else self.x_sf.data_ptr()
+        if sh.routing == "precomputed":
+            plan = (h, T, self.topk_idx.data_ptr(), None, None, None, P, self.ws.data_ptr(), nb, s)
+        else:
+            plan = (h, T, None, self.logits.data_ptr(), self.topk_idx.data_ptr(), self.topk_w.data_ptr(), P,
+                    self.ws.data_ptr(), nb, s)
+        gu = (h, T, self.x.data_ptr(), x_sf, W, P, self.h.data_ptr(), hsf, s)
+        if self.fuse:
+            dn = (h, T, self.h.data_ptr(), hsf, W, P, self.topk_w.data_ptr(), self.y.data_ptr(), None, None,
+                  self.out.data_ptr(), s)
+        else:
+            dn = (h, T, self.h.data_ptr(), hsf, W, P, self.y.data_ptr(), s)
+        comb = (h, T, self.y.data_ptr(), self.topk_w.data_ptr(), P, self.out.data_ptr(), s)
+        self._calls = (lib, plan, gu, dn, comb)
+
+    def step(self, legs=None):
+        """One pass of the whole path.  legs: optional hipEvent_t handles (gate_up
+        start/stop, down start/stop) that the two GEMM launches carry themselves."""
+        if self._calls is None:
+            self._build_calls()
+        lib, plan, gu, dn, comb = self._calls
+        st = lib.moe_plan(*plan)
+        if legs is None:
+            st |= lib.moe_ffn_gate_up(*gu)
+            st |= lib.moe_ffn_down_combine(*dn) if self.fuse else lib.moe_ffn_down(*dn)
+        else:
+            st |= lib.moe_ffn_gate_up_timed(*gu, legs[0], legs[1])
+            st |= lib.moe_ffn_down_combine_timed(*dn, legs[2], legs[3]) if self.fuse else \
+                lib.moe_ffn_down_timed(*dn, legs[2], legs[3])
+        if not self.fuse:
+            st |= lib.moe_combine(*comb)
+        if st != 0:
+            raise RuntimeError(f"a step's C ABI call failed (status bits {st})")
 
     def counts(self):
         c = self.plan["expert_counts"].cpu().numpy()
@@ -249,8 +404,10 @@ def timed_steps(leg: Leg, steps: int, step_markers: bool, scrub=None):
     previous step.  Returns (elapsed s, per-step ms list or None, gate_up ms, down ms)."""
     import numpy as np
     import torch
+    from mixture_experts_ffn_topk_amd import _event_handles
     stride = max(1, steps // 10)
     legs = {i: _events(4) for i in range(0, steps, stride)}
+    handles = {i: _event_handles(e[:2]) + _event_handles(e[2:]) for i, e in legs.items()}
     marks = [_events(2) for _ in range(steps)] if step_markers else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -259,7 +416,7 @@ def timed_steps(leg: Leg, steps: int, step_markers: bool, scrub=None):
             torch.add(scrub, 1, out=scrub)
         if marks:
             marks[i][0].record(leg.stream)
-        leg.step(legs.get(i))
+        leg.step(handles.get(i))
         if marks:
             marks[i][1].record(leg.stream)
     torch.cuda.synchronize()
@@ -315,16 +472,22 @@ def main() -> int:
     ap.add_argument("--decode-workload", default="decode_fp8",
                     help="the weight-bound workload measured beside it (with a cache scrub); 'none' to skip")
     ap.add_argument("--scrub-mb", type=int, default=512, help="cache scrub between the weight-bound steps (MB)")
+    ap.add_argument("--fuse-combine", type=int, default=0, choices=(0, 1),
+                    help="1: the combine runs in the down GEMM's epilogue (moe_ffn_down_combine)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/gate_up_counters.json from two rocprofv3 --pmc output folders and exit")
     ap.add_argument("--counters-command", default="", help="the command the --pmc runs used (recorded)")
+    ap.add_argument("--counter-summary", nargs="+", metavar=("OUT_MD", "DIR"),
+                    help="summarise rocprofv3 --pmc folders (one per pass) of --workload into OUT_MD and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.write_counters:
         return write_counters(args.workload, args.write_counters[0], args.write_counters[1], args.counters_command)
+    if args.counter_summary:
+        return counter_summary(args.workload, args.counter_summary[0], args.counter_summary[1:], args.counters_command)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -339,13 +502,13 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    leg = Leg(args.workload)
+    leg = Leg(args.workload, args.fuse_combine)
     sh = leg.sh
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter
     scrub = torch.zeros(args.scrub_mb << 18, dtype=torch.float32, device="cuda") if args.scrub_mb > 0 else None
 
     log(f"warmup {args.warmup} steps")
-    leg.step()  # (at least one step, so that the plan's counts exist)
+    leg.checked_step()  # (at least one step, through the checked binding; the plan's counts then exist)
     for _ in range(args.warmup - 1):
         leg.step()
     torch.cuda.synchronize()
@@ -353,10 +516,19 @@ def main() -> int:
     weight_bound = roofline(leg, 1.0, 1.0)["bound"] == "hbm"
 
     # The timed region: exactly `steps` steps back to back; an event pair around every
-    # step gives the median and minimum (the weight-bound shapes also rewrite the
-    # scrub buffer before each step, outside the step's events).
+    # step gives the median and minimum.  A weight-bound workload then runs as many
+    # steps again with the scrub buffer rewritten before each step (outside the step's
+    # events), for its median and minimum without memory-side cache reuse.
     log(f"timing {args.steps} steps")
-    elapsed, per, gate_ms, down_ms = timed_steps(leg, args.steps, True, scrub if weight_bound else None)
+    elapsed, per, gate_ms, down_ms = timed_steps(leg, args.steps, True)
+    scrubbed = None
+    if weight_bound and scrub is not None:
+        _, per_s, gu_s, dn_s = timed_steps(leg, args.steps, True, scrub)
+        med = float(np.median(per_s))
+        scrubbed = {"scrub_mb": args.scrub_mb, "step_ms_median": round(med, 4),
+                    "step_ms_min": round(float(np.min(per_s)), 4),
+                    "step_hbm_frac_median": step_fracs(leg, med)["step_hbm_frac"],
+                    "gate_up_avg_launch_ms": round(gu_s, 4), "down_avg_launch_ms": round(dn_s, 4)}
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -382,15 +554,16 @@ def main() -> int:
         "step_tflops": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         **step_fracs(leg, ms_per_step),
-        "scrubbed": bool(weight_bound and scrub is not None),
+        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine),
         "roofline": roofline(leg, gate_ms, down_ms),
     }
 
     # The weight-bound decode shape beside it: its own warm-up, then the same number of
     # steps back to back, then as many with the cache scrub between steps.
     if args.decode_workload != "none" and args.decode_workload != args.workload:
-        dec = Leg(args.decode_workload)
-        for _ in range(max(1, args.warmup)):
+        dec = Leg(args.decode_workload, args.fuse_combine)
+        dec.checked_step()
+        for _ in range(args.warmup - 1):
             dec.step()
         el, _, gu, dn = timed_steps(dec, args.steps, False)
         _, per_s, gu_s, dn_s = timed_steps(dec, args.steps, True, scrub)

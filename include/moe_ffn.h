@@ -16,7 +16,7 @@
  *                 expert_start_indices, expert_ids, num_active_experts, src_info,
  *                 estimated_total_m (tile-regime gate), clamp_activation.
  *   [ActPack]     flashinfer.fused_moe.MoEActivationPack — operand encodings
- *                 (DeepSeek FP8, MXFP8, MXFP4 x MXFP8, BF16) and routing input
+ *                 (DeepSeek FP8, MXFP8, MXFP4 x MXFP8, BF16, NVFP4) and routing input
  *                 modes (precomputed ids/weights, FromLogits).
  *   [EPCombine]   DistributedEPCombine (MAX ep) — router_weights scale each
  *                 expert's contribution in the combine.
@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 6
+#define MOE_FFN_ABI_VERSION 8
 
 typedef enum {
   MOE_OK = 0,
@@ -79,7 +79,17 @@ typedef enum {
      [E,H,I/16] + w2_gs [E].  A weight is e2m1 * block scale * global scale
      ([MegaFFN] gate_up_expert_scales / down_expert_scales carry the per-expert
      scale).  The intermediate is bf16.  H and I multiples of 64. */
-  MOE_FMT_NVFP4_W4A16 = 3
+  MOE_FMT_NVFP4_W4A16 = 3,
+  /* "NVFP4 x NVFP4": x packed E2M1 [T,H/2] + E4M3 block scales [T,H/16] (x_sf);
+     weights as MOE_FMT_NVFP4_W4A16.  The per-expert scales are those of [MegaFFN]:
+     w13_gs = gate_up_expert_scales (the gate_up leg's output scale: the
+     activations' global scale times the weight's), w2_gs = down_expert_scales
+     (the down leg's output scale), c_input_scales = the global scale the
+     intermediate is requantised against: per (row, 16 columns) block scale
+     E4M3_RNE_sat(amax / (6 c)) and codes E2M1_RNE_sat(h / (s c)); the down leg
+     consumes codes x block scales (held exactly as bf16 in the caller-visible h
+     [T*k, I] of the split legs, h_sf unused).  H and I multiples of 64. */
+  MOE_FMT_NVFP4 = 4
 } moe_format;
 
 /* Routing input modes ([ActPack] routing_input_mode). */
@@ -110,6 +120,10 @@ typedef struct moe_config {
   int32_t out_fp32;             /* dtype of the combine output ([EPConfig] combine_dtype and the
                                    mega_ffn combine_dtype parameter leave it open): 0 = bf16
                                    [T,H] (one rounding of the fp32 sum), 1 = fp32 [T,H] */
+  int32_t fuse_combine;         /* 1: moe_forward runs the combine inside the down GEMM's
+                                   epilogue (moe_ffn_down_combine) instead of as its own
+                                   launch ([EPConfig] fuse_ffn_combine_send); same result, bit
+                                   for bit */
 } moe_config;
 
 /* (host struct of device pointers) Expert weights of this GPU: the canonical
@@ -124,6 +138,8 @@ typedef struct moe_weights {
                           (no relayout; a prepared struct points at the same
                           buffer); NULL for the other formats */
   const float* w2_gs;  /* NVFP4: likewise for down_weight */
+  const float* c_input_scales; /* NVFP4 x NVFP4: per-expert global scale of the requantised
+                                  intermediate [E] ([MegaFFN] c_input_scales); NULL otherwise */
 } moe_weights;
 
 /* (host struct of device pointers) Routing plan, int32 each ([MegaFFN] Args). */
@@ -135,6 +151,9 @@ typedef struct moe_plan_buffers {
   int32_t* src_info;              /* [T*k] row -> pair p = t*k + j (rows of an expert keep p order) */
   int32_t* pair_row;              /* [T*k] pair -> row, -1 for a masked slot */
   int32_t* status;                /* [1]   count of ids outside [0,E) other than -1 */
+  int32_t* combine_counters;      /* [T * ceil(H/128)] or NULL: arrival counters of the fused
+                                     combine ([MegaFFN] arrival_count), zeroed by moe_plan;
+                                     needed by moe_ffn_down_combine only */
 } moe_plan_buffers;
 
 typedef struct moe_handle moe_handle;
@@ -258,6 +277,28 @@ moe_status moe_ffn_down_timed(const moe_handle* h, int32_t num_tokens, const voi
                               const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
                               void* y, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+/* The down leg with the router-weighted combine fused into its epilogue
+   ([EPConfig] fuse_ffn_combine_send: the expert FFN's down epilogue feeds the
+   combine; [MegaFFN] arrival_count: per-destination arrival counts).  Each tile
+   stores its y rows, then counts them as arrived at their (token, column tile)
+   counters in plan->combine_counters (which moe_plan of the same plan zeroed;
+   NULL is MOE_ERR_INVALID_ARGUMENT); the tile whose arrival completes a token's
+   valid slots reduces that token's columns in slot order, exactly as moe_combine
+   (moe_combine_ex's addends shared / residual, NULL = absent; bf16 or fp32 out per
+   out_fp32).  y [T,k,H] bf16 is still written (the tiles exchange rows through
+   it); out [T,H] receives the result, bit for bit that of moe_ffn_down followed
+   by moe_combine_ex.  Tokens with no valid slot get the addends (or zeros). */
+moe_status moe_ffn_down_combine(const moe_handle* h, int32_t num_tokens, const void* h_in, const void* h_sf_in,
+                                const moe_weights* w /* host struct */,
+                                const moe_plan_buffers* plan /* host struct */, const float* topk_weights,
+                                void* y, const void* shared, const void* residual, void* out, hipStream_t stream);
+/* moe_ffn_down_combine with the launch-carried timing events of moe_ffn_down_timed. */
+moe_status moe_ffn_down_combine_timed(const moe_handle* h, int32_t num_tokens, const void* h_in,
+                                      const void* h_sf_in, const moe_weights* w /* host struct */,
+                                      const moe_plan_buffers* plan /* host struct */, const float* topk_weights,
+                                      void* y, const void* shared, const void* residual, void* out,
+                                      hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 /* Router-weighted combine ([EPCombine] router_weights): out[t] = sum over valid
    slots j in ascending order of topk_weights[t,j] * y[t,j,:], accumulated in
    fp32, written as bf16 [T,H] (fp32 [T,H] when moe_config.out_fp32).  A token with
@@ -280,7 +321,7 @@ moe_status moe_combine_ex(const moe_handle* h, int32_t num_tokens, const void* y
                           void* out, hipStream_t stream);
 
 /* The whole path in one call: plan (into ws), FFN (y in ws), combine into out
-   [T,H] bf16.  PRECOMPUTED: topk_idx / topk_weights are inputs and are not
+   [T,H] bf16 (fused into the down leg when fuse_combine).  PRECOMPUTED: topk_idx / topk_weights are inputs and are not
    modified.  FROM_LOGITS: routing_logits is the input and topk_idx / topk_weights
    receive the routing result.  w: prepared layout. */
 moe_status moe_forward(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,

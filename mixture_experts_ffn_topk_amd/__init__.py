@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
-FORMATS = {"fp8_block128": 0, "bf16": 1, "w4a8_mx": 2, "nvfp4_w4a16": 3}
+FORMATS = {"fp8_block128": 0, "bf16": 1, "w4a8_mx": 2, "nvfp4_w4a16": 3, "nvfp4": 4}
 ROUTE_MODES = {"precomputed": 0, "from_logits": 1}
 TILE_REGIMES = {"auto": 0, "decode": 1, "prefill": 2}
 
@@ -38,18 +38,19 @@ class _Config(ctypes.Structure):
                 ("max_num_tokens", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
                 ("format", ctypes.c_int32), ("route_mode", ctypes.c_int32),
                 ("topk_idx_bits", ctypes.c_int32), ("fast_math", ctypes.c_int32),
-                ("tile_regime", ctypes.c_int32), ("out_fp32", ctypes.c_int32)]
+                ("tile_regime", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("fuse_combine", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_sf", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p),
-                ("w13_gs", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p)]
+                ("w13_gs", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p), ("c_input_scales", ctypes.c_void_p)]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("expert_counts", "expert_start_indices", "expert_ids",
-                                               "num_active_experts", "src_info", "pair_row", "status")]
+                                               "num_active_experts", "src_info", "pair_row", "status",
+                                               "combine_counters")]
 
 
 class _PreparedSizes(ctypes.Structure):
@@ -60,6 +61,7 @@ PLAN_FIELDS = [f for f, _ in _Plan._fields_]
 EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
             "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_ffn_gate_up_timed", "moe_ffn_down_timed",
+            "moe_ffn_down_combine", "moe_ffn_down_combine_timed",
             "moe_forward_static", "moe_status_string", "moe_abi_version"]
 STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 
@@ -97,6 +99,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_gate_up_timed.restype = i32
     lib.moe_ffn_down_timed.argtypes = lib.moe_ffn_down.argtypes + [vp, vp]
     lib.moe_ffn_down_timed.restype = i32
+    lib.moe_ffn_down_combine.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp,
+                                         vp, vp, vp, vp]
+    lib.moe_ffn_down_combine.restype = i32
+    lib.moe_ffn_down_combine_timed.argtypes = lib.moe_ffn_down_combine.argtypes + [vp, vp]
+    lib.moe_ffn_down_combine_timed.restype = i32
     lib.moe_combine.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Plan), vp, vp]
     lib.moe_combine.restype = i32
     lib.moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, sz, vp]
@@ -193,11 +200,13 @@ class MoEFFN:
     def __init__(self, hidden: int, intermediate_hidden: int, num_experts: int, num_topk: int,
                  max_num_tokens: int, fmt: str = "fp8_block128", route_mode: str = "precomputed",
                  activation_clamp: float = 10.0, topk_idx_bits: int = 64, fast_math: bool = True,
-                 tile_regime: str = "auto", out_fp32: bool = False):
+                 tile_regime: str = "auto", out_fp32: bool = False, fuse_combine: bool = False):
         self.lib = load_library()
         self.cfg = _Config(hidden, intermediate_hidden, num_experts, num_topk, max_num_tokens,
                            float(activation_clamp), FORMATS[fmt], ROUTE_MODES[route_mode], topk_idx_bits,
-                           int(bool(fast_math)), TILE_REGIMES[tile_regime], int(bool(out_fp32)))
+                           int(bool(fast_math)), TILE_REGIMES[tile_regime], int(bool(out_fp32)),
+                           int(bool(fuse_combine)))
+        self.fuse_combine = bool(fuse_combine)
         self.out_fp32 = bool(out_fp32)
         self.fmt, self.route_mode = fmt, route_mode
         self.hidden, self.inter, self.experts, self.topk = hidden, intermediate_hidden, num_experts, num_topk
@@ -219,12 +228,21 @@ class MoEFFN:
             pass
 
     # ---------------------------------------------------------------- argument checks
+    def _x_bytes(self, n: int) -> int:
+        """Bytes of an activation row of n elements."""
+        return {"bf16": 2 * n, "nvfp4_w4a16": 2 * n, "nvfp4": n // 2}.get(self.fmt, n)
+
+    def _x_sf_row(self) -> int:
+        """Bytes of activation scales per token."""
+        H = self.hidden
+        return {"fp8_block128": H // 128 * 4, "w4a8_mx": H // 32, "nvfp4": H // 16}.get(self.fmt, 0)
+
     def _esz(self) -> int:
-        """Bytes per activation / intermediate element."""
-        return 2 if self.fmt in ("bf16", "nvfp4_w4a16") else 1
+        """Bytes per intermediate element."""
+        return 2 if self.fmt in ("bf16", "nvfp4_w4a16", "nvfp4") else 1
 
     def _sf_row(self, n: int) -> int:
-        """Bytes of activation scales per row of n elements."""
+        """Bytes of intermediate scales per row of n elements."""
         return {"fp8_block128": n // 128 * 4, "w4a8_mx": n // 32}.get(self.fmt, 0)
 
     def _idx_dtypes(self):
@@ -235,13 +253,13 @@ class MoEFFN:
         import torch
         E, n = self.experts, T * self.topk
         sizes = {"expert_counts": E, "expert_start_indices": E + 1, "expert_ids": E, "num_active_experts": 1,
-                 "src_info": n, "pair_row": n, "status": 1}
+                 "src_info": n, "pair_row": n, "status": 1, "combine_counters": T * self._cnt_stride()}
         for f in PLAN_FIELDS:
-            _need(plan.get(f), f"plan['{f}']", 4 * sizes[f], (torch.int32,))
+            _need(plan.get(f), f"plan['{f}']", 4 * sizes[f], (torch.int32,), required=f != "combine_counters")
 
     def _check_x(self, x, x_sf, T: int):
-        _need(x, "x", T * self.hidden * self._esz())
-        _need(x_sf, "x_sf", T * self._sf_row(self.hidden), required=self._sf_row(self.hidden) > 0)
+        _need(x, "x", T * self._x_bytes(self.hidden))
+        _need(x_sf, "x_sf", T * self._x_sf_row(), required=self._x_sf_row() > 0)
 
     def _check_weights(self, w: dict):
         import torch
@@ -249,8 +267,8 @@ class MoEFFN:
             self._psizes = self.prepared_weights_size()
         for n, b in self._psizes.items():
             _need(w.get(n), f"weights['{n}']", b, required=b > 0)
-        if self.fmt == "nvfp4_w4a16":
-            for g in ("w13_gs", "w2_gs"):
+        if self.fmt in ("nvfp4_w4a16", "nvfp4"):
+            for g in ("w13_gs", "w2_gs") + (("c_input_scales",) if self.fmt == "nvfp4" else ()):
                 _need(w.get(g), f"weights['{g}']", 4 * self.experts, (torch.float32,))
 
     def _check_routing_in(self, T: int, topk_idx, routing_logits, routing_bias):
@@ -283,7 +301,7 @@ class MoEFFN:
             dev = weights["w13"].device
             out = {n: (torch.empty(b, dtype=torch.uint8, device=dev) if b else None)
                    for n, b in self.prepared_weights_size().items()}
-        for g in ("w13_gs", "w2_gs"):  # NVFP4 global scales: read as given, no relayout
+        for g in ("w13_gs", "w2_gs", "c_input_scales"):  # NVFP4 per-expert scales: read as given, no relayout
             if weights.get(g) is not None:
                 out.setdefault(g, weights[g])
         cw, pw = self._weights_struct(weights), self._weights_struct(out)
@@ -295,17 +313,22 @@ class MoEFFN:
         import torch
         E, np_ = self.experts, max(1, num_tokens * self.topk)
         sizes = {"expert_counts": E, "expert_start_indices": E + 1, "expert_ids": E, "num_active_experts": 1,
-                 "src_info": np_, "pair_row": np_, "status": 1}
+                 "src_info": np_, "pair_row": np_, "status": 1,
+                 "combine_counters": max(1, num_tokens) * self._cnt_stride()}
         return {k: torch.empty(v, dtype=torch.int32, device=device) for k, v in sizes.items()}
+
+    def _cnt_stride(self) -> int:
+        """Fused-combine arrival counters per token: ceil(H / 128)."""
+        return (self.hidden + 127) // 128
 
     @staticmethod
     def _plan_struct(plan: dict) -> _Plan:
-        return _Plan(*[_ptr(plan[f]) for f in PLAN_FIELDS])
+        return _Plan(*[_ptr(plan.get(f)) for f in PLAN_FIELDS])
 
     @staticmethod
     def _weights_struct(w: dict) -> _Weights:
         return _Weights(_ptr(w["w13"]), _ptr(w.get("w13_sf")), _ptr(w["w2"]), _ptr(w.get("w2_sf")),
-                        _ptr(w.get("w13_gs")), _ptr(w.get("w2_gs")))
+                        _ptr(w.get("w13_gs")), _ptr(w.get("w2_gs")), _ptr(w.get("c_input_scales")))
 
     @staticmethod
     def _nbytes(t) -> int:
@@ -351,7 +374,7 @@ class MoEFFN:
         """(h, h_sf) buffers for moe_ffn_gate_up / moe_ffn_down."""
         import torch
         n = max(1, num_tokens * self.topk)
-        if self.fmt in ("bf16", "nvfp4_w4a16"):
+        if self.fmt in ("bf16", "nvfp4_w4a16", "nvfp4"):
             return torch.empty((n, self.inter), dtype=torch.bfloat16, device=device), None
         h = torch.empty((n, self.inter), dtype=torch.uint8, device=device)
         if self.fmt == "fp8_block128":
@@ -395,6 +418,31 @@ class MoEFFN:
             _check(self.lib.moe_ffn_down(*args), "moe_ffn_down")
         else:
             _check(self.lib.moe_ffn_down_timed(*args, *_event_handles(events)), "moe_ffn_down_timed")
+
+    def ffn_down_combine(self, num_tokens, h, h_sf, weights: dict, plan: dict, topk_weights, y, out, stream=None,
+                         shared=None, residual=None, events=None):
+        """moe_ffn_down_combine(_timed): the down leg with the combine fused into its
+        epilogue; plan must hold combine_counters zeroed by moe_plan."""
+        import torch
+        T = num_tokens
+        _need(h, "h", T * self.topk * self.inter * self._esz())
+        _need(h_sf, "h_sf", T * self.topk * self._sf_row(self.inter), required=self._sf_row(self.inter) > 0)
+        self._check_weights(weights)
+        self._check_plan(plan, T)
+        _need(plan.get("combine_counters"), "plan['combine_counters']", 4 * T * self._cnt_stride(), (torch.int32,))
+        _need(topk_weights, "topk_weights", T * self.topk * 4, (torch.float32,))
+        _need(y, "y", T * self.topk * self.hidden * 2, elem=2)
+        self._check_out(T, out, shared, residual)
+        _on_gpu(h=h, h_sf=h_sf, weights=weights, plan=plan, topk_weights=topk_weights, y=y, out=out, shared=shared,
+                residual=residual)
+        ws_ = self._weights_struct(weights)
+        ps = self._plan_struct(plan)
+        args = (self._h, T, _ptr(h), _ptr(h_sf), ctypes.byref(ws_), ctypes.byref(ps), _ptr(topk_weights), _ptr(y),
+                _ptr(shared), _ptr(residual), _ptr(out), _stream(stream))
+        if events is None:
+            _check(self.lib.moe_ffn_down_combine(*args), "moe_ffn_down_combine")
+        else:
+            _check(self.lib.moe_ffn_down_combine_timed(*args, *_event_handles(events)), "moe_ffn_down_combine_timed")
 
     def _check_out(self, T, out, shared, residual):
         _need(out, "out", T * self.hidden * (4 if self.out_fp32 else 2), elem=4 if self.out_fp32 else 2)

@@ -20,7 +20,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   // moe_forward: [plan buffers][y][union(plan scratch, h + h_sf)]
-  size_t counts, start, ids, nact, status, src, prow, plan_end;
+  size_t counts, start, ids, nact, status, src, prow, cnt, plan_end;
   size_t y, y_end;
   size_t scratch;  // plan scratch or h, h_sf
   size_t h_off, hsf_off, ffn_bytes, plan_scratch_bytes, total;
@@ -31,11 +31,16 @@ moe::Fmt to_fmt(int f) {
     case MOE_FMT_FP8_BLOCK128: return moe::Fmt::FP8;
     case MOE_FMT_BF16: return moe::Fmt::BF16;
     case MOE_FMT_NVFP4_W4A16: return moe::Fmt::NV4;
+    case MOE_FMT_NVFP4: return moe::Fmt::NVF4;
     default: return moe::Fmt::MX;
   }
 }
-// bf16 activations and intermediate, no activation scales
+// the encoding of the weights (NVFP4 x NVFP4 shares NVFP4 x BF16's)
+moe::Fmt weight_fmt(int f) { return f == MOE_FMT_NVFP4 ? moe::Fmt::NV4 : to_fmt(f); }
+// bf16 activations, no activation scales
 bool bf16_acts(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_NVFP4_W4A16; }
+// bf16 intermediate, no intermediate scales
+bool bf16_inter(int f) { return bf16_acts(f) || f == MOE_FMT_NVFP4; }
 
 Layout layout_for(const moe_config& c, int T) {
   Layout L{};
@@ -48,6 +53,7 @@ Layout layout_for(const moe_config& c, int T) {
   L.status = o; o = align_up(o + 4);
   L.src = o; o = align_up(o + np * 4);
   L.prow = o; o = align_up(o + np * 4);
+  L.cnt = o; o = align_up(o + (size_t)T * moe::combine_counter_stride(c.hidden) * 4);
   L.plan_end = o;
   L.y = o; o = align_up(o + np * (size_t)c.hidden * 2);
   L.y_end = o;
@@ -63,9 +69,10 @@ Layout layout_for(const moe_config& c, int T) {
 
 bool valid_T(const moe_handle* h, int32_t T) { return h && T >= 0 && T <= h->cfg.max_num_tokens; }
 
-moe::PlanPtrs plan_ptrs(const moe_plan_buffers* p) {
+moe::PlanPtrs plan_ptrs(const moe_plan_buffers* p, int T, int H) {
   return moe::PlanPtrs{p->expert_counts, p->expert_start_indices, p->expert_ids, p->num_active_experts,
-                       p->src_info,      p->pair_row,             p->status};
+                       p->src_info,      p->pair_row,             p->status,     p->combine_counters,
+                       p->combine_counters ? T * moe::combine_counter_stride(H) : 0};
 }
 
 bool plan_complete(const moe_plan_buffers* p) {
@@ -101,12 +108,21 @@ moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const flo
     if (e != hipSuccess) return MOE_ERR_HIP;
     ids = idx_out;
   }
-  return hip_status(moe::launch_plan(ids, idx64, T * c.num_topk, c.num_experts, plan_ptrs(plan), (int*)scratch, s));
+  return hip_status(
+      moe::launch_plan(ids, idx64, T * c.num_topk, c.num_experts, plan_ptrs(plan, T, c.hidden), (int*)scratch, s));
 }
+
+// The combine fused into the down leg: router weights, addends and the output.
+struct Fused {
+  const float* topk_w;
+  const void* shared;
+  const void* residual;
+  void* out;
+};
 
 moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
                   const moe_plan_buffers* plan, void* y, void* hbuf, void* hsf, hipStream_t s, int stage,
-                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr, const Fused* fused = nullptr) {
   const moe_config& c = h->cfg;
   moe::FfnArgs a{};
   a.fmt = to_fmt(c.format);
@@ -128,18 +144,30 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
   a.w2_sf = w->w2_sf;
   a.w13_gs = w->w13_gs;
   a.w2_gs = w->w2_gs;
+  a.c_scales = w->c_input_scales;
   a.h = hbuf;
   a.h_sf = hsf;
   a.y = y;
   if (stage == 1) a.ev[0] = e0, a.ev[1] = e1;
   if (stage == 2) a.ev[2] = e0, a.ev[3] = e1;
+  if (fused) {
+    a.fuse_combine = true;
+    a.pair_row = plan->pair_row;
+    a.topk_w = fused->topk_w;
+    a.counters = plan->combine_counters;
+    a.out = fused->out;
+    a.shared = fused->shared;
+    a.residual = fused->residual;
+    a.out_f32 = c.out_fp32 != 0;
+  }
   return hip_status(moe::launch_ffn(a, s, stage));
 }
 
 bool weights_ok(const moe_config& c, const moe_weights* w) {
   if (!w || !w->w13 || !w->w2) return false;
   if (c.format != MOE_FMT_BF16 && (!w->w13_sf || !w->w2_sf)) return false;
-  if (c.format == MOE_FMT_NVFP4_W4A16 && (!w->w13_gs || !w->w2_gs)) return false;
+  if ((c.format == MOE_FMT_NVFP4_W4A16 || c.format == MOE_FMT_NVFP4) && (!w->w13_gs || !w->w2_gs)) return false;
+  if (c.format == MOE_FMT_NVFP4 && !w->c_input_scales) return false;
   return true;
 }
 
@@ -155,13 +183,16 @@ bool sizes_supported(const moe_config& c) {
   const unsigned long long T = (unsigned long long)c.max_num_tokens, H = (unsigned long long)c.hidden,
                            I = (unsigned long long)c.intermediate_hidden, k = (unsigned long long)c.num_topk;
   const unsigned long long act = bf16_acts(c.format) ? 2 : 1;  // bytes per activation element
-  if (T * H * act > kMaxBytes || T * k * I * act > kMaxBytes) return false;
+  const unsigned long long inter = bf16_inter(c.format) ? 2 : 1;  // bytes per intermediate element
+  if (T * H * act > kMaxBytes || T * k * I * inter > kMaxBytes) return false;
   // prepared weight bytes per expert
-  const moe::Fmt f = to_fmt(c.format);
+  const moe::Fmt f = weight_fmt(c.format);
   if (moe::prepared_expert_bytes(f, (int)(2 * I), (int)H) > kMaxBytes ||
       moe::prepared_expert_bytes(f, (int)H, (int)I) > kMaxBytes)
     return false;
   if (c.format == MOE_FMT_FP8_BLOCK128 && (H / 128 > 256 || I / 128 > 256)) return false;
+  // the fused combine addresses y [T*k, H] bf16 through a buffer resource
+  if (c.fuse_combine && T * k * H * 2 > kMaxBytes) return false;
   return true;
 }
 
@@ -194,6 +225,7 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
   if (c.route_mode != MOE_ROUTE_PRECOMPUTED && c.route_mode != MOE_ROUTE_FROM_LOGITS) return MOE_ERR_INVALID_ARGUMENT;
   if (c.tile_regime < MOE_TILES_AUTO || c.tile_regime > MOE_TILES_PREFILL) return MOE_ERR_INVALID_ARGUMENT;
   if (c.out_fp32 != 0 && c.out_fp32 != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.fuse_combine != 0 && c.fuse_combine != 1) return MOE_ERR_INVALID_ARGUMENT;
   switch (c.format) {
     case MOE_FMT_FP8_BLOCK128:
       if (c.hidden % 128 || c.intermediate_hidden % 128) return MOE_ERR_INVALID_ARGUMENT;
@@ -205,6 +237,7 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
       if (c.hidden % 32 || c.intermediate_hidden % 32) return MOE_ERR_INVALID_ARGUMENT;
       break;
     case MOE_FMT_NVFP4_W4A16:
+    case MOE_FMT_NVFP4:
       if (c.hidden % 64 || c.intermediate_hidden % 64) return MOE_ERR_INVALID_ARGUMENT;
       break;
     default:
@@ -224,7 +257,7 @@ void moe_destroy(moe_handle* h) { delete h; }
 moe_status moe_prepared_weights_size(const moe_handle* h, moe_prepared_sizes* out) {
   if (!h || !out) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = h->cfg;
-  const moe::Fmt f = to_fmt(c.format);
+  const moe::Fmt f = weight_fmt(c.format);
   const size_t E = (size_t)c.num_experts;
   const int H = c.hidden, I = c.intermediate_hidden;
   out->w13 = E * moe::prepared_expert_bytes(f, 2 * I, H);
@@ -247,7 +280,7 @@ moe_status moe_prepare_weights(const moe_handle* h, const moe_weights* canonical
     return MOE_ERR_INVALID_ARGUMENT;
   if (prepared->w13 == canonical->w13 || prepared->w2 == canonical->w2) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = h->cfg;
-  const moe::Fmt f = to_fmt(c.format);
+  const moe::Fmt f = weight_fmt(c.format);
   hipError_t e = moe::launch_prepare(f, c.num_experts, 2 * c.intermediate_hidden, c.hidden, true, canonical->w13,
                                      canonical->w13_sf, (void*)prepared->w13, (void*)prepared->w13_sf, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -300,7 +333,7 @@ moe_status moe_ffn_gate_up_timed(const moe_handle* h, int32_t T, const void* x, 
                                  const moe_weights* w, const moe_plan_buffers* plan, void* h_out, void* h_sf_out,
                                  hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (!bf16_acts(h->cfg.format) && !h_sf_out)))
+  if (T > 0 && (!x_ok(h->cfg, x, x_sf) || !h_out || (!bf16_inter(h->cfg.format) && !h_sf_out)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!al(x, 16) || !al(x_sf, 4) || !al(h_out, 16) || !al(h_sf_out, 4)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
@@ -316,7 +349,7 @@ moe_status moe_ffn_down_timed(const moe_handle* h, int32_t T, const void* h_in, 
                               const moe_weights* w, const moe_plan_buffers* plan, void* y, hipStream_t stream,
                               hipEvent_t start, hipEvent_t stop) {
   if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!h_in || !y || (!bf16_acts(h->cfg.format) && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!h_in || !y || (!bf16_inter(h->cfg.format) && !h_sf_in))) return MOE_ERR_INVALID_ARGUMENT;
   if (!al(h_in, 16) || !al(h_sf_in, 4) || !al(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2,
@@ -326,6 +359,31 @@ moe_status moe_ffn_down_timed(const moe_handle* h, int32_t T, const void* h_in, 
 moe_status moe_ffn_down(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in, const moe_weights* w,
                         const moe_plan_buffers* plan, void* y, hipStream_t stream) {
   return moe_ffn_down_timed(h, T, h_in, h_sf_in, w, plan, y, stream, nullptr, nullptr);
+}
+
+moe_status moe_ffn_down_combine_timed(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in,
+                                      const moe_weights* w, const moe_plan_buffers* plan, const float* topk_weights,
+                                      void* y, const void* shared, const void* residual, void* out,
+                                      hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!h_in || !y || !out || !topk_weights || !plan->combine_counters ||
+                (!bf16_inter(h->cfg.format) && !h_sf_in)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(h_in, 16) || !al(h_sf_in, 4) || !al(y, 16) || !al(out, 16) || !al(shared, 16) || !al(residual, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((unsigned long long)h->cfg.max_num_tokens * h->cfg.num_topk * h->cfg.hidden * 2 > 0x7FFFFFFFull)
+    return MOE_ERR_UNSUPPORTED;  // y is addressed through a 32-bit buffer offset
+  if (T == 0) return MOE_OK;
+  const Fused f{topk_weights, shared, residual, out};
+  return do_ffn(h, T, nullptr, nullptr, w, plan, y, const_cast<void*>(h_in), const_cast<void*>(h_sf_in), stream, 2,
+                start, stop, &f);
+}
+
+moe_status moe_ffn_down_combine(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in,
+                                const moe_weights* w, const moe_plan_buffers* plan, const float* topk_weights,
+                                void* y, const void* shared, const void* residual, void* out, hipStream_t stream) {
+  return moe_ffn_down_combine_timed(h, T, h_in, h_sf_in, w, plan, topk_weights, y, shared, residual, out, stream,
+                                    nullptr, nullptr);
 }
 
 moe_status moe_combine_ex(const moe_handle* h, int32_t T, const void* y, const float* topk_weights,
@@ -361,11 +419,17 @@ moe_status moe_forward_ex(const moe_handle* h, int32_t T, const void* x, const v
   char* base = (char*)ws;
   moe_plan_buffers plan{(int32_t*)(base + L.counts), (int32_t*)(base + L.start), (int32_t*)(base + L.ids),
                         (int32_t*)(base + L.nact),   (int32_t*)(base + L.src),   (int32_t*)(base + L.prow),
-                        (int32_t*)(base + L.status)};
+                        (int32_t*)(base + L.status),
+                        c.fuse_combine ? (int32_t*)(base + L.cnt) : nullptr};
   moe_status st =
       do_plan(h, T, topk_idx, routing_logits, routing_bias, topk_idx, topk_weights, &plan, base + L.scratch, stream);
   if (st != MOE_OK || T == 0) return st;
   void* y = base + L.y;
+  if (c.fuse_combine) {
+    const Fused f{topk_weights, shared, residual, out};
+    return do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0,
+                  nullptr, nullptr, &f);
+  }
   st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, shared, residual, out,

@@ -32,6 +32,21 @@ MOE_DEV uint32_t f32x2_to_e4m3_sat(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// fp32 -> the nearest E2M1 value (0, .5, 1, 1.5, 2, 3, 4, 6 and negatives), ties to
+// the even code, saturated at +-6: E2M1 steps by 0.5 below 2, by 1 in [2, 4) and
+// by 2 from 4, and rintf rounds half to even, which is the even code on each grid.
+MOE_DEV float e2m1_rne_sat(float v) {
+  const float a = fminf(fabsf(v), 6.0f);
+  float r;
+  if (a < 2.0f)
+    r = __builtin_rintf(a * 2.0f) * 0.5f;
+  else if (a < 4.0f)
+    r = __builtin_rintf(a);
+  else
+    r = __builtin_rintf(a * 0.5f) * 2.0f;
+  return __builtin_copysignf(r, v);
+}
+
 // ---------------------------------------------------------------- activation
 // x * sigmoid(x).  fast: hardware exp2 and reciprocal; else IEEE expf / divide.
 template <bool FAST>

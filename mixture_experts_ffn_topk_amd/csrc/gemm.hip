@@ -53,7 +53,9 @@ constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
 // Formats whose MFMA runs on bf16 operands (32x32x16): BF16, and NV4, whose
 // E2M1 weights are decoded to bf16 in registers.  Both take bf16 activations.
-constexpr bool bf16_mma(Fmt f) { return f == Fmt::BF16 || f == Fmt::NV4; }
+constexpr bool bf16_mma(Fmt f) { return f == Fmt::BF16 || f == Fmt::NV4 || f == Fmt::NVF4; }
+// Formats whose weights are NVFP4, decoded to bf16 in registers.
+constexpr bool nv4w(Fmt f) { return f == Fmt::NV4 || f == Fmt::NVF4; }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -94,7 +96,8 @@ struct Tile {
   // spread over all LDS banks (a padded row stride still halves the read rate).
   // Weight-bound BF16 tiles keep a padded 144-byte row instead: the swizzle's
   // per-sub-step offsets do not fit their register budget.
-  static constexpr bool kDma = F != Fmt::MX && BM > 96;  // direct-to-LDS staging (below)
+  // direct-to-LDS staging (below); NVFP4 activations are decoded on the way to LDS
+  static constexpr bool kDma = F != Fmt::MX && F != Fmt::NVF4 && BM > 96;
   static constexpr int kSwz = bf16_mma(F) && !kDma ? 0 : 7;
   static constexpr int kARowBytes = bf16_mma(F) && !kDma ? 144 : 128;
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
@@ -123,6 +126,67 @@ struct Tile {
   static constexpr int kNB = GATEUP ? 2 * kHB : BN / 128 + 1;
   static constexpr int kLds = kUnion + kABufs * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? kNB * kMaxKSteps * 4 : 0);
 };
+
+// out[t, col .. col+8) = the sum over token t's valid slots j, in ascending order,
+// of w[t,j] * y[t,j, col .. col+8) in fp32, then + shared + residual, rounded once
+// to bf16 (or stored as fp32): the arithmetic of the separate combine kernel.
+// The y rows are read with device-scope coherent loads (they were stored by
+// other workgroups, possibly on other XCDs, with device-scope stores), all of a
+// group of 8 slots issued before the first is used (a masked slot's row is read
+// but not added).
+MOE_DEV void combine_chunk8(const GemmParams& p, __amdgpu_buffer_rsrc_t y_rs, int t, int col) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const long long p0 = (long long)t * p.topk;
+  for (int j0 = 0; j0 < p.topk; j0 += 8) {
+    i32x4 v[8];
+    bool ok[8];
+    float wj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const bool in = j < p.topk;
+      ok[u] = in && p.pair_row[p0 + (in ? j : 0)] >= 0;
+      wj[u] = p.topk_w[p0 + (in ? j : 0)];
+      v[u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     y_rs, (uint32_t)((p0 + (in ? j : 0)) * p.c_row_bytes + (long long)col * 2), 0, kCpolDevice));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t e = (uint32_t)v[u][q];
+        acc[2 * q] = fmaf(wj[u], bf16_to_f32((uint16_t)(e & 0xFFFFu)), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wj[u], bf16_to_f32((uint16_t)(e >> 16)), acc[2 * q + 1]);
+      }
+    }
+  }
+  const uint16_t* add[2] = {p.shared, p.residual};
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if (add[a] == nullptr) continue;
+    const i32x4 v = *(const i32x4*)(add[a] + (long long)t * p.N + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t e = (uint32_t)v[q];
+      acc[2 * q] += bf16_to_f32((uint16_t)(e & 0xFFFFu));
+      acc[2 * q + 1] += bf16_to_f32((uint16_t)(e >> 16));
+    }
+  }
+  if (p.out_f32) {
+    f32x4* o = (f32x4*)((float*)p.out + (long long)t * p.N + col);
+    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    i32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
+    *(i32x4*)((uint16_t*)p.out + (long long)t * p.N + col) = o;
+  }
+}
+constexpr int kZeroSlotTokens = 64;  // tokens per workgroup that looks for tokens without a valid slot
 
 // WAVES waves per workgroup and room for WGS workgroups per CU: the second
 // launch bound is the minimum number of waves per SIMD, which caps a wave's
@@ -153,6 +217,19 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   float* sb_lds = red_lds + WAVES * BM;                      // FP8: [kNB][kMaxKSteps] weight scales
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+
+  // Fused combine: the workgroups past the GEMM grid write the output of the tokens
+  // that have no valid slot (no tile will reduce them): the addends, or zeros.
+  if (!GATEUP && p.fuse && (int)blockIdx.x >= p.m_grid) {
+    const int t0 = ((int)blockIdx.x - p.m_grid) * kZeroSlotTokens;
+    for (int t = t0; t < min(p.T, t0 + kZeroSlotTokens); ++t) {
+      bool any = false;
+      for (int j = 0; j < p.topk; ++j) any |= p.pair_row[(long long)t * p.topk + j] >= 0;
+      if (any) continue;  // (uniform: every thread reads the same entries)
+      for (int col = tid * 8; col < p.N; col += kThreads * 8) combine_chunk8(p, make_rsrc(p.C, p.y_bytes), t, col);
+    }
+    return;
+  }
 
   // ---------------------------------------------------------------- tile decode
   // The grid is sized for the worst case; the real m-tile count (per-expert tile
@@ -227,7 +304,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   constexpr bool kMxDenseSc = F == Fmt::MX && NT == 4;
   uint32_t bsc_dense = kOOB;
   {
-    if (F == Fmt::MX || F == Fmt::NV4)
+    if (F == Fmt::MX || nv4w(F))
       bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -250,7 +327,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       const bool ok = col0 < p.N;
       b_off[nt] = ok ? tiles0 * p.b_tile + (uint32_t)lane * 16u : kOOB;
       // MX: the lane's scale byte; NV4: the four scale bytes of the lane's tile row
-      bsc_off[nt] = ok ? (F == Fmt::NV4 ? tiles0 * 128u + (uint32_t)(lane & 31) * 4u : tiles0 * 64u + (uint32_t)lane)
+      bsc_off[nt] = ok ? (nv4w(F) ? tiles0 * 128u + (uint32_t)(lane & 31) * 4u : tiles0 * 64u + (uint32_t)lane)
                        : kOOB;
       if (kMxDenseSc && (lane >> 4) == nt) bsc_dense = ok ? tiles0 * 64u + (uint32_t)(lane & 15) * 4u : kOOB;
     }
@@ -303,7 +380,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       }
       return;
     }
-    if constexpr (F == Fmt::NV4) {
+    if constexpr (nv4w(F)) {
       // 32-row tile t: one 1 KB load of E2M1 data and the lanes' block scales
 #pragma unroll
       for (int t = 0; t < NT32; ++t) {
@@ -367,6 +444,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   for (int d = 0; d < (TL::kDma ? KSG : DEPTH); ++d) load_b(bq[d], d);
   __builtin_amdgcn_sched_barrier(0);
   uint32_t a_off[TL::kAChunks];
+  uint32_t a_sfo[F == Fmt::NVF4 ? TL::kAChunks : 1];
 #pragma unroll
   for (int i = 0; i < TL::kAChunks; ++i) {
     const int c = tid + kThreads * i;
@@ -374,7 +452,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     const uint32_t arow = GATEUP ? (uint32_t)(a_src[i] / p.topk) : (uint32_t)(row0 + r);
     // direct-to-LDS: slot c of the K-step block holds row r's chunk (c & 7) ^ (r & 7)
     const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ (r & 7)) : (uint32_t)(c & 7);
-    a_off[i] = r < rows ? arow * p.a_row_bytes + chunk * 16u : kOOB;
+    // NVF4: a chunk of 8 activations is 4 packed bytes
+    a_off[i] = r < rows ? arow * p.a_row_bytes + chunk * (F == Fmt::NVF4 ? 4u : 16u) : kOOB;
+    // NVF4: the E4M3 scale of the chunk's 16-element block (elements 64 ks + 8 (c & 7) ..)
+    if constexpr (F == Fmt::NVF4) a_sfo[i] = r < rows ? arow * (uint32_t)p.a_sf_row + ((c & 7) >> 1) : kOOB;
   }
   // FP8: the fp32 A scale of row tid per K-step; threads past the tile's rows load zeros
   const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
@@ -421,7 +502,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       for (int i = 0; i < TL::kAChunks; ++i) {
         uint32_t o = a_off[i] | dead;
         if (F == Fmt::MX) o |= oob_if(ks * 128 + (((tid + kThreads * i) & 7) * 16) >= p.K);  // K tail
-        v[u][i] = bload16(a_rs, o, (uint32_t)ks * 128u);
+        if constexpr (F == Fmt::NVF4) {
+          // 8 packed E2M1 values and their block's E4M3 scale, decoded in store_a
+          v[u][i][0] = (int)__builtin_amdgcn_raw_buffer_load_b32(a_rs, o, (uint32_t)ks * 32u, 0);
+          v[u][i][1] = (int)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, a_sfo[i] | dead, (uint32_t)ks * 4u, 0);
+        } else {
+          v[u][i] = bload16(a_rs, o, (uint32_t)ks * 128u);
+        }
       }
     }
     if constexpr (F == Fmt::FP8) {
@@ -448,7 +535,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
       for (int i = 0; i < TL::kAChunks; ++i) {
         const int c = tid + kThreads * i, r = c >> 3;
-        *(i32x4*)(base + r * TL::kARowBytes + (((c & 7) ^ (r & TL::kSwz)) * 16)) = v[u][i];
+        // NVF4: e2m1 x E4M3 block scale, exact in bf16
+        const i32x4 val = F == Fmt::NVF4 ? nv4_bf16x8((uint32_t)v[u][i][0], __builtin_amdgcn_cvt_f32_fp8(v[u][i][1], 0))
+                                         : v[u][i];
+        *(i32x4*)(base + r * TL::kARowBytes + (((c & 7) ^ (r & TL::kSwz)) * 16)) = val;
       }
     }
     if constexpr (F == Fmt::FP8) {
@@ -492,7 +582,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   };
   // VMEM instructions per stage: the A loads (D) and the weight-ring refills (R)
-  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * (F == Fmt::NV4 ? NT : NT * 2);
+  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * (nv4w(F) ? NT : NT * 2);
 
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
   uint32_t as[TL::kDma ? 1 : 2][kSfN] = {};
@@ -592,7 +682,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       auto rd_a = [&](int mt, int sub) {
         return *(const i32x4*)(abuf + (mt * 32 + r32) * TL::kARowBytes + 16 * ((2 * sub + h32) ^ (r32 & TL::kSwz)));
       };
-      if constexpr (F == Fmt::NV4) {
+      if constexpr (nv4w(F)) {
         // Sub-step outer: the weights of sub-step sub + 1 are decoded (VALU) while
         // the MFMAs of sub-step sub, issued just before, run on the matrix core.
         // Every token slice but the last is computed unconditionally (slices past
@@ -787,7 +877,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // tile's rows 8*(i/4) + 4*h32 + i%4 (i < 16); in a gate_up tile rows < 16 are
   // gate rows and row 16 + j the up row of gate row j, so acc32[..][i] pairs with [i + 8].
   const int r32 = lane & 31, h32 = lane >> 5;
-  if constexpr (F == Fmt::NV4) {
+  if constexpr (nv4w(F)) {
     // the expert's global weight scale multiplies every output of the leg
     const float gsc = p.B_gs[expert];
 #pragma unroll
@@ -798,7 +888,44 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   if (GATEUP) {
     constexpr int NJ = NT / 2;  // gate (and up) column tiles per wave
     const float c = p.clamp;
-    if constexpr (bf16_mma(F)) {
+    if constexpr (F == Fmt::NVF4) {
+      // NVFP4 requantisation of h against the expert's intermediate scale c_e (the
+      // c_input_scales of the max mega_ffn page): per (row, 16 columns) block scale
+      // s = E4M3_RNE_sat(amax / (6 c_e)) and codes E2M1_RNE_sat(h / (s c_e)).  The
+      // intermediate stores the codes times their block scale, exact in bf16; the
+      // down leg's output scale carries c_e.  A 32-row tile holds 16 h columns:
+      // lanes l and l ^ 32 share a token and hold 8 columns each.
+      const float ce = p.C_gs[expert];
+      const float six_c = 6.0f * ce;
+#pragma unroll
+      for (int mt = 0; mt < MT32; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT32; ++t) {
+          float v[2][4];
+          float m = 0.f;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[q][i] = swiglu_clamped<FAST>(acc32[mt][t][4 * q + i], acc32[mt][t][4 * q + i + 8], c);
+              m = fmaxf(m, fabsf(v[q][i]));
+            }
+          m = fmaxf(m, __shfl_xor(m, 32));
+          const float sb = __builtin_amdgcn_cvt_f32_fp8((int)f32x2_to_e4m3_sat(m / six_c, 0.f), 0);
+          const float den = sb * ce;
+          const float inv = den > 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = e2m1_rne_sat(v[q][i] * inv) * sb;
+            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+            *(uint2*)(out_lds + (mt * 32 + r32) * TL::kOutStride + (wave * HW + 16 * t + 8 * q + 4 * h32) * 2) =
+                uint2{w0, w1};
+          }
+        }
+    } else if constexpr (bf16_mma(F)) {
 #pragma unroll
       for (int mt = 0; mt < MT32; ++mt)
 #pragma unroll
@@ -907,15 +1034,54 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     if (tid < BM) pair_lds[tid] = pair_of_row;
     __syncthreads();
     constexpr int CPR = BN * 2 / 16;
+    const __amdgpu_buffer_rsrc_t y_rs = make_rsrc(p.C, p.y_bytes);
     for (int c = tid; c < BM * CPR; c += kThreads) {
       const int r = c / CPR, cc = c % CPR;
       const int col = n_tile * BN + cc * 8;
       if (r < rows && col < p.N) {
         const long long pair = pair_lds[r];
-        // y is read once, by the combine: a non-temporal store (decode down -6 %,
-        // prefill down -4 %: the weights the tiles re-read stay cached)
-        __builtin_nontemporal_store(*(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16),
-                                    (i32x4*)((uint8_t*)p.C + pair * p.c_row_bytes + (long long)col * 2));
+        const i32x4 v = *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
+        if (p.fuse) {
+          // fused combine: a device-scope store, written through to the level that
+          // every XCD reads coherently (another workgroup may reduce this row)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                                 y_rs, (uint32_t)(pair * p.c_row_bytes + (long long)col * 2), 0,
+                                                 kCpolDevice | kCpolNt);
+        } else {
+          // y is read once, by the combine: a non-temporal store (decode down -6 %,
+          // prefill down -4 %: the weights the tiles re-read stay cached)
+          __builtin_nontemporal_store(v, (i32x4*)((uint8_t*)p.C + pair * p.c_row_bytes + (long long)col * 2));
+        }
+      }
+    }
+    if (p.fuse) {
+      // Fused combine (the single-GPU form of the EPConfig page's fuse_ffn_combine_send;
+      // per-destination arrival counts as in the mega_ffn page's arrival_count).
+      // Each thread waits for its device-scope y stores to complete; then each tile
+      // row arrives at its (token, column tile) counter.  The arrival that completes
+      // a token's valid slots finds every other slot's row stored at device scope,
+      // and its workgroup reduces that token's column block with device-scope loads,
+      // in slot order: the result, bit for bit, of the separate combine, with no
+      // data atomics, no cache-wide write-back or invalidation, and no waiting.
+      __builtin_amdgcn_s_waitcnt(0);
+      int* comp = pair_lds + BM;       // [BM] tokens this tile completed
+      int* ncomp = pair_lds + 2 * BM;  // [1]
+      static_assert(WAVES * BM >= 2 * BM + 1, "room for the completion list");
+      if (tid == 0) *ncomp = 0;
+      __syncthreads();
+      if (tid < rows) {
+        const int t = pair_lds[tid] / p.topk;
+        int valid = 0;
+        for (int j = 0; j < p.topk; ++j) valid += p.pair_row[(long long)t * p.topk + j] >= 0;
+        const int old = atomicAdd(p.counters + (long long)t * p.cnt_stride + n_tile, 1);
+        if (old + 1 == valid) comp[atomicAdd(ncomp, 1)] = t;
+      }
+      __syncthreads();
+      const int nc = *ncomp;
+      constexpr int C8 = BN / 8;  // 8-column chunks of the tile's columns
+      for (int it = tid; it < nc * C8; it += kThreads) {
+        const int col = n_tile * BN + (it % C8) * 8;
+        if (col < p.N) combine_chunk8(p, y_rs, comp[it / C8], col);
       }
     }
   }
@@ -936,8 +1102,12 @@ int ffn_max_m_tiles(int npairs, int E, int bm) {
 template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, int WGS>
 // With timing events the launch carries them in its own dispatch, so they hold the
 // kernel's start and end, not those of separate marker commands in the stream.
-static void launch_one(const GemmParams& gp, bool fast, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const int grid = gp.m_tiles_max * gp.n_tiles;
+static void launch_one(const GemmParams& gp_in, bool fast, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  GemmParams gp = gp_in;
+  gp.m_grid = gp.m_tiles_max * gp.n_tiles;
+  int grid = gp.m_grid;
+  // fused combine: workgroups for the tokens without a valid slot
+  if (!GATEUP && gp.fuse) grid += (gp.T + kZeroSlotTokens - 1) / kZeroSlotTokens;
   if (grid <= 0) return;
   if (fast)
     hipExtLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, true>), dim3(grid),
@@ -999,6 +1169,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   const int elem_k = bf16_mma(a.fmt) ? 64 : 128;
   const uint32_t esz = bf16_mma(a.fmt) ? 2 : 1;
   const int sf_div = a.fmt == Fmt::FP8 ? 128 : 32;
+  const Fmt wf = a.fmt == Fmt::NVF4 ? Fmt::NV4 : a.fmt;  // the weights' encoding
   GemmParams g1{}, g2{};
   // gate_up: A = x rows gathered through src_info, B = w13 [E, 2I, H]
   g1.start = a.start;
@@ -1013,15 +1184,16 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.N = a.I;
   g1.n_rows = 2 * a.I;
   g1.A = (const uint8_t*)a.x;
-  g1.a_row_bytes = (uint32_t)a.H * esz;
+  g1.a_row_bytes = a.fmt == Fmt::NVF4 ? (uint32_t)a.H / 2 : (uint32_t)a.H * esz;  // NVF4: packed E2M1
   g1.a_bytes = g1.a_row_bytes * (uint32_t)a.T;
   g1.A_sf = a.x_sf;
-  g1.a_sf_row = a.H / sf_div;
+  g1.a_sf_row = a.fmt == Fmt::NVF4 ? a.H / 16 : a.H / sf_div;  // NVF4: one E4M3 scale per 16
   g1.a_sf_bytes = (uint32_t)a.T * (uint32_t)g1.a_sf_row * (a.fmt == Fmt::FP8 ? 4u : 1u);
   g1.B = (const uint8_t*)a.w13;
-  g1.b_tile = (uint32_t)prepared_tile_bytes(a.fmt);
-  g1.b_expert_bytes = (uint32_t)(prepared_expert_bytes(a.fmt, 2 * a.I, a.H));
-  g1.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(a.fmt, 2 * a.I, a.H));
+  g1.b_tile = (uint32_t)prepared_tile_bytes(wf);
+  g1.b_expert_bytes = (uint32_t)(prepared_expert_bytes(wf, 2 * a.I, a.H));
+  g1.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(wf, 2 * a.I, a.H));
+  g1.C_gs = a.c_scales;
   g1.B_sf = a.w13_sf;
   g1.b_sf_row = a.H / sf_div;
   g1.B_gs = a.w13_gs;
@@ -1044,8 +1216,8 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g2.a_sf_row = a.I / sf_div;
   g2.a_sf_bytes = (uint32_t)npairs * (uint32_t)g2.a_sf_row * (a.fmt == Fmt::FP8 ? 4u : 1u);
   g2.B = (const uint8_t*)a.w2;
-  g2.b_expert_bytes = (uint32_t)(prepared_expert_bytes(a.fmt, a.H, a.I));
-  g2.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(a.fmt, a.H, a.I));
+  g2.b_expert_bytes = (uint32_t)(prepared_expert_bytes(wf, a.H, a.I));
+  g2.bsc_expert_bytes = (uint32_t)(prepared_scale_expert_bytes(wf, a.H, a.I));
   g2.B_sf = a.w2_sf;
   g2.b_sf_row = a.I / sf_div;
   g2.B_gs = a.w2_gs;
@@ -1053,6 +1225,19 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g2.c_row_bytes = (long long)a.H * 2;
   g2.C_sf = nullptr;
   g2.c_sf_row = 0;
+  if (a.fuse_combine) {
+    g2.fuse = 1;
+    g2.T = a.T;
+    g2.pair_row = a.pair_row;
+    g2.topk_w = a.topk_w;
+    g2.counters = a.counters;
+    g2.cnt_stride = combine_counter_stride(a.H);
+    g2.out = a.out;
+    g2.shared = (const uint16_t*)a.shared;
+    g2.residual = (const uint16_t*)a.residual;
+    g2.out_f32 = a.out_f32 ? 1 : 0;
+    g2.y_bytes = (uint32_t)((size_t)npairs * a.H * 2);
+  }
   switch (a.fmt) {
     case Fmt::FP8:
       if (a.bm == 128) launch_pair<Fmt::FP8, 128>(g1, g2, a.fast, s, stage, a.ev);
@@ -1069,6 +1254,15 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
     case Fmt::NV4:
       if (bm == 128) launch_pair<Fmt::NV4, 128>(g1, g2, a.fast, s, stage, a.ev);
       else launch_pair<Fmt::NV4, 96>(g1, g2, a.fast, s, stage, a.ev);
+      break;
+    case Fmt::NVF4:  // gate_up decodes the NVFP4 activations; down is NV4's on the bf16 intermediate
+      if (bm == 128) {
+        if (stage != 2) launch_pair<Fmt::NVF4, 128>(g1, g2, a.fast, s, 1, a.ev);
+        if (stage != 1) launch_pair<Fmt::NV4, 128>(g1, g2, a.fast, s, 2, a.ev);
+      } else {
+        if (stage != 2) launch_pair<Fmt::NVF4, 96>(g1, g2, a.fast, s, 1, a.ev);
+        if (stage != 1) launch_pair<Fmt::NV4, 96>(g1, g2, a.fast, s, 2, a.ev);
+      }
       break;
   }
   return hipGetLastError();

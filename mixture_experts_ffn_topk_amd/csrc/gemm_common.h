@@ -50,13 +50,34 @@ struct GemmParams {
   uint32_t bsc_expert_bytes;  // MX: prepared scale bytes per expert
   const void* B_sf;
   int b_sf_row;  // FP8: K/128 floats per 128-row block
-  const float* B_gs;  // NV4: global weight scale per expert
+  const float* B_gs;  // NV4, NVF4: the leg's per-expert output scale (the weights' global scale)
+  const float* C_gs;  // NVF4 gate_up: per-expert global scale the intermediate is requantised against
   void* C;
   long long c_row_bytes;
   void* C_sf;
   int c_sf_row;
   float clamp;
+  // down leg with the combine fused into its epilogue (fuse != 0): the tile that
+  // stores the last valid slot of a token's column block reduces that block
+  int fuse;
+  int T;
+  const int* pair_row;    // [T*k] pair -> row, -1 for a masked slot
+  const float* topk_w;    // [T, k] router weights
+  int* counters;          // [T, cnt_stride] arrivals per (token, column tile), zero on entry
+  int cnt_stride;
+  void* out;              // [T, N] bf16 (fp32 if out_f32)
+  const uint16_t* shared;    // optional bf16 [T, N] addends
+  const uint16_t* residual;
+  int out_f32;
+  int m_grid;             // GEMM workgroups of the grid; those past it write the tokens without a valid slot
+  uint32_t y_bytes;       // size of y (fused combine: y is addressed through a buffer resource)
 };
+
+// Cache-policy bits of buffer loads and stores (gfx950): device-scope coherence
+// (stores write through to the level all XCDs share; loads do not hit lines that
+// another XCD may have changed), and the non-temporal hint.
+constexpr int kCpolDevice = 16;
+constexpr int kCpolNt = 2;
 
 MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);

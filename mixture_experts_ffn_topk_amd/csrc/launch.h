@@ -7,7 +7,10 @@
 
 namespace moe {
 
-enum class Fmt : int { FP8 = 0, BF16 = 1, MX = 2, NV4 = 3 };  // NV4: NVFP4 weights x bf16 activations
+// NV4: NVFP4 weights x bf16 activations; NVF4: NVFP4 weights x NVFP4 activations (its gate_up
+// leg decodes the activations while staging them; its down leg is NV4's on the bf16
+// intermediate that holds the requantised codes times their block scales)
+enum class Fmt : int { FP8 = 0, BF16 = 1, MX = 2, NV4 = 3, NVF4 = 4 };
 
 struct PlanPtrs {
   int* expert_counts;
@@ -17,6 +20,8 @@ struct PlanPtrs {
   int* src_info;
   int* pair_row;
   int* status;
+  int* counters;   // fused-combine arrival counters to zero, or nullptr
+  int n_counters;
 };
 
 // Routing plan: one fused block up to this many pairs, else count/scan/scatter
@@ -57,15 +62,28 @@ struct FfnArgs {
   const void* w13_sf;
   const void* w2;
   const void* w2_sf;
-  const float* w13_gs;  // NV4: fp32 global scale per expert [E]
+  const float* w13_gs;  // NV4: fp32 global scale per expert [E]; NVF4: the legs' per-expert output scales
   const float* w2_gs;
+  const float* c_scales;  // NVF4: per-expert global scale of the requantised intermediate [E]
   void* h;     // intermediate [T*k, I] (E4M3 or bf16)
   void* h_sf;  // its scales: fp32 [T*k, I/128] (FP8) or UE8M0 [T*k, I/32] (MX)
   void* y;     // [T*k, H] bf16, row p = src_info[row]
   // optional timing events (hipEvent_t or null) carried by the launch of each leg's
   // kernel: gate_up start/stop, down start/stop
   hipEvent_t ev[4];
+  // combine fused into the down leg (fuse_combine): out = sum_j w[t,j] y[t,j] (+ addends)
+  bool fuse_combine;
+  const int* pair_row;
+  const float* topk_w;
+  int* counters;  // [T, combine_counter_stride(H)] zeroed by the plan
+  void* out;
+  const void* shared;
+  const void* residual;
+  bool out_f32;
 };
+// int32 arrival counters per token that the fused combine needs: one per column
+// tile of the down leg, at most ceil(H / 128)
+inline int combine_counter_stride(int H) { return (H + 127) / 128; }
 size_t ffn_h_bytes(Fmt f, int rows, int I);
 size_t ffn_hsf_bytes(Fmt f, int rows, int I);
 int ffn_max_m_tiles(int npairs, int E, int bm);

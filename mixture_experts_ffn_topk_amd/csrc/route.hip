@@ -204,6 +204,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(const IdxT* __
   uint8_t* wcnt = (uint8_t*)(misc + 2 * kPlanWaves + 1);  // [kPlanWaves * E]
   short* ex = (short*)(wcnt + ((kPlanWaves * E + 15) & ~15));  // [npairs]
   const int tid = threadIdx.x;
+  // the fused combine's arrival counters start every call at zero
+  if (out.counters != nullptr)
+    for (int i = tid; i < out.n_counters; i += kPlanThreads) out.counters[i] = 0;
   for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
   for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcnt[i] = 0;
   if (tid == 0) misc[2 * kPlanWaves] = 0;
@@ -227,10 +230,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(const IdxT* __
 template <typename IdxT>
 __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const IdxT* __restrict__ ids, int npairs, int E,
                                                                   int per_block, int* __restrict__ hist,
-                                                                  int* __restrict__ bad_out) {
+                                                                  int* __restrict__ bad_out, int* __restrict__ counters,
+                                                                  int n_counters) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   int* cnt = lds;
   const int tid = threadIdx.x, b = blockIdx.x;
+  // the fused combine's arrival counters start every call at zero
+  if (counters != nullptr)
+    for (int i = b * kPlanThreads + tid; i < n_counters; i += gridDim.x * kPlanThreads) counters[i] = 0;
   for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
   if (tid == 0) lds[E] = 0;
   __syncthreads();
@@ -344,7 +351,7 @@ static hipError_t launch_plan_t(const IdxT* ids, int npairs, int E, const PlanPt
   int* hist = ws;
   int* bad = ws + (size_t)nb * E;
   hipLaunchKernelGGL(plan_count_kernel<IdxT>, dim3(nb), dim3(kPlanThreads), (E + 1) * sizeof(int), s, ids, npairs,
-                     E, kPlanPairsPerBlock, hist, bad);
+                     E, kPlanPairsPerBlock, hist, bad, out.counters, out.n_counters);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), (2 * E + 2 * kPlanWaves + 1) * sizeof(int), s,
                      nb, E, hist, (const int*)bad, out);
   hipLaunchKernelGGL(plan_scatter_kernel<IdxT>, dim3(nb), dim3(kPlanThreads),

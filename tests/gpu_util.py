@@ -23,11 +23,12 @@ def geometry(shape) -> "oracle.Geometry":
     return oracle.Geometry(shape.hidden, shape.inter, shape.experts, shape.topk, shape.fmt, shape.clamp)
 
 
-def make_moe(shape, max_tokens=None, tile_regime="auto", topk_idx_bits=64, fast_math=True, out_fp32=False) -> MoEFFN:
+def make_moe(shape, max_tokens=None, tile_regime="auto", topk_idx_bits=64, fast_math=True, out_fp32=False,
+             fuse_combine=False) -> MoEFFN:
     return MoEFFN(shape.hidden, shape.inter, shape.experts, shape.topk,
                   max_tokens if max_tokens is not None else shape.tokens, fmt=shape.fmt,
                   route_mode=shape.routing, activation_clamp=shape.clamp, topk_idx_bits=topk_idx_bits,
-                  fast_math=fast_math, tile_regime=tile_regime, out_fp32=out_fp32)
+                  fast_math=fast_math, tile_regime=tile_regime, out_fp32=out_fp32, fuse_combine=fuse_combine)
 
 
 def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.int64) -> dict:
@@ -35,7 +36,8 @@ def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.i
     d = {"x": dev(inp["x"]), "x_sf": dev(inp["x_sf"]),
          "weights": {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]),
                      "w2": dev(inp["w2"]), "w2_sf": dev(inp["w2_sf"]),
-                     "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs"))},
+                     "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs")),
+                     "c_input_scales": dev(inp.get("c_scales"))},
          "logits": dev(inp["logits"])}
     if sh.routing == "precomputed":
         ids = inp["topk_idx"] if topk_idx is None else topk_idx
@@ -51,6 +53,19 @@ def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.i
 def gs_kwargs(inp: dict) -> dict:
     """The NVFP4 per-expert global scales as oracle keywords (empty for the other formats)."""
     return {"w13_gs": inp["w13_gs"], "w2_gs": inp["w2_gs"]} if "w13_gs" in inp else {}
+
+
+def fwd_kwargs(inp: dict) -> dict:
+    """gs_kwargs plus NVFP4 x NVFP4's per-expert intermediate scales (oracle.forward)."""
+    kw = gs_kwargs(inp)
+    if "c_scales" in inp:
+        kw["c_scales"] = inp["c_scales"]
+    return kw
+
+
+def c_scale(inp: dict, e: int):
+    """NVFP4 x NVFP4: expert e's intermediate scale (None for the other formats)."""
+    return None if "c_scales" not in inp else float(inp["c_scales"][e])
 
 
 def prepared(moe: MoEFFN, d: dict) -> dict:
@@ -170,7 +185,7 @@ def run_ffn_intermediates(moe: MoEFFN, d: dict, T: int):
     torch.cuda.synchronize()
     n = T * moe.topk
     hc = h[:n].cpu()
-    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt in ("bf16", "nvfp4_w4a16") else hc.numpy()
+    hc = hc.view(torch.int16).numpy().view(np.uint16) if moe.fmt in ("bf16", "nvfp4_w4a16", "nvfp4") else hc.numpy()
     hs = None if hsf is None else hsf[:n].cpu().numpy()
     return out[:T], plan, y, hc, hs
 
@@ -184,10 +199,58 @@ TIE_REL = 2e-4   # of the requantisation block's maximum (FP8 / MX)
 BF16_TIE_REL = 1e-5
 
 
-def check_intermediate(fmt, hx, codes, hsf, I):
+def _check_nvfp4_intermediate(hx, codes, c):
+    """NVFP4 x NVFP4: the GPU stores codes x block scale as bf16 (exact).  A value may
+    differ from the oracle's where the exact h / (s c) lies within a tie window of
+    an E2M1 rounding midpoint, or, for a whole block, where amax / (6 c) lies within
+    that window of an E4M3 midpoint (the block scale then rounds the other way and
+    the block is requantised against the neighbouring scale).  Returns (values, flips)."""
+    hg = oracle.bf16_decode(codes)
+    hr, s = oracle.requant_nvfp4(hx, c)
+    R, I = hx.shape
+    hb, gb, rb = hx.reshape(R, I // 16, 16), hg.reshape(R, I // 16, 16), hr.reshape(R, I // 16, 16)
+    bad_blocks = np.argwhere((gb != rb).any(axis=2))
+    grid = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))  # E4M3 values 0 .. 448, ascending
+    flips = 0
+    for r, b in bad_blocks:
+        x, g = hb[r, b], gb[r, b]
+        a = np.abs(x).max()
+        # candidate block scales: the oracle's, and its E4M3 neighbours when amax/(6c) is near a midpoint
+        t = a / (6.0 * c)
+        cands = [s[r, b]]
+        i = int(np.searchsorted(grid, t))
+        for j in (i - 1, i):
+            if 0 <= j < grid.size - 1:
+                mid = 0.5 * (grid[j] + grid[j + 1])
+                if abs(t - mid) <= TIE_REL * max(t, 1e-30):
+                    cands += [grid[j], grid[j + 1]]
+        ok = False
+        for sc in cands:
+            den = sc * c
+            if den == 0:
+                if np.all(g == 0):
+                    ok = True
+                    break
+                continue
+            v = x / den
+            q_ref = oracle.round_e2m1_sat(v)
+            diff = q_ref * sc != g
+            mids = 0.5 * (q_ref + g / sc)
+            if not diff.any() or np.all(np.abs(v[diff] - mids[diff]) <= TIE_REL * 6.0):
+                ok = True
+                break
+        assert ok, f"NVFP4 intermediate differs beyond rounding ties in row {r}, block {b}"
+        flips += int((g != rb[r, b]).sum())
+    return hg, flips
+
+
+def check_intermediate(fmt, hx, codes, hsf, I, c=None):
     """Check the GPU's requantised intermediate rows (codes, scales) against the
-    oracle's requantisation of the exact rows hx.  Returns (GPU values, flips)."""
+    oracle's requantisation of the exact rows hx.  Returns (GPU values, flips).
+    c: NVFP4 x NVFP4's intermediate scale of the rows' expert."""
     R = hx.shape[0]
+    if fmt == "nvfp4":
+        return _check_nvfp4_intermediate(hx, codes, c)
     if fmt in ("bf16", "nvfp4_w4a16"):
         hr = oracle.round_bf16(hx)
         hg = oracle.bf16_decode(codes)
@@ -253,10 +316,11 @@ def staged_check(shape, inp: dict, res: dict, ref_plan: dict, topk_idx, topk_wei
                                           **gs_kwargs(inp))
         X = xd[src[r0:r1] // k]
         hx = oracle.swiglu_clamped(X @ w13d[:I].T, X @ w13d[I:].T, geo.clamp)
-        hg, f = check_intermediate(shape.fmt, hx, h_g[r0:r1], None if hsf_g is None else hsf_g[r0:r1], I)
+        hg, f = check_intermediate(shape.fmt, hx, h_g[r0:r1], None if hsf_g is None else hsf_g[r0:r1], I,
+                                   c_scale(inp, e))
         flips += f
         y_ref2[r0:r1] = hg @ w2d.T
-        y_ref[r0:r1] = oracle.requant(geo, hx) @ w2d.T
+        y_ref[r0:r1] = oracle.requant(geo, hx, c_scale(inp, e)) @ w2d.T
     check_y_rows(y_g.float().cpu().numpy().astype(np.float64)[src], y_ref2)
     w = np.asarray(topk_weights, dtype=np.float64)
     pr = ref_plan["pair_row"]

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 8
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -67,6 +67,9 @@ def _cfg(**kw):
     ({"format": 2, "hidden": 2880 + 16, "intermediate_hidden": 2880}, 1),
     ({"format": 3}, 0),                                          # NVFP4: multiples of 64
     ({"format": 3, "hidden": 7168 + 32}, 1),
+    ({"format": 4}, 0),                                          # NVFP4 x NVFP4: multiples of 64
+    ({"format": 4, "intermediate_hidden": 2048 + 32}, 1),
+    ({"format": 5}, 1),
     ({"route_mode": 1, "num_experts": 600, "num_topk": 4}, 2),   # FromLogits over > 512 experts
     ({"max_num_tokens": -1}, 1),
     ({"hidden": 32768 + 128}, 2),                # FP8 weight scales of > 256 K-steps

@@ -9,7 +9,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import (check_against_oracle, device_inputs, geometry, gs_kwargs, make_moe,
+from gpu_util import (check_against_oracle, device_inputs, fwd_kwargs, geometry, make_moe,
                       prepared_layout_reference, run_ffn_intermediates, run_forward, run_split)
 
 pytestmark = pytest.mark.gpu
@@ -162,6 +162,9 @@ SMALL = [
     ("fp8_clamp_fires", dict(T=48, H=256, I=256, E=4, k=2, fmt="fp8_block128", x_scale=20.0), "auto"),
     ("bf16_clamp_fires", dict(T=48, H=256, I=128, E=4, k=2, fmt="bf16", x_scale=20.0), "auto"),
     ("mx_clamp_fires", dict(T=48, H=256, I=160, E=4, k=2, fmt="w4a8_mx", x_scale=20.0), "auto"),
+    ("nvfp4x4_decode_tiles", dict(T=100, H=512, I=320, E=8, k=4, fmt="nvfp4"), "decode"),
+    ("nvfp4x4_prefill_tiles", dict(T=300, H=448, I=384, E=4, k=2, fmt="nvfp4"), "prefill"),
+    ("nvfp4x4_clamp_fires", dict(T=48, H=256, I=128, E=4, k=2, fmt="nvfp4", x_scale=20.0), "auto"),
     ("mx_clamp_fires_prefill", dict(T=160, H=320, I=192, E=3, k=2, fmt="w4a8_mx", routing="from_logits",
                                     x_scale=20.0), "prefill"),
 ]
@@ -185,7 +188,7 @@ def test_ffn_small_against_oracle(name, kw, regime):
         np.testing.assert_allclose(d["topk_weights"].cpu().numpy(), w, rtol=1e-5, atol=1e-7)
         w = d["topk_weights"].cpu().numpy()  # the combine uses the GPU's fp32 weights
     ref = oracle.forward(geo, inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
-                         topk_idx=ids, topk_weights=w, **gs_kwargs(inp))
+                         topk_idx=ids, topk_weights=w, **fwd_kwargs(inp))
     # end to end against the pure oracle, and stage by stage with the rounding-tie
     # flips of the requantised intermediate accounted for
     res = run_ffn_intermediates(moe, d, sh.tokens)

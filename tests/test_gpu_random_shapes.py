@@ -12,13 +12,13 @@ import moe_synth
 import oracle
 import torch
 
-from gpu_util import (check_against_oracle, device_inputs, geometry, gs_kwargs, make_moe, run_ffn_intermediates,
+from gpu_util import (check_against_oracle, device_inputs, fwd_kwargs, geometry, make_moe, run_ffn_intermediates,
                       run_forward)
 
 pytestmark = pytest.mark.gpu
 
 # (H, I) granularity per format: the library's moe_create constraints
-_GRAIN = {"fp8_block128": 128, "bf16": 64, "w4a8_mx": 32, "nvfp4_w4a16": 64}
+_GRAIN = {"fp8_block128": 128, "bf16": 64, "w4a8_mx": 32, "nvfp4_w4a16": 64, "nvfp4": 64}
 
 
 def _shape(fmt, seed):
@@ -51,7 +51,7 @@ def test_random_shape_forward(fmt, seed, regime):
         assert np.array_equal(ids, ref_ids)
         np.testing.assert_allclose(w, ref_w, rtol=1e-5, atol=1e-7)
     ref = oracle.forward(geometry(sh), inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
-                         topk_idx=ids, topk_weights=w, **gs_kwargs(inp))
+                         topk_idx=ids, topk_weights=w, **fwd_kwargs(inp))
     res = run_ffn_intermediates(moe, d, sh.tokens)
     assert torch.equal(res[0].view(torch.int16), out.view(torch.int16))
     check_against_oracle(sh, inp, out, ref, res, ids, w, sh.name)

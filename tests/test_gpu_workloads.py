@@ -15,7 +15,8 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import check_intermediate, check_y_rows, compare_out, device_inputs, geometry, gs_kwargs, make_moe, prepared
+from gpu_util import (c_scale, check_intermediate, check_y_rows, compare_out, device_inputs, fwd_kwargs, geometry,
+                      gs_kwargs, make_moe, prepared)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +29,7 @@ SAMPLE = 24
 def _rows_of(h, hsf, rows, fmt):
     ridx = torch.as_tensor(rows, dtype=torch.int64, device="cuda")
     hc = h.index_select(0, ridx).cpu()
-    hc = hc.view(torch.int16).numpy().view(np.uint16) if fmt in ("bf16", "nvfp4_w4a16") else hc.numpy()
+    hc = hc.view(torch.int16).numpy().view(np.uint16) if fmt in ("bf16", "nvfp4_w4a16", "nvfp4") else hc.numpy()
     hs = None if hsf is None else hsf.index_select(0, ridx).cpu().numpy()
     return hc, hs
 
@@ -44,11 +45,11 @@ def _check_whole_expert(sh, inp, geo, e, ref_plan, y, h, hsf):
     w13d, w2d = oracle.dequant_expert(geo, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"], e, **gs_kwargs(inp))
     hx = oracle.swiglu_clamped(X @ w13d[:I].T, X @ w13d[I:].T, geo.clamp)
     del X
-    y_pure = oracle.requant(geo, hx) @ w2d.T
+    y_pure = oracle.requant(geo, hx, c_scale(inp, e)) @ w2d.T
     y_gpu = y.index_select(0, torch.as_tensor(src, dtype=torch.int64, device="cuda")).float().cpu()
     rl2, mr = compare_out(y_gpu, y_pure)
     hc, hs = _rows_of(h, hsf, np.arange(r0, r1), sh.fmt)
-    hg, flips = check_intermediate(sh.fmt, hx, hc, hs, I)
+    hg, flips = check_intermediate(sh.fmt, hx, hc, hs, I, c_scale(inp, e))
     check_y_rows(y_gpu.numpy().astype(np.float64), hg @ w2d.T)
     return r1 - r0, rl2, mr, flips
 
@@ -72,7 +73,7 @@ def _gather_intermediate(moe, d, T, rows):
     return plan, y, hc, hs, h, hsf
 
 
-@pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER + ["nvfp4_decode"])
+@pytest.mark.parametrize("name", moe_synth.CONFIG_ORDER + ["nvfp4_decode", "nvfp4x4_decode"])
 def test_named_workload_full_size(name):
     sh = moe_synth.WORKLOADS[name]
     print(f"[fullsize] {name}: generating inputs", flush=True)
@@ -124,7 +125,7 @@ def test_named_workload_full_size(name):
                                           **gs_kwargs(inp))
         X = xd[[tpos[pairs[n][0]] for n in lst]]
         hx = oracle.swiglu_clamped(X @ w13d[:I].T, X @ w13d[I:].T, geo.clamp)
-        hg, f = check_intermediate(sh.fmt, hx, h_g[lst], None if hsf_g is None else hsf_g[lst], I)
+        hg, f = check_intermediate(sh.fmt, hx, h_g[lst], None if hsf_g is None else hsf_g[lst], I, c_scale(inp, e))
         flips += f
         y_ref2[lst] = hg @ w2d.T
     # y rows at their pair slots
@@ -136,7 +137,7 @@ def test_named_workload_full_size(name):
     compare_out(torch.from_numpy(out_np[toks]), out_ref2)
     # and the pure oracle on the sample, relative L2
     ref = oracle.forward_tokens(geo, toks, inp["x"], inp["x_sf"], inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"],
-                                ids, w, **gs_kwargs(inp))
+                                ids, w, **fwd_kwargs(inp))
     rl2, mr = compare_out(torch.from_numpy(out_np[toks]), ref)
     print(f"[fullsize] {name}: sampled tokens: rel-L2 {rl2:.2e}, max-abs/RMS {mr:.2e} against the pure oracle "
           f"({len(pairs)} pairs, {flips} rounding-tie flips)", flush=True)
