@@ -14,14 +14,17 @@ variants of the leg entry points) on the stream they run on.
 
 The timed workload (default: the prefill shape, T = 8192, the largest one-GPU
 configuration) runs W warm-up steps, then exactly K steps back to back between
-two device synchronisations: `value` is T * K / that wall time.  An event pair
-around each step gives the median and minimum step time.  A weight-bound
-workload rewrites a 512 MB scrub buffer before each step, outside the step's
-events, so that no weight byte stays in the memory-side cache between steps.
+two device synchronisations: `value` is T * K / that wall time.  Then K more
+steps with an event pair around each give the median and minimum step time.  A
+weight-bound workload also reads a 512 MB scrub buffer before each of K further
+steps, outside the step's events, so that no weight byte stays in the
+memory-side cache between steps.
 
 The weight-bound decode shape is measured beside it in the same run (the
-`decode` object): its own W warm-up steps, K steps back to back, then K steps
-with the scrub between them (median and minimum).
+`decode` object), after the timed workload's buffers are freed: its own W
+warm-up steps, K steps back to back, K steps with the scrub between them
+(median and minimum), then 100 steps with per-step events (the start-up
+transient, in means of 5) and K steps back to back once more (`settled`).
 
 Prints one JSON line with tokens/s, the dominant kernel's roofline fraction
 (from its live HIP-event duration), whole-step roofline fractions, and the CPU
@@ -47,7 +50,7 @@ PEAK_TFLOPS = {"fp8_block128": 5000.0, "bf16": 2500.0, "w4a8_mx": 5000.0, "nvfp4
 DTYPE = {"fp8_block128": "fp8_e4m3", "bf16": "bf16", "w4a8_mx": "mxfp4xmxfp8", "nvfp4_w4a16": "nvfp4xbf16",
          "nvfp4": "nvfp4xnvfp4"}
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "device.h", "prepare.hip")]
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h", "device.h", "launch.h", "prepare.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -127,8 +130,8 @@ def cpu_baseline(sh, inp, ids, w, budget_s: float) -> dict:
 
 def write_counters(workload: str, fetch_dir: str, write_dir: str, command: str) -> int:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
-    both with --copy-calibration) into profiles/gate_up_counters.json: the gate_up
-    kernel's HBM bytes per launch, each counter scaled by what it reads for the
+    both with --copy-calibration) into the workload's entry of profiles/gate_up_counters.json:
+    the gate_up kernel's HBM bytes per launch, each counter scaled by what it reads for the
     plain 1 GiB elementwise copy of the same run."""
     import csv
     import glob
@@ -157,8 +160,15 @@ def write_counters(workload: str, fetch_dir: str, write_dir: str, command: str) 
     out = {"workload": workload, "kernel_source_sha": kernel_source_hash(), "kernel": "ffn_gemm_kernel gate_up",
            "fetch_kb_per_launch": f_kb, "write_kb_per_launch": w_kb, "fetch_copy_factor": f_factor,
            "write_copy_factor": w_factor, "traffic_bytes_per_launch": round(traffic), "command": command}
+    table = {}
+    if os.path.exists(COUNTERS):
+        try:
+            table = json.load(open(COUNTERS)).get("workloads", {})
+        except (ValueError, AttributeError):
+            table = {}
+    table[workload] = out
     with open(COUNTERS, "w") as fh:
-        json.dump(out, fh, indent=1)
+        json.dump({"workloads": table}, fh, indent=1)
     print(json.dumps(out))
     return 0
 
@@ -197,7 +207,7 @@ def counter_summary(workload: str, out_md: str, dirs: list, command: str) -> int
             return "copy"
         return None
 
-    vals, durs = {}, {}
+    vals, durs, per_launch = {}, {}, {}
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
@@ -205,7 +215,9 @@ def counter_summary(workload: str, out_md: str, dirs: list, command: str) -> int
                 if k is None:
                     continue
                 vals.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-                durs.setdefault(k, {})[(f, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                dkey = (f, int(r["Dispatch_Id"]))
+                durs.setdefault(k, {})[dkey] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                per_launch.setdefault(k, {}).setdefault(dkey, {})[r["Counter_Name"]] = float(r["Counter_Value"])
     gib_kb = float(1 << 20)
 
     def mean(k, c, pred=None):
@@ -235,7 +247,7 @@ def counter_summary(workload: str, out_md: str, dirs: list, command: str) -> int
                 lines.append(f"| {c} | {m:,.0f} |")
         lines += ["", "| derived | value |", "|---|---|"]
         busy, grbm = mean(k, "SQ_VALU_MFMA_BUSY_CYCLES"), mean(k, "GRBM_GUI_ACTIVE")
-        if busy is not None and grbm is not None:
+        if busy is not None and grbm is not None and dur > 50.0:  # (a few-us kernel's GRBM count is mostly overhead)
             per_xcd = grbm / 8.0
             lines.append(f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs)) | "
                          f"{busy / 1024.0 / per_xcd:.3f} |")
@@ -256,6 +268,14 @@ def counter_summary(workload: str, out_md: str, dirs: list, command: str) -> int
         if hit is not None and miss is not None and hit + miss > 0:
             lines.append(f"| L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) | {hit / (hit + miss):.3f} |")
         lines.append("")
+        seq = [(key, c) for key, c in sorted(per_launch.get(k, {}).items())
+               if "GRBM_GUI_ACTIVE" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c]
+        if seq and busy and dur > 50.0:
+            lines += ["Launches of the counter pass in dispatch order (duration, effective clock, MFMA busy):", ""]
+            lines.append("; ".join(f"{durs[k][key]:.0f} us, {c['GRBM_GUI_ACTIVE'] / 8 / durs[k][key] / 1e3:.2f} GHz, "
+                                   f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (c['GRBM_GUI_ACTIVE'] / 8):.3f}"
+                                   for key, c in seq) + ".")
+            lines.append("")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
@@ -372,6 +392,13 @@ class Leg:
         if st != 0:
             raise RuntimeError(f"a step's C ABI call failed (status bits {st})")
 
+    def release(self):
+        """Drop the leg's device buffers (the host inputs stay)."""
+        for name in ("x", "x_sf", "logits", "topk_idx", "topk_w", "moe", "weights", "plan", "ws", "h", "hsf", "y",
+                     "out", "_calls", "_ws_s", "_ps"):
+            if hasattr(self, name):
+                setattr(self, name, None)
+
     def counts(self):
         c = self.plan["expert_counts"].cpu().numpy()
         return int((c > 0).sum()), int(c.sum())
@@ -396,12 +423,31 @@ def _events(n):
     return ev
 
 
+def warm_up(leg: Leg, steps: int):
+    """`steps` untimed steps back to back, each between two events: the mean step
+    time of the first and of the last five, which shows the start-up ramp (the
+    kernels themselves run slower over the first ~20 steps after start-up)."""
+    import torch
+    marks = [_events(2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in marks:
+        a.record(leg.stream)
+        leg.step()
+        b.record(leg.stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in marks]
+    if len(per) < 10:
+        return None
+    return {"steps": len(per), "first_5_ms": round(sum(per[:5]) / 5, 4), "last_5_ms": round(sum(per[-5:]) / 5, 4)}
+
+
 def timed_steps(leg: Leg, steps: int, step_markers: bool, scrub=None):
     """`steps` steps between two device synchronisations.  The two GEMM launches of
     every (steps/10)-th step carry timing events.  step_markers: an event pair around
-    every step (median and minimum step time).  scrub: a buffer rewritten before each
-    step, outside the step's events, so that no weight byte is still cached from the
-    previous step.  Returns (elapsed s, per-step ms list or None, gate_up ms, down ms)."""
+    every step (median and minimum step time).  scrub: (buffer, 0-d output) -- the
+    buffer is read (summed) before each step, outside the step's events, so that no
+    weight byte is still cached from the previous step (a read, so that no dirty
+    lines are left for the step to write back).  Returns (elapsed s, per-step ms list or None, gate_up ms, down ms)."""
     import numpy as np
     import torch
     from mixture_experts_ffn_topk_amd import _event_handles
@@ -413,7 +459,7 @@ def timed_steps(leg: Leg, steps: int, step_markers: bool, scrub=None):
     t0 = time.perf_counter()
     for i in range(steps):
         if scrub is not None:
-            torch.add(scrub, 1, out=scrub)
+            torch.sum(scrub[0], 0, out=scrub[1])  # reads every byte of the buffer, writes 4
         if marks:
             marks[i][0].record(leg.stream)
         leg.step(handles.get(i))
@@ -441,8 +487,8 @@ def roofline(leg: Leg, gate_ms: float, down_ms: float) -> dict:
     traffic = None
     if os.path.exists(COUNTERS):
         try:
-            c = json.load(open(COUNTERS))
-            if c.get("workload") == sh.name and c.get("kernel_source_sha") == kernel_source_hash():
+            c = json.load(open(COUNTERS)).get("workloads", {}).get(sh.name, {})
+            if c.get("kernel_source_sha") == kernel_source_hash():
                 traffic = c["traffic_bytes_per_launch"]
         except Exception:
             traffic = None
@@ -465,8 +511,9 @@ def step_fracs(leg: Leg, ms: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the first ~20 steps after start-up run slower (warmup_curve)")
     ap.add_argument("--workload", default="prefill_fp8_zipf",
                     help="the timed workload (default: the largest one-GPU configuration, the prefill shape)")
     ap.add_argument("--decode-workload", default="decode_fp8",
@@ -505,22 +552,23 @@ def main() -> int:
     leg = Leg(args.workload, args.fuse_combine)
     sh = leg.sh
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter
-    scrub = torch.zeros(args.scrub_mb << 18, dtype=torch.float32, device="cuda") if args.scrub_mb > 0 else None
+    scrub = ((torch.zeros(args.scrub_mb << 18, dtype=torch.float32, device="cuda"),
+              torch.zeros((), dtype=torch.float32, device="cuda")) if args.scrub_mb > 0 else None)
 
     log(f"warmup {args.warmup} steps")
     leg.checked_step()  # (at least one step, through the checked binding; the plan's counts then exist)
-    for _ in range(args.warmup - 1):
-        leg.step()
-    torch.cuda.synchronize()
+    curve = warm_up(leg, args.warmup - 1)
     active, pairs = leg.counts()
     weight_bound = roofline(leg, 1.0, 1.0)["bound"] == "hbm"
 
-    # The timed region: exactly `steps` steps back to back; an event pair around every
-    # step gives the median and minimum.  A weight-bound workload then runs as many
-    # steps again with the scrub buffer rewritten before each step (outside the step's
-    # events), for its median and minimum without memory-side cache reuse.
+    # The timed region: exactly `steps` steps back to back (the GEMM launches of every
+    # (steps/10)-th step carry their timing events).  Then as many steps with an event
+    # pair around each, for the median and minimum step time.  A weight-bound workload
+    # then runs as many again with the scrub buffer rewritten before each step
+    # (outside the step's events): its median and minimum without memory-side cache reuse.
     log(f"timing {args.steps} steps")
-    elapsed, per, gate_ms, down_ms = timed_steps(leg, args.steps, True)
+    elapsed, _, gate_ms, down_ms = timed_steps(leg, args.steps, False)
+    _, per, _, _ = timed_steps(leg, args.steps, True)
     scrubbed = None
     if weight_bound and scrub is not None:
         _, per_s, gu_s, dn_s = timed_steps(leg, args.steps, True, scrub)
@@ -554,37 +602,53 @@ def main() -> int:
         "step_tflops": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         **step_fracs(leg, ms_per_step),
-        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine),
+        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine), "warmup_curve": curve,
         "roofline": roofline(leg, gate_ms, down_ms),
     }
 
+    ids = leg.inp["topk_idx"] if sh.routing == "precomputed" else leg.topk_idx.cpu().numpy()
+    w = leg.inp["topk_weights"] if sh.routing == "precomputed" else leg.topk_w.cpu().numpy()
+    leg.release()
+    torch.cuda.empty_cache()
+
     # The weight-bound decode shape beside it: its own warm-up, then the same number of
-    # steps back to back, then as many with the cache scrub between steps.
+    # steps back to back, then as many with the cache scrub between steps.  Then the
+    # same steps once more after 100 further steps: a sustained weight-streaming load
+    # runs its kernels up to ~12 % slower from ~4 to ~15 ms after it starts (a transient
+    # of the part's power management, not of the work: the kernel durations rise and
+    # fall back with identical work), which W = 5 warm-up steps leave inside the timed
+    # steps; `startup_ms_per_5_steps` shows it step by step.
     if args.decode_workload != "none" and args.decode_workload != args.workload:
         dec = Leg(args.decode_workload, args.fuse_combine)
         dec.checked_step()
-        for _ in range(args.warmup - 1):
-            dec.step()
+        dcurve = warm_up(dec, args.warmup - 1)
         el, _, gu, dn = timed_steps(dec, args.steps, False)
         _, per_s, gu_s, dn_s = timed_steps(dec, args.steps, True, scrub)
-        ms_b2b = el * 1e3 / args.steps
+        _, per_settle, _, _ = timed_steps(dec, 100, True)
+        el2, _, gu2, dn2 = timed_steps(dec, args.steps, False)
+        ms_b2b, ms_settled = el * 1e3 / args.steps, el2 * 1e3 / args.steps
         med = float(np.median(per_s))
         result["decode"] = {
             "workload": dec.sh.name, "tokens": dec.sh.tokens, "ms_per_step": round(ms_b2b, 4),
             "tokens_per_s": round(dec.sh.tokens / (ms_b2b * 1e-3), 1), **step_fracs(dec, ms_b2b),
-            "scrubbed": {"scrub_mb": args.scrub_mb, "step_ms_median": round(med, 4),
+            "scrubbed": {"scrub_mb": args.scrub_mb, "scrub": "read", "step_ms_median": round(med, 4),
                          "step_ms_min": round(float(np.min(per_s)), 4),
                          "step_hbm_frac_median": step_fracs(dec, med)["step_hbm_frac"],
                          "gate_up": roofline(dec, gu_s, dn_s)},
-            "roofline": roofline(dec, gu, dn)}
+            "roofline": roofline(dec, gu, dn), "warmup_curve": dcurve,
+            "settled": {"after_steps": args.warmup + 2 * args.steps + 100, "ms_per_step": round(ms_settled, 4),
+                        "tokens_per_s": round(dec.sh.tokens / (ms_settled * 1e-3), 1),
+                        **step_fracs(dec, ms_settled), "gate_up_avg_launch_ms": round(gu2, 4),
+                        "down_avg_launch_ms": round(dn2, 4),
+                        "startup_ms_per_5_steps": [round(float(np.mean(per_settle[i:i + 5])), 4)
+                                                   for i in range(0, len(per_settle), 5)]}}
         for r in (result["decode"]["roofline"], result["decode"]["scrubbed"]["gate_up"]):
             r.pop("algorithmic_flops", None)
+        dec.release()
         del dec
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
-        ids = leg.inp["topk_idx"] if sh.routing == "precomputed" else leg.topk_idx.cpu().numpy()
-        w = leg.inp["topk_weights"] if sh.routing == "precomputed" else leg.topk_w.cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(sh, leg.inp, ids, w, args.cpu_budget)
     else:
         result["cpu_baseline"] = None

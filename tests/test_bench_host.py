@@ -24,10 +24,13 @@ def test_stored_counters_name_their_workload_and_source():
     sys.path.insert(0, ROOT)
     import bench
     with open(bench.COUNTERS) as f:
-        c = json.load(f)
-    assert c["workload"] == "decode_fp8"
-    assert len(c["kernel_source_sha"]) == 16 and len(bench.kernel_source_hash()) == 16
-    assert c["traffic_bytes_per_launch"] > 0 and "rocprofv3 --pmc FETCH_SIZE" in c["command"]
+        table = json.load(f)["workloads"]
+    assert {"decode_fp8", "prefill_fp8_zipf"} <= set(table)
+    for name, c in table.items():
+        assert c["workload"] == name
+        assert len(c["kernel_source_sha"]) == 16 and len(bench.kernel_source_hash()) == 16
+        assert c["traffic_bytes_per_launch"] > 0 and "rocprofv3 --pmc" in c["command"]
+        assert "FETCH_SIZE" in c["command"] and "WRITE_SIZE" in c["command"]
 
 
 def test_timing_events_must_exist_before_a_launch():
