@@ -21,7 +21,7 @@ steps, outside the step's events, so that no weight byte stays in the
 memory-side cache between steps.
 
 The weight-bound decode shape is measured beside it in the same run (the
-`decode` object), after the timed workload's buffers are freed: its own W
+`decode` object), right after the timed workload's steps: its own W
 warm-up steps, K steps back to back, K steps with the scrub between them
 (median and minimum), then 100 steps with per-step events (the start-up
 transient, in means of 5) and K steps back to back once more (`settled`).
@@ -550,6 +550,10 @@ def main() -> int:
         return 2
 
     leg = Leg(args.workload, args.fuse_combine)
+    # the weight-bound leg is set up now (inputs, prepared weights), so that it runs
+    # right after the timed workload's steps, with no idle gap between them
+    with_decode = args.decode_workload != "none" and args.decode_workload != args.workload
+    dec = Leg(args.decode_workload, args.fuse_combine) if with_decode else None
     sh = leg.sh
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter
     scrub = ((torch.zeros(args.scrub_mb << 18, dtype=torch.float32, device="cuda"),
@@ -606,10 +610,6 @@ def main() -> int:
         "roofline": roofline(leg, gate_ms, down_ms),
     }
 
-    ids = leg.inp["topk_idx"] if sh.routing == "precomputed" else leg.topk_idx.cpu().numpy()
-    w = leg.inp["topk_weights"] if sh.routing == "precomputed" else leg.topk_w.cpu().numpy()
-    leg.release()
-    torch.cuda.empty_cache()
 
     # The weight-bound decode shape beside it: its own warm-up, then the same number of
     # steps back to back, then as many with the cache scrub between steps.  Then the
@@ -618,8 +618,7 @@ def main() -> int:
     # of the part's power management, not of the work: the kernel durations rise and
     # fall back with identical work), which W = 5 warm-up steps leave inside the timed
     # steps; `startup_ms_per_5_steps` shows it step by step.
-    if args.decode_workload != "none" and args.decode_workload != args.workload:
-        dec = Leg(args.decode_workload, args.fuse_combine)
+    if with_decode:
         dec.checked_step()
         dcurve = warm_up(dec, args.warmup - 1)
         el, _, gu, dn = timed_steps(dec, args.steps, False)
@@ -647,6 +646,9 @@ def main() -> int:
         dec.release()
         del dec
 
+    ids = leg.inp["topk_idx"] if sh.routing == "precomputed" else leg.topk_idx.cpu().numpy()
+    w = leg.inp["topk_weights"] if sh.routing == "precomputed" else leg.topk_w.cpu().numpy()
+    leg.release()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(sh, leg.inp, ids, w, args.cpu_budget)
