@@ -286,7 +286,7 @@ class Leg:
     """The step's kernels on one workload: inputs resident in HBM, weights in the
     prepared layout (written once, untimed), caller-owned plan, intermediate and y."""
 
-    def __init__(self, name: str, fuse_combine: bool = False):
+    def __init__(self, name: str, fuse_combine: bool = False, fuse_plan: bool = False):
         import numpy as np
         import torch
 
@@ -308,6 +308,7 @@ class Leg:
 
         self.sh, self.inp = sh, inp
         self.fuse = fuse_combine
+        self.fuse_plan = fuse_plan  # the plan built in the gate_up launch (moe_plan_ffn_gate_up)
         self.x, self.x_sf = dev(inp["x"]), dev(inp["x_sf"])
         canonical = {"w13": dev(inp["w13"]), "w13_sf": dev(inp["w13_sf"]), "w2": dev(inp["w2"]),
                      "w2_sf": dev(inp["w2_sf"]), "w13_gs": dev(inp.get("w13_gs")), "w2_gs": dev(inp.get("w2_gs")),
@@ -341,6 +342,14 @@ class Leg:
             m.plan(T, self.plan, routing_logits=self.logits, topk_idx_out=self.topk_idx, topk_weights_out=self.topk_w,
                    ws=self.ws, stream=s)
         m.ffn_gate_up(T, self.x, self.x_sf, self.weights, self.plan, self.h, self.hsf, stream=s)
+        if self.fuse_plan:  # the same plan and h again, from the one-launch form
+            if self.sh.routing == "precomputed":
+                m.plan_ffn_gate_up(T, self.x, self.x_sf, self.weights, self.plan, self.h, self.hsf,
+                                   topk_idx=self.topk_idx, ws=self.ws, stream=s)
+            else:
+                m.plan_ffn_gate_up(T, self.x, self.x_sf, self.weights, self.plan, self.h, self.hsf,
+                                   routing_logits=self.logits, topk_idx_out=self.topk_idx,
+                                   topk_weights_out=self.topk_w, ws=self.ws, stream=s)
         if self.fuse:
             m.ffn_down_combine(T, self.h, self.hsf, self.weights, self.plan, self.topk_w, self.y, self.out, stream=s)
         else:
@@ -365,26 +374,30 @@ class Leg:
             plan = (h, T, None, self.logits.data_ptr(), self.topk_idx.data_ptr(), self.topk_w.data_ptr(), P,
                     self.ws.data_ptr(), nb, s)
         gu = (h, T, self.x.data_ptr(), x_sf, W, P, self.h.data_ptr(), hsf, s)
+        # moe_plan_ffn_gate_up: the routing arguments of moe_plan, then those of the gate_up leg
+        pgu = plan[:6] + (self.x.data_ptr(), x_sf, W, P, self.h.data_ptr(), hsf, self.ws.data_ptr(), nb, s)
         if self.fuse:
             dn = (h, T, self.h.data_ptr(), hsf, W, P, self.topk_w.data_ptr(), self.y.data_ptr(), None, None,
                   self.out.data_ptr(), s)
         else:
             dn = (h, T, self.h.data_ptr(), hsf, W, P, self.y.data_ptr(), s)
         comb = (h, T, self.y.data_ptr(), self.topk_w.data_ptr(), P, self.out.data_ptr(), s)
-        self._calls = (lib, plan, gu, dn, comb)
+        self._calls = (lib, plan, gu, dn, comb, pgu)
 
     def step(self, legs=None):
         """One pass of the whole path.  legs: optional hipEvent_t handles (gate_up
         start/stop, down start/stop) that the two GEMM launches carry themselves."""
         if self._calls is None:
             self._build_calls()
-        lib, plan, gu, dn, comb = self._calls
-        st = lib.moe_plan(*plan)
+        lib, plan, gu, dn, comb, pgu = self._calls
         if legs is None:
-            st |= lib.moe_ffn_gate_up(*gu)
+            st = lib.moe_plan_ffn_gate_up(*pgu) if self.fuse_plan else lib.moe_plan(*plan) | lib.moe_ffn_gate_up(*gu)
             st |= lib.moe_ffn_down_combine(*dn) if self.fuse else lib.moe_ffn_down(*dn)
         else:
-            st |= lib.moe_ffn_gate_up_timed(*gu, legs[0], legs[1])
+            if self.fuse_plan:
+                st = lib.moe_plan_ffn_gate_up_timed(*pgu, legs[0], legs[1])
+            else:
+                st = lib.moe_plan(*plan) | lib.moe_ffn_gate_up_timed(*gu, legs[0], legs[1])
             st |= lib.moe_ffn_down_combine_timed(*dn, legs[2], legs[3]) if self.fuse else \
                 lib.moe_ffn_down_timed(*dn, legs[2], legs[3])
         if not self.fuse:
@@ -521,6 +534,9 @@ def main() -> int:
     ap.add_argument("--scrub-mb", type=int, default=512, help="cache scrub between the weight-bound steps (MB)")
     ap.add_argument("--fuse-combine", type=int, default=0, choices=(0, 1),
                     help="1: the combine runs in the down GEMM's epilogue (moe_ffn_down_combine)")
+    ap.add_argument("--fuse-plan", type=int, default=1, choices=(0, 1),
+                    help="1: the routing plan is built inside the gate_up launch where that applies "
+                         "(moe_plan_ffn_gate_up; otherwise that call launches the plan kernel itself)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -549,11 +565,11 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    leg = Leg(args.workload, args.fuse_combine)
+    leg = Leg(args.workload, args.fuse_combine, args.fuse_plan)
     # the weight-bound leg is set up now (inputs, prepared weights), so that it runs
     # right after the timed workload's steps, with no idle gap between them
     with_decode = args.decode_workload != "none" and args.decode_workload != args.workload
-    dec = Leg(args.decode_workload, args.fuse_combine) if with_decode else None
+    dec = Leg(args.decode_workload, args.fuse_combine, args.fuse_plan) if with_decode else None
     sh = leg.sh
     T, k, E, H, I = sh.tokens, sh.topk, sh.experts, sh.hidden, sh.inter
     scrub = ((torch.zeros(args.scrub_mb << 18, dtype=torch.float32, device="cuda"),
@@ -606,7 +622,8 @@ def main() -> int:
         "step_tflops": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         **step_fracs(leg, ms_per_step),
-        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine), "warmup_curve": curve,
+        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine), "plan_in_gate_up": bool(args.fuse_plan),
+        "warmup_curve": curve,
         "roofline": roofline(leg, gate_ms, down_ms),
     }
 

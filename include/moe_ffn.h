@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 8
+#define MOE_FFN_ABI_VERSION 9
 
 typedef enum {
   MOE_OK = 0,
@@ -124,6 +124,9 @@ typedef struct moe_config {
                                    epilogue (moe_ffn_down_combine) instead of as its own
                                    launch ([EPConfig] fuse_ffn_combine_send); same result, bit
                                    for bit */
+  int32_t fuse_plan;            /* 1: moe_forward builds the routing plan inside the gate_up
+                                   launch (as moe_plan_ffn_gate_up) where that applies;
+                                   same plan and result, bit for bit */
 } moe_config;
 
 /* (host struct of device pointers) Expert weights of this GPU: the canonical
@@ -276,6 +279,32 @@ moe_status moe_ffn_gate_up_timed(const moe_handle* h, int32_t num_tokens, const 
 moe_status moe_ffn_down_timed(const moe_handle* h, int32_t num_tokens, const void* h_in, const void* h_sf_in,
                               const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
                               void* y, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+/* moe_plan followed by moe_ffn_gate_up, as one kernel launch where the sizes
+   allow ([EPConfig] fused_moe_ready: dispatch, FFN and combine as few launches;
+   here the routing plan moves into the gate_up launch).  Arguments are those of
+   the two calls: routing as moe_plan (PRECOMPUTED: topk_idx_in; FROM_LOGITS:
+   routing_logits with topk_idx_out / topk_weights_out, whose top-k keeps its own
+   launch), the plan buffers (outputs, complete when the call's work is done),
+   ws / ws_bytes as for moe_plan, then x, x_sf, w, h_out, h_sf_out as for
+   moe_ffn_gate_up.  In the weight-bound tile regime with at most 8192 pairs, every
+   workgroup of the gate_up launch counts the ids and gathers its own rows itself,
+   and the launch writes the whole plan; otherwise the call launches moe_plan's
+   kernels and then the gate_up leg.  Plan and h are bit for bit those of the two
+   separate calls.  Validation and errors: the union of theirs.  The _timed form's
+   events travel with the gate_up kernel's launch (which then includes the plan's
+   work where it is built in that launch). */
+moe_status moe_plan_ffn_gate_up(const moe_handle* h, int32_t num_tokens, const void* topk_idx_in,
+                                const float* routing_logits, void* topk_idx_out, float* topk_weights_out,
+                                const void* x, const void* x_sf, const moe_weights* w /* host struct */,
+                                const moe_plan_buffers* plan /* host struct */, void* h_out, void* h_sf_out,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_plan_ffn_gate_up_timed(const moe_handle* h, int32_t num_tokens, const void* topk_idx_in,
+                                      const float* routing_logits, void* topk_idx_out, float* topk_weights_out,
+                                      const void* x, const void* x_sf, const moe_weights* w /* host struct */,
+                                      const moe_plan_buffers* plan /* host struct */, void* h_out, void* h_sf_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start,
+                                      hipEvent_t stop);
 
 /* The down leg with the router-weighted combine fused into its epilogue
    ([EPConfig] fuse_ffn_combine_send: the expert FFN's down epilogue feeds the

@@ -38,7 +38,8 @@ class _Config(ctypes.Structure):
                 ("max_num_tokens", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
                 ("format", ctypes.c_int32), ("route_mode", ctypes.c_int32),
                 ("topk_idx_bits", ctypes.c_int32), ("fast_math", ctypes.c_int32),
-                ("tile_regime", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("fuse_combine", ctypes.c_int32)]
+                ("tile_regime", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("fuse_combine", ctypes.c_int32),
+                ("fuse_plan", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -61,7 +62,7 @@ PLAN_FIELDS = [f for f, _ in _Plan._fields_]
 EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
             "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_ffn_gate_up_timed", "moe_ffn_down_timed",
-            "moe_ffn_down_combine", "moe_ffn_down_combine_timed",
+            "moe_ffn_down_combine", "moe_ffn_down_combine_timed", "moe_plan_ffn_gate_up", "moe_plan_ffn_gate_up_timed",
             "moe_forward_static", "moe_status_string", "moe_abi_version"]
 STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 
@@ -97,6 +98,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_down.restype = i32
     lib.moe_ffn_gate_up_timed.argtypes = lib.moe_ffn_gate_up.argtypes + [vp, vp]
     lib.moe_ffn_gate_up_timed.restype = i32
+    lib.moe_plan_ffn_gate_up.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights),
+                                         ctypes.POINTER(_Plan), vp, vp, vp, sz, vp]
+    lib.moe_plan_ffn_gate_up.restype = i32
+    lib.moe_plan_ffn_gate_up_timed.argtypes = lib.moe_plan_ffn_gate_up.argtypes + [vp, vp]
+    lib.moe_plan_ffn_gate_up_timed.restype = i32
     lib.moe_ffn_down_timed.argtypes = lib.moe_ffn_down.argtypes + [vp, vp]
     lib.moe_ffn_down_timed.restype = i32
     lib.moe_ffn_down_combine.argtypes = [vp, i32, vp, vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Plan), vp, vp,
@@ -200,13 +206,15 @@ class MoEFFN:
     def __init__(self, hidden: int, intermediate_hidden: int, num_experts: int, num_topk: int,
                  max_num_tokens: int, fmt: str = "fp8_block128", route_mode: str = "precomputed",
                  activation_clamp: float = 10.0, topk_idx_bits: int = 64, fast_math: bool = True,
-                 tile_regime: str = "auto", out_fp32: bool = False, fuse_combine: bool = False):
+                 tile_regime: str = "auto", out_fp32: bool = False, fuse_combine: bool = False,
+                 fuse_plan: bool = False):
         self.lib = load_library()
         self.cfg = _Config(hidden, intermediate_hidden, num_experts, num_topk, max_num_tokens,
                            float(activation_clamp), FORMATS[fmt], ROUTE_MODES[route_mode], topk_idx_bits,
                            int(bool(fast_math)), TILE_REGIMES[tile_regime], int(bool(out_fp32)),
-                           int(bool(fuse_combine)))
+                           int(bool(fuse_combine)), int(bool(fuse_plan)))
         self.fuse_combine = bool(fuse_combine)
+        self.fuse_plan = bool(fuse_plan)
         self.out_fp32 = bool(out_fp32)
         self.fmt, self.route_mode = fmt, route_mode
         self.hidden, self.inter, self.experts, self.topk = hidden, intermediate_hidden, num_experts, num_topk
@@ -400,6 +408,35 @@ class MoEFFN:
             _check(self.lib.moe_ffn_gate_up(*args), "moe_ffn_gate_up")
         else:
             _check(self.lib.moe_ffn_gate_up_timed(*args, *_event_handles(events)), "moe_ffn_gate_up_timed")
+
+    def plan_ffn_gate_up(self, num_tokens, x, x_sf, weights: dict, plan: dict, h, h_sf, topk_idx=None,
+                         routing_logits=None, topk_idx_out=None, topk_weights_out=None, ws=None, stream=None,
+                         events=None):
+        """plan() followed by ffn_gate_up(), in one kernel launch where the sizes allow
+        (moe_plan_ffn_gate_up); events as for ffn_gate_up."""
+        import torch
+        T = num_tokens
+        self._check_plan(plan, T)
+        self._check_routing_in(T, topk_idx, routing_logits, None)
+        if self.route_mode == "from_logits":
+            _need(topk_idx_out, "topk_idx_out", T * self.topk * self.topk_idx_bits // 8, self._idx_dtypes())
+            _need(topk_weights_out, "topk_weights_out", T * self.topk * 4, (torch.float32,))
+        _need(ws, "ws", 0, required=False)
+        self._check_x(x, x_sf, T)
+        self._check_weights(weights)
+        _need(h, "h", T * self.topk * self.inter * self._esz())
+        _need(h_sf, "h_sf", T * self.topk * self._sf_row(self.inter), required=self._sf_row(self.inter) > 0)
+        _on_gpu(plan=plan, topk_idx=topk_idx, routing_logits=routing_logits, topk_idx_out=topk_idx_out,
+                topk_weights_out=topk_weights_out, ws=ws, x=x, x_sf=x_sf, weights=weights, h=h, h_sf=h_sf)
+        ws_ = self._weights_struct(weights)
+        ps = self._plan_struct(plan)
+        args = (self._h, num_tokens, _ptr(topk_idx), _ptr(routing_logits), _ptr(topk_idx_out), _ptr(topk_weights_out),
+                _ptr(x), _ptr(x_sf), ctypes.byref(ws_), ctypes.byref(ps), _ptr(h), _ptr(h_sf), _ptr(ws),
+                self._nbytes(ws), _stream(stream))
+        if events is None:
+            _check(self.lib.moe_plan_ffn_gate_up(*args), "moe_plan_ffn_gate_up")
+        else:
+            _check(self.lib.moe_plan_ffn_gate_up_timed(*args, *_event_handles(events)), "moe_plan_ffn_gate_up_timed")
 
     def ffn_down(self, num_tokens, h, h_sf, weights: dict, plan: dict, y, stream=None, events=None):
         """events: as for ffn_gate_up (moe_ffn_down_timed)."""

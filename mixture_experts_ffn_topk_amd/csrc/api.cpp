@@ -97,19 +97,32 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // carving.  A null pointer passes (presence is checked separately).
 bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// FROM_LOGITS: the top-k launch; returns the ids the plan reads (the caller's
+// PRECOMPUTED ids, or idx_out)
+moe_status do_route(const moe_handle* h, int32_t T, const void* idx_in, const float* logits, const float* bias,
+                    void* idx_out, float* w_out, hipStream_t s, const void** ids) {
+  const moe_config& c = h->cfg;
+  *ids = idx_in;
+  if (c.route_mode != MOE_ROUTE_FROM_LOGITS) return MOE_OK;
+  hipError_t e = moe::launch_route_logits_topk(logits, bias, T, c.num_experts, c.num_topk, idx_out,
+                                               c.topk_idx_bits == 64, w_out, c.fast_math != 0, s);
+  *ids = idx_out;
+  return hip_status(e);
+}
+
 moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const float* logits, const float* bias,
                    void* idx_out, float* w_out, const moe_plan_buffers* plan, void* scratch, hipStream_t s) {
   const moe_config& c = h->cfg;
-  const bool idx64 = c.topk_idx_bits == 64;
-  const void* ids = idx_in;
-  if (c.route_mode == MOE_ROUTE_FROM_LOGITS) {
-    hipError_t e = moe::launch_route_logits_topk(logits, bias, T, c.num_experts, c.num_topk, idx_out, idx64, w_out,
-                                                 c.fast_math != 0, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    ids = idx_out;
-  }
-  return hip_status(
-      moe::launch_plan(ids, idx64, T * c.num_topk, c.num_experts, plan_ptrs(plan, T, c.hidden), (int*)scratch, s));
+  const void* ids = nullptr;
+  moe_status st = do_route(h, T, idx_in, logits, bias, idx_out, w_out, s, &ids);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_plan(ids, c.topk_idx_bits == 64, T * c.num_topk, c.num_experts,
+                                     plan_ptrs(plan, T, c.hidden), (int*)scratch, s));
+}
+
+// Whether the gate_up launch builds the plan itself for T tokens.
+bool plan_in_gate_up(const moe_config& c, int32_t T) {
+  return T > 0 && moe::ffn_plan_fusable(choose_bm(c, T), T * c.num_topk);
 }
 
 // The combine fused into the down leg: router weights, addends and the output.
@@ -120,9 +133,11 @@ struct Fused {
   void* out;
 };
 
+// plan_ids: the gate_up launch builds the plan from these ids (plan_in_gate_up)
 moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_sf, const moe_weights* w,
                   const moe_plan_buffers* plan, void* y, void* hbuf, void* hsf, hipStream_t s, int stage,
-                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr, const Fused* fused = nullptr) {
+                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr, const Fused* fused = nullptr,
+                  const void* plan_ids = nullptr) {
   const moe_config& c = h->cfg;
   moe::FfnArgs a{};
   a.fmt = to_fmt(c.format);
@@ -159,6 +174,11 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
     a.shared = fused->shared;
     a.residual = fused->residual;
     a.out_f32 = c.out_fp32 != 0;
+  }
+  if (plan_ids) {
+    a.plan_ids = plan_ids;
+    a.ids64 = c.topk_idx_bits == 64;
+    a.plan = plan_ptrs(plan, T, c.hidden);
   }
   return hip_status(moe::launch_ffn(a, s, stage));
 }
@@ -226,6 +246,7 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
   if (c.tile_regime < MOE_TILES_AUTO || c.tile_regime > MOE_TILES_PREFILL) return MOE_ERR_INVALID_ARGUMENT;
   if (c.out_fp32 != 0 && c.out_fp32 != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c.fuse_combine != 0 && c.fuse_combine != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.fuse_plan != 0 && c.fuse_plan != 1) return MOE_ERR_INVALID_ARGUMENT;
   switch (c.format) {
     case MOE_FMT_FP8_BLOCK128:
       if (c.hidden % 128 || c.intermediate_hidden % 128) return MOE_ERR_INVALID_ARGUMENT;
@@ -345,6 +366,44 @@ moe_status moe_ffn_gate_up(const moe_handle* h, int32_t T, const void* x, const 
   return moe_ffn_gate_up_timed(h, T, x, x_sf, w, plan, h_out, h_sf_out, stream, nullptr, nullptr);
 }
 
+moe_status moe_plan_ffn_gate_up_timed(const moe_handle* h, int32_t T, const void* topk_idx_in,
+                                      const float* routing_logits, void* topk_idx_out, float* topk_weights_out,
+                                      const void* x, const void* x_sf, const moe_weights* w,
+                                      const moe_plan_buffers* plan, void* h_out, void* h_sf_out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  // the union of moe_plan's and moe_ffn_gate_up's checks, all before any launch
+  if (!valid_T(h, T) || !plan_complete(plan) || !weights_ok(h->cfg, w)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = h->cfg;
+  if (c.route_mode == MOE_ROUTE_PRECOMPUTED) {
+    if (T > 0 && !topk_idx_in) return MOE_ERR_INVALID_ARGUMENT;
+  } else if (T > 0 && (!routing_logits || !topk_idx_out || !topk_weights_out)) {
+    return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if (T > 0 && (!x_ok(c, x, x_sf) || !h_out || (!bf16_inter(c.format) && !h_sf_out))) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al(x, 16) || !al(x_sf, 4) || !al(h_out, 16) || !al(h_sf_out, 4) || !al(ws, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = layout_for(c, T).plan_scratch_bytes;
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!plan_in_gate_up(c, T)) {
+    moe_status st = do_plan(h, T, topk_idx_in, routing_logits, nullptr, topk_idx_out, topk_weights_out, plan, ws,
+                            stream);
+    if (st != MOE_OK || T == 0) return st;
+    return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1, start, stop);
+  }
+  const void* ids = nullptr;
+  moe_status st = do_route(h, T, topk_idx_in, routing_logits, nullptr, topk_idx_out, topk_weights_out, stream, &ids);
+  if (st != MOE_OK) return st;
+  return do_ffn(h, T, x, x_sf, w, plan, nullptr, h_out, h_sf_out, stream, 1, start, stop, nullptr, ids);
+}
+
+moe_status moe_plan_ffn_gate_up(const moe_handle* h, int32_t T, const void* topk_idx_in, const float* routing_logits,
+                                void* topk_idx_out, float* topk_weights_out, const void* x, const void* x_sf,
+                                const moe_weights* w, const moe_plan_buffers* plan, void* h_out, void* h_sf_out,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_plan_ffn_gate_up_timed(h, T, topk_idx_in, routing_logits, topk_idx_out, topk_weights_out, x, x_sf, w,
+                                    plan, h_out, h_sf_out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
 moe_status moe_ffn_down_timed(const moe_handle* h, int32_t T, const void* h_in, const void* h_sf_in,
                               const moe_weights* w, const moe_plan_buffers* plan, void* y, hipStream_t stream,
                               hipEvent_t start, hipEvent_t stop) {
@@ -421,16 +480,23 @@ moe_status moe_forward_ex(const moe_handle* h, int32_t T, const void* x, const v
                         (int32_t*)(base + L.nact),   (int32_t*)(base + L.src),   (int32_t*)(base + L.prow),
                         (int32_t*)(base + L.status),
                         c.fuse_combine ? (int32_t*)(base + L.cnt) : nullptr};
-  moe_status st =
-      do_plan(h, T, topk_idx, routing_logits, routing_bias, topk_idx, topk_weights, &plan, base + L.scratch, stream);
+  // fuse_plan: the gate_up launch builds the plan (the top-k from logits keeps its launch)
+  const void* in_launch = nullptr;
+  moe_status st;
+  if (c.fuse_plan && plan_in_gate_up(c, T)) {
+    st = do_route(h, T, topk_idx, routing_logits, routing_bias, topk_idx, topk_weights, stream, &in_launch);
+  } else {
+    st = do_plan(h, T, topk_idx, routing_logits, routing_bias, topk_idx, topk_weights, &plan, base + L.scratch, stream);
+  }
   if (st != MOE_OK || T == 0) return st;
   void* y = base + L.y;
   if (c.fuse_combine) {
     const Fused f{topk_weights, shared, residual, out};
     return do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0,
-                  nullptr, nullptr, &f);
+                  nullptr, nullptr, &f, in_launch);
   }
-  st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0);
+  st = do_ffn(h, T, x, x_sf, w, &plan, y, base + L.scratch + L.h_off, base + L.scratch + L.hsf_off, stream, 0, nullptr,
+              nullptr, nullptr, in_launch);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_combine(y, topk_weights, plan.pair_row, T, c.num_topk, c.hidden, shared, residual, out,
                                         c.out_fp32 != 0, stream));

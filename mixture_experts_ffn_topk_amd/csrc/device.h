@@ -10,6 +10,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 #define MOE_DEV __device__ __forceinline__
+#define MOE_HOST_DEV __host__ __device__
 
 MOE_DEV int lane_id() { return __lane_id(); }
 

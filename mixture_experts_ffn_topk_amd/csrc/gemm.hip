@@ -191,6 +191,154 @@ constexpr int kZeroSlotTokens = 64;  // tokens per workgroup that looks for toke
 // WAVES waves per workgroup and room for WGS workgroups per CU: the second
 // launch bound is the minimum number of waves per SIMD, which caps a wave's
 // registers at 512 / that number.
+// ---------------------------------------------------------------- routing plan inside the gate_up launch
+// (the plan of the Struct_mega_ffn_ep_combine_send page's operands: expert_start_indices,
+// expert_ids, num_active_experts, src_info; pair_row is its inverse).  Every
+// workgroup of a weight-bound gate_up launch builds what it needs in LDS -- the
+// per-expert counts and offsets, and its own rows' pair indices -- so that no
+// separate launch precedes it; the results equal launch_plan's bit for bit (rows
+// of an expert in pair order, masked and bad ids as there).
+struct PlanLds {
+  int* cnt;    // [E]
+  int* st;     // [E+1] exclusive offsets
+  int* misc;   // [4]: bad-id count
+  int* wc;     // [nch * waves] matches per (chunk, wave), then their exclusive offsets
+  int* srcl;   // [BM] pair index of each of the tile's rows
+  short* ex;   // [npairs] expert of each pair, -1 if masked
+};
+MOE_HOST_DEV inline size_t plan_lds_ints(int E, int npairs, int threads, int bm) {
+  const int nch = (npairs + threads - 1) / threads;
+  return ((size_t)(2 * E + 1 + 4 + nch * (threads / 64) + bm) + 3) & ~(size_t)3;  // 16-byte multiple
+}
+MOE_HOST_DEV inline size_t plan_lds_bytes(int E, int npairs, int threads, int bm) {
+  return plan_lds_ints(E, npairs, threads, bm) * 4 + (size_t)npairs * 2;
+}
+MOE_DEV PlanLds plan_lds_carve(int* base, int E, int npairs, int threads, int bm) {
+  const int nch = (npairs + threads - 1) / threads;
+  PlanLds L;
+  L.cnt = base;
+  L.st = base + E;
+  L.misc = L.st + E + 1;
+  L.wc = L.misc + 4;
+  L.srcl = L.wc + nch * (threads / 64);
+  L.ex = (short*)(base + plan_lds_ints(E, npairs, threads, bm));
+  return L;
+}
+
+// Counts and exclusive offsets of every expert into LDS; workgroup 0 also writes
+// the plan's counts, offsets, active list (ascending, then -1), status, the pair
+// rows of masked slots (-1) and zeroes the fused combine's counters.
+template <int kThreads>
+MOE_DEV void plan_counts_in_lds(const GemmParams& p, const PlanLds& L) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, E = p.E, np = p.npairs;
+  for (int e = tid; e < E; e += kThreads) L.cnt[e] = 0;
+  if (tid == 0) L.misc[0] = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int q = tid; q < np; q += kThreads) {
+    const long long v = p.ids64 ? ((const long long*)p.plan_ids)[q] : (long long)((const int*)p.plan_ids)[q];
+    int e = -1;
+    if (v >= 0 && v < E) e = (int)v;
+    else if (v != -1) ++bad;
+    L.ex[q] = (short)e;
+    if (e >= 0) atomicAdd(&L.cnt[e], 1);
+  }
+  if (bad) atomicAdd(&L.misc[0], bad);
+  __syncthreads();
+  const bool head = blockIdx.x == 0;
+  if (wave == 0) {
+    int carry = 0, acarry = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? L.cnt[e] : 0;
+      const int a = c > 0;
+      int incl = c, ainc = a;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d), oa = __shfl_up(ainc, d);
+        if (lane >= d) {
+          incl += o;
+          ainc += oa;
+        }
+      }
+      if (e < E) {
+        L.st[e] = carry + incl - c;
+        if (head) {
+          p.plan_out.expert_counts[e] = c;
+          p.plan_out.expert_start_indices[e] = carry + incl - c;
+          if (a) p.plan_out.expert_ids[acarry + ainc - a] = e;
+        }
+      }
+      carry += __shfl(incl, 63);
+      acarry += __shfl(ainc, 63);
+    }
+    if (lane == 0) L.st[E] = carry;
+    if (head) {
+      if (lane == 0) {
+        p.plan_out.expert_start_indices[E] = carry;
+        *p.plan_out.num_active = acarry;
+        *p.plan_out.status = L.misc[0];
+      }
+      for (int e = acarry + lane; e < E; e += 64) p.plan_out.expert_ids[e] = -1;
+    }
+  }
+  if (head) {
+    for (int q = tid; q < np; q += kThreads)
+      if (L.ex[q] < 0) p.plan_out.pair_row[q] = -1;
+    if (p.plan_out.counters != nullptr)
+      for (int i = tid; i < p.plan_out.n_counters; i += kThreads) p.plan_out.counters[i] = 0;
+  }
+  __syncthreads();
+}
+
+// A workgroup barrier that waits for this wave's LDS accesses only (outstanding
+// global loads, such as a weight ring already in flight, keep flying).
+MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The pair indices of rows [lo, lo + rows) of `expert` (its pairs in pair order)
+// into L.srcl (the workgroups of column tile 0 store them as the plan's src_info
+// and pair_row at the end of the kernel).  Pair q = c * kThreads + tid is visited
+// in (chunk c, wave, lane) order, which is pair order.
+template <int kThreads>
+MOE_DEV void plan_rows_in_lds(const GemmParams& p, const PlanLds& L, int expert, int lo, int rows) {
+  constexpr int W = kThreads / 64;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, np = p.npairs;
+  const int nch = (np + kThreads - 1) / kThreads;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int c = 0; c < nch; ++c) {
+    const int q = c * kThreads + tid;
+    const uint64_t bal = __ballot(q < np && L.ex[q] == expert);
+    if (lane == 0) L.wc[c * W + wave] = (int)__popcll(bal);
+  }
+  lds_barrier();
+  if (wave == 0) {
+    int carry = 0;
+    for (int i0 = 0; i0 < nch * W; i0 += 64) {
+      const int i = i0 + lane;
+      const int v = i < nch * W ? L.wc[i] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      if (i < nch * W) L.wc[i] = carry + incl - v;
+      carry += __shfl(incl, 63);
+    }
+  }
+  lds_barrier();
+  for (int c = 0; c < nch; ++c) {
+    const int q = c * kThreads + tid;
+    const bool m = q < np && L.ex[q] == expert;
+    const uint64_t bal = __ballot(m);
+    if (m) {
+      const int r = L.wc[c * W + wave] + (int)__popcll(bal & lt) - lo;
+      if (r >= 0 && r < rows) L.srcl[r] = q;
+    }
+  }
+  lds_barrier();
+}
+
 template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, int WGS, bool FAST>
 __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_kernel(GemmParams p) {
   using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
@@ -231,6 +379,22 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     return;
   }
 
+  // ---------------------------------------------------------------- routing plan (in-launch form)
+  // Weight-bound gate_up launches may build the plan themselves (plan_ids set): the
+  // offsets and the tile's row sources then come from LDS instead of the plan buffers.
+  extern __shared__ __attribute__((aligned(16))) int plan_dyn[];  // dynamic LDS: the in-launch plan
+  const int* st_p = p.start;
+  PlanLds PL{};
+  constexpr bool kPlanHere = GATEUP && BM <= 96;
+  const bool plan_here = kPlanHere && p.plan_ids != nullptr;
+  if constexpr (kPlanHere) {
+    if (plan_here) {
+      PL = plan_lds_carve(plan_dyn, p.E, p.npairs, kThreads, BM);
+      plan_counts_in_lds<kThreads>(p, PL);
+      st_p = PL.st;
+    }
+  }
+
   // ---------------------------------------------------------------- tile decode
   // The grid is sized for the worst case; the real m-tile count (per-expert tile
   // counts summed) sends the surplus workgroups home at once, so that the
@@ -238,7 +402,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   int total_m = 0;
   for (int e0 = 0; e0 < p.E; e0 += 64) {
     const int e = e0 + lane;
-    int t = e < p.E ? (p.start[e + 1] - p.start[e] + BM - 1) / BM : 0;
+    int t = e < p.E ? (st_p[e + 1] - st_p[e] + BM - 1) / BM : 0;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
     total_m += t;
@@ -258,8 +422,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     int base = 0;
     for (int e0 = 0; e0 < p.E; e0 += 64) {
       const int e = e0 + lane;
-      const int st_e = e < p.E ? p.start[e] : 0;
-      const int cnt = e < p.E ? p.start[e + 1] - st_e : 0;
+      const int st_e = e < p.E ? st_p[e] : 0;
+      const int cnt = e < p.E ? st_p[e + 1] - st_e : 0;
       const int tiles = (cnt + BM - 1) / BM;
       int incl = tiles;
 #pragma unroll
@@ -286,6 +450,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   if (expert < 0) return;  // (not reached: L < G)
   const int row0 = __builtin_amdgcn_readfirstlane(e_start) + tile_in_e * BM;
   const int rows = min(BM, __builtin_amdgcn_readfirstlane(e_count) - tile_in_e * BM);
+  // the sources of the tile's rows: the plan's src_info, or (in-launch plan) LDS,
+  // filled after the weight ring is issued (below)
+  const int* src_p = p.src_info + row0;
 
   // ---------------------------------------------------------------- B (weight) addressing
   // Weights arrive in the prepared layout: per expert, tiles of 16 rows x one
@@ -414,10 +581,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // weights' instead of preceding it.
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
   int a_src[TL::kAChunks];
+  auto gather_a_src = [&]() {
 #pragma unroll
-  for (int i = 0; i < TL::kAChunks; ++i)
-    a_src[i] = GATEUP ? p.src_info[row0 + min((tid + kThreads * i) >> 3, rows - 1)] : 0;
-  const int asf_src = GATEUP && F == Fmt::FP8 ? p.src_info[row0 + min(tid, rows - 1)] : 0;
+    for (int i = 0; i < TL::kAChunks; ++i)
+      a_src[i] = GATEUP ? src_p[min((tid + kThreads * i) >> 3, rows - 1)] : 0;
+  };
+  if (!plan_here) gather_a_src();
+  int asf_src = GATEUP && F == Fmt::FP8 && !plan_here ? src_p[min(tid, rows - 1)] : 0;
   // MX activation scales per stage: the BM x 4 UE8M0 bytes of each of its KSG
   // K-steps, loaded densely, one byte per lane and load (entry e: K-step e / (4 BM),
   // tile row (e % (4 BM)) / 4, K-block e % 4), so that a wave issues one or two
@@ -430,11 +600,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   static_assert(F != Fmt::MX || KSG == 1 || (BM * 4) % kThreads == 0, "MX scale entries: K-step per load");
   auto sf_u = [](int q) { return KSG == 1 ? 0 : kThreads * q / (BM * 4); };
   int asf_srcq[kSfQ];
+  auto gather_sf_src = [&]() {
 #pragma unroll
-  for (int q = 0; q < kSfQ; ++q) {
-    const int row = ((tid + kThreads * q) % (BM * 4)) >> 2;
-    asf_srcq[q] = GATEUP && F == Fmt::MX ? p.src_info[row0 + min(row, rows - 1)] : 0;
-  }
+    for (int q = 0; q < kSfQ; ++q) {
+      const int row = ((tid + kThreads * q) % (BM * 4)) >> 2;
+      asf_srcq[q] = GATEUP && F == Fmt::MX ? src_p[min(row, rows - 1)] : 0;
+    }
+  };
+  if (!plan_here) gather_sf_src();
   // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed.
   // Issued first, before the activation rows' addresses are known (direct-to-LDS
   // tiles: the first stage's K-steps here, the rest after the first activation stage).
@@ -442,6 +615,23 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   BFrag<F, NT> bq[DEPTH];
 #pragma unroll
   for (int d = 0; d < (TL::kDma ? KSG : DEPTH); ++d) load_b(bq[d], d);
+  __builtin_amdgcn_sched_barrier(0);
+  // In-launch plan: the tile's rows are gathered while the weight ring is in flight
+  // (its barriers wait for LDS traffic only, not for those loads).
+  // (LDS reads through an LDS pointer: through a generic one they would be flat
+  // loads, whose wait would also wait for the weight ring)
+  if constexpr (kPlanHere) {
+    if (plan_here) {
+      plan_rows_in_lds<kThreads>(p, PL, expert, tile_in_e * BM, rows);
+      const LDS3 int* sl = (const LDS3 int*)PL.srcl;
+#pragma unroll
+      for (int i = 0; i < TL::kAChunks; ++i) a_src[i] = sl[min((tid + kThreads * i) >> 3, rows - 1)];
+#pragma unroll
+      for (int q = 0; q < kSfQ; ++q)
+        if (F == Fmt::MX) asf_srcq[q] = sl[min(((tid + kThreads * q) % (BM * 4)) >> 2, rows - 1)];
+      if (F == Fmt::FP8) asf_src = sl[min(tid, rows - 1)];
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   uint32_t a_off[TL::kAChunks];
   uint32_t a_sfo[F == Fmt::NVF4 ? TL::kAChunks : 1];
@@ -1005,6 +1195,18 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
                   cc * 16) = *(const i32x4*)(out_lds + r * TL::kOutStride + cc * 16);
       }
     }
+    // in-launch plan: the workgroups of column tile 0 store their rows' src_info and
+    // pair_row (here, not in the prologue, where the stores would hold up the first
+    // wait on the activation loads behind the weight ring)
+    if constexpr (kPlanHere) {
+      if (plan_here && n_tile == 0) {
+        for (int r = tid; r < rows; r += kThreads) {
+          const int q = PL.srcl[r];
+          p.plan_out.src_info[row0 + r] = q;
+          p.plan_out.pair_row[q] = row0 + r;
+        }
+      }
+    }
   } else {
     // down: bf16 rows scattered to their pair slots y[src_info[row]]
     if constexpr (bf16_mma(F)) {
@@ -1109,12 +1311,15 @@ static void launch_one(const GemmParams& gp_in, bool fast, hipStream_t s, hipEve
   // fused combine: workgroups for the tokens without a valid slot
   if (!GATEUP && gp.fuse) grid += (gp.T + kZeroSlotTokens - 1) / kZeroSlotTokens;
   if (grid <= 0) return;
+  // the in-launch routing plan's LDS (weight-bound gate_up only)
+  const size_t dyn = (GATEUP && BM <= 96 && gp.plan_ids != nullptr) ? plan_lds_bytes(gp.E, gp.npairs, 64 * WAVES, BM)
+                                                                   : 0;
   if (fast)
     hipExtLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, true>), dim3(grid),
-                          dim3(64 * WAVES), 0, s, e0, e1, 0, gp);
+                          dim3(64 * WAVES), dyn, s, e0, e1, 0, gp);
   else
     hipExtLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, false>), dim3(grid),
-                          dim3(64 * WAVES), 0, s, e0, e1, 0, gp);
+                          dim3(64 * WAVES), dyn, s, e0, e1, 0, gp);
 }
 
 // Launch configuration per format, regime and leg: waves per workgroup, 16-row
@@ -1202,8 +1407,16 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.C_sf = a.h_sf;
   g1.c_sf_row = a.I / sf_div;
   g1.clamp = a.clamp;
+  // the routing plan built by the gate_up launch itself (weight-bound tiles only)
+  if (a.plan_ids != nullptr && ffn_plan_fusable(bm, npairs)) {
+    g1.plan_ids = a.plan_ids;
+    g1.ids64 = a.ids64 ? 1 : 0;
+    g1.npairs = npairs;
+    g1.plan_out = a.plan;
+  }
   // down: A = h rows, B = w2 [E, H, I]
   g2 = g1;
+  g2.plan_ids = nullptr;
   // (n_tiles of both legs are set at launch from their tile widths)
   g2.K = a.I;
   g2.ksteps = (a.I + elem_k - 1) / elem_k;

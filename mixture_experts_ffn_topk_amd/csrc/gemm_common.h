@@ -71,6 +71,15 @@ struct GemmParams {
   int out_f32;
   int m_grid;             // GEMM workgroups of the grid; those past it write the tokens without a valid slot
   uint32_t y_bytes;       // size of y (fused combine: y is addressed through a buffer resource)
+  // gate_up leg that builds the routing plan itself (plan_ids != nullptr): every
+  // workgroup histograms the ids into LDS and gathers its own rows; workgroup 0
+  // writes the counts, offsets, active list and status, the workgroups of column
+  // tile 0 their rows' src_info and pair_row (start / src_info above are then
+  // outputs of this launch, read by the down leg and the combine)
+  const void* plan_ids;   // [npairs] int64 (ids64) or int32 expert ids
+  int ids64;
+  int npairs;
+  PlanPtrs plan_out;
 };
 
 // Cache-policy bits of buffer loads and stores (gfx950): device-scope coherence

@@ -80,7 +80,15 @@ struct FfnArgs {
   const void* shared;
   const void* residual;
   bool out_f32;
+  // routing plan built inside the gate_up launch (plan_ids != nullptr; weight-bound
+  // tiles, npairs <= kPlanFusedMaxPairs): `plan` receives what launch_plan writes
+  const void* plan_ids;
+  bool ids64;
+  PlanPtrs plan;
 };
+// Whether the gate_up launch can build the routing plan itself: weight-bound tiles
+// (one launch reads the ids once per workgroup) and at most kPlanFusedMaxPairs pairs.
+inline bool ffn_plan_fusable(int bm, int npairs) { return bm <= 96 && npairs > 0 && npairs <= kPlanFusedMaxPairs; }
 // int32 arrival counters per token that the fused combine needs: one per column
 // tile of the down leg, at most ceil(H / 128)
 inline int combine_counter_stride(int H) { return (H + 127) / 128; }

@@ -24,11 +24,12 @@ def geometry(shape) -> "oracle.Geometry":
 
 
 def make_moe(shape, max_tokens=None, tile_regime="auto", topk_idx_bits=64, fast_math=True, out_fp32=False,
-             fuse_combine=False) -> MoEFFN:
+             fuse_combine=False, fuse_plan=False) -> MoEFFN:
     return MoEFFN(shape.hidden, shape.inter, shape.experts, shape.topk,
                   max_tokens if max_tokens is not None else shape.tokens, fmt=shape.fmt,
                   route_mode=shape.routing, activation_clamp=shape.clamp, topk_idx_bits=topk_idx_bits,
-                  fast_math=fast_math, tile_regime=tile_regime, out_fp32=out_fp32, fuse_combine=fuse_combine)
+                  fast_math=fast_math, tile_regime=tile_regime, out_fp32=out_fp32, fuse_combine=fuse_combine,
+                  fuse_plan=fuse_plan)
 
 
 def device_inputs(inp: dict, topk_idx=None, topk_weights=None, idx_dtype=torch.int64) -> dict:

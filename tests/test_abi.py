@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 8
+    assert lib.moe_abi_version() == 9
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -263,3 +263,39 @@ def test_binding_checks_tensors_before_the_call():
         moe32.combine(64, y, torch.zeros((64, 2)), plan, torch.zeros((64, 256), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="x holds"):
         moe.ffn_gate_up(64, torch.zeros(100, dtype=torch.uint8), torch.zeros((64, 2)), {}, plan, None, None)
+
+
+def test_plan_ffn_gate_up_validates_on_host():
+    """moe_plan_ffn_gate_up checks what moe_plan and moe_ffn_gate_up check, before any
+    launch; fuse_plan is a 0/1 switch."""
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=1)), ctypes.byref(h)) == 0  # PRECOMPUTED, FP8
+    plan = mx._Plan(*([16] * 7))
+    w = mx._Weights(16, 16, 16, 16)
+    f = lib.moe_plan_ffn_gate_up
+    assert f(h, 10, None, None, None, None, 16, 16, ctypes.byref(w), ctypes.byref(plan), 16, 16, None, 0,
+             None) == 1  # ids missing
+    assert f(h, 10, 16, None, None, None, None, 16, ctypes.byref(w), ctypes.byref(plan), 16, 16, None, 0,
+             None) == 1  # x missing
+    assert f(h, 10, 16, None, None, None, 16, None, ctypes.byref(w), ctypes.byref(plan), 16, 16, None, 0,
+             None) == 1  # FP8 x_sf missing
+    assert f(h, 10, 16, None, None, None, 16, 16, ctypes.byref(w), ctypes.byref(plan), None, 16, None, 0,
+             None) == 1  # h missing
+    assert f(h, 10, 16, None, None, None, 8, 16, ctypes.byref(w), ctypes.byref(plan), 16, 16, None, 0,
+             None) == 1  # x misaligned
+    assert f(h, 10, 16, None, None, None, 16, 16, ctypes.byref(w), ctypes.byref(plan), 16, 16, 128, 1 << 30,
+             None) == 1  # workspace misaligned
+    bad_plan = mx._Plan(*([16] * 6), None)  # status missing
+    assert f(h, 10, 16, None, None, None, 16, 16, ctypes.byref(w), ctypes.byref(bad_plan), 16, 16, None, 0,
+             None) == 1
+    assert lib.moe_plan_ffn_gate_up_timed(h, 10, None, None, None, None, 16, 16, ctypes.byref(w), ctypes.byref(plan),
+                                          16, 16, None, 0, None, None, None) == 1
+    lib.moe_destroy(h)
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(route_mode=1)), ctypes.byref(h)) == 0  # FROM_LOGITS
+    assert f(h, 10, None, 16, None, 16, 16, 16, ctypes.byref(w), ctypes.byref(plan), 16, 16, None, 0,
+             None) == 1  # topk_idx_out missing
+    lib.moe_destroy(h)
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=2)), ctypes.byref(h)) == 1
