@@ -825,9 +825,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // one 16x16x128 FP8 MFMA per K-step (unit hardware scales) into a fresh
       // partial, then acc += (sa[token] * sb[block]) * partial
       const int kc = min(ks, KS - 1);  // a step past the end multiplies zeros
-      float sbv[NT];
+      // A wave's weight rows of one kind lie in one 128-row scale block (gate_up: 8 NT
+      // gate and as many up rows per wave, 32-aligned; down: 16 NT rows, 64-aligned),
+      // so a token slice needs sa * sb once per kind, not once per tile.
+      static_assert(!GATEUP || (8 * NT <= 128 && 128 % (8 * NT) == 0), "a wave's gate rows share a scale block");
+      static_assert(GATEUP || (16 * NT <= 128 && 128 % (16 * NT) == 0), "a wave's down rows share a scale block");
+      constexpr int kKinds = GATEUP ? 2 : 1;
+      float sbk[kKinds];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sbv[nt] = sb_lds[sb_row(nt) * TL::kMaxKSteps + kc];
+      for (int j = 0; j < kKinds; ++j) sbk[j] = sb_lds[sb_row(j * (NT / kKinds)) * TL::kMaxKSteps + kc];
       // Software-pipelined: the scale update of MFMA i is issued after MFMA i+1
       // (two partials in flight), and the activation fragment of the next token
       // slice is read one slice ahead, so that the matrix core never waits on the
@@ -837,6 +843,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       auto rd_sa = [&](int mt) { return __builtin_bit_cast(float, sbuf[mt * 16 + r16]); };
       i32x8 a_cur = rd8(0), a_nxt = rd8(MT > 1 ? 1 : 0);
       float sa_cur = rd_sa(0), sa_nxt = rd_sa(MT > 1 ? 1 : 0);
+      float ssb[kKinds];  // sa * sb of the current token slice, per kind
+#pragma unroll
+      for (int j = 0; j < kKinds; ++j) ssb[j] = sa_cur * sbk[j];
       f32x4 prev = {};
       float s_prev = 0.f;
 #pragma unroll
@@ -845,11 +854,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         const i32x8 b8 = __builtin_shufflevector(bq_.lo[nt], bq_.hi[nt], 0, 1, 2, 3, 4, 5, 6, 7);
         const f32x4 cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a_cur, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
                                                                            0, 0, 127, 0, 127);
-        const float s_cur = sa_cur * sbv[nt];
+        const float s_cur = ssb[nt / (NT / kKinds)];
         if (i > 0) acc[(i - 1) / NT][(i - 1) % NT] += prev * s_prev;
         if (nt == NT - 1 && mt + 1 < MT) {
           a_cur = a_nxt;
           sa_cur = sa_nxt;
+#pragma unroll
+          for (int j = 0; j < kKinds; ++j) ssb[j] = sa_cur * sbk[j];
           if (mt + 2 < MT) {
             a_nxt = rd8(mt + 2);
             sa_nxt = rd_sa(mt + 2);
