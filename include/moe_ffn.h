@@ -124,9 +124,11 @@ typedef struct moe_config {
                                    epilogue (moe_ffn_down_combine) instead of as its own
                                    launch ([EPConfig] fuse_ffn_combine_send); same result, bit
                                    for bit */
-  int32_t fuse_plan;            /* 1: moe_forward builds the routing plan inside the gate_up
-                                   launch (as moe_plan_ffn_gate_up) where that applies;
-                                   same plan and result, bit for bit */
+  int32_t fuse_plan;            /* routing plan inside the gate_up launch (moe_plan_ffn_gate_up;
+                                   same plan and result, bit for bit): 0 = moe_forward keeps the
+                                   plan's own launch; 1 = moe_forward builds it in the gate_up
+                                   launch where that pays; 2 = wherever the sizes allow (also
+                                   for moe_plan_ffn_gate_up) */
 } moe_config;
 
 /* (host struct of device pointers) Expert weights of this GPU: the canonical
@@ -287,10 +289,13 @@ moe_status moe_ffn_down_timed(const moe_handle* h, int32_t num_tokens, const voi
    routing_logits with topk_idx_out / topk_weights_out, whose top-k keeps its own
    launch), the plan buffers (outputs, complete when the call's work is done),
    ws / ws_bytes as for moe_plan, then x, x_sf, w, h_out, h_sf_out as for
-   moe_ffn_gate_up.  In the weight-bound tile regime with at most 8192 pairs, every
-   workgroup of the gate_up launch counts the ids and gathers its own rows itself,
-   and the launch writes the whole plan; otherwise the call launches moe_plan's
-   kernels and then the gate_up leg.  Plan and h are bit for bit those of the two
+   moe_ffn_gate_up.  Where it pays -- the weight-bound tile regime, at most 8192
+   pairs, and pairs x rounds of gate_up workgroups per CU (worst-case grid over 512
+   workgroup slots) at most 4096, since every workgroup reads all the ids; with the
+   handle's fuse_plan = 2, wherever the first two hold -- every workgroup of the
+   gate_up launch counts the ids and gathers its own rows itself, and the launch
+   writes the whole plan; otherwise the call launches moe_plan's kernels and then
+   the gate_up leg.  Plan and h are bit for bit those of the two
    separate calls.  Validation and errors: the union of theirs.  The _timed form's
    events travel with the gate_up kernel's launch (which then includes the plan's
    work where it is built in that launch). */

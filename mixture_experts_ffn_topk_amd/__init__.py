@@ -207,14 +207,14 @@ class MoEFFN:
                  max_num_tokens: int, fmt: str = "fp8_block128", route_mode: str = "precomputed",
                  activation_clamp: float = 10.0, topk_idx_bits: int = 64, fast_math: bool = True,
                  tile_regime: str = "auto", out_fp32: bool = False, fuse_combine: bool = False,
-                 fuse_plan: bool = False):
+                 fuse_plan: int = 0):
         self.lib = load_library()
         self.cfg = _Config(hidden, intermediate_hidden, num_experts, num_topk, max_num_tokens,
                            float(activation_clamp), FORMATS[fmt], ROUTE_MODES[route_mode], topk_idx_bits,
                            int(bool(fast_math)), TILE_REGIMES[tile_regime], int(bool(out_fp32)),
-                           int(bool(fuse_combine)), int(bool(fuse_plan)))
+                           int(bool(fuse_combine)), int(fuse_plan))
         self.fuse_combine = bool(fuse_combine)
-        self.fuse_plan = bool(fuse_plan)
+        self.fuse_plan = int(fuse_plan)  # 0, 1 (where it pays) or 2 (wherever the sizes allow)
         self.out_fp32 = bool(out_fp32)
         self.fmt, self.route_mode = fmt, route_mode
         self.hidden, self.inter, self.experts, self.topk = hidden, intermediate_hidden, num_experts, num_topk

@@ -121,8 +121,10 @@ moe_status do_plan(const moe_handle* h, int32_t T, const void* idx_in, const flo
 }
 
 // Whether the gate_up launch builds the plan itself for T tokens.
+// (fuse_plan 2: wherever the sizes allow, without the cost rule)
 bool plan_in_gate_up(const moe_config& c, int32_t T) {
-  return T > 0 && moe::ffn_plan_fusable(choose_bm(c, T), T * c.num_topk);
+  return T > 0 && moe::ffn_plan_fusable(to_fmt(c.format), choose_bm(c, T), T * c.num_topk, c.num_experts,
+                                        c.intermediate_hidden, c.fuse_plan != 2);
 }
 
 // The combine fused into the down leg: router weights, addends and the output.
@@ -246,7 +248,7 @@ moe_status moe_create(const moe_config* cfg, moe_handle** out) {
   if (c.tile_regime < MOE_TILES_AUTO || c.tile_regime > MOE_TILES_PREFILL) return MOE_ERR_INVALID_ARGUMENT;
   if (c.out_fp32 != 0 && c.out_fp32 != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c.fuse_combine != 0 && c.fuse_combine != 1) return MOE_ERR_INVALID_ARGUMENT;
-  if (c.fuse_plan != 0 && c.fuse_plan != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.fuse_plan < 0 || c.fuse_plan > 2) return MOE_ERR_INVALID_ARGUMENT;
   switch (c.format) {
     case MOE_FMT_FP8_BLOCK128:
       if (c.hidden % 128 || c.intermediate_hidden % 128) return MOE_ERR_INVALID_ARGUMENT;

@@ -1379,6 +1379,22 @@ static void launch_pair(const GemmParams& g1_in, const GemmParams& g2_in, bool f
   }
 }
 
+bool ffn_plan_fusable(Fmt f, int bm, int npairs, int E, int I, bool pays) {
+  if (npairs <= 0 || npairs > kPlanFusedMaxPairs) return false;
+  if (bf16_mma(f) && bm <= 96) bm = 96;
+  if (bm > 96) return false;  // MFMA-bound tiles: thousands of workgroups
+  if (!pays) return true;
+  // weight-bound gate_up tiles: 4 waves x 64 weight rows (128 h columns), two workgroups per CU
+  static_assert(leg_config<Fmt::FP8, true, 80>().waves == 4 && leg_config<Fmt::FP8, true, 80>().nt == 4 &&
+                    leg_config<Fmt::MX, true, 80>().waves == 4 && leg_config<Fmt::BF16, true, 96>().waves == 4 &&
+                    leg_config<Fmt::NV4, true, 96>().nt == 4,
+                "the weight-bound gate_up tile the cost rule assumes");
+  constexpr long long kSlots = 256LL * 2;  // CUs of the part x workgroups per CU
+  const long long grid = (long long)ffn_max_m_tiles(npairs, E, bm) * ((I + 127) / 128);
+  const long long rounds = (grid + kSlots - 1) / kSlots;
+  return rounds * npairs <= 4096;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   const int npairs = a.T * a.topk;
   if (npairs == 0) return hipSuccess;
@@ -1419,7 +1435,8 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g1.c_sf_row = a.I / sf_div;
   g1.clamp = a.clamp;
   // the routing plan built by the gate_up launch itself (weight-bound tiles only)
-  if (a.plan_ids != nullptr && ffn_plan_fusable(bm, npairs)) {
+  if (a.plan_ids != nullptr) {
+    if (!ffn_plan_fusable(a.fmt, a.bm, npairs, a.E, a.I, false)) return hipErrorInvalidValue;
     g1.plan_ids = a.plan_ids;
     g1.ids64 = a.ids64 ? 1 : 0;
     g1.npairs = npairs;

@@ -87,8 +87,12 @@ struct FfnArgs {
   PlanPtrs plan;
 };
 // Whether the gate_up launch can build the routing plan itself: weight-bound tiles
-// (one launch reads the ids once per workgroup) and at most kPlanFusedMaxPairs pairs.
-inline bool ffn_plan_fusable(int bm, int npairs) { return bm <= 96 && npairs > 0 && npairs <= kPlanFusedMaxPairs; }
+// and at most kPlanFusedMaxPairs pairs.  `pays` adds the cost rule: every workgroup
+// of the launch reads and counts all the ids, so the pairs times the rounds of
+// workgroups a CU runs must stay small (decode: 2048 pairs, 2 rounds of the
+// worst-case grid; the W4A8 shape, 8192 pairs over ~11 rounds, is not).  The host
+// API decides; the launcher builds the plan in the launch when handed the ids.
+bool ffn_plan_fusable(Fmt f, int bm, int npairs, int E, int I, bool pays);
 // int32 arrival counters per token that the fused combine needs: one per column
 // tile of the down leg, at most ceil(H / 128)
 inline int combine_counter_stride(int H) { return (H + 127) / 128; }

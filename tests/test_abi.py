@@ -267,7 +267,7 @@ def test_binding_checks_tensors_before_the_call():
 
 def test_plan_ffn_gate_up_validates_on_host():
     """moe_plan_ffn_gate_up checks what moe_plan and moe_ffn_gate_up check, before any
-    launch; fuse_plan is a 0/1 switch."""
+    launch; fuse_plan is 0, 1 or 2."""
     lib = _lib()
     h = ctypes.c_void_p()
     assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=1)), ctypes.byref(h)) == 0  # PRECOMPUTED, FP8
@@ -298,4 +298,7 @@ def test_plan_ffn_gate_up_validates_on_host():
              None) == 1  # topk_idx_out missing
     lib.moe_destroy(h)
     h = ctypes.c_void_p()
-    assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=2)), ctypes.byref(h)) == 1
+    assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=2)), ctypes.byref(h)) == 0
+    lib.moe_destroy(h)
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=3)), ctypes.byref(h)) == 1

@@ -4,7 +4,8 @@ the ids and gathers its own rows, and the launch writes the plan.  Plan buffers
 and the intermediate must equal moe_plan + moe_ffn_gate_up bit for bit, and the
 forward pass moe_forward's without it.  Covered: every format, int32 and int64
 ids, masked / bad / duplicate ids and a token without a valid slot, routing
-from logits, 1024 experts at the 8192-pair limit, one token, repeated calls on
+from logits, 1024 experts at the 8192-pair limit (fuse_plan = 2 forces the
+in-launch form where the cost rule would keep the plan kernel), one token, repeated calls on
 one set of plan buffers, the prefill regime (where the call launches the plan
 kernel itself), the fused combine alongside, and the full decode and W4A8
 workloads."""
@@ -117,7 +118,7 @@ def test_plan_in_gate_up_equals_separate(name, kw, bits):
     inp = moe_synth.make_inputs(sh)
     ids = _odd_ids(inp, sh) if sh.routing == "precomputed" else None
     d = device_inputs(inp, topk_idx=ids, idx_dtype=torch.int64 if bits == 64 else torch.int32)
-    m = make_moe(sh, tile_regime="decode", topk_idx_bits=bits)
+    m = make_moe(sh, tile_regime="decode", topk_idx_bits=bits, fuse_plan=2)  # in-launch wherever possible
     res = _run_both(sh, inp, d, m)
     _assert_equal(res, name)
     if ids is not None and sh.tokens >= 12:
@@ -131,7 +132,7 @@ def test_repeated_calls_on_one_plan():
     sh = _shape("fused_plan_repeat", dict(T=120, H=512, I=256, E=12, k=3, fmt="fp8_block128"))
     inp = moe_synth.make_inputs(sh)
     T, k = sh.tokens, sh.topk
-    m = make_moe(sh, tile_regime="decode")
+    m = make_moe(sh, tile_regime="decode", fuse_plan=2)
     d = device_inputs(inp)
     w = prepared(m, d)
     ws = m.alloc_workspace(T)
@@ -161,7 +162,7 @@ def test_prefill_regime_launches_the_plan_itself():
     sh = _shape("fused_plan_prefill", dict(T=300, H=896, I=384, E=4, k=2, fmt="fp8_block128"))
     inp = moe_synth.make_inputs(sh)
     d = device_inputs(inp, topk_idx=_odd_ids(inp, sh))
-    m = make_moe(sh, tile_regime="prefill")
+    m = make_moe(sh, tile_regime="prefill", fuse_plan=2)
     _assert_equal(_run_both(sh, inp, d, m), "prefill")
 
 
@@ -181,7 +182,7 @@ def test_forward_with_fuse_plan(name, kw, fuse_combine):
     ids = _odd_ids(inp, sh) if sh.routing == "precomputed" else None
     T, H = sh.tokens, sh.hidden
     outs = []
-    for fp, fc in ((False, False), (True, fuse_combine)):
+    for fp, fc in ((0, False), (2, fuse_combine)):
         d = device_inputs(inp, topk_idx=ids)
         m = make_moe(sh, tile_regime="decode", fuse_combine=fc, fuse_plan=fp)
         w = prepared(m, d)
@@ -201,11 +202,11 @@ def test_full_size_workloads(workload):
     print(f"[fused-plan] {workload}: generating inputs", flush=True)
     inp = moe_synth.make_inputs(sh)
     d = device_inputs(inp)
-    m = make_moe(sh)
+    m = make_moe(sh, fuse_plan=2)  # in the gate_up launch even where the cost rule would not (W4A8)
     _assert_equal(_run_both(sh, inp, d, m), workload)
     T, H = sh.tokens, sh.hidden
     outs = []
-    for fp in (False, True):
+    for fp in (0, 2):
         m2 = make_moe(sh, fuse_plan=fp)
         w = prepared(m2, d)
         out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
