@@ -216,3 +216,27 @@ def test_full_size_workloads(workload):
         outs.append(out)
     assert torch.isfinite(outs[1].float()).all()
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("fill", [-1, 1000])
+def test_no_valid_pair(fill):
+    """Every slot masked (-1) or out of range: the in-launch plan has no tile to run,
+    and workgroup 0 alone must still write counts, offsets, the active list, status
+    and every pair_row; the forward output is zero."""
+    sh = _shape("fused_plan_empty", dict(T=16, H=256, I=128, E=8, k=4, fmt="fp8_block128"))
+    inp = moe_synth.make_inputs(sh)
+    ids = np.full((sh.tokens, sh.topk), fill, dtype=np.int64)
+    d = device_inputs(inp, topk_idx=ids)
+    m = make_moe(sh, tile_regime="decode", fuse_plan=2)
+    res = _run_both(sh, inp, d, m)
+    _assert_equal(res, f"fill {fill}")
+    plan = res[1][0]
+    assert int(plan["num_active_experts"].item()) == 0 and (plan["expert_ids"] == -1).all()
+    assert int(plan["status"].item()) == (0 if fill == -1 else sh.tokens * sh.topk)
+    assert (plan["pair_row"] == -1).all()
+    T, H = sh.tokens, sh.hidden
+    out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    m.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], prepared(m, d), out,
+              m.alloc_workspace(T))
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()
