@@ -229,7 +229,8 @@ def counter_summary(workload: str, out_md: str, dirs: list, command: str) -> int
     f_fac = gib_kb / f_copy if f_copy else None
     w_fac = gib_kb / w_copy if w_copy else None
     lines = [f"# Counters: {workload} (T={sh.tokens}, hidden {sh.hidden}, intermediate {sh.inter}, {sh.experts} experts, "
-             f"top-{sh.topk}, {sh.fmt})", "", "One rocprofv3 `--pmc` pass per counter group, each its own run:", "",
+             f"top-{sh.topk}, {sh.fmt})", "", "One rocprofv3 `--pmc` pass per counter group, each its own run (on one MI355X; `$REPO` is the repository "
+             "root, `$OUT` an output folder):", "",
              "```", command, "```", "",
              f"Routing: {active} active experts, {pairs} routed pairs.  Copy calibration: FETCH_SIZE factor "
              f"{f_fac if f_fac is None else round(f_fac, 3)}, WRITE_SIZE factor {w_fac if w_fac is None else round(w_fac, 3)} "
