@@ -14,10 +14,13 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("fmt,routing", [("fp8_block128", "precomputed"), ("w4a8_mx", "from_logits"),
                                          ("nvfp4_w4a16", "precomputed")])
-def test_graph_replays_match_eager(fmt, routing):
+@pytest.mark.parametrize("plan_in_launch", [False, True])
+def test_graph_replays_match_eager(fmt, routing, plan_in_launch):
+    """plan_in_launch: the step's plan and gate_up leg are moe_plan_ffn_gate_up (the
+    plan built inside the gate_up launch)."""
     sh = moe_synth.MoEShape("graph_" + fmt, 41, 96, 512, 256, 8, 2, fmt, routing)
     inp = moe_synth.make_inputs(sh)
-    moe = make_moe(sh)
+    moe = make_moe(sh, fuse_plan=2 if plan_in_launch else 0)
     d = device_inputs(inp)
     w = prepared(moe, d)
     T, k = sh.tokens, sh.topk
@@ -29,6 +32,13 @@ def test_graph_replays_match_eager(fmt, routing):
     s = torch.cuda.Stream()
 
     def step():
+        if plan_in_launch:
+            kw = (dict(topk_idx=d["topk_idx"]) if routing == "precomputed" else
+                  dict(routing_logits=d["logits"], topk_idx_out=d["topk_idx"], topk_weights_out=d["topk_weights"]))
+            moe.plan_ffn_gate_up(T, d["x"], d["x_sf"], w, plan, h, hsf, ws=ws, stream=s, **kw)
+            moe.ffn_down(T, h, hsf, w, plan, y, stream=s)
+            moe.combine(T, y, d["topk_weights"], plan, out, stream=s)
+            return
         if routing == "precomputed":
             moe.plan(T, plan, topk_idx=d["topk_idx"], ws=ws, stream=s)
         else:
