@@ -5,7 +5,11 @@
 //
 // Both legs walk one shared expert list (Struct_mega_ffn_ep_combine_send page:
 // num_active_experts / expert_start_indices); each workgroup finds its tile
-// from the per-expert prefix sums, so no device-side tile list is needed.
+// from the per-expert prefix sums, so no device-side tile list is needed.  A
+// weight-bound gate_up launch can also build that plan itself (plan_ids set):
+// every workgroup counts the ids into LDS, finds its tile there, and ranks its
+// own expert's pairs while its weight ring is in flight; the launch writes the
+// plan for the down leg and the combine (the plan kernel then leaves the step).
 //
 // Workgroup: WAVES wavefronts, BM rows x BN = WAVES*16*NT weight rows per tile.
 //   * A (activation rows, gathered through src_info for gate_up) is staged in
