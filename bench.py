@@ -53,11 +53,20 @@ COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_topk_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h", "device.h", "launch.h", "prepare.hip")]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and whitespace runs removed: what the compiler sees
+    of it, so that an edit of a comment does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
