@@ -198,8 +198,9 @@ bool x_ok(const moe_config& c, const void* x, const void* x_sf) {
 }
 
 // The GEMM kernels address every operand through buffer resources with 32-bit
-// lane offsets (an offset of 2^31 or more reads zeros), and FP8 stages the
-// weight scales of at most 256 K-steps of 128 in LDS.
+// lane offsets (an offset of 2^31 or more reads zeros), FP8 stages the weight
+// scales of at most 256 K-steps of 128 in LDS, and a weight-bound MX tile stages
+// its rows' activation-scale rows (K/32 bytes each, K up to 32768) in LDS.
 bool sizes_supported(const moe_config& c) {
   constexpr unsigned long long kMaxBytes = 0x7FFFFFFFull;
   const unsigned long long T = (unsigned long long)c.max_num_tokens, H = (unsigned long long)c.hidden,
@@ -212,7 +213,7 @@ bool sizes_supported(const moe_config& c) {
   if (moe::prepared_expert_bytes(f, (int)(2 * I), (int)H) > kMaxBytes ||
       moe::prepared_expert_bytes(f, (int)H, (int)I) > kMaxBytes)
     return false;
-  if (c.format == MOE_FMT_FP8_BLOCK128 && (H / 128 > 256 || I / 128 > 256)) return false;
+  if ((c.format == MOE_FMT_FP8_BLOCK128 || c.format == MOE_FMT_W4A8_MX) && (H > 32768 || I > 32768)) return false;
   // the fused combine addresses y [T*k, H] bf16 through a buffer resource
   if (c.fuse_combine && T * k * H * 2 > kMaxBytes) return false;
   return true;

@@ -46,6 +46,8 @@
 // K elements [8h, 8h+8) of its 16-element sub-step, row r.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -120,6 +122,10 @@ struct Tile {
   // weight-bound tiles, whose weight stream then starts before the activation
   // addresses are known).
   static constexpr int kABufs = kDma ? 4 : 2;
+  // Weight-bound MX tiles stage their rows' whole UE8M0 scale rows in LDS once per
+  // tile (dynamic LDS) instead of four bytes per row and K-step: one cache line per
+  // row and K-step was as many L2 requests as the weights' own.
+  static constexpr bool kSfTab = F == Fmt::MX && BM <= 96;
   static constexpr int kABytes = kABufs * KSG * kAStepBytes;
   static constexpr int kOutBytes = BM * kOutStride;
   static constexpr int kUnion = kABytes > kOutBytes ? kABytes : kOutBytes;
@@ -216,6 +222,15 @@ MOE_HOST_DEV inline size_t plan_lds_ints(int E, int npairs, int threads, int bm)
 }
 MOE_HOST_DEV inline size_t plan_lds_bytes(int E, int npairs, int threads, int bm) {
   return plan_lds_ints(E, npairs, threads, bm) * 4 + (size_t)npairs * 2;
+}
+// MX scale table: a row of sf_row scale bytes padded to a multiple of 4 with an odd
+// dword count (the 16 rows a K-step's lanes read then fall in distinct banks).
+MOE_HOST_DEV inline int mx_table_stride(int sf_row) {
+  const int s = (sf_row + 3) & ~3;
+  return ((s >> 2) & 1) ? s : s + 4;
+}
+MOE_HOST_DEV inline size_t plan_region_bytes(bool plan, int E, int npairs, int threads, int bm) {
+  return plan ? (plan_lds_bytes(E, npairs, threads, bm) + 15) & ~(size_t)15 : 0;
 }
 MOE_DEV PlanLds plan_lds_carve(int* base, int E, int npairs, int threads, int bm) {
   const int nch = (npairs + threads - 1) / threads;
@@ -712,7 +727,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         s[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, (asf_off + 4u * u) | oob_if(ks >= p.ksteps),
                                                               (uint32_t)st * (KSG * 4u), 0);
       }
-    } else if constexpr (F == Fmt::MX) {
+    } else if constexpr (F == Fmt::MX && !TL::kSfTab) {
       // byte 4 ks + (e % 4) of the row; K-blocks past the row's end and entries past
       // the stage's read zeros (no branch in the main loop)
 #pragma unroll
@@ -738,7 +753,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     if constexpr (F == Fmt::FP8) {
 #pragma unroll
       for (int u = 0; u < KSG; ++u) sa_lds[(buf * KSG + u) * TL::kSA + tid] = s[u];
-    } else if constexpr (F == Fmt::MX) {
+    } else if constexpr (F == Fmt::MX && !TL::kSfTab) {
       // the four lanes of a quad hold the four bytes of one row's scale word (entry
       // e = 4 row + block): the quad's first lane gathers them (DPP quad
       // permutations) and stores the word
@@ -780,6 +795,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
   uint32_t as[TL::kDma ? 1 : 2][kSfN] = {};
+  const LDS3 uint32_t* sft = nullptr;  // weight-bound MX: the tile's scale rows ([BM][sft_dw] dwords)
+  int sft_dw = 0;
   if constexpr (TL::kDma) {
     // Ring K-steps of stage 0 (above), A(0), the ring K-steps of stage 1, A(1),
     // in this order (the scheduling barriers keep it).  When stage st waits for
@@ -800,6 +817,72 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   } else {
     load_a(av[0], as[0], 0);
     load_a(av[1], as[1], 1);
+    if constexpr (TL::kSfTab) {
+      // the tile's scale rows: sf_row bytes per row (UE8M0 per 32 activations), rows
+      // past the tile's and bytes past a row's end zero (so that every K-block of
+      // the padded last K-step reads a finite scale); byte entries i = tid +
+      // kThreads j of the [BM][stride] table, 16 loads in flight per thread
+      uint8_t* tb = (uint8_t*)plan_dyn + plan_region_bytes(plan_here, p.E, p.npairs, kThreads, BM);
+      const int sfr = p.a_sf_row, stride = mx_table_stride(sfr);
+      sft = (const LDS3 uint32_t*)tb;
+      sft_dw = stride >> 2;
+      int* rtok = (int*)red_lds;  // gate_up: the token of each tile row (the epilogue reuses the space)
+      if (GATEUP) {
+        if ((tid & 7) == 0) {
+#pragma unroll
+          for (int i = 0; i < TL::kAChunks; ++i) {
+            const int r = (tid + kThreads * i) >> 3;
+            if (r < BM) rtok[r] = r < rows ? a_src[i] / p.topk : -1;
+          }
+        }
+        lds_barrier();
+      }
+      // entries of W bytes (the widest the row length's alignment allows: a scale row
+      // starts at a multiple of sf_row bytes), 16 loads in flight per thread
+      auto fill = [&](auto wbytes) {
+        constexpr int W = decltype(wbytes)::value;
+        const int per_row = stride / W, n = BM * per_row;
+        const int dr = kThreads / per_row, du = kThreads % per_row;
+        for (int j0 = 0; j0 * kThreads < n; j0 += 16) {
+          uint32_t v[16];
+          int r = (j0 * kThreads + tid) / per_row, u = (j0 * kThreads + tid) % per_row;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int tok = r >= BM ? -1 : GATEUP ? rtok[r] : (r < rows ? row0 + r : -1);
+            const uint32_t off =
+                (tok >= 0 && u * W < sfr) ? (uint32_t)tok * (uint32_t)sfr + (uint32_t)(u * W) : kOOB;
+            if constexpr (W == 4) v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, off, 0, 0);
+            else if constexpr (W == 2) v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(asf_rs, off, 0, 0);
+            else v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, off, 0, 0);
+            u += du;
+            r += dr;
+            if (u >= per_row) {
+              u -= per_row;
+              ++r;
+            }
+          }
+          r = (j0 * kThreads + tid) / per_row;
+          u = (j0 * kThreads + tid) % per_row;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (r < BM) {
+              if constexpr (W == 4) *(uint32_t*)(tb + r * stride + u * 4) = v[j];
+              else if constexpr (W == 2) *(uint16_t*)(tb + r * stride + u * 2) = (uint16_t)v[j];
+              else tb[r * stride + u] = (uint8_t)v[j];
+            }
+            u += du;
+            r += dr;
+            if (u >= per_row) {
+              u -= per_row;
+              ++r;
+            }
+          }
+        }
+      };
+      if ((sfr & 3) == 0) fill(std::integral_constant<int, 4>{});
+      else if ((sfr & 1) == 0) fill(std::integral_constant<int, 2>{});
+      else fill(std::integral_constant<int, 1>{});
+    }
     store_a(av[0], as[0], 0);
   }
   if (F == Fmt::FP8) {
@@ -979,7 +1062,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
           // weights E2M1 (first operand, format 4), activations E4M3 (format 0);
           // each lane's scale byte: its row (weight row / token) in K-block g
           const i32x8 a8 = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const int sa = (int)((sbuf[mt * 16 + r16] >> (8 * g)) & 0xFFu);
+          const uint32_t sw = TL::kSfTab ? sft[(mt * 16 + r16) * sft_dw + min(ks, KS - 1)] : sbuf[mt * 16 + r16];
+          const int sa = (int)((sw >> (8 * g)) & 0xFFu);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             const i32x8 b8 = {bq_.lo[nt][0], bq_.lo[nt][1], bq_.lo[nt][2], bq_.lo[nt][3], 0, 0, 0, 0};
@@ -1326,9 +1410,11 @@ static void launch_one(const GemmParams& gp_in, bool fast, hipStream_t s, hipEve
   // fused combine: workgroups for the tokens without a valid slot
   if (!GATEUP && gp.fuse) grid += (gp.T + kZeroSlotTokens - 1) / kZeroSlotTokens;
   if (grid <= 0) return;
-  // the in-launch routing plan's LDS (weight-bound gate_up only)
-  const size_t dyn = (GATEUP && BM <= 96 && gp.plan_ids != nullptr) ? plan_lds_bytes(gp.E, gp.npairs, 64 * WAVES, BM)
-                                                                   : 0;
+  // dynamic LDS: the in-launch routing plan (weight-bound gate_up only), then the
+  // weight-bound MX tiles' scale table
+  using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
+  const size_t dyn = plan_region_bytes(GATEUP && BM <= 96 && gp.plan_ids != nullptr, gp.E, gp.npairs, 64 * WAVES, BM) +
+                     (TL::kSfTab ? (size_t)BM * mx_table_stride(gp.a_sf_row) : 0);
   if (fast)
     hipExtLaunchKernelGGL((ffn_gemm_kernel<F, GATEUP, BM, WAVES, NT, DEPTH, KSG, WGS, true>), dim3(grid),
                           dim3(64 * WAVES), dyn, s, e0, e1, 0, gp);

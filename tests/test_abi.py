@@ -65,6 +65,7 @@ def _cfg(**kw):
     ({"format": 2, "hidden": 2880, "intermediate_hidden": 2880, "num_experts": 128, "num_topk": 4,
       "route_mode": 1}, 0),                    # MX: multiples of 32, logits routing
     ({"format": 2, "hidden": 2880 + 16, "intermediate_hidden": 2880}, 1),
+    ({"format": 2, "hidden": 32768 + 32, "intermediate_hidden": 2880, "max_num_tokens": 16}, 2),  # MX scale rows in LDS
     ({"format": 3}, 0),                                          # NVFP4: multiples of 64
     ({"format": 3, "hidden": 7168 + 32}, 1),
     ({"format": 4}, 0),                                          # NVFP4 x NVFP4: multiples of 64
