@@ -134,6 +134,9 @@ struct Tile {
   // FP8 weight-scale blocks (128 rows) a tile touches: gate and up block, or a down window of BN rows
   static constexpr int kHB = BN / 2 / 128;  // gate_up: 128-column h blocks per tile
   static constexpr int kNB = GATEUP ? 2 * kHB : BN / 128 + 1;
+  // a down tile starts at a multiple of BN: with BN a multiple of 64 it starts 0 or
+  // 64 rows into a block, so BN / 128 + 1 blocks cover it
+  static_assert(F != Fmt::FP8 || GATEUP || BN % 64 == 0, "FP8 down tiles cover whole 64-row halves of scale blocks");
   static constexpr int kLds = kUnion + kABufs * KSG * kSA * 4 + WAVES * BM * 4 + (F == Fmt::FP8 ? kNB * kMaxKSteps * 4 : 0);
 };
 
