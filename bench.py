@@ -632,7 +632,8 @@ def main() -> int:
         "step_tflops": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         **step_fracs(leg, ms_per_step),
-        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine), "plan_in_gate_up": bool(args.fuse_plan),
+        "scrubbed": scrubbed, "fused_combine": bool(args.fuse_combine),
+        "plan_in_gate_up": bool(args.fuse_plan) and leg.moe.plan_in_gate_up(T),
         "warmup_curve": curve,
         "roofline": roofline(leg, gate_ms, down_ms),
     }
@@ -656,6 +657,7 @@ def main() -> int:
         med = float(np.median(per_s))
         result["decode"] = {
             "workload": dec.sh.name, "tokens": dec.sh.tokens, "ms_per_step": round(ms_b2b, 4),
+            "plan_in_gate_up": bool(args.fuse_plan) and dec.moe.plan_in_gate_up(dec.sh.tokens),
             "tokens_per_s": round(dec.sh.tokens / (ms_b2b * 1e-3), 1), **step_fracs(dec, ms_b2b),
             "scrubbed": {"scrub_mb": args.scrub_mb, "scrub": "read", "step_ms_median": round(med, 4),
                          "step_ms_min": round(float(np.min(per_s)), 4),

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 9
+#define MOE_FFN_ABI_VERSION 10
 
 typedef enum {
   MOE_OK = 0,
@@ -310,6 +310,12 @@ moe_status moe_plan_ffn_gate_up_timed(const moe_handle* h, int32_t num_tokens, c
                                       const moe_plan_buffers* plan /* host struct */, void* h_out, void* h_sf_out,
                                       void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start,
                                       hipEvent_t stop);
+
+/* (host) 1 if moe_plan_ffn_gate_up (and moe_forward with fuse_plan set) builds the
+   routing plan inside the gate_up launch for num_tokens tokens (the rule above:
+   [EPConfig] fused_moe_ready), 0 if it launches the plan kernels first or if
+   h or num_tokens is invalid.  Launches nothing. */
+int32_t moe_plan_in_gate_up(const moe_handle* h, int32_t num_tokens);
 
 /* The down leg with the router-weighted combine fused into its epilogue
    ([EPConfig] fuse_ffn_combine_send: the expert FFN's down epilogue feeds the

@@ -59,7 +59,7 @@ class _PreparedSizes(ctypes.Structure):
 
 
 PLAN_FIELDS = [f for f, _ in _Plan._fields_]
-EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_prepared_weights_size", "moe_prepare_weights",
+EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_plan_in_gate_up", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
             "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_ffn_gate_up_timed", "moe_ffn_down_timed",
             "moe_ffn_down_combine", "moe_ffn_down_combine_timed", "moe_plan_ffn_gate_up", "moe_plan_ffn_gate_up_timed",
@@ -84,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_destroy.restype = None
     lib.moe_workspace_size.argtypes = [vp, i32]
     lib.moe_workspace_size.restype = sz
+    lib.moe_plan_in_gate_up.argtypes = [vp, i32]
+    lib.moe_plan_in_gate_up.restype = i32
     lib.moe_prepared_weights_size.argtypes = [vp, ctypes.POINTER(_PreparedSizes)]
     lib.moe_prepared_weights_size.restype = i32
     lib.moe_prepare_weights.argtypes = [vp, ctypes.POINTER(_Weights), ctypes.POINTER(_Weights), vp]
@@ -290,6 +292,11 @@ class MoEFFN:
     # ---------------------------------------------------------------- helpers (torch allocation)
     def workspace_size(self, num_tokens: int) -> int:
         return int(self.lib.moe_workspace_size(self._h, num_tokens))
+
+    def plan_in_gate_up(self, num_tokens: int) -> bool:
+        """Whether plan_ffn_gate_up (and forward with fuse_plan) builds the routing
+        plan inside the gate_up launch for num_tokens tokens."""
+        return bool(self.lib.moe_plan_in_gate_up(self._h, num_tokens))
 
     def alloc_workspace(self, num_tokens: int, device="cuda"):
         import torch

@@ -318,6 +318,11 @@ size_t moe_workspace_size(const moe_handle* h, int32_t T) {
   return layout_for(h->cfg, T).total;
 }
 
+int32_t moe_plan_in_gate_up(const moe_handle* h, int32_t T) {
+  if (!valid_T(h, T)) return 0;
+  return plan_in_gate_up(h->cfg, T) ? 1 : 0;
+}
+
 moe_status moe_plan_ex(const moe_handle* h, int32_t T, const void* topk_idx_in, const float* routing_logits,
                        const float* routing_bias, void* topk_idx_out, float* topk_weights_out,
                        const moe_plan_buffers* plan, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 9
+    assert lib.moe_abi_version() == 10
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -264,6 +264,32 @@ def test_binding_checks_tensors_before_the_call():
         moe32.combine(64, y, torch.zeros((64, 2)), plan, torch.zeros((64, 256), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="x holds"):
         moe.ffn_gate_up(64, torch.zeros(100, dtype=torch.uint8), torch.zeros((64, 2)), {}, plan, None, None)
+
+
+@pytest.mark.parametrize("kw,T,fuse_plan,expect", [
+    ({}, 256, 1, 1),                                   # decode: weight-bound tiles, 2048 pairs, one round
+    ({"max_num_tokens": 8192}, 8192, 1, 0),            # prefill: MFMA-bound tiles (2048 rows per expert)
+    ({"max_num_tokens": 8192}, 8192, 2, 0),            # (not even where forced)
+    ({"format": 2, "hidden": 2880, "intermediate_hidden": 2880, "num_experts": 128, "num_topk": 4,
+      "max_num_tokens": 2048}, 2048, 1, 0),            # W4A8: 11 rounds x 8192 pairs > 4096
+    ({"format": 2, "hidden": 2880, "intermediate_hidden": 2880, "num_experts": 128, "num_topk": 4,
+      "max_num_tokens": 2048}, 2048, 2, 1),            # forced: the sizes allow it
+    ({"hidden": 256, "intermediate_hidden": 128, "num_experts": 8, "num_topk": 2, "max_num_tokens": 64}, 64, 1, 1),
+    ({"format": 1, "hidden": 4096, "intermediate_hidden": 14336, "num_experts": 8, "num_topk": 2,
+      "max_num_tokens": 4096}, 4096, 1, 0),            # Mixtral: MFMA-bound tiles
+    ({}, 0, 1, 0),                                     # no tokens
+    ({}, 257, 1, 0),                                   # beyond max_num_tokens
+])
+def test_plan_in_gate_up_rule(kw, T, fuse_plan, expect):
+    """The host's answer to whether the routing plan is built inside the gate_up
+    launch: the weight-bound tile regime, at most 8192 pairs, and (unless forced)
+    pairs x rounds of gate_up workgroups at most 4096."""
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(fuse_plan=fuse_plan, **kw)), ctypes.byref(h)) == 0
+    assert lib.moe_plan_in_gate_up(h, T) == expect
+    lib.moe_destroy(h)
+    assert lib.moe_plan_in_gate_up(None, 16) == 0
 
 
 def test_plan_ffn_gate_up_validates_on_host():
