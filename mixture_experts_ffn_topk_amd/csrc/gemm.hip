@@ -823,8 +823,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     if constexpr (TL::kSfTab) {
       // the tile's scale rows: sf_row bytes per row (UE8M0 per 32 activations), rows
       // past the tile's and bytes past a row's end zero (so that every K-block of
-      // the padded last K-step reads a finite scale); byte entries i = tid +
-      // kThreads j of the [BM][stride] table, 16 loads in flight per thread
+      // the padded last K-step reads a finite scale), into the [BM][stride] table
       uint8_t* tb = (uint8_t*)plan_dyn + plan_region_bytes(plan_here, p.E, p.npairs, kThreads, BM);
       const int sfr = p.a_sf_row, stride = mx_table_stride(sfr);
       sft = (const LDS3 uint32_t*)tb;
@@ -840,8 +839,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         }
         lds_barrier();
       }
-      // entries of W bytes (the widest the row length's alignment allows: a scale row
-      // starts at a multiple of sf_row bytes), 16 loads in flight per thread
+      // entries i = tid + kThreads j of W bytes each (the widest the row length's
+      // alignment allows: a scale row starts at a multiple of sf_row bytes), 16
+      // loads in flight per thread
       auto fill = [&](auto wbytes) {
         constexpr int W = decltype(wbytes)::value;
         const int per_row = stride / W, n = BM * per_row;
