@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
     i32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
+      o[q] = (int)bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
     *(i32x4*)((uint16_t*)out + (long long)t * H + col) = o;
   }
 }

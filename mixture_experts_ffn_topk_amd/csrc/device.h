@@ -15,12 +15,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 MOE_DEV int lane_id() { return __lane_id(); }
 
 // ---------------------------------------------------------------- conversions
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-MOE_DEV uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 -> two bf16 (a in the low half), round to nearest even; a NaN stays a
+// NaN.  One v_cvt_pk_bf16_f32 (gfx950's conversion) instead of the six or so VALU
+// operations per value of rounding the bits by hand.
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
+MOE_DEV uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_cvt{a, b}, bf16x2_cvt));
 }
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

@@ -195,7 +195,7 @@ MOE_DEV void combine_chunk8(const GemmParams& p, __amdgpu_buffer_rsrc_t y_rs, in
     i32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
+      o[q] = (int)bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
     *(i32x4*)((uint16_t*)p.out + (long long)t * p.N + col) = o;
   }
 }
@@ -1211,8 +1211,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
             float o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = e2m1_rne_sat(v[q][i] * inv) * sb;
-            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+            const uint32_t w0 = bf16x2_rne(o[0], o[1]);
+            const uint32_t w1 = bf16x2_rne(o[2], o[3]);
             *(uint2*)(out_lds + (mt * 32 + r32) * TL::kOutStride + (wave * HW + 16 * t + 8 * q + 4 * h32) * 2) =
                 uint2{w0, w1};
           }
@@ -1227,8 +1227,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = swiglu_clamped<FAST>(acc32[mt][t][4 * q + i], acc32[mt][t][4 * q + i + 8], c);
-            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            const uint32_t w0 = bf16x2_rne(v[0], v[1]);
+            const uint32_t w1 = bf16x2_rne(v[2], v[3]);
             *(uint2*)(out_lds + (mt * 32 + r32) * TL::kOutStride + (wave * HW + 16 * t + 8 * q + 4 * h32) * 2) =
                 uint2{w0, w1};
           }
@@ -1319,8 +1319,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
           for (int q = 0; q < 4; ++q) {  // rows 8q + 4*h32 + (0..3) of the tile
             const f32x16& a = acc32[mt][t];
-            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(a[4 * q]) | ((uint32_t)f32_to_bf16_rne(a[4 * q + 1]) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(a[4 * q + 2]) | ((uint32_t)f32_to_bf16_rne(a[4 * q + 3]) << 16);
+            const uint32_t w0 = bf16x2_rne(a[4 * q], a[4 * q + 1]);
+            const uint32_t w1 = bf16x2_rne(a[4 * q + 2], a[4 * q + 3]);
             *(uint2*)(out_lds + (mt * 32 + r32) * TL::kOutStride + (wave * 16 * NT + 32 * t + 8 * q + 4 * h32) * 2) =
                 uint2{w0, w1};
           }
@@ -1329,8 +1329,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][0]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][1]) << 16);
-          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[mt][nt][2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][3]) << 16);
+          const uint32_t w0 = bf16x2_rne(acc[mt][nt][0], acc[mt][nt][1]);
+          const uint32_t w1 = bf16x2_rne(acc[mt][nt][2], acc[mt][nt][3]);
           *(uint2*)(out_lds + (mt * 16 + r16) * TL::kOutStride + (wave * 16 * NT + 16 * nt + 4 * g) * 2) = uint2{w0, w1};
         }
     }
