@@ -927,7 +927,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // Software-pipelined: the scale update of MFMA i is issued after MFMA i+2
       // (three partials in flight: with two, the update read a partial the matrix
       // core was still writing, and the compiler padded every other MFMA with a
-      // 7-cycle wait; prefill gate_up -3.3 %, down -4.1 %), and the activation
+      // 7-cycle wait; prefill gate_up -3.5 %, down -3 %), and the activation
       // fragment of the next token slice is read one slice ahead, so that the
       // matrix core never waits on the VALU or on LDS within a wave.  Every token
       // slice is computed (slices past the tile's rows multiply zeros).
