@@ -102,8 +102,10 @@ struct Tile {
   // spread over all LDS banks (a padded row stride still halves the read rate).
   // Weight-bound BF16 tiles keep a padded 144-byte row instead: the swizzle's
   // per-sub-step offsets do not fit their register budget.
-  // direct-to-LDS staging (below); NVFP4 activations are decoded on the way to LDS
-  static constexpr bool kDma = F != Fmt::MX && F != Fmt::NVF4 && BM > 96;
+  // direct-to-LDS staging (below); NVFP4 activations are decoded on the way to LDS.
+  // Weight-bound MX tiles take their activation scales from a per-tile table
+  // (kSfTab), so their activations can go direct-to-LDS too (W4A8 gate_up -1.5 %).
+  static constexpr bool kDma = (F != Fmt::MX && F != Fmt::NVF4 && BM > 96) || (F == Fmt::MX && BM <= 96);
   static constexpr int kSwz = bf16_mma(F) && !kDma ? 0 : 7;
   static constexpr int kARowBytes = bf16_mma(F) && !kDma ? 144 : 128;
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
@@ -113,14 +115,14 @@ struct Tile {
   static constexpr int kOutRowBytes = GATEUP ? (BN / 2) * (bf16_mma(F) ? 2 : 1) : BN * 2;
   static constexpr int kOutStride = kOutRowBytes + 16;
   static constexpr int kAStepBytes = kARows * kARowBytes;
-  // MFMA-bound FP8 / BF16 tiles stage A with direct-to-LDS loads, two stages
-  // ahead, into four buffers (at least three: the load two stages ahead cannot
-  // land in the buffer being read; four keep the unrolled K loop a divisor of the
-  // usual K-step counts, so that it runs no padding steps): no staging
-  // registers, which also leaves BF16 room for the swizzled layout.  The others
-  // load A into registers and store it, double-buffered (measured faster for the
-  // weight-bound tiles, whose weight stream then starts before the activation
-  // addresses are known).
+  // MFMA-bound FP8 / BF16 tiles and weight-bound MX tiles stage A with
+  // direct-to-LDS loads, two stages ahead, into four buffers (at least three: the
+  // load two stages ahead cannot land in the buffer being read; four keep the
+  // unrolled K loop a divisor of the usual K-step counts, so that it runs no
+  // padding steps): no staging registers, which also leaves BF16 room for the
+  // swizzled layout.  The others load A into registers and store it,
+  // double-buffered (measured faster for the weight-bound FP8 and BF16 tiles,
+  // whose weight stream then starts before the activation addresses are known).
   static constexpr int kABufs = kDma ? 4 : 2;
   // Weight-bound MX tiles stage their rows' whole UE8M0 scale rows in LDS once per
   // tile (dynamic LDS) instead of four bytes per row and K-step: one cache line per
@@ -786,15 +788,25 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       const uint32_t dead = oob_if(ks >= p.ksteps);
       uint8_t* base = a_lds + (buf * KSG + u) * TL::kAStepBytes;
 #pragma unroll
-      for (int i = 0; i < TL::kAChunks; ++i)
-        lds_load16(a_rs, base + (i * kThreads + wave * 64) * 16, a_off[i] | dead, (uint32_t)ks * 128u);
+      for (int i = 0; i < TL::kAChunks; ++i) {
+        uint32_t o = a_off[i] | dead;
+        if constexpr (F == Fmt::MX) {
+          // K tail (MX rows need only be a multiple of 32 long): the chunk this slot
+          // holds, (c & 7) ^ (r & 7), past the row's end reads zeros
+          const int c = tid + kThreads * i;
+          o |= oob_if(ks * 128 + (((c & 7) ^ ((c >> 3) & 7)) * 16) >= p.K);
+        }
+        lds_load16(a_rs, base + (i * kThreads + wave * 64) * 16, o, (uint32_t)ks * 128u);
+      }
       if constexpr (F == Fmt::FP8)
         lds_load4(asf_rs, sa_lds + (buf * KSG + u) * TL::kSA + wave * 64, (asf_off + 4u * u) | dead,
                   (uint32_t)st * (KSG * 4u));
     }
   };
   // VMEM instructions per stage: the A loads (D) and the weight-ring refills (R)
-  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0)), kR = KSG * (nv4w(F) ? NT : NT * 2);
+  // (MX with dense weight scales: NT weight loads and one scale load per K-step)
+  constexpr int kD = KSG * (TL::kAChunks + (F == Fmt::FP8 ? 1 : 0));
+  constexpr int kR = KSG * (nv4w(F) ? NT : kMxDenseSc ? NT + 1 : NT * 2);
 
   i32x4 av[TL::kDma ? 1 : 2][KSG][TL::kAChunks];
   uint32_t as[TL::kDma ? 1 : 2][kSfN] = {};
@@ -820,73 +832,75 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   } else {
     load_a(av[0], as[0], 0);
     load_a(av[1], as[1], 1);
-    if constexpr (TL::kSfTab) {
-      // the tile's scale rows: sf_row bytes per row (UE8M0 per 32 activations), rows
-      // past the tile's and bytes past a row's end zero (so that every K-block of
-      // the padded last K-step reads a finite scale), into the [BM][stride] table
-      uint8_t* tb = (uint8_t*)plan_dyn + plan_region_bytes(plan_here, p.E, p.npairs, kThreads, BM);
-      const int sfr = p.a_sf_row, stride = mx_table_stride(sfr);
-      sft = (const LDS3 uint32_t*)tb;
-      sft_dw = stride >> 2;
-      int* rtok = (int*)red_lds;  // gate_up: the token of each tile row (the epilogue reuses the space)
-      if (GATEUP) {
-        if ((tid & 7) == 0) {
-#pragma unroll
-          for (int i = 0; i < TL::kAChunks; ++i) {
-            const int r = (tid + kThreads * i) >> 3;
-            if (r < BM) rtok[r] = r < rows ? a_src[i] / p.topk : -1;
-          }
-        }
-        lds_barrier();
-      }
-      // entries i = tid + kThreads j of W bytes each (the widest the row length's
-      // alignment allows: a scale row starts at a multiple of sf_row bytes), 16
-      // loads in flight per thread
-      auto fill = [&](auto wbytes) {
-        constexpr int W = decltype(wbytes)::value;
-        const int per_row = stride / W, n = BM * per_row;
-        const int dr = kThreads / per_row, du = kThreads % per_row;
-        for (int j0 = 0; j0 * kThreads < n; j0 += 16) {
-          uint32_t v[16];
-          int r = (j0 * kThreads + tid) / per_row, u = (j0 * kThreads + tid) % per_row;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int tok = r >= BM ? -1 : GATEUP ? rtok[r] : (r < rows ? row0 + r : -1);
-            const uint32_t off =
-                (tok >= 0 && u * W < sfr) ? (uint32_t)tok * (uint32_t)sfr + (uint32_t)(u * W) : kOOB;
-            if constexpr (W == 4) v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, off, 0, 0);
-            else if constexpr (W == 2) v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(asf_rs, off, 0, 0);
-            else v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, off, 0, 0);
-            u += du;
-            r += dr;
-            if (u >= per_row) {
-              u -= per_row;
-              ++r;
-            }
-          }
-          r = (j0 * kThreads + tid) / per_row;
-          u = (j0 * kThreads + tid) % per_row;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            if (r < BM) {
-              if constexpr (W == 4) *(uint32_t*)(tb + r * stride + u * 4) = v[j];
-              else if constexpr (W == 2) *(uint16_t*)(tb + r * stride + u * 2) = (uint16_t)v[j];
-              else tb[r * stride + u] = (uint8_t)v[j];
-            }
-            u += du;
-            r += dr;
-            if (u >= per_row) {
-              u -= per_row;
-              ++r;
-            }
-          }
-        }
-      };
-      if ((sfr & 3) == 0) fill(std::integral_constant<int, 4>{});
-      else if ((sfr & 1) == 0) fill(std::integral_constant<int, 2>{});
-      else fill(std::integral_constant<int, 1>{});
-    }
     store_a(av[0], as[0], 0);
+  }
+  if constexpr (TL::kSfTab) {
+    // (after the prologue's activation and ring loads: the fill waits for its own
+    // loads, and so for every older one, before the first stage's wait counts apply)
+    // the tile's scale rows: sf_row bytes per row (UE8M0 per 32 activations), rows
+    // past the tile's and bytes past a row's end zero (so that every K-block of
+    // the padded last K-step reads a finite scale), into the [BM][stride] table
+    uint8_t* tb = (uint8_t*)plan_dyn + plan_region_bytes(plan_here, p.E, p.npairs, kThreads, BM);
+    const int sfr = p.a_sf_row, stride = mx_table_stride(sfr);
+    sft = (const LDS3 uint32_t*)tb;
+    sft_dw = stride >> 2;
+    int* rtok = (int*)red_lds;  // gate_up: the token of each tile row (the epilogue reuses the space)
+    if (GATEUP) {
+      if ((tid & 7) == 0) {
+#pragma unroll
+        for (int i = 0; i < TL::kAChunks; ++i) {
+          const int r = (tid + kThreads * i) >> 3;
+          if (r < BM) rtok[r] = r < rows ? a_src[i] / p.topk : -1;
+        }
+      }
+      lds_barrier();
+    }
+    // entries i = tid + kThreads j of W bytes each (the widest the row length's
+    // alignment allows: a scale row starts at a multiple of sf_row bytes), 16
+    // loads in flight per thread
+    auto fill = [&](auto wbytes) {
+      constexpr int W = decltype(wbytes)::value;
+      const int per_row = stride / W, n = BM * per_row;
+      const int dr = kThreads / per_row, du = kThreads % per_row;
+      for (int j0 = 0; j0 * kThreads < n; j0 += 16) {
+        uint32_t v[16];
+        int r = (j0 * kThreads + tid) / per_row, u = (j0 * kThreads + tid) % per_row;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int tok = r >= BM ? -1 : GATEUP ? rtok[r] : (r < rows ? row0 + r : -1);
+          const uint32_t off =
+              (tok >= 0 && u * W < sfr) ? (uint32_t)tok * (uint32_t)sfr + (uint32_t)(u * W) : kOOB;
+          if constexpr (W == 4) v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, off, 0, 0);
+          else if constexpr (W == 2) v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(asf_rs, off, 0, 0);
+          else v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asf_rs, off, 0, 0);
+          u += du;
+          r += dr;
+          if (u >= per_row) {
+            u -= per_row;
+            ++r;
+          }
+        }
+        r = (j0 * kThreads + tid) / per_row;
+        u = (j0 * kThreads + tid) % per_row;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (r < BM) {
+            if constexpr (W == 4) *(uint32_t*)(tb + r * stride + u * 4) = v[j];
+            else if constexpr (W == 2) *(uint16_t*)(tb + r * stride + u * 2) = (uint16_t)v[j];
+            else tb[r * stride + u] = (uint8_t)v[j];
+          }
+          u += du;
+          r += dr;
+          if (u >= per_row) {
+            u -= per_row;
+            ++r;
+          }
+        }
+      }
+    };
+    if ((sfr & 3) == 0) fill(std::integral_constant<int, 4>{});
+    else if ((sfr & 1) == 0) fill(std::integral_constant<int, 2>{});
+    else fill(std::integral_constant<int, 1>{});
   }
   if (F == Fmt::FP8) {
 #pragma unroll
