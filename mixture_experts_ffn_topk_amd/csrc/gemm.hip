@@ -98,7 +98,7 @@ struct Tile {
   static constexpr int BN = WAVES * 16 * NT;  // weight rows per workgroup tile
   static constexpr int MT = BM / 16;
   // A is staged per K-step as kARows rows of 128 bytes, the 16-byte chunk c of
-  // row r stored at chunk c ^ (r & 7), so that the rows of an MFMA fragment read
+  // row r stored at chunk c ^ swz(r) (r & 7, below), so that the rows of an MFMA fragment read
   // spread over all LDS banks (a padded row stride still halves the read rate).
   // Weight-bound BF16 tiles keep a padded 144-byte row instead: the swizzle's
   // per-sub-step offsets do not fit their register budget.
@@ -107,6 +107,14 @@ struct Tile {
   // (kSfTab), so their activations can go direct-to-LDS too (W4A8 gate_up -1.5 %).
   static constexpr bool kDma = (F != Fmt::MX && F != Fmt::NVF4 && BM > 96) || (F == Fmt::MX && BM <= 96);
   static constexpr int kSwz = bf16_mma(F) && !kDma ? 0 : 7;
+  // By the bank-conflict counter, the LDS serves a 128-bit read to lanes 0-7 and
+  // 16-23 (8-15 and 24-31, ...) together.  A 32x32 BF16 fragment puts rows r and
+  // r + 16 in lanes r and r + 16, and rows 16 x 128 bytes apart share banks, so the
+  // swizzle of those tiles also flips chunk bit 0 with row bit 4 (Mixtral gate_up:
+  // 125 M conflict cycles per launch to 2 M, -0.5 % time; 16x16 FP8 / MX
+  // fragments put one row in lanes r and r + 16, which the XOR already spreads).
+  static constexpr bool kSwz16 = bf16_mma(F) && kDma;
+  MOE_HOST_DEV static constexpr int swz(int r) { return (r & kSwz) ^ (kSwz16 ? (r >> 4) & 1 : 0); }
   static constexpr int kARowBytes = bf16_mma(F) && !kDma ? 144 : 128;
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread and K-step
   // A buffer rows: BM rounded up so that every thread stores every chunk it loads
@@ -664,8 +672,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     const int c = tid + kThreads * i;
     const int r = c >> 3;
     const uint32_t arow = GATEUP ? (uint32_t)(a_src[i] / p.topk) : (uint32_t)(row0 + r);
-    // direct-to-LDS: slot c of the K-step block holds row r's chunk (c & 7) ^ (r & 7)
-    const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ (r & 7)) : (uint32_t)(c & 7);
+    // direct-to-LDS: slot c of the K-step block holds row r's chunk (c & 7) ^ swz(r)
+    const uint32_t chunk = TL::kDma ? (uint32_t)((c & 7) ^ TL::swz(r)) : (uint32_t)(c & 7);
     // NVF4: a chunk of 8 activations is 4 packed bytes
     a_off[i] = r < rows ? arow * p.a_row_bytes + chunk * (F == Fmt::NVF4 ? 4u : 16u) : kOOB;
     // NVF4: the E4M3 scale of the chunk's 16-element block (elements 64 ks + 8 (c & 7) ..)
@@ -792,9 +800,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         uint32_t o = a_off[i] | dead;
         if constexpr (F == Fmt::MX) {
           // K tail (MX rows need only be a multiple of 32 long): the chunk this slot
-          // holds, (c & 7) ^ (r & 7), past the row's end reads zeros
+          // holds, (c & 7) ^ swz(r), past the row's end reads zeros
           const int c = tid + kThreads * i;
-          o |= oob_if(ks * 128 + (((c & 7) ^ ((c >> 3) & 7)) * 16) >= p.K);
+          o |= oob_if(ks * 128 + (((c & 7) ^ TL::swz(c >> 3)) * 16) >= p.K);
         }
         lds_load16(a_rs, base + (i * kThreads + wave * 64) * 16, o, (uint32_t)ks * 128u);
       }
@@ -990,7 +998,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // decoded from word sub of bq_.lo[t] with block scale byte sub of bq_.sc[t] (NV4)
       const int r32 = lane & 31, h32 = lane >> 5;
       auto rd_a = [&](int mt, int sub) {
-        return *(const i32x4*)(abuf + (mt * 32 + r32) * TL::kARowBytes + 16 * ((2 * sub + h32) ^ (r32 & TL::kSwz)));
+        return *(const i32x4*)(abuf + (mt * 32 + r32) * TL::kARowBytes + 16 * ((2 * sub + h32) ^ TL::swz(r32)));
       };
       if constexpr (nv4w(F)) {
         // Sub-step outer: the weights of sub-step sub + 1 are decoded (VALU) while
