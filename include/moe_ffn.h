@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 10
+#define MOE_FFN_ABI_VERSION 11
 
 typedef enum {
   MOE_OK = 0,
@@ -159,6 +159,10 @@ typedef struct moe_plan_buffers {
   int32_t* combine_counters;      /* [T * ceil(H/128)] or NULL: arrival counters of the fused
                                      combine ([MegaFFN] arrival_count), zeroed by moe_plan;
                                      needed by moe_ffn_down_combine only */
+  void* down_split;               /* moe_down_split_size bytes, 256-byte aligned, or NULL: the
+                                     down leg's split tail (below); its arrival counters are
+                                     zeroed by moe_plan / moe_plan_ffn_gate_up of the same
+                                     plan and left zero by the down leg */
 } moe_plan_buffers;
 
 typedef struct moe_handle moe_handle;
@@ -221,6 +225,18 @@ moe_status moe_prepare_weights(const moe_handle* h, const moe_weights* canonical
    is caller-owned device memory, 256-byte aligned (a misaligned workspace is
    MOE_ERR_INVALID_ARGUMENT); one workspace per concurrently running stream. */
 size_t moe_workspace_size(const moe_handle* h, int32_t num_tokens);
+
+/* Bytes of plan->down_split for this handle (0: its down leg never splits, and
+   the field may stay NULL).  Split tail of the down leg: when the prefill-regime
+   down tiles (see moe_tile_regime) leave a last partial round of at most half
+   the workgroups the part runs at once, each of those tiles is cut over K into
+   up to 8 pieces that run side by side; each piece stores an fp32 partial tile
+   there and the last to arrive ([MegaFFN] arrival_count: cross-workgroup arrival
+   counts) sums them in piece order and writes the tile.  The result is
+   deterministic; it differs from the unsplit sum only in fp32 summation order.
+   With down_split NULL nothing splits.  Calls that share a plan's down_split must
+   not overlap. */
+size_t moe_down_split_size(const moe_handle* h);
 
 /* Routing plan ([MegaFFN] expert_start_indices, expert_ids, num_active_experts,
    src_info; [ActPack] routing modes).

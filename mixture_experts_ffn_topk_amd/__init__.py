@@ -51,7 +51,7 @@ class _Weights(ctypes.Structure):
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("expert_counts", "expert_start_indices", "expert_ids",
                                                "num_active_experts", "src_info", "pair_row", "status",
-                                               "combine_counters")]
+                                               "combine_counters", "down_split")]
 
 
 class _PreparedSizes(ctypes.Structure):
@@ -59,7 +59,7 @@ class _PreparedSizes(ctypes.Structure):
 
 
 PLAN_FIELDS = [f for f, _ in _Plan._fields_]
-EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_plan_in_gate_up", "moe_prepared_weights_size", "moe_prepare_weights",
+EXPORTED = ["moe_create", "moe_destroy", "moe_workspace_size", "moe_down_split_size", "moe_plan_in_gate_up", "moe_prepared_weights_size", "moe_prepare_weights",
             "moe_plan", "moe_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_forward",
             "moe_plan_ex", "moe_combine_ex", "moe_forward_ex", "moe_ffn_gate_up_timed", "moe_ffn_down_timed",
             "moe_ffn_down_combine", "moe_ffn_down_combine_timed", "moe_plan_ffn_gate_up", "moe_plan_ffn_gate_up_timed",
@@ -84,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_destroy.restype = None
     lib.moe_workspace_size.argtypes = [vp, i32]
     lib.moe_workspace_size.restype = sz
+    lib.moe_down_split_size.argtypes = [vp]
+    lib.moe_down_split_size.restype = sz
     lib.moe_plan_in_gate_up.argtypes = [vp, i32]
     lib.moe_plan_in_gate_up.restype = i32
     lib.moe_prepared_weights_size.argtypes = [vp, ctypes.POINTER(_PreparedSizes)]
@@ -263,9 +265,11 @@ class MoEFFN:
         import torch
         E, n = self.experts, T * self.topk
         sizes = {"expert_counts": E, "expert_start_indices": E + 1, "expert_ids": E, "num_active_experts": 1,
-                 "src_info": n, "pair_row": n, "status": 1, "combine_counters": T * self._cnt_stride()}
+                 "src_info": n, "pair_row": n, "status": 1, "combine_counters": T * self._cnt_stride(),
+                 "down_split": self.down_split_size() // 4}
         for f in PLAN_FIELDS:
-            _need(plan.get(f), f"plan['{f}']", 4 * sizes[f], (torch.int32,), required=f != "combine_counters")
+            _need(plan.get(f), f"plan['{f}']", 4 * sizes[f], (torch.int32,),
+                  required=f not in ("combine_counters", "down_split"))
 
     def _check_x(self, x, x_sf, T: int):
         _need(x, "x", T * self._x_bytes(self.hidden))
@@ -292,6 +296,10 @@ class MoEFFN:
     # ---------------------------------------------------------------- helpers (torch allocation)
     def workspace_size(self, num_tokens: int) -> int:
         return int(self.lib.moe_workspace_size(self._h, num_tokens))
+
+    def down_split_size(self) -> int:
+        """Bytes of plan['down_split'] (the down leg's split tail; 0: it never splits)."""
+        return int(self.lib.moe_down_split_size(self._h))
 
     def plan_in_gate_up(self, num_tokens: int) -> bool:
         """Whether plan_ffn_gate_up (and forward with fuse_plan) builds the routing
@@ -330,7 +338,11 @@ class MoEFFN:
         sizes = {"expert_counts": E, "expert_start_indices": E + 1, "expert_ids": E, "num_active_experts": 1,
                  "src_info": np_, "pair_row": np_, "status": 1,
                  "combine_counters": max(1, num_tokens) * self._cnt_stride()}
-        return {k: torch.empty(v, dtype=torch.int32, device=device) for k, v in sizes.items()}
+        plan = {k: torch.empty(v, dtype=torch.int32, device=device) for k, v in sizes.items()}
+        # the down leg's split tail (its counters start at zero; moe_plan zeroes them too)
+        if self.down_split_size() > 0:
+            plan["down_split"] = torch.zeros(self.down_split_size() // 4, dtype=torch.int32, device=device)
+        return plan
 
     def _cnt_stride(self) -> int:
         """Fused-combine arrival counters per token: ceil(H / 128)."""

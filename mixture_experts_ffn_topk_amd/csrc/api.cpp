@@ -19,8 +19,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  // moe_forward: [plan buffers][y][union(plan scratch, h + h_sf)]
-  size_t counts, start, ids, nact, status, src, prow, cnt, plan_end;
+  // moe_forward: [plan buffers, split tail][y][union(plan scratch, h + h_sf)]
+  size_t counts, start, ids, nact, status, src, prow, cnt, split, plan_end;
   size_t y, y_end;
   size_t scratch;  // plan scratch or h, h_sf
   size_t h_off, hsf_off, ffn_bytes, plan_scratch_bytes, total;
@@ -42,6 +42,8 @@ bool bf16_acts(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_NVFP4_W4A16; }
 // bf16 intermediate, no intermediate scales
 bool bf16_inter(int f) { return bf16_acts(f) || f == MOE_FMT_NVFP4; }
 
+int choose_bm(const moe_config& c, int T);
+
 Layout layout_for(const moe_config& c, int T) {
   Layout L{};
   const size_t E = (size_t)c.num_experts, np = (size_t)T * c.num_topk;
@@ -54,6 +56,8 @@ Layout layout_for(const moe_config& c, int T) {
   L.src = o; o = align_up(o + np * 4);
   L.prow = o; o = align_up(o + np * 4);
   L.cnt = o; o = align_up(o + (size_t)T * moe::combine_counter_stride(c.hidden) * 4);
+  // the down leg's split tail, where T tokens take the prefill tile regime
+  L.split = o; o = align_up(o + (choose_bm(c, T) > 96 ? moe::ffn_split_bytes(to_fmt(c.format)) : 0));
   L.plan_end = o;
   L.y = o; o = align_up(o + np * (size_t)c.hidden * 2);
   L.y_end = o;
@@ -70,14 +74,23 @@ Layout layout_for(const moe_config& c, int T) {
 bool valid_T(const moe_handle* h, int32_t T) { return h && T >= 0 && T <= h->cfg.max_num_tokens; }
 
 moe::PlanPtrs plan_ptrs(const moe_plan_buffers* p, int T, int H) {
-  return moe::PlanPtrs{p->expert_counts, p->expert_start_indices, p->expert_ids, p->num_active_experts,
-                       p->src_info,      p->pair_row,             p->status,     p->combine_counters,
-                       p->combine_counters ? T * moe::combine_counter_stride(H) : 0};
+  return moe::PlanPtrs{p->expert_counts,
+                       p->expert_start_indices,
+                       p->expert_ids,
+                       p->num_active_experts,
+                       p->src_info,
+                       p->pair_row,
+                       p->status,
+                       p->combine_counters,
+                       p->combine_counters ? T * moe::combine_counter_stride(H) : 0,
+                       (int*)p->down_split,
+                       p->down_split ? moe::kSplitMaxSlots : 0};
 }
 
+// (down_split is optional, 256-byte aligned)
 bool plan_complete(const moe_plan_buffers* p) {
   return p && p->expert_counts && p->expert_start_indices && p->expert_ids && p->num_active_experts && p->src_info &&
-         p->pair_row && p->status;
+         p->pair_row && p->status && ((uintptr_t)p->down_split & 255) == 0;
 }
 
 int choose_bm(const moe_config& c, int T) {
@@ -88,6 +101,13 @@ int choose_bm(const moe_config& c, int T) {
   // uniform load, and the weight stream dominates.
   const long long mean = ((long long)T * c.num_topk + c.num_experts - 1) / c.num_experts;
   return mean <= 64 ? 80 : 128;
+}
+
+// The down leg splits only in the prefill tile regime (some token count up to
+// the capacity reaches it).
+size_t down_split_bytes(const moe_config& c) {
+  if (choose_bm(c, c.max_num_tokens) <= 96) return 0;
+  return moe::ffn_split_bytes(to_fmt(c.format));
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -165,6 +185,7 @@ moe_status do_ffn(const moe_handle* h, int32_t T, const void* x, const void* x_s
   a.h = hbuf;
   a.h_sf = hsf;
   a.y = y;
+  a.split = plan->down_split;
   if (stage == 1) a.ev[0] = e0, a.ev[1] = e1;
   if (stage == 2) a.ev[2] = e0, a.ev[3] = e1;
   if (fused) {
@@ -317,6 +338,8 @@ size_t moe_workspace_size(const moe_handle* h, int32_t T) {
   if (!valid_T(h, T)) return 0;
   return layout_for(h->cfg, T).total;
 }
+
+size_t moe_down_split_size(const moe_handle* h) { return h ? down_split_bytes(h->cfg) : 0; }
 
 int32_t moe_plan_in_gate_up(const moe_handle* h, int32_t T) {
   if (!valid_T(h, T)) return 0;
@@ -487,7 +510,8 @@ moe_status moe_forward_ex(const moe_handle* h, int32_t T, const void* x, const v
   moe_plan_buffers plan{(int32_t*)(base + L.counts), (int32_t*)(base + L.start), (int32_t*)(base + L.ids),
                         (int32_t*)(base + L.nact),   (int32_t*)(base + L.src),   (int32_t*)(base + L.prow),
                         (int32_t*)(base + L.status),
-                        c.fuse_combine ? (int32_t*)(base + L.cnt) : nullptr};
+                        c.fuse_combine ? (int32_t*)(base + L.cnt) : nullptr,
+                        L.split < L.plan_end ? (void*)(base + L.split) : nullptr};
   // fuse_plan: the gate_up launch builds the plan (the top-k from logits keeps its launch)
   const void* in_launch = nullptr;
   moe_status st;

@@ -106,6 +106,9 @@ struct Tile {
   // Weight-bound MX tiles take their activation scales from a per-tile table
   // (kSfTab), so their activations can go direct-to-LDS too (W4A8 gate_up -1.5 %).
   static constexpr bool kDma = (F != Fmt::MX && F != Fmt::NVF4 && BM > 96) || (F == Fmt::MX && BM <= 96);
+  // MFMA-bound FP8 and BF16 down tiles may split a last partial round over K (the
+  // split tail; NVFP4 x BF16's would spill registers)
+  static constexpr bool kSplit = !GATEUP && BM > 96 && kDma && (F == Fmt::FP8 || F == Fmt::BF16);
   static constexpr int kSwz = bf16_mma(F) && !kDma ? 0 : 7;
   // By the bank-conflict counter, the LDS serves a 128-bit read to lanes 0-7 and
   // 16-23 (8-15 and 24-31, ...) together.  A 32x32 BF16 fragment puts rows r and
@@ -259,7 +262,7 @@ MOE_DEV PlanLds plan_lds_carve(int* base, int E, int npairs, int threads, int bm
 
 // Counts and exclusive offsets of every expert into LDS; workgroup 0 also writes
 // the plan's counts, offsets, active list (ascending, then -1), status, the pair
-// rows of masked slots (-1) and zeroes the fused combine's counters.
+// rows of masked slots (-1) and zeroes the fused combine's and the split tail's counters.
 template <int kThreads>
 MOE_DEV void plan_counts_in_lds(const GemmParams& p, const PlanLds& L) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, E = p.E, np = p.npairs;
@@ -319,6 +322,8 @@ MOE_DEV void plan_counts_in_lds(const GemmParams& p, const PlanLds& L) {
       if (L.ex[q] < 0) p.plan_out.pair_row[q] = -1;
     if (p.plan_out.counters != nullptr)
       for (int i = tid; i < p.plan_out.n_counters; i += kThreads) p.plan_out.counters[i] = 0;
+    if (p.plan_out.split_counters != nullptr)
+      for (int i = tid; i < p.plan_out.n_split; i += kThreads) p.plan_out.split_counters[i] = 0;
   }
   __syncthreads();
 }
@@ -441,8 +446,40 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   }
   total_m = __builtin_amdgcn_readfirstlane(total_m);
   const int G = total_m * p.n_tiles;
-  if ((int)blockIdx.x >= G) return;
-  const int L = xcd_remap(blockIdx.x, G);
+  // Split tail (MFMA-bound down tiles, split buffers given): when the tiles leave
+  // a last partial round of at most half the slots (the workgroups the part runs
+  // at once), each of those tail tiles is cut over K into S pieces of whole
+  // K-loop trips, which run side by side after the whole tiles; each piece stores
+  // its fp32 partial tile, and the last to arrive sums the partials in piece
+  // order (the same result whichever arrives last) and runs the epilogue.
+  constexpr bool kSplit = TL::kSplit;
+  constexpr int U = lcm_c(TL::kABufs * KSG, DEPTH);  // K-steps per trip of the unrolled K loop
+  int tail = 0, nparts = 1, piece = -1, tail_j = 0;
+  if constexpr (kSplit) {
+    if (p.split_slots > 0) {
+      const int rem = G % p.split_slots;
+      const int S = rem > 0 ? min(min(p.split_slots / rem, kSplitMaxPieces), (p.ksteps + U - 1) / U) : 1;
+      if (S >= 2) tail = rem, nparts = S;
+    }
+  }
+  const int Gw = G - tail;  // whole tiles
+  int L;
+  if ((int)blockIdx.x < Gw) {
+    L = xcd_remap(blockIdx.x, Gw);
+  } else {
+    const int q = (int)blockIdx.x - Gw;
+    if (q >= tail * nparts) return;
+    tail_j = q / nparts;
+    piece = q - tail_j * nparts;
+    L = Gw + tail_j;
+  }
+  // this workgroup's K-steps [k0, k0 + KS)
+  int k0 = 0, KS = p.ksteps;
+  if (piece >= 0) {
+    const int nu = (p.ksteps + U - 1) / U;
+    k0 = piece * nu / nparts * U;
+    KS = min(p.ksteps, (piece + 1) * nu / nparts * U) - k0;
+  }
   // Weight-bound tiles (about one m-tile per expert: no weight reuse between
   // m-tiles) run expert-major, so that an expert's activation rows stay in the
   // XCD's L2 across its column tiles.  MFMA-bound tiles run column-tile-major, so
@@ -491,7 +528,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // K-step, row block major then K-step, each tile contiguous in MFMA lane order
   // (lane l's 16 bytes at 16*l, FP8/BF16 second halves 1 KB further), so one
   // load instruction of a wave reads 1 KB of consecutive bytes.
-  const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + (size_t)expert * p.b_expert_bytes, p.b_expert_bytes);
+  // (a split piece's resources start at its first K-step: tile ks of a row block
+  // lies ks tiles past the block's first)
+  const __amdgpu_buffer_rsrc_t b_rs =
+      make_rsrc(p.B + (size_t)expert * p.b_expert_bytes + (size_t)k0 * p.b_tile, p.b_expert_bytes - (uint32_t)k0 * p.b_tile);
   // FP8 weight scales of the tile, per thread (kNB rows of at most kMaxKSteps)
   constexpr int kSbPer = F == Fmt::FP8 ? (TL::kNB * TL::kMaxKSteps + kThreads - 1) / kThreads : 1;
   float sb_pre[kSbPer];
@@ -504,7 +544,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   uint32_t bsc_dense = kOOB;
   {
     if (F == Fmt::MX || nv4w(F))
-      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);
+      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);  // (no split)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       int wrow0, col0;  // first weight row and first output column of the 16-row tile
@@ -536,14 +576,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
       // tile's first (blocks past the last stand in for dead columns).  Loaded
       // here, stored to LDS after the prologue's weight and activation loads are
       // issued, so that their round trip overlaps those loads.
-      const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row;
+      const float* sfe = (const float*)p.B_sf + (size_t)expert * (p.n_rows / 128) * p.b_sf_row + k0;
       const int nblk = p.n_rows / 128;
 #pragma unroll
       for (int q = 0; q < kSbPer; ++q) {
         const int i = tid + q * kThreads;
         sb_pre[q] = 0.f;
-        if (i < TL::kNB * p.ksteps) {
-          const int j = i / p.ksteps, k = i - j * p.ksteps;
+        if (i < TL::kNB * KS) {
+          const int j = i / KS, k = i - j * KS;
           const int hb = TL::kHB, hblk = p.N / 128;
           const int blk = GATEUP ? (j < hb ? min(n_tile * hb + j, hblk - 1) : hblk + min(n_tile * hb + j - hb, hblk - 1))
                                  : min(n_tile * BN / 128 + j, nblk - 1);
@@ -566,7 +606,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     return BM <= 96 ? bload16_nt(b_rs, voff, soff) : bload16(b_rs, voff, soff);
   };
   auto load_b = [&](BFrag<F, NT>& b, int ks) {
-    const uint32_t dead = oob_if(ks >= p.ksteps);  // (the prepared layout is zero past a row's end)
+    const uint32_t dead = oob_if(ks >= KS);  // (the prepared layout is zero past a row's end)
     if constexpr (F == Fmt::BF16) {
       // 32-row tile t: four 1 KB sub-step pieces
 #pragma unroll
@@ -611,7 +651,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // past the tile's read its last entry and are then masked), before the weight
   // ring is issued, and used after it: their round trip then overlaps the
   // weights' instead of preceding it.
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(p.A + (size_t)k0 * 128u, p.a_bytes - (uint32_t)k0 * 128u);
   int a_src[TL::kAChunks];
   auto gather_a_src = [&]() {
 #pragma unroll
@@ -643,7 +683,6 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // weight ring: DEPTH K-steps per wave, DEPTH-1 of them in flight while one is consumed.
   // Issued first, before the activation rows' addresses are known (direct-to-LDS
   // tiles: the first stage's K-steps here, the rest after the first activation stage).
-  const int KS = p.ksteps;
   BFrag<F, NT> bq[DEPTH];
 #pragma unroll
   for (int d = 0; d < (TL::kDma ? KSG : DEPTH); ++d) load_b(bq[d], d);
@@ -680,7 +719,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     if constexpr (F == Fmt::NVF4) a_sfo[i] = r < rows ? arow * (uint32_t)p.a_sf_row + ((c & 7) >> 1) : kOOB;
   }
   // FP8: the fp32 A scale of row tid per K-step; threads past the tile's rows load zeros
-  const __amdgpu_buffer_rsrc_t asf_rs = make_rsrc(p.A_sf, p.a_sf_bytes);
+  const __amdgpu_buffer_rsrc_t asf_rs = F == Fmt::FP8 ? make_rsrc((const uint8_t*)p.A_sf + (size_t)k0 * 4u, p.a_sf_bytes - (uint32_t)k0 * 4u)
+                                                       : make_rsrc(p.A_sf, p.a_sf_bytes);
   const uint32_t asf_off =
       (F == Fmt::FP8 && tid < rows)
           ? (GATEUP ? (uint32_t)(asf_src / p.topk) : (uint32_t)(row0 + tid)) * (uint32_t)p.a_sf_row * (F == Fmt::FP8 ? 4u : 1u)
@@ -719,7 +759,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
       const int ks = st * KSG + u;
-      const uint32_t dead = oob_if(ks >= p.ksteps);
+      const uint32_t dead = oob_if(ks >= KS);
 #pragma unroll
       for (int i = 0; i < TL::kAChunks; ++i) {
         uint32_t o = a_off[i] | dead;
@@ -737,7 +777,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
       for (int u = 0; u < KSG; ++u) {
         const int ks = st * KSG + u;
-        s[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, (asf_off + 4u * u) | oob_if(ks >= p.ksteps),
+        s[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(asf_rs, (asf_off + 4u * u) | oob_if(ks >= KS),
                                                               (uint32_t)st * (KSG * 4u), 0);
       }
     } else if constexpr (F == Fmt::MX && !TL::kSfTab) {
@@ -793,7 +833,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
       const int ks = st * KSG + u;
-      const uint32_t dead = oob_if(ks >= p.ksteps);
+      const uint32_t dead = oob_if(ks >= KS);
       uint8_t* base = a_lds + (buf * KSG + u) * TL::kAStepBytes;
 #pragma unroll
       for (int i = 0; i < TL::kAChunks; ++i) {
@@ -914,9 +954,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
 #pragma unroll
     for (int q = 0; q < kSbPer; ++q) {
       const int i = tid + q * kThreads;
-      if (i < TL::kNB * p.ksteps) {
-        const int j = i / p.ksteps;
-        sb_lds[j * TL::kMaxKSteps + (i - j * p.ksteps)] = sb_pre[q];
+      if (i < TL::kNB * KS) {
+        const int j = i / KS;
+        sb_lds[j * TL::kMaxKSteps + (i - j * KS)] = sb_pre[q];
       }
     }
   }
@@ -1171,7 +1211,6 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   // up to the unroll: the extra steps load zeros and add zeros, and the loop has
   // no early exit (an exit per step would make the compiler drain every
   // outstanding load there).
-  constexpr int U = lcm_c(TL::kABufs * KSG, DEPTH);
   constexpr int SU = U / KSG;
   const int KS_PAD = (KS + U - 1) / U * U;
   if constexpr (TL::kDma) {
@@ -1188,6 +1227,74 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     }
   }
   __syncthreads();  // every wave is done with the A buffers; the output tile reuses them
+
+  // ---------------------------------------------------------------- split tail
+  if constexpr (kSplit) {
+    if (piece >= 0) {
+      // Partial tile of piece s of tail tile j in slot j * nparts + s, lane-major
+      // (f32x4 v of thread tid at (v * threads + tid) * 16 bytes), stored at device
+      // scope; once every thread's stores have completed, the workgroup arrives at
+      // the tile's counter.  The piece that completes the count (it resets the
+      // counter for the next launch) reads every partial at device scope and sums
+      // them in piece order; the others are done.  No waiting, no data atomics.
+      constexpr int kV = bf16_mma(F) ? MT32 * NT32 * 4 : MT * NT;  // f32x4 per lane
+      const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.split_part, (uint32_t)p.split_slots * kV * kThreads * 16u);
+      auto off = [&](int slot, int v) { return (uint32_t)(((slot * kV + v) * kThreads + tid) * 16); };
+      auto get = [&](int v) -> f32x4 {
+        if constexpr (bf16_mma(F)) {
+          const f32x16& a = acc32[v / (NT32 * 4)][(v / 4) % NT32];
+          const int q = v % 4;
+          return f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        } else {
+          return acc[v / NT][v % NT];
+        }
+      };
+      auto put = [&](int v, f32x4 x) {
+        if constexpr (bf16_mma(F)) {
+          f32x16& a = acc32[v / (NT32 * 4)][(v / 4) % NT32];
+          const int q = v % 4;
+          a[4 * q] = x[0], a[4 * q + 1] = x[1], a[4 * q + 2] = x[2], a[4 * q + 3] = x[3];
+        } else {
+          acc[v / NT][v % NT] = x;
+        }
+      };
+      const int slot0 = tail_j * nparts;
+#pragma unroll
+      for (int v = 0; v < kV; ++v)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, get(v)), ws, off(slot0 + piece, v), 0,
+                                               kCpolDevice | kCpolNt);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      int* last_lds = (int*)red_lds;
+      if (tid == 0) {
+        const bool last = atomicAdd(p.split_cnt + tail_j, 1) == nparts - 1;
+        if (last) atomicExch(p.split_cnt + tail_j, 0);
+        *last_lds = last;
+      }
+      __syncthreads();
+      const bool last = *last_lds != 0;
+      __syncthreads();  // every wave has read the flag before the epilogue reuses the space
+      if (!last) return;  // (uniform)
+#pragma unroll
+      for (int v = 0; v < kV; ++v) put(v, f32x4{0.f, 0.f, 0.f, 0.f});
+      // kB loads in flight before the first add (one at a time, each would wait
+      // out a full memory round trip)
+      constexpr int kB = 16;
+      static_assert(kV % kB == 0, "whole load batches");
+      for (int sp = 0; sp < nparts; ++sp) {
+#pragma unroll
+        for (int v0 = 0; v0 < kV; v0 += kB) {
+          f32x4 t[kB];
+#pragma unroll
+          for (int i = 0; i < kB; ++i)
+            t[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, off(slot0 + sp, v0 + i), 0,
+                                                                                   kCpolDevice));
+#pragma unroll
+          for (int i = 0; i < kB; ++i) put(v0 + i, get(v0 + i) + t[i]);
+        }
+      }
+    }
+  }
 
   // ---------------------------------------------------------------- epilogue
   // Lane (r16, g) holds, for token slice mt, token row mt*16 + r16 and the wave's
@@ -1430,19 +1537,46 @@ int ffn_max_m_tiles(int npairs, int E, int bm) {
   return (int)(((long long)npairs + act * (bm - 1)) / bm);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Split tail buffer: the counters, then one partial tile per slot (the
+// MFMA-bound down tiles: 512 threads x 128 fp32 accumulators each).
+constexpr size_t kSplitSlotBytes = (size_t)512 * 128 * 4;
+size_t ffn_split_bytes(Fmt f) {
+  if (f != Fmt::FP8 && f != Fmt::BF16) return 0;
+  return ffn_split_counter_bytes() + (size_t)kSplitMaxSlots * kSplitSlotBytes;
+}
+
 template <Fmt F, bool GATEUP, int BM, int WAVES, int NT, int DEPTH, int KSG, int WGS>
 // With timing events the launch carries them in its own dispatch, so they hold the
 // kernel's start and end, not those of separate marker commands in the stream.
 static void launch_one(const GemmParams& gp_in, bool fast, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   GemmParams gp = gp_in;
-  gp.m_grid = gp.m_tiles_max * gp.n_tiles;
+  using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
+  // split tail: the workgroups the part runs at once, and room in the grid for the
+  // pieces past the whole tiles (at most one per slot)
+  // (a partial tile: BM x NT / 16 fp32 x 4 per thread)
+  static_assert(!TL::kSplit || (size_t)64 * WAVES * BM * NT <= kSplitSlotBytes, "a partial tile fits its slot");
+  const int slots = device_cus() * WGS;
+  gp.split_slots = (TL::kSplit && gp.split_part != nullptr) ? (slots < kSplitMaxSlots ? slots : kSplitMaxSlots) : 0;
+  gp.m_grid = gp.m_tiles_max * gp.n_tiles + gp.split_slots;
   int grid = gp.m_grid;
   // fused combine: workgroups for the tokens without a valid slot
   if (!GATEUP && gp.fuse) grid += (gp.T + kZeroSlotTokens - 1) / kZeroSlotTokens;
   if (grid <= 0) return;
   // dynamic LDS: the in-launch routing plan (weight-bound gate_up only), then the
   // weight-bound MX tiles' scale table
-  using TL = Tile<F, GATEUP, BM, WAVES, NT, KSG>;
   const size_t dyn = plan_region_bytes(GATEUP && BM <= 96 && gp.plan_ids != nullptr, gp.E, gp.npairs, 64 * WAVES, BM) +
                      (TL::kSfTab ? (size_t)BM * mx_table_stride(gp.a_sf_row) : 0);
   if (fast)
@@ -1586,6 +1720,11 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, int stage) {
   g2.c_row_bytes = (long long)a.H * 2;
   g2.C_sf = nullptr;
   g2.c_sf_row = 0;
+  // the split tail's buffers (used where the down tiles can split; ffn_split_bytes)
+  if (a.split != nullptr && ffn_split_bytes(a.fmt) > 0) {
+    g2.split_cnt = (int*)a.split;
+    g2.split_part = (float*)((uint8_t*)a.split + ffn_split_counter_bytes());
+  }
   if (a.fuse_combine) {
     g2.fuse = 1;
     g2.T = a.T;

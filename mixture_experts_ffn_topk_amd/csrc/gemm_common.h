@@ -9,6 +9,7 @@ namespace moe {
 
 #define LDS3 __attribute__((address_space(3)))  // LDS pointers of the direct-to-LDS loads
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that reads zeros
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // kOOB if dead, else 0: OR-ed into a lane offset below 2^31 it turns the load
 // into one that reads zeros, without a branch or a select (a uniform condition
@@ -71,6 +72,10 @@ struct GemmParams {
   int out_f32;
   int m_grid;             // GEMM workgroups of the grid; those past it write the tokens without a valid slot
   uint32_t y_bytes;       // size of y (fused combine: y is addressed through a buffer resource)
+  // down leg, MFMA-bound tiles: the split tail's buffers (split_slots 0: no split)
+  int* split_cnt;      // [split_slots] arrival counters, zero on entry, left zero
+  float* split_part;   // [split_slots] fp32 partial tiles
+  int split_slots;     // workgroups the part runs at once (at most kSplitMaxSlots)
   // gate_up leg that builds the routing plan itself (plan_ids != nullptr): every
   // workgroup histograms the ids into LDS and gathers its own rows; workgroup 0
   // writes the counts, offsets, active list and status, the workgroups of column

@@ -22,6 +22,8 @@ struct PlanPtrs {
   int* status;
   int* counters;   // fused-combine arrival counters to zero, or nullptr
   int n_counters;
+  int* split_counters;  // the down leg's split-tail arrival counters to zero, or nullptr
+  int n_split;
 };
 
 // Routing plan: one fused block up to this many pairs, else count/scan/scatter
@@ -76,6 +78,9 @@ struct FfnArgs {
   const int* pair_row;
   const float* topk_w;
   int* counters;  // [T, combine_counter_stride(H)] zeroed by the plan
+  // the down leg's split tail (MFMA-bound tiles): ffn_split_bytes(fmt) bytes, its
+  // counters zeroed by the plan; nullptr: no split
+  void* split;
   void* out;
   const void* shared;
   const void* residual;
@@ -96,6 +101,14 @@ bool ffn_plan_fusable(Fmt f, int bm, int npairs, int E, int I, bool pays);
 // int32 arrival counters per token that the fused combine needs: one per column
 // tile of the down leg, at most ceil(H / 128)
 inline int combine_counter_stride(int H) { return (H + 127) / 128; }
+// Split tail of the MFMA-bound down leg: at most this many workgroups at once
+// (partial tiles and counters) and pieces per tile.  The buffer holds the
+// kSplitMaxSlots counters (ffn_split_counter_bytes), then the partial tiles;
+// ffn_split_bytes is 0 for formats whose down leg never splits.
+constexpr int kSplitMaxSlots = 256;
+constexpr int kSplitMaxPieces = 8;
+constexpr size_t ffn_split_counter_bytes() { return (size_t)kSplitMaxSlots * 4; }
+size_t ffn_split_bytes(Fmt f);
 size_t ffn_h_bytes(Fmt f, int rows, int I);
 size_t ffn_hsf_bytes(Fmt f, int rows, int I);
 int ffn_max_m_tiles(int npairs, int E, int bm);

@@ -207,6 +207,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(const IdxT* __
   // the fused combine's arrival counters start every call at zero
   if (out.counters != nullptr)
     for (int i = tid; i < out.n_counters; i += kPlanThreads) out.counters[i] = 0;
+  // and so do the down leg's split-tail counters
+  if (out.split_counters != nullptr)
+    for (int i = tid; i < out.n_split; i += kPlanThreads) out.split_counters[i] = 0;
   for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
   for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcnt[i] = 0;
   if (tid == 0) misc[2 * kPlanWaves] = 0;
@@ -261,6 +264,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(int nblocks, in
   int* base = lds + E;      // [E]
   int* misc = lds + 2 * E;  // [2*kPlanWaves + 1]
   const int tid = threadIdx.x;
+  // the down leg's split-tail counters start every call at zero
+  if (out.split_counters != nullptr)
+    for (int i = tid; i < out.n_split; i += kPlanThreads) out.split_counters[i] = 0;
   if (tid < E) {
     int s = 0;
     for (int b = 0; b < nblocks; ++b) s += hist[(size_t)b * E + tid];

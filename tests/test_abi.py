@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 10
+    assert lib.moe_abi_version() == 11
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -290,6 +290,40 @@ def test_plan_in_gate_up_rule(kw, T, fuse_plan, expect):
     assert lib.moe_plan_in_gate_up(h, T) == expect
     lib.moe_destroy(h)
     assert lib.moe_plan_in_gate_up(None, 16) == 0
+
+
+SPLIT_BYTES = 256 * 4 + 256 * 512 * 128 * 4  # counters, then one fp32 partial tile per slot
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, 0),                                                   # decode: weight-bound tiles only
+    ({"max_num_tokens": 8192}, SPLIT_BYTES),                   # FP8 reaching the prefill regime
+    ({"tile_regime": 2}, SPLIT_BYTES),                         # forced prefill tiles
+    ({"tile_regime": 1, "max_num_tokens": 8192}, 0),           # forced decode tiles
+    ({"format": 1, "hidden": 4096, "intermediate_hidden": 14336, "num_experts": 8, "num_topk": 2,
+      "max_num_tokens": 4096}, SPLIT_BYTES),                   # Mixtral BF16
+    ({"format": 2, "hidden": 2880, "intermediate_hidden": 2880, "num_experts": 128, "num_topk": 4,
+      "max_num_tokens": 8192}, 0),                             # W4A8: its down tiles never split
+])
+def test_down_split_size(kw, expect):
+    """Bytes of the down leg's split-tail buffer: kSplitMaxSlots counters and partial
+    tiles where the prefill tile regime can run an FP8 or BF16 down leg, else 0."""
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg(**kw)), ctypes.byref(h)) == 0
+    assert lib.moe_down_split_size(h) == expect
+    lib.moe_destroy(h)
+    assert lib.moe_down_split_size(None) == 0
+
+
+def test_plan_down_split_must_be_aligned():
+    """plan->down_split is optional but 256-byte aligned."""
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_create(ctypes.byref(_cfg()), ctypes.byref(h)) == 0
+    plan = mx._Plan(*([16] * 7), None, 128)
+    assert lib.moe_plan(h, 10, 16, None, None, None, ctypes.byref(plan), None, 0, None) == 1
+    lib.moe_destroy(h)
 
 
 def test_plan_ffn_gate_up_validates_on_host():

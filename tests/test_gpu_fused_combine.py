@@ -23,6 +23,10 @@ CASES = [
     ("mx_logits", dict(T=80, H=576, I=352, E=6, k=3, fmt="w4a8_mx", routing="from_logits"), "decode"),
     ("nvfp4", dict(T=100, H=512, I=320, E=8, k=4, fmt="nvfp4_w4a16"), "decode"),
     ("nvfp4x4", dict(T=100, H=512, I=320, E=8, k=4, fmt="nvfp4"), "prefill"),
+    # down tiles in a partial last round split over K (the split tail): the
+    # completing piece's epilogue runs the fused combine
+    ("fp8_prefill_split", dict(T=256, H=896, I=1152, E=4, k=2, fmt="fp8_block128"), "prefill"),
+    ("bf16_prefill_split", dict(T=200, H=448, I=1088, E=3, k=2, fmt="bf16"), "prefill"),
 ]
 
 

@@ -9,7 +9,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import (check_against_oracle, device_inputs, fwd_kwargs, geometry, make_moe,
+from gpu_util import (check_against_oracle, device_inputs, fwd_kwargs, geometry, make_moe, prepared,
                       prepared_layout_reference, run_ffn_intermediates, run_forward, run_split)
 
 pytestmark = pytest.mark.gpu
@@ -167,6 +167,10 @@ SMALL = [
     ("nvfp4x4_clamp_fires", dict(T=48, H=256, I=128, E=4, k=2, fmt="nvfp4", x_scale=20.0), "auto"),
     ("mx_clamp_fires_prefill", dict(T=160, H=320, I=192, E=3, k=2, fmt="w4a8_mx", routing="from_logits",
                                     x_scale=20.0), "prefill"),
+    # fewer down tiles than the part runs at once: each splits over K into pieces of
+    # whole K-loop trips (17 K-steps: 5 pieces, the last one partly past the end)
+    ("fp8_prefill_split", dict(T=256, H=512, I=2176, E=4, k=2, fmt="fp8_block128"), "prefill"),
+    ("bf16_prefill_split", dict(T=200, H=448, I=1088, E=3, k=2, fmt="bf16"), "prefill"),
 ]
 
 
@@ -212,6 +216,47 @@ def test_split_calls_match_forward_and_are_deterministic():
     check_plan(plan, ref["plan"], sh.tokens, sh.topk)
     res = run_ffn_intermediates(moe, d, sh.tokens)
     check_against_oracle(sh, inp, a, ref, res, inp["topk_idx"], inp["topk_weights"], "split")
+
+
+@pytest.mark.parametrize("fmt,I", [("fp8_block128", 2176), ("bf16", 1088)])
+def test_down_split_tail_repeats_and_matches_unsplit(fmt, I):
+    """The split tail of the down leg (prefill tiles, fewer than the part runs at
+    once, each cut over K): three down calls on one plan -- the arrival counters
+    come back to zero after each -- give the same bits; without the split buffer
+    (no split) the result differs only by the fp32 summation order: one bf16
+    rounding step per element, or the reassociation error of a cancelling sum."""
+    sh = small("split_tail_" + fmt, 5, 256, 512, I, 4, 2, fmt)
+    print(f"[split tail] {fmt} I={I}", flush=True)
+    inp = moe_synth.make_inputs(sh)
+    moe = make_moe(sh, tile_regime="prefill")
+    assert moe.down_split_size() > 0
+    d = device_inputs(inp)
+    pw = prepared(moe, d)
+    T = sh.tokens
+    plan = moe.alloc_plan(T)
+    assert "down_split" in plan
+    ws = moe.alloc_workspace(T)
+    moe.plan(T, plan, topk_idx=d["topk_idx"], ws=ws)
+    h, hsf = moe.alloc_intermediate(T)
+    moe.ffn_gate_up(T, d["x"], d["x_sf"], pw, plan, h, hsf)
+    ys = []
+    for _ in range(3):
+        y = torch.zeros((T * sh.topk, sh.hidden), dtype=torch.bfloat16, device="cuda")
+        moe.ffn_down(T, h, hsf, pw, plan, y)
+        ys.append(y)
+    unsplit = {f: v for f, v in plan.items() if f != "down_split"}
+    y0 = torch.zeros((T * sh.topk, sh.hidden), dtype=torch.bfloat16, device="cuda")
+    moe.ffn_down(T, h, hsf, pw, unsplit, y0)
+    torch.cuda.synchronize()
+    assert not plan["down_split"][:256].any(), "split counters left nonzero"
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    a, b = ys[0].float(), y0.float()
+    assert torch.isfinite(a).all()
+    # one bf16 step (2^-7 of the magnitude), plus the fp32 reassociation error of
+    # sums that nearly cancel, far below a missing or repeated piece (~1/5 of a value)
+    rms = b.pow(2).mean().sqrt()
+    assert bool(((a - b).abs() <= b.abs() * 2.0 ** -7 + 1e-3 * rms).all())
 
 
 @pytest.mark.parametrize("case", ["masked_and_bad", "one_expert", "dup_slots", "single_token", "zero_tokens"])
