@@ -531,6 +531,54 @@ def step_fracs(leg: Leg, ms: float) -> dict:
             "step_mfma_frac": round((gu_flops + dn_flops) / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[leg.sh.fmt], 4)}
 
 
+def dense_reference(workload: str, reps: int) -> int:
+    """Context for the MFMA-bound legs: the vendor library's dense GEMM (hipBLASLt
+    through torch.matmul for bf16, torch._scaled_mm with one scale per tensor for
+    FP8) at each leg's flop count -- M = routed pairs, no gather, no SwiGLU, no
+    block scales -- timed on the GPU.  Prints one JSON line."""
+    import torch
+    import moe_synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    sh = moe_synth.WORKLOADS[workload]
+    if sh.fmt not in ("bf16", "fp8_block128"):
+        print(f"no dense vendor GEMM for {sh.fmt}", file=sys.stderr)
+        return 2
+    M = sh.tokens * sh.topk
+    peak = PEAK_TFLOPS[sh.fmt] * 1e12
+    legs = {"gate_up": (M, 2 * sh.inter, sh.hidden), "down": (M, sh.hidden, sh.inter)}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    for name, (m, n, kk) in legs.items():
+        if sh.fmt == "bf16":
+            a = torch.randn((m, kk), generator=g, device="cuda").to(torch.bfloat16)
+            b = torch.randn((kk, n), generator=g, device="cuda").to(torch.bfloat16)
+            fn, lib = (lambda: torch.matmul(a, b)), "torch.matmul bf16"
+        else:
+            a = (0.5 * torch.randn((m, kk), generator=g, device="cuda")).to(torch.float8_e4m3fn)
+            bt = (0.5 * torch.randn((n, kk), generator=g, device="cuda")).to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda")
+            fn = lambda: torch._scaled_mm(a, bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            lib = "torch._scaled_mm e4m3 per-tensor scales"
+        for _ in range(10):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = 2.0 * m * n * kk
+        res[name] = {"m_n_k": [m, n, kk], "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "frac_of_peak": round(fl / (ms * 1e-3) / peak, 4), "library": lib}
+        del a
+    print(json.dumps({"dense_reference": workload, "legs": res}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -556,7 +604,12 @@ def main() -> int:
                     help="summarise rocprofv3 --pmc folders (one per pass) of --workload into OUT_MD and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration under rocprofv3)")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="time the vendor dense GEMM at each leg's flop count for --workload (bf16, FP8), "
+                         "print one JSON line and exit")
     args = ap.parse_args()
+    if args.dense_reference:
+        return dense_reference(args.workload, args.steps)
     if args.write_counters:
         return write_counters(args.workload, args.write_counters[0], args.write_counters[1], args.counters_command)
     if args.counter_summary:
