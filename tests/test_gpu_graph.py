@@ -12,15 +12,20 @@ from gpu_util import device_inputs, make_moe, prepared
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fmt,routing", [("fp8_block128", "precomputed"), ("w4a8_mx", "from_logits"),
-                                         ("nvfp4_w4a16", "precomputed")])
+@pytest.mark.parametrize("fmt,routing,regime,I", [
+    ("fp8_block128", "precomputed", "auto", 256), ("w4a8_mx", "from_logits", "auto", 256),
+    ("nvfp4_w4a16", "precomputed", "auto", 256),
+    # prefill tiles whose down leg splits over K (8 tiles, 17 K-steps: 5 pieces each):
+    # the arrival counters must come back to zero within every replay
+    ("fp8_block128", "precomputed", "prefill", 2176), ("bf16", "precomputed", "prefill", 1088)])
 @pytest.mark.parametrize("plan_in_launch", [False, True])
-def test_graph_replays_match_eager(fmt, routing, plan_in_launch):
+def test_graph_replays_match_eager(fmt, routing, regime, I, plan_in_launch):
     """plan_in_launch: the step's plan and gate_up leg are moe_plan_ffn_gate_up (the
-    plan built inside the gate_up launch)."""
-    sh = moe_synth.MoEShape("graph_" + fmt, 41, 96, 512, 256, 8, 2, fmt, routing)
+    plan built inside the gate_up launch where the tiles allow it)."""
+    sh = moe_synth.MoEShape("graph_" + fmt, 41, 96, 512, I, 8, 2, fmt, routing)
+    print(f"[graph] {fmt} {regime} I={I} plan_in_launch={plan_in_launch}", flush=True)
     inp = moe_synth.make_inputs(sh)
-    moe = make_moe(sh, fuse_plan=2 if plan_in_launch else 0)
+    moe = make_moe(sh, fuse_plan=2 if plan_in_launch else 0, tile_regime=regime)
     d = device_inputs(inp)
     w = prepared(moe, d)
     T, k = sh.tokens, sh.topk
