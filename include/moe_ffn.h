@@ -274,7 +274,8 @@ moe_status moe_ffn(const moe_handle* h, int32_t num_tokens, const void* x, const
      h_sf            fp32 [T*k, I/128] (FP8), UE8M0 bytes [T*k, I/32] (MX), NULL (BF16)
    moe_ffn_gate_up: gate/up GEMM of every plan row, clamped SwiGLU, requantisation
    ([MegaFFN]: L1 GEMM, clamp_activation, the re-quant ahead of L2).
-   moe_ffn_down: down GEMM of every plan row into y [T,k,H] bf16 at p = src_info[row].
+   moe_ffn_down: down GEMM of every plan row into y [T,k,H] bf16 at p = src_info[row]
+   (with plan->down_split set, the split tail of moe_down_split_size may run).
    w: prepared layout. */
 moe_status moe_ffn_gate_up(const moe_handle* h, int32_t num_tokens, const void* x, const void* x_sf,
                            const moe_weights* w /* host struct */, const moe_plan_buffers* plan /* host struct */,
