@@ -3,8 +3,9 @@ moe_ffn_down_combine): the tile that completes a token's valid slots reduces
 that token's column block, in slot order, so the output must equal the separate
 combine's bit for bit.  Covered: every format and both tile regimes, masked
 slots and tokens without any valid slot, duplicate experts in a token, the
-shared-expert and residual addends, fp32 output, the split entry points, and
-repeated calls on one plan (the plan zeroes the arrival counters each call)."""
+shared-expert and residual addends, fp32 output, the split entry points,
+repeated calls on one plan (the plan zeroes the arrival counters each call), and
+down tiles split over K (the split tail), at small sizes and the full Mixtral shape."""
 import numpy as np
 import pytest
 import torch
@@ -117,3 +118,25 @@ def test_fused_split_entry_points_and_repeated_calls(regime):
             assert torch.equal(va, vb), f"call {call} out_f32={out_f32}"
             assert (a[3] == 0).all()
             assert ev[0].elapsed_time(ev[1]) > 0
+
+
+def test_fused_full_mixtral_split_tail():
+    """The Mixtral-shaped BF16 workload at full size: its down leg leaves 24 tiles
+    for a last round of 256 slots, which split over K; the completing piece's
+    epilogue runs the fused combine.  Fused and separate outputs bit for bit."""
+    sh = moe_synth.WORKLOADS["mixtral_bf16"]
+    print(f"[fused] {sh.name} full size", flush=True)
+    inp = moe_synth.make_inputs(sh)
+    d = device_inputs(inp)
+    m0 = make_moe(sh)
+    m1 = make_moe(sh, fuse_combine=True)
+    w = prepared(m0, d)
+    T, H = sh.tokens, sh.hidden
+    outs = []
+    for m in (m0, m1):
+        out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        m.forward(T, d["x"], d["x_sf"], d["topk_idx"], d["topk_weights"], d["logits"], w, out, m.alloc_workspace(T))
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.isfinite(outs[1].float()).all()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
