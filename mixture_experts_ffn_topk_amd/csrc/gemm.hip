@@ -544,7 +544,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
   uint32_t bsc_dense = kOOB;
   {
     if (F == Fmt::MX || nv4w(F))
-      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);  // (no split)
+      bsc_rs = make_rsrc((const uint8_t*)p.B_sf + (size_t)expert * p.bsc_expert_bytes, p.bsc_expert_bytes);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       int wrow0, col0;  // first weight row and first output column of the 16-row tile
