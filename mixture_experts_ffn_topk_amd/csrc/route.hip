@@ -339,9 +339,15 @@ size_t plan_workspace_bytes(int npairs, int E) {
   return ((size_t)nb * E + nb) * sizeof(int);
 }
 
+int plan_pairs_per_block(int npairs) {
+  const int per = ((npairs + 15) / 16 + 1023) / 1024 * 1024;  // 16 blocks, whole 1024-pair chunks
+  return per < 1024 ? 1024 : per > kPlanMaxPairsPerBlock ? kPlanMaxPairsPerBlock : per;
+}
+
 int plan_num_blocks(int npairs) {
-  if (npairs <= kPlanFusedMaxPairs) return 1;
-  return (npairs + kPlanPairsPerBlock - 1) / kPlanPairsPerBlock;
+  if (npairs <= kPlanSingleBlockMaxPairs) return 1;
+  const int per = plan_pairs_per_block(npairs);
+  return (npairs + per - 1) / per;
 }
 
 static size_t wcnt_bytes(int E) { return (size_t)((kPlanWaves * E + 15) & ~15); }
@@ -356,13 +362,14 @@ static hipError_t launch_plan_t(const IdxT* ids, int npairs, int E, const PlanPt
   }
   int* hist = ws;
   int* bad = ws + (size_t)nb * E;
+  const int per = plan_pairs_per_block(npairs);
   hipLaunchKernelGGL(plan_count_kernel<IdxT>, dim3(nb), dim3(kPlanThreads), (E + 1) * sizeof(int), s, ids, npairs,
-                     E, kPlanPairsPerBlock, hist, bad, out.counters, out.n_counters);
+                     E, per, hist, bad, out.counters, out.n_counters);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), (2 * E + 2 * kPlanWaves + 1) * sizeof(int), s,
                      nb, E, hist, (const int*)bad, out);
   hipLaunchKernelGGL(plan_scatter_kernel<IdxT>, dim3(nb), dim3(kPlanThreads),
-                     E * sizeof(int) + wcnt_bytes(E) + (size_t)kPlanPairsPerBlock * 2, s, ids, npairs, E,
-                     kPlanPairsPerBlock, (const int*)hist, out);
+                     E * sizeof(int) + wcnt_bytes(E) + (size_t)per * 2, s, ids, npairs, E, per,
+                     (const int*)hist, out);
   return hipGetLastError();
 }
 
