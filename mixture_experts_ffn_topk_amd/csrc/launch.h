@@ -29,10 +29,10 @@ struct PlanPtrs {
 // Routing plan built inside the gate_up launch: at most this many pairs.
 constexpr int kPlanFusedMaxPairs = 8192;
 // The plan's own kernels: one block up to kPlanSingleBlockMaxPairs pairs, else
-// count / scan / scatter over blocks of plan_pairs_per_block(npairs) pairs: 1024
+// a count and a scatter launch over blocks of plan_pairs_per_block(npairs) pairs: 1024
 // to 4096 (a multiple of 1024), as few blocks as keep 16 busy (measured: 8192
 // pairs over 8 blocks 7 us faster than in one; 65536 over 16 of 4096 faster than
-// over 64 of 1024, whose scan sums more per-block counts).
+// over 64 of 1024: more blocks, more per-block counts to sum per expert).
 constexpr int kPlanSingleBlockMaxPairs = 2048;
 constexpr int kPlanMaxPairsPerBlock = 4096;
 int plan_pairs_per_block(int npairs);
