@@ -4,39 +4,43 @@
 // when given, + shared[t, :] (a shared expert's output fused into the combine:
 // the fused_shared_expert option of the MAX mega_ffn / EP pages) and
 // + residual[t, :] (a downstream elementwise epilogue: has_epilogue_fusion).
-// HBM-bound gather-reduce: each thread owns 8 consecutive bf16 columns and reads
-// the k slot rows with 16-byte loads; fp32 accumulation; one bf16 rounding at
-// the store, or an fp32 store (the combine dtype is a choice on the EPConfig and
-// DistributedEPCombine pages).
+// HBM-bound gather-reduce: each thread owns 8 consecutive bf16 columns of one
+// token (the threads of the launch cover the [T, H/8] chunks in order, so no
+// lane idles at a row's end) and reads the k slot rows with 16-byte loads, G at
+// a time (G = k rounded up to 2, 4 or 8: Mixtral's k = 2 read 8 rows per group,
+// six of them dummies, when G was always 8); fp32 accumulation; one bf16 rounding
+// at the store, or an fp32 store (the combine dtype is a choice on the EPConfig
+// and DistributedEPCombine pages).
 #include "device.h"
 #include "launch.h"
 
 namespace moe {
 
 constexpr int kCombineThreads = 256;
-constexpr int kCombineCols = kCombineThreads * 8;  // columns per workgroup
 
-template <bool OUT_F32>
+template <bool OUT_F32, int G>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                                   const float* __restrict__ w,
-                                                                  const int* __restrict__ pair_row, int topk, int H,
-                                                                  const uint16_t* __restrict__ shared,
+                                                                  const int* __restrict__ pair_row, int T, int topk,
+                                                                  int H, const uint16_t* __restrict__ shared,
                                                                   const uint16_t* __restrict__ residual,
                                                                   void* __restrict__ out) {
-  const int t = blockIdx.x;
-  const int col = blockIdx.y * kCombineCols + threadIdx.x * 8;
-  if (col >= H) return;
+  const int cpt = H / 8;  // 8-column chunks per token
+  const long long c = (long long)blockIdx.x * kCombineThreads + threadIdx.x;
+  if (c >= (long long)T * cpt) return;
+  const int t = (int)(c / cpt);
+  const int col = (int)(c - (long long)t * cpt) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const long long p0 = (long long)t * topk;
-  // Slots in groups of 8 with every row load issued before the first is used (a
+  // Slots in groups of G with every row load issued before the first is used (a
   // masked slot's row, never written, is read but not added).  The rows are read
   // once: non-temporal loads.
-  for (int j0 = 0; j0 < topk; j0 += 8) {
-    i32x4 v[8];
-    bool ok[8];
-    float wj[8];
+  for (int j0 = 0; j0 < topk; j0 += G) {
+    i32x4 v[G];
+    bool ok[G];
+    float wj[G];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int j = j0 + u;
       ok[u] = j < topk && pair_row[p0 + j] >= 0;
       wj[u] = ok[u] ? w[p0 + j] : 0.f;
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
       v[u] = __builtin_bit_cast(i32x4, __builtin_nontemporal_load((const i32x4*)(y + row * H + col)));
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < G; ++u) {
       if (!ok[u]) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -83,13 +87,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
 hipError_t launch_combine(const void* y, const float* w, const int* pair_row, int T, int topk, int H,
                           const void* shared, const void* residual, void* out, bool out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid(T, (H + kCombineCols - 1) / kCombineCols);
-  if (out_f32)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row, topk,
-                       H, (const uint16_t*)shared, (const uint16_t*)residual, out);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row,
-                       topk, H, (const uint16_t*)shared, (const uint16_t*)residual, out);
+  const long long chunks = (long long)T * (H / 8);
+  const dim3 grid((unsigned)((chunks + kCombineThreads - 1) / kCombineThreads));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kCombineThreads), 0, s, (const uint16_t*)y, w, pair_row, T, topk, H,
+                       (const uint16_t*)shared, (const uint16_t*)residual, out);
+  };
+  if (topk <= 2) out_f32 ? go(combine_kernel<true, 2>) : go(combine_kernel<false, 2>);
+  else if (topk <= 4) out_f32 ? go(combine_kernel<true, 4>) : go(combine_kernel<false, 4>);
+  else out_f32 ? go(combine_kernel<true, 8>) : go(combine_kernel<false, 8>);
   return hipGetLastError();
 }
 
