@@ -21,6 +21,67 @@ constexpr int kPlanThreads = 1024;  // 16 waves; also the largest expert count
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // ------------------------------------------------------------------ top-k
+// Order-preserving map of a float key to 32 bits (larger key, larger value;
+// -0 and +0 equal, as the float comparison has them).
+MOE_DEV uint32_t key_bits(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The wave's largest 64-bit (key, ~index) word, uniform: butterflies inside each
+// row of 16 lanes by DPP (quad swaps, half-row and row mirrors), then the four
+// row results read into scalars.  (Cross-lane shuffles through the LDS crossbar
+// made each of the k selection rounds a chain of 18 round trips.)
+template <int CTRL>
+MOE_DEV uint64_t dpp_max_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t y = ((uint64_t)hi << 32) | lo;
+  return y > x ? y : x;
+}
+MOE_DEV uint64_t wave_max_u64(uint64_t x) {
+  x = dpp_max_u64<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max_u64<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max_u64<0x141>(x);  // row_half_mirror
+  x = dpp_max_u64<0x140>(x);  // row_mirror
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 16 * r);
+    m = v > m ? v : m;
+  }
+  return m;
+}
+
+// The wave's maximum and sum of a float (uniform), by the same DPP butterflies
+// and row read-outs; the sum adds the four row sums in row order.
+template <int CTRL>
+MOE_DEV float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+MOE_DEV float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16 * r)));
+  return m;
+}
+MOE_DEV float wave_sum_f32(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+#pragma unroll
+  for (int r = 1; r < 4; ++r) m += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16 * r));
+  return m;
+}
+
 // One wavefront per token.  Each lane holds logits e = lane + 64*i (i < 8),
 // k rounds of wave-wide argmax with key (logit + bias desc, index asc), then a
 // softmax over the k selected logits.  The optional per-expert bias (the
@@ -60,16 +121,11 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __r
         bi = e;
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      float ok_ = __shfl_xor(bk, m), ov = __shfl_xor(bv, m);
-      int oi = __shfl_xor(bi, m);
-      if (ok_ > bk || (ok_ == bk && oi < bi)) {
-        bk = ok_;
-        bv = ov;
-        bi = oi;
-      }
-    }
+    // the wave's winner: largest key, then smallest index (a lane without a
+    // candidate, ~0x7FFFFFFF, loses to any expert at an equal key)
+    const uint64_t w = wave_max_u64(((uint64_t)key_bits(bk) << 32) | (uint32_t)~bi);
+    bi = (int)~(uint32_t)w;
+    bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), bi & 63));
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == s) {
       my_v = bv;
@@ -77,14 +133,10 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(const float* __r
     }
   }
   // the largest selected logit (the first one when there is no bias)
-  float vmax = lane < k ? my_v : -INFINITY;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, m));
+  const float vmax = wave_max_f32(lane < k ? my_v : -INFINITY);
   float ex = 0.0f;
   if (lane < k) ex = FAST ? __builtin_amdgcn_exp2f((my_v - vmax) * 1.4426950408889634f) : expf(my_v - vmax);
-  float sum = ex;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  const float sum = wave_sum_f32(ex);
   if (lane < k) {
     idx_out[(size_t)t * k + lane] = (IdxT)my_i;
     w_out[(size_t)t * k + lane] = FAST ? ex * __builtin_amdgcn_rcpf(sum) : ex / sum;
