@@ -1036,10 +1036,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
         // that path (bit-identical; prefill gate_up -2.1 %, down -1.5 %; after MFMA
         // 1: -1.4 %; after 11 or 19: no gain).
         constexpr int kIssueAfter = MT * NT > 5 ? 5 : 0;
-        if (i == kIssueAfter) {
-          issue();
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        if (i == kIssueAfter) issue();
       }
       if (MT * NT > 1) acc[(MT * NT - 2) / NT][(MT * NT - 2) % NT] += prev2 * s_prev2;
       acc[MT - 1][NT - 1] += prev * s_prev;
@@ -1202,7 +1199,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES * WGS + 3) / 4) void ffn_gemm_ke
     __builtin_amdgcn_sched_barrier(0);
     // A(st + 2), issued inside the first K-step: the same VMEM order (the A loads,
     // then the ring refills), so the wait count above still holds
-    auto issue_a = [&] { dma_a(st + 2, (su + 2) % TL::kABufs); };
+    auto issue_a = [&] {
+      dma_a(st + 2, (su + 2) % TL::kABufs);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < KSG; ++u) {
